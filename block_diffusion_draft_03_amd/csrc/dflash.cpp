@@ -1,0 +1,665 @@
+// dflash.cpp - the C ABI of include/dflash.h: argument validation, the head's
+// device memory (repacked weights, paged KV pool, scratch), per-sequence
+// state, and the ordered launches of the propose and precompute passes.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <climits>
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/dflash.h"
+#include "host_core.hpp"
+#include "kernels.hpp"
+
+using namespace dflash;
+
+namespace {
+
+thread_local std::string g_err;
+
+int set_err(int code, const std::string &m) {
+  g_err = m;
+  return code;
+}
+
+constexpr uint64_t HEAD_MAGIC = 0x44464c4153484844ull;   // "DFLASHHD"
+constexpr uint64_t STATE_MAGIC = 0x44464c4153485354ull;  // "DFLASHST"
+constexpr uint64_t DEAD_MAGIC = 0xdeadull;
+constexpr int ATTN_SLOTS = 1024;   // (sequence, kv head, key chunk) partials per layer, at least
+constexpr int ATTN_MIN_CHUNK = 64;
+
+#define HIP_TRY(expr)                                                                          \
+  do {                                                                                         \
+    hipError_t e_ = (expr);                                                                    \
+    if (e_ != hipSuccess) return set_err(DFLASH_E_HIP, std::string(#expr) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+hipStream_t to_stream(uint64_t s) { return (hipStream_t)(uintptr_t)s; }
+
+}  // namespace
+
+struct dflash_state {
+  uint64_t magic = STATE_MAGIC;
+  dflash_head *owner = nullptr;
+  SeqRows rows;
+  int32_t *d_bt = nullptr;   // device block table
+  int32_t *h_bt = nullptr;   // pinned host copy (entries written once, then uploaded)
+  int32_t cap_blocks = 0;
+  int32_t uploaded = 0;      // leading entries of d_bt already uploaded
+};
+
+struct dflash_head {
+  uint64_t magic = HEAD_MAGIC;
+  dflash_config cfg{};
+  Geo g{};
+  std::mutex mu;
+  BlockPool pool;
+  std::vector<dflash_state *> states;
+  std::vector<void *> dev_allocs;
+
+  // repacked drafter weights (bf16 unless noted), layer-major
+  uint16_t *w_qkv = nullptr, *w_o = nullptr, *w_gu = nullptr, *w_down = nullptr, *w_fc = nullptr, *w_fkv = nullptr;
+  float *g_in = nullptr, *g_post = nullptr, *g_hidden = nullptr, *g_final = nullptr;
+  const uint16_t *embed = nullptr, *lm = nullptr;
+  const uint8_t *lm8 = nullptr;
+  const float *lm8_scale = nullptr;
+  double *inv_freq = nullptr;
+  float *kv_scale = nullptr;
+  void *kv_pool = nullptr;
+  size_t kv_elem = 2;
+
+  // scratch
+  float *hid = nullptr;
+  uint16_t *act = nullptr, *qkv = nullptr, *attn = nullptr, *mlp = nullptr;
+  float2 *cs = nullptr;
+  float *ws = nullptr;
+  int *counters = nullptr;
+  float *o_part = nullptr, *ml_part = nullptr;
+  float *lm_mx = nullptr, *lm_se = nullptr;
+  uint32_t *lm_idx = nullptr;
+  int lm_P = 0;
+  int attn_slots = 0;
+  float *pre_u = nullptr;
+  uint16_t *pre_c = nullptr;
+
+  template <class T>
+  int alloc(T **p, size_t count) {
+    void *q = nullptr;
+    const size_t bytes = std::max<size_t>(count * sizeof(T), 256);
+    hipError_t e = hipMalloc(&q, bytes);
+    if (e != hipSuccess) return set_err(DFLASH_E_NOMEM, std::string("hipMalloc of ") + std::to_string(bytes) + " bytes: " + hipGetErrorString(e));
+    dev_allocs.push_back(q);
+    *p = (T *)q;
+    return DFLASH_OK;
+  }
+};
+
+namespace {
+
+bool head_ok(const dflash_head *h) { return h && h->magic == HEAD_MAGIC; }
+bool state_ok(const dflash_head *h, const dflash_state *s) { return s && s->magic == STATE_MAGIC && s->owner == h; }
+
+void free_head_memory(dflash_head *h) {
+  for (void *p : h->dev_allocs) (void)hipFree(p);
+  h->dev_allocs.clear();
+}
+
+void free_state_memory(dflash_state *s) {
+  if (s->d_bt) (void)hipFree(s->d_bt);
+  if (s->h_bt) (void)hipHostFree(s->h_bt);
+  s->d_bt = nullptr;
+  s->h_bt = nullptr;
+}
+
+#define TRY(expr)                  \
+  do {                             \
+    int r_ = (expr);               \
+    if (r_ != DFLASH_OK) return r_; \
+  } while (0)
+
+// Repack the drafter tensors and allocate everything; called under no lock
+// on a fresh head.
+int build_impl(dflash_head *H, const dflash_weights *w, hipStream_t st) {
+  const Geo &g = H->g;
+  const bool f32 = g.w_f32;
+  const size_t h = g.h;
+  if (!w->fc || !w->hidden_norm || !w->norm || !w->embed_tokens || !w->layers)
+    return set_err(DFLASH_E_INVALID, "weights: fc, hidden_norm, norm, embed_tokens and layers are required");
+  if (!w->lm_head && !(g.head_fp8 && w->lm_head_fp8))
+    return set_err(DFLASH_E_INVALID, "weights: lm_head is required (or lm_head_fp8 for an FP8 head)");
+  if (w->lm_head_fp8 && (!g.head_fp8 || !w->lm_head_scale))
+    return set_err(DFLASH_E_INVALID, "weights: lm_head_fp8 needs lm_head_dtype FP8_E4M3 and lm_head_scale");
+  if (g.kv_fp8 && !w->kv_scale) return set_err(DFLASH_E_INVALID, "weights: kv_scale is required for an FP8 KV cache");
+  for (int l = 0; l < g.L; ++l) {
+    const dflash_layer_weights &lw = w->layers[l];
+    if (!lw.in_norm || !lw.q || !lw.k || !lw.v || !lw.o || !lw.post_norm || !lw.gate || !lw.up || !lw.down)
+      return set_err(DFLASH_E_INVALID, "weights: layer " + std::to_string(l) + " has a NULL tensor");
+  }
+  if (g.kv_fp8) {
+    for (int i = 0; i < g.L * 2 * g.n_kv; ++i)
+      if (!(w->kv_scale[i] > 0.0f) || !std::isfinite(w->kv_scale[i]))
+        return set_err(DFLASH_E_INVALID, "weights: kv_scale entries must be finite and > 0");
+  }
+
+  // drafter tensors -> bf16, repacked
+  TRY(H->alloc(&H->w_qkv, (size_t)g.L * g.qkv_dim * h));
+  TRY(H->alloc(&H->w_o, (size_t)g.L * h * g.q_dim));
+  TRY(H->alloc(&H->w_gu, (size_t)g.L * 2 * g.I * h));
+  TRY(H->alloc(&H->w_down, (size_t)g.L * h * g.I));
+  TRY(H->alloc(&H->w_fc, h * g.fc_in));
+  TRY(H->alloc(&H->w_fkv, (size_t)g.fkv_dim * h));
+  TRY(H->alloc(&H->g_in, (size_t)g.L * h));
+  TRY(H->alloc(&H->g_post, (size_t)g.L * h));
+  TRY(H->alloc(&H->g_hidden, h));
+  TRY(H->alloc(&H->g_final, h));
+  for (int l = 0; l < g.L; ++l) {
+    const dflash_layer_weights &lw = w->layers[l];
+    uint16_t *qkv = H->w_qkv + (size_t)l * g.qkv_dim * h;
+    HIP_TRY(launch_convert_rows(qkv, lw.q, nullptr, g.q_dim, g.h, f32, false, st));
+    HIP_TRY(launch_convert_rows(qkv + (size_t)g.q_dim * h, lw.k, nullptr, g.kv_dim, g.h, f32, false, st));
+    HIP_TRY(launch_convert_rows(qkv + (size_t)(g.q_dim + g.kv_dim) * h, lw.v, nullptr, g.kv_dim, g.h, f32, false, st));
+    HIP_TRY(launch_convert_rows(H->w_o + (size_t)l * h * g.q_dim, lw.o, nullptr, g.h, g.q_dim, f32, false, st));
+    HIP_TRY(launch_convert_rows(H->w_gu + (size_t)l * 2 * g.I * h, lw.gate, lw.up, 2 * g.I, g.h, f32, true, st));
+    HIP_TRY(launch_convert_rows(H->w_down + (size_t)l * h * g.I, lw.down, nullptr, g.h, g.I, f32, false, st));
+    // fused ctx K/V weight: rows [K0; V0; K1; V1; ...]
+    uint16_t *fk = H->w_fkv + (size_t)(2 * l) * g.kv_dim * h;
+    HIP_TRY(launch_convert_rows(fk, lw.k, nullptr, g.kv_dim, g.h, f32, false, st));
+    HIP_TRY(launch_convert_rows(fk + (size_t)g.kv_dim * h, lw.v, nullptr, g.kv_dim, g.h, f32, false, st));
+    HIP_TRY(launch_to_f32(H->g_in + (size_t)l * h, lw.in_norm, g.h, f32, st));
+    HIP_TRY(launch_to_f32(H->g_post + (size_t)l * h, lw.post_norm, g.h, f32, st));
+  }
+  HIP_TRY(launch_convert_rows(H->w_fc, w->fc, nullptr, g.h, g.fc_in, f32, false, st));
+  HIP_TRY(launch_to_f32(H->g_hidden, w->hidden_norm, g.h, f32, st));
+  HIP_TRY(launch_to_f32(H->g_final, w->norm, g.h, f32, st));
+
+  // target's shared tensors: borrowed when bf16
+  if (f32) {
+    uint16_t *e = nullptr;
+    TRY(H->alloc(&e, (size_t)g.V * h));
+    HIP_TRY(launch_convert_rows(e, w->embed_tokens, nullptr, g.V, g.h, true, false, st));
+    H->embed = e;
+    if (w->lm_head) {
+      uint16_t *m = nullptr;
+      TRY(H->alloc(&m, (size_t)g.V * h));
+      HIP_TRY(launch_convert_rows(m, w->lm_head, nullptr, g.V, g.h, true, false, st));
+      H->lm = m;
+    }
+  } else {
+    H->embed = (const uint16_t *)w->embed_tokens;
+    H->lm = (const uint16_t *)w->lm_head;
+  }
+  if (g.head_fp8) {
+    if (w->lm_head_fp8) {
+      H->lm8 = (const uint8_t *)w->lm_head_fp8;
+      H->lm8_scale = w->lm_head_scale;
+    } else {
+      uint8_t *c = nullptr;
+      float *s = nullptr;
+      TRY(H->alloc(&c, (size_t)g.V * h));
+      TRY(H->alloc(&s, (size_t)g.V));
+      HIP_TRY(launch_fp8_mirror(H->lm, g.V, g.h, c, s, st));
+      H->lm8 = c;
+      H->lm8_scale = s;
+    }
+  }
+
+  // RoPE inverse frequencies in double
+  std::vector<double> inv(g.d / 2);
+  for (int i = 0; i < g.d / 2; ++i)
+    inv[i] = w->inv_freq ? (double)w->inv_freq[i] : std::pow((double)H->cfg.rope_theta, -2.0 * i / g.d);
+  TRY(H->alloc(&H->inv_freq, inv.size()));
+  HIP_TRY(hipMemcpyAsync(H->inv_freq, inv.data(), inv.size() * sizeof(double), hipMemcpyHostToDevice, st));
+  TRY(H->alloc(&H->kv_scale, (size_t)g.L * 2 * g.n_kv));
+  if (g.kv_fp8)
+    HIP_TRY(hipMemcpyAsync(H->kv_scale, w->kv_scale, (size_t)g.L * 2 * g.n_kv * sizeof(float), hipMemcpyHostToDevice, st));
+
+  // paged KV pool [block][L][K|V][n_kv][16][d]
+  H->kv_elem = g.kv_fp8 ? 1 : 2;
+  const size_t pool_bytes = (size_t)H->cfg.kv_pool_blocks * g.L * 2 * g.n_kv * DFLASH_KV_BLOCK * g.d * H->kv_elem;
+  {
+    uint8_t *p = nullptr;
+    TRY(H->alloc(&p, pool_bytes));
+    HIP_TRY(hipMemsetAsync(p, 0, pool_bytes, st));
+    H->kv_pool = p;
+  }
+  H->pool = BlockPool(H->cfg.kv_pool_blocks);
+
+  // scratch sized for max_batch * gamma rows
+  const size_t M = g.m_max;
+  TRY(H->alloc(&H->hid, M * h));
+  TRY(H->alloc(&H->act, M * h));
+  TRY(H->alloc(&H->qkv, M * g.qkv_dim));
+  TRY(H->alloc(&H->attn, M * g.q_dim));
+  TRY(H->alloc(&H->mlp, M * g.I));
+  TRY(H->alloc(&H->cs, M * (g.d / 2)));
+  const int shapes[6][2] = {{g.qkv_dim, g.h}, {g.h, g.q_dim}, {2 * g.I, g.h}, {g.h, g.I}, {g.h, g.fc_in}, {g.fkv_dim, g.h}};
+  size_t ws = 0;
+  int groups = 0;
+  for (auto &sh : shapes) {
+    ws = std::max(ws, gemm_ws_floats(sh[0], sh[1]));
+    groups = std::max(groups, gemm_groups(sh[0]));
+  }
+  TRY(H->alloc(&H->ws, ws));
+  TRY(H->alloc(&H->counters, (size_t)groups));
+  HIP_TRY(hipMemsetAsync(H->counters, 0, (size_t)groups * sizeof(int), st));
+  const size_t R = (size_t)g.rep * g.gamma;
+  H->attn_slots = std::max(ATTN_SLOTS, g.max_batch * g.n_kv);
+  TRY(H->alloc(&H->o_part, (size_t)H->attn_slots * R * g.d));
+  TRY(H->alloc(&H->ml_part, (size_t)H->attn_slots * R * 2));
+  H->lm_P = lm_parts(g.V);
+  TRY(H->alloc(&H->lm_mx, (size_t)H->lm_P * M));
+  TRY(H->alloc(&H->lm_se, (size_t)H->lm_P * M));
+  TRY(H->alloc(&H->lm_idx, (size_t)H->lm_P * M));
+  TRY(H->alloc(&H->pre_u, (size_t)GEMM_MAX_ROWS * h));
+  TRY(H->alloc(&H->pre_c, (size_t)GEMM_MAX_ROWS * h));
+  HIP_TRY(hipStreamSynchronize(st));
+  return DFLASH_OK;
+}
+
+// One GEMM over M rows in chunks of GEMM_MAX_ROWS. The epilogue output
+// pointers and the RoPE table are advanced with the rows.
+int gemm_rows(dflash_head *H, int epi, const uint16_t *A, int lda, int M, const uint16_t *W, int N, int K,
+              EpiArgs e, hipStream_t st) {
+  GemmArgs ga{};
+  ga.lda = lda;
+  ga.W = W;
+  ga.N = N;
+  ga.K = K;
+  gemm_plan(N, K, &ga.kslice, &ga.splits);
+  ga.ws = H->ws;
+  ga.counters = H->counters;
+  const int half = H->g.d / 2;
+  for (int r0 = 0; r0 < M; r0 += GEMM_MAX_ROWS) {
+    ga.A = A + (size_t)r0 * lda;
+    ga.M = std::min(GEMM_MAX_ROWS, M - r0);
+    EpiArgs ec = e;
+    if (e.out_f32) ec.out_f32 = e.out_f32 + (size_t)r0 * e.ldo;
+    if (e.out_bf16) ec.out_bf16 = e.out_bf16 + (size_t)r0 * e.ldo;
+    if (e.cs) ec.cs = e.cs + (size_t)r0 * half;
+    HIP_TRY(launch_gemm(epi, false, ga, ec, st));
+  }
+  return DFLASH_OK;
+}
+
+int propose_impl(dflash_head *H, dflash_state *const *states, int n, const uint32_t *tokens, const int64_t *positions,
+                 int num_drafts, const int32_t *bitmasks, uint32_t *ids, float *conf, float *row_prob, float *logits,
+                 hipStream_t st) {
+  const Geo &g = H->g;
+  if (n < 1 || n > g.max_batch)
+    return set_err(DFLASH_E_DECLINED, "batch of " + std::to_string(n) + " outside [1, " + std::to_string(g.max_batch) + "]");
+  if (!states || !tokens || !positions) return set_err(DFLASH_E_INVALID, "states, last_tokens and positions are required");
+  if (num_drafts < 1 || num_drafts > g.gamma - 1)
+    return set_err(DFLASH_E_INVALID, "num_drafts must be in [1, gamma - 1]");
+  if (!ids || !conf) return set_err(DFLASH_E_INVALID, "ids and conf outputs are required");
+  for (int i = 0; i < n; ++i) {
+    if (!state_ok(H, states[i])) return set_err(DFLASH_E_INVALID, "state " + std::to_string(i) + " is not a live state of this head");
+    if (tokens[i] >= (uint32_t)g.V) return set_err(DFLASH_E_INVALID, "last_token " + std::to_string(tokens[i]) + " >= vocab");
+    if (positions[i] < 0 || positions[i] > (int64_t)INT_MAX - g.gamma)
+      return set_err(DFLASH_E_INVALID, "position out of range");
+  }
+  const int M = n * g.gamma;
+  const int h = g.h;
+
+  SetupArgs sa{};
+  sa.embed = H->embed;
+  sa.gain = H->g_in;
+  sa.eps = H->cfg.rms_eps;
+  sa.h = h;
+  sa.gamma = g.gamma;
+  sa.half_dim = g.d / 2;
+  sa.mask_id = g.mask_id;
+  sa.inv_freq = H->inv_freq;
+  sa.hid = H->hid;
+  sa.a = H->act;
+  sa.cs = H->cs;
+  for (int i = 0; i < n; ++i) {
+    sa.token[i] = tokens[i];
+    sa.position[i] = (int32_t)positions[i];
+  }
+  HIP_TRY(launch_setup(sa, M, st));
+
+  AttnArgs aa{};
+  aa.qkv = H->qkv;
+  aa.ld = g.qkv_dim;
+  aa.gamma = g.gamma;
+  aa.rep = g.rep;
+  aa.n_kv = g.n_kv;
+  aa.head_dim = g.d;
+  aa.k_off = g.q_dim;
+  aa.v_off = g.q_dim + g.kv_dim;
+  aa.pool = H->kv_pool;
+  aa.L = g.L;
+  aa.kv_fp8 = g.kv_fp8;
+  aa.kv_scale = H->kv_scale;
+  aa.o_part = H->o_part;
+  aa.ml_part = H->ml_part;
+  aa.out = H->attn;
+  aa.out_ld = g.q_dim;
+  int max_S = 0;
+  for (int i = 0; i < n; ++i) {
+    const int c = states[i]->rows.ctx_len;
+    const int lo = g.W > 0 ? std::max(0, c - g.W) : c;
+    aa.seq[i].ctx_len = c;
+    aa.seq[i].win_start = lo;
+    aa.seq[i].bt = states[i]->d_bt;
+    max_S = std::max(max_S, c - lo + g.gamma);
+  }
+  {
+    int splits = std::max(1, std::min((max_S + ATTN_MIN_CHUNK - 1) / ATTN_MIN_CHUNK, H->attn_slots / (n * g.n_kv)));
+    int chunk = (max_S + splits - 1) / splits;
+    chunk = (chunk + 31) / 32 * 32;
+    aa.chunk = chunk;
+    aa.max_splits = (max_S + chunk - 1) / chunk;
+  }
+
+  EpiArgs e{};
+  for (int l = 0; l < g.L; ++l) {
+    if (l > 0) HIP_TRY(launch_rmsnorm(H->hid, h, H->g_in + (size_t)l * h, H->cfg.rms_eps, h, H->act, h, M, st));
+    e = EpiArgs{};
+    e.out_bf16 = H->qkv;
+    e.ldo = g.qkv_dim;
+    e.cs = H->cs;
+    e.head_dim = g.d;
+    e.q_dim = g.q_dim;
+    e.kv_dim = g.kv_dim;
+    TRY(gemm_rows(H, EPI_QKV_ROPE, H->act, h, M, H->w_qkv + (size_t)l * g.qkv_dim * h, g.qkv_dim, h, e, st));
+    aa.layer = l;
+    HIP_TRY(launch_attention(aa, n, st));
+    e = EpiArgs{};
+    e.out_f32 = H->hid;
+    e.ldo = h;
+    TRY(gemm_rows(H, EPI_RESID, H->attn, g.q_dim, M, H->w_o + (size_t)l * h * g.q_dim, h, g.q_dim, e, st));
+    HIP_TRY(launch_rmsnorm(H->hid, h, H->g_post + (size_t)l * h, H->cfg.rms_eps, h, H->act, h, M, st));
+    e = EpiArgs{};
+    e.out_bf16 = H->mlp;
+    e.ldo = g.I;
+    TRY(gemm_rows(H, EPI_SWIGLU, H->act, h, M, H->w_gu + (size_t)l * 2 * g.I * h, 2 * g.I, h, e, st));
+    e = EpiArgs{};
+    e.out_f32 = H->hid;
+    e.ldo = h;
+    TRY(gemm_rows(H, EPI_RESID, H->mlp, g.I, M, H->w_down + (size_t)l * h * g.I, h, g.I, e, st));
+  }
+  HIP_TRY(launch_rmsnorm(H->hid, h, H->g_final, H->cfg.rms_eps, h, H->act, h, M, st));
+
+  LmArgs la{};
+  la.K = h;
+  la.W = g.head_fp8 ? (const void *)H->lm8 : (const void *)H->lm;
+  la.scale = H->lm8_scale;
+  la.V = g.V;
+  la.bitmask = bitmasks;
+  la.words = g.words;
+  la.gamma = g.gamma;
+  la.ld_part = M;
+  la.part_mx = H->lm_mx;
+  la.part_se = H->lm_se;
+  la.part_idx = H->lm_idx;
+  for (int r0 = 0; r0 < M; r0 += GEMM_MAX_ROWS) {
+    la.z = H->act + (size_t)r0 * h;
+    la.M = std::min(GEMM_MAX_ROWS, M - r0);
+    la.row0 = r0;
+    la.logits = logits ? logits + (size_t)r0 * g.V : nullptr;
+    HIP_TRY(launch_lm_head(g.head_fp8, la, st));
+  }
+  LmFinishArgs fa{};
+  fa.part_mx = H->lm_mx;
+  fa.part_se = H->lm_se;
+  fa.part_idx = H->lm_idx;
+  fa.P = H->lm_P;
+  fa.M = M;
+  fa.gamma = g.gamma;
+  fa.num_drafts = num_drafts;
+  fa.ids = ids;
+  fa.conf = conf;
+  fa.row_prob = row_prob;
+  HIP_TRY(launch_lm_finish(fa, n, st));
+  return DFLASH_OK;
+}
+
+// Upload block-table entries that are not yet on the device.
+int sync_block_table(dflash_state *s, hipStream_t st) {
+  const int32_t nb = (int32_t)s->rows.blocks.size();
+  if (nb <= s->uploaded) return DFLASH_OK;
+  if (nb > s->cap_blocks) return set_err(DFLASH_E_NO_BLOCKS, "block table capacity exceeded");
+  for (int32_t i = s->uploaded; i < nb; ++i) s->h_bt[i] = s->rows.blocks[i];
+  HIP_TRY(hipMemcpyAsync(s->d_bt + s->uploaded, s->h_bt + s->uploaded, (size_t)(nb - s->uploaded) * sizeof(int32_t),
+                         hipMemcpyHostToDevice, st));
+  s->uploaded = nb;
+  return DFLASH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *dflash_last_error(void) { return g_err.c_str(); }
+
+int dflash_build(const dflash_config *cfg, const dflash_weights *w, uint64_t stream, dflash_head **out) {
+  if (!cfg || !w || !out) return set_err(DFLASH_E_INVALID, "cfg, weights and out are required");
+  *out = nullptr;
+  Geo g;
+  std::string err;
+  int rc = validate_config(*cfg, &g, &err);
+  if (rc != DFLASH_OK) return set_err(rc, err);
+  int dev_count = 0;
+  if (hipGetDeviceCount(&dev_count) != hipSuccess || dev_count < 1) return set_err(DFLASH_E_HIP, "no HIP device");
+  dflash_head *H = new dflash_head();
+  H->cfg = *cfg;
+  H->g = g;
+  rc = build_impl(H, w, to_stream(stream));
+  if (rc != DFLASH_OK) {
+    (void)hipStreamSynchronize(to_stream(stream));
+    free_head_memory(H);
+    H->magic = DEAD_MAGIC;
+    delete H;
+    return rc;
+  }
+  *out = H;
+  g_err.clear();
+  return DFLASH_OK;
+}
+
+void dflash_destroy(dflash_head *head) {
+  if (!head_ok(head)) return;
+  (void)hipDeviceSynchronize();
+  for (dflash_state *s : head->states) {
+    free_state_memory(s);
+    s->magic = DEAD_MAGIC;
+    delete s;
+  }
+  head->states.clear();
+  free_head_memory(head);
+  head->magic = DEAD_MAGIC;
+  delete head;
+}
+
+int dflash_block_gamma(const dflash_head *head) {
+  if (!head_ok(head)) return set_err(DFLASH_E_INVALID, "invalid head");
+  return head->g.gamma;
+}
+
+int dflash_propose_batch_max(const dflash_head *head) {
+  if (!head_ok(head)) return set_err(DFLASH_E_INVALID, "invalid head");
+  return head->g.max_batch;
+}
+
+int dflash_state_create(dflash_head *head, int64_t budget_tokens, const int32_t *block_ids, int32_t n_ids,
+                        dflash_state **out) {
+  if (!head_ok(head) || !out) return set_err(DFLASH_E_INVALID, "invalid head or out");
+  *out = nullptr;
+  std::lock_guard<std::mutex> lk(head->mu);
+  dflash_state *s = new dflash_state();
+  s->owner = head;
+  std::string err;
+  int rc = seq_init(&s->rows, &head->pool, budget_tokens, block_ids, n_ids, head->cfg.max_seq_len, &err);
+  if (rc != DFLASH_OK) {
+    delete s;
+    return set_err(rc, err);
+  }
+  s->cap_blocks = (int32_t)((s->rows.cap_rows + DFLASH_KV_BLOCK - 1) / DFLASH_KV_BLOCK);
+  s->cap_blocks = std::max<int32_t>(s->cap_blocks, (int32_t)s->rows.blocks.size());
+  s->cap_blocks = std::max<int32_t>(s->cap_blocks, 1);
+  hipError_t e = hipMalloc(&s->d_bt, (size_t)s->cap_blocks * sizeof(int32_t));
+  if (e == hipSuccess) e = hipHostMalloc(&s->h_bt, (size_t)s->cap_blocks * sizeof(int32_t), hipHostMallocDefault);
+  if (e == hipSuccess) e = hipMemset(s->d_bt, 0, (size_t)s->cap_blocks * sizeof(int32_t));
+  if (e == hipSuccess && !s->rows.blocks.empty()) {
+    for (size_t i = 0; i < s->rows.blocks.size(); ++i) s->h_bt[i] = s->rows.blocks[i];
+    e = hipMemcpy(s->d_bt, s->h_bt, s->rows.blocks.size() * sizeof(int32_t), hipMemcpyHostToDevice);
+    s->uploaded = (int32_t)s->rows.blocks.size();
+  }
+  if (e != hipSuccess) {
+    seq_release(&s->rows, &head->pool);
+    free_state_memory(s);
+    delete s;
+    return set_err(DFLASH_E_NOMEM, std::string("state allocation: ") + hipGetErrorString(e));
+  }
+  head->states.push_back(s);
+  *out = s;
+  return DFLASH_OK;
+}
+
+int dflash_state_free(dflash_head *head, dflash_state *st) {
+  if (!head_ok(head)) return set_err(DFLASH_E_INVALID, "invalid head");
+  std::lock_guard<std::mutex> lk(head->mu);
+  if (!state_ok(head, st)) return set_err(DFLASH_E_INVALID, "not a live state of this head");
+  HIP_TRY(hipDeviceSynchronize());
+  seq_release(&st->rows, &head->pool);
+  free_state_memory(st);
+  head->states.erase(std::remove(head->states.begin(), head->states.end(), st), head->states.end());
+  st->magic = DEAD_MAGIC;
+  delete st;
+  return DFLASH_OK;
+}
+
+int dflash_state_ctx_len(const dflash_state *st) {
+  if (!st || st->magic != STATE_MAGIC) return set_err(DFLASH_E_INVALID, "invalid state");
+  return st->rows.ctx_len;
+}
+
+int dflash_precompute_ctx_kv(dflash_head *head, dflash_state *const *states, int32_t n, const int32_t *n_new,
+                             const void *stack, uint64_t stream) {
+  if (!head_ok(head)) return set_err(DFLASH_E_INVALID, "invalid head");
+  std::lock_guard<std::mutex> lk(head->mu);
+  dflash_head *H = head;
+  const Geo &g = H->g;
+  if (n < 1 || !states || !n_new) return set_err(DFLASH_E_INVALID, "n >= 1, states and n_new are required");
+  int64_t total = 0;
+  for (int i = 0; i < n; ++i) {
+    if (!state_ok(H, states[i])) return set_err(DFLASH_E_INVALID, "state " + std::to_string(i) + " is not a live state of this head");
+    if (n_new[i] < 0) return set_err(DFLASH_E_INVALID, "n_new must be >= 0");
+    for (int j = 0; j < i; ++j)
+      if (states[j] == states[i] && n_new[i] > 0 && n_new[j] > 0)
+        return set_err(DFLASH_E_INVALID, "a state appears twice with rows to append");
+    total += n_new[i];
+  }
+  if (total > INT_MAX / 2) return set_err(DFLASH_E_INVALID, "too many rows");
+  if (total > 0 && !stack) return set_err(DFLASH_E_INVALID, "stack is required when rows are appended");
+  // reserve blocks for every state first (no device work yet)
+  for (int i = 0; i < n; ++i) {
+    std::string err;
+    int32_t first = 0;
+    int rc = seq_reserve(&states[i]->rows, &H->pool, n_new[i], &first, &err);
+    if (rc != DFLASH_OK) return set_err(rc, "state " + std::to_string(i) + ": " + err);
+    if ((int32_t)states[i]->rows.blocks.size() > states[i]->cap_blocks)
+      return set_err(DFLASH_E_NO_BLOCKS, "block table capacity exceeded");
+  }
+  hipStream_t st = to_stream(stream);
+  for (int i = 0; i < n; ++i) TRY(sync_block_table(states[i], st));
+  if (total == 0) return DFLASH_OK;
+
+  // row -> (position, block table)
+  std::vector<int> pos;
+  std::vector<const int32_t *> bts;
+  pos.reserve(total);
+  bts.reserve(total);
+  for (int i = 0; i < n; ++i)
+    for (int k = 0; k < n_new[i]; ++k) {
+      pos.push_back(states[i]->rows.ctx_len + k);
+      bts.push_back(states[i]->d_bt);
+    }
+  const int h = g.h;
+  for (int r0 = 0; r0 < (int)total; r0 += GEMM_MAX_ROWS) {
+    const int m = std::min<int>(GEMM_MAX_ROWS, (int)total - r0);
+    EpiArgs e{};
+    e.out_f32 = H->pre_u;
+    e.ldo = h;
+    TRY(gemm_rows(H, EPI_F32, (const uint16_t *)stack + (size_t)r0 * g.fc_in, g.fc_in, m, H->w_fc, h, g.fc_in, e, st));
+    HIP_TRY(launch_rmsnorm(H->pre_u, h, H->g_hidden, H->cfg.rms_eps, h, H->pre_c, h, m, st));
+    e = EpiArgs{};
+    e.head_dim = g.d;
+    e.pool = H->kv_pool;
+    e.L = g.L;
+    e.n_kv = g.n_kv;
+    e.kv_fp8 = g.kv_fp8;
+    e.kv_scale = H->kv_scale;
+    e.inv_freq = H->inv_freq;
+    for (int r = 0; r < m; ++r) {
+      e.row_pos[r] = pos[r0 + r];
+      e.row_bt[r] = bts[r0 + r];
+    }
+    TRY(gemm_rows(H, EPI_KV_SCATTER, H->pre_c, h, m, H->w_fkv, g.fkv_dim, h, e, st));
+  }
+  for (int i = 0; i < n; ++i) states[i]->rows.ctx_len += n_new[i];
+  return DFLASH_OK;
+}
+
+int dflash_propose(dflash_head *head, dflash_state *st, uint32_t last_token, int64_t position, int32_t num_drafts,
+                   const int32_t *bitmask, uint32_t *ids, float *conf, float *row_prob, float *logits,
+                   uint64_t stream) {
+  if (!head_ok(head)) return set_err(DFLASH_E_INVALID, "invalid head");
+  std::lock_guard<std::mutex> lk(head->mu);
+  dflash_state *states[1] = {st};
+  int rc = propose_impl(head, states, 1, &last_token, &position, num_drafts, bitmask, ids, conf, row_prob, logits,
+                        to_stream(stream));
+  if (rc == DFLASH_E_DECLINED) return set_err(DFLASH_E_INVALID, g_err);
+  return rc;
+}
+
+int dflash_propose_batch(dflash_head *head, dflash_state *const *states, int32_t n, const uint32_t *last_tokens,
+                         const int64_t *positions, int32_t num_drafts, const int32_t *bitmasks, uint32_t *ids,
+                         float *conf, float *row_prob, float *logits, uint64_t stream) {
+  if (!head_ok(head)) return set_err(DFLASH_E_INVALID, "invalid head");
+  std::lock_guard<std::mutex> lk(head->mu);
+  return propose_impl(head, states, n, last_tokens, positions, num_drafts, bitmasks, ids, conf, row_prob, logits,
+                      to_stream(stream));
+}
+
+int dflash_after_verify(dflash_head *head, dflash_state *st, int32_t num_accepted) {
+  if (!head_ok(head)) return set_err(DFLASH_E_INVALID, "invalid head");
+  std::lock_guard<std::mutex> lk(head->mu);
+  if (!state_ok(head, st)) return set_err(DFLASH_E_INVALID, "not a live state of this head");
+  std::string err;
+  int rc = seq_trim(&st->rows, num_accepted, &err);
+  return rc == DFLASH_OK ? rc : set_err(rc, err);
+}
+
+int dflash_state_read_kv(dflash_head *head, const dflash_state *st, int32_t layer, int32_t row0, int32_t n_rows,
+                         void *k_out, void *v_out, uint64_t stream) {
+  if (!head_ok(head)) return set_err(DFLASH_E_INVALID, "invalid head");
+  std::lock_guard<std::mutex> lk(head->mu);
+  if (!state_ok(head, st)) return set_err(DFLASH_E_INVALID, "not a live state of this head");
+  const Geo &g = head->g;
+  if (layer < 0 || layer >= g.L) return set_err(DFLASH_E_INVALID, "layer out of range");
+  if (row0 < 0 || n_rows < 0 || (int64_t)row0 + n_rows > st->rows.ctx_len)
+    return set_err(DFLASH_E_INVALID, "rows outside [0, ctx_len)");
+  if (n_rows == 0) return DFLASH_OK;
+  HIP_TRY(launch_read_kv(head->kv_pool, st->d_bt, g.L, layer, g.n_kv, g.d, (int)head->kv_elem, row0, n_rows, k_out,
+                         v_out, to_stream(stream)));
+  return DFLASH_OK;
+}
+
+int dflash_read_lm_head_fp8(dflash_head *head, void *codes_out, float *scale_out, uint64_t stream) {
+  if (!head_ok(head)) return set_err(DFLASH_E_INVALID, "invalid head");
+  std::lock_guard<std::mutex> lk(head->mu);
+  const Geo &g = head->g;
+  if (!g.head_fp8) return set_err(DFLASH_E_INVALID, "the head's LM head is bf16");
+  hipStream_t st = to_stream(stream);
+  if (codes_out) HIP_TRY(hipMemcpyAsync(codes_out, head->lm8, (size_t)g.V * g.h, hipMemcpyDeviceToDevice, st));
+  if (scale_out) HIP_TRY(hipMemcpyAsync(scale_out, head->lm8_scale, (size_t)g.V * sizeof(float), hipMemcpyDeviceToDevice, st));
+  return DFLASH_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,166 @@
+// host_core.cpp - see host_core.hpp.
+#include "host_core.hpp"
+
+#include <climits>
+#include <cmath>
+
+namespace dflash {
+
+static int fail(std::string *err, int code, const std::string &msg) {
+  if (err) *err = msg;
+  return code;
+}
+
+int validate_config(const dflash_config &c, Geo *g, std::string *err) {
+  auto bad = [&](const std::string &m) { return fail(err, DFLASH_E_INVALID, "config: " + m); };
+  if (c.num_layers < 1 || c.num_layers > 64) return bad("num_layers must be in [1, 64]");
+  if (c.hidden < 64 || c.hidden % 64) return bad("hidden must be a positive multiple of 64");
+  if (c.intermediate < 64 || c.intermediate % 64) return bad("intermediate must be a positive multiple of 64");
+  if (!(c.head_dim == 16 || c.head_dim == 32 || c.head_dim == 64 || c.head_dim == 128))
+    return bad("head_dim must be 16, 32, 64 or 128");
+  if (c.num_q_heads < 1 || c.num_kv_heads < 1 || c.num_q_heads % c.num_kv_heads)
+    return bad("num_kv_heads must divide num_q_heads");
+  if ((c.num_q_heads * c.head_dim) % 64 || (c.num_kv_heads * c.head_dim) % 16)
+    return bad("num_q_heads * head_dim must be a multiple of 64");
+  if (c.gamma < 2 || c.gamma > 64) return bad("gamma must be in [2, 64]");
+  if ((c.num_q_heads / c.num_kv_heads) * c.gamma > 128)
+    return bad("(num_q_heads / num_kv_heads) * gamma must be at most 128");
+  if (c.vocab < 2) return bad("vocab must be >= 2");
+  if (c.mask_token_id >= (uint32_t)c.vocab) return bad("mask_token_id must be < vocab");
+  if (c.num_target_layers < 1 || c.target_hidden < 1) return bad("num_target_layers and target_hidden must be >= 1");
+  if (((int64_t)c.num_target_layers * c.target_hidden) % 8)
+    return bad("num_target_layers * target_hidden must be a multiple of 8");
+  if (c.ctx_window < 0) return bad("ctx_window must be >= 0");
+  if (!(c.rope_theta > 1.0f) || !std::isfinite(c.rope_theta)) return bad("rope_theta must be finite and > 1");
+  if (!(c.rms_eps >= 0.0f) || !std::isfinite(c.rms_eps)) return bad("rms_eps must be finite and >= 0");
+  if (c.kv_block_size != DFLASH_KV_BLOCK) return bad("kv_block_size must be 16");
+  if (c.kv_pool_blocks < 1) return bad("kv_pool_blocks must be >= 1");
+  if (c.max_batch < 1 || c.max_batch > DFLASH_MAX_BATCH) return bad("max_batch must be in [1, 64]");
+  if (c.max_seq_len < 1) return bad("max_seq_len must be >= 1");
+  if (c.weight_dtype != DFLASH_F32 && c.weight_dtype != DFLASH_BF16) return bad("weight_dtype must be F32 or BF16");
+  if (c.lm_head_dtype != DFLASH_BF16 && c.lm_head_dtype != DFLASH_FP8_E4M3)
+    return bad("lm_head_dtype must be BF16 or FP8_E4M3");
+  if (c.kv_dtype != DFLASH_BF16 && c.kv_dtype != DFLASH_FP8_E4M3) return bad("kv_dtype must be BF16 or FP8_E4M3");
+  if (g) {
+    g->L = c.num_layers;
+    g->h = c.hidden;
+    g->I = c.intermediate;
+    g->n_q = c.num_q_heads;
+    g->n_kv = c.num_kv_heads;
+    g->d = c.head_dim;
+    g->V = c.vocab;
+    g->gamma = c.gamma;
+    g->T = c.num_target_layers;
+    g->Ht = c.target_hidden;
+    g->W = c.ctx_window;
+    g->q_dim = c.num_q_heads * c.head_dim;
+    g->kv_dim = c.num_kv_heads * c.head_dim;
+    g->qkv_dim = g->q_dim + 2 * g->kv_dim;
+    g->fc_in = c.num_target_layers * c.target_hidden;
+    g->fkv_dim = c.num_layers * 2 * g->kv_dim;
+    g->words = (c.vocab + 31) / 32;
+    g->rep = c.num_q_heads / c.num_kv_heads;
+    g->max_batch = c.max_batch;
+    g->m_max = c.max_batch * c.gamma;
+    g->mask_id = c.mask_token_id;
+    g->kv_fp8 = c.kv_dtype == DFLASH_FP8_E4M3;
+    g->head_fp8 = c.lm_head_dtype == DFLASH_FP8_E4M3;
+    g->w_f32 = c.weight_dtype == DFLASH_F32;
+  }
+  return DFLASH_OK;
+}
+
+BlockPool::BlockPool(int32_t n) : used_(n > 0 ? n : 0, 0), free_(n > 0 ? n : 0) {}
+
+int32_t BlockPool::alloc() {
+  for (int32_t i = hint_; i < size(); ++i) {
+    if (!used_[i]) {
+      used_[i] = 1;
+      --free_;
+      hint_ = i + 1;
+      return i;
+    }
+  }
+  hint_ = size();
+  return -1;
+}
+
+bool BlockPool::take(int32_t id) {
+  if (!is_free(id)) return false;
+  used_[id] = 1;
+  --free_;
+  return true;
+}
+
+void BlockPool::release(int32_t id) {
+  if (id < 0 || id >= size() || !used_[id]) return;
+  used_[id] = 0;
+  ++free_;
+  if (id < hint_) hint_ = id;
+}
+
+int seq_init(SeqRows *s, BlockPool *pool, int64_t budget_tokens, const int32_t *block_ids, int32_t n_ids,
+             int32_t max_seq_len, std::string *err) {
+  *s = SeqRows();
+  if (budget_tokens < 0) return fail(err, DFLASH_E_INVALID, "budget_tokens must be >= 0");
+  if (block_ids || n_ids) {
+    if (!block_ids || n_ids <= 0) return fail(err, DFLASH_E_INVALID, "block_ids and n_ids must be given together");
+    for (int32_t i = 0; i < n_ids; ++i) {
+      if (!pool->is_free(block_ids[i])) {
+        for (int32_t j = 0; j < i; ++j) pool->release(block_ids[j]);
+        return fail(err, DFLASH_E_NO_BLOCKS, "explicit block " + std::to_string(block_ids[i]) + " is not a free pool block");
+      }
+      pool->take(block_ids[i]);
+    }
+    s->blocks.assign(block_ids, block_ids + n_ids);
+    s->cap_rows = (int64_t)n_ids * DFLASH_KV_BLOCK;
+    if (budget_tokens != INT64_MAX && budget_tokens < s->cap_rows) s->cap_rows = budget_tokens;
+    s->grow = false;
+    return DFLASH_OK;
+  }
+  if (budget_tokens == INT64_MAX) {
+    s->cap_rows = max_seq_len;
+    s->grow = true;
+    return DFLASH_OK;
+  }
+  if (budget_tokens > (int64_t)INT32_MAX - DFLASH_KV_BLOCK) return fail(err, DFLASH_E_INVALID, "budget_tokens too large");
+  int64_t nb = (budget_tokens + DFLASH_KV_BLOCK - 1) / DFLASH_KV_BLOCK;
+  if (nb > pool->free_count()) return fail(err, DFLASH_E_NO_BLOCKS, "KV pool has too few free blocks for the budget");
+  for (int64_t i = 0; i < nb; ++i) s->blocks.push_back(pool->alloc());
+  s->cap_rows = budget_tokens;
+  s->grow = false;
+  return DFLASH_OK;
+}
+
+int seq_reserve(SeqRows *s, BlockPool *pool, int32_t n, int32_t *first_new_block, std::string *err) {
+  if (first_new_block) *first_new_block = (int32_t)s->blocks.size();
+  if (n < 0) return fail(err, DFLASH_E_INVALID, "row count must be >= 0");
+  int64_t need_rows = (int64_t)s->ctx_len + n;
+  if (need_rows > s->cap_rows) return fail(err, DFLASH_E_NO_BLOCKS, "the state's token budget is exhausted");
+  int64_t need_blocks = (need_rows + DFLASH_KV_BLOCK - 1) / DFLASH_KV_BLOCK;
+  int64_t have = (int64_t)s->blocks.size();
+  if (need_blocks <= have) return DFLASH_OK;
+  if (!s->grow) return fail(err, DFLASH_E_NO_BLOCKS, "the state's blocks are exhausted");
+  if (need_blocks - have > pool->free_count()) return fail(err, DFLASH_E_NO_BLOCKS, "the KV pool is exhausted");
+  for (int64_t i = have; i < need_blocks; ++i) s->blocks.push_back(pool->alloc());
+  return DFLASH_OK;
+}
+
+int seq_trim(SeqRows *s, int32_t a, std::string *err) {
+  int32_t pending = s->ctx_len - s->pending_base;
+  if (a < 0 || a > pending)
+    return fail(err, DFLASH_E_INVALID,
+                "num_accepted " + std::to_string(a) + " outside [0, " + std::to_string(pending) + "]");
+  s->ctx_len = s->pending_base + a;
+  s->pending_base = s->ctx_len;
+  return DFLASH_OK;
+}
+
+void seq_release(SeqRows *s, BlockPool *pool) {
+  for (int32_t b : s->blocks) pool->release(b);
+  s->blocks.clear();
+  s->ctx_len = 0;
+  s->pending_base = 0;
+}
+
+}  // namespace dflash

@@ -1,0 +1,160 @@
+// k_misc.hip - row-wise kernels of the DFlash head for gfx950: block setup
+// (embedding gather, first RMSNorm, RoPE table), RMSNorm, build-time weight
+// conversion and repacking, the FP8 LM-head mirror, and KV inspection.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace dflash {
+
+namespace {
+
+// One workgroup per block row m of the call: sequence s = m / gamma, row
+// j = m % gamma. Token = last verified token for j == 0, else the mask
+// token; position = position[s] + j. Writes the fp32 residual row (embedding
+// row widened), its RMSNorm with the first layer's input gain as bf16, and
+// the row's (cos, sin) RoPE table computed in double precision.
+__global__ __launch_bounds__(256) void k_setup(SetupArgs a) {
+  __shared__ float red[4];
+  const int m = blockIdx.x, s = m / a.gamma, j = m % a.gamma;
+  const uint32_t tok = j == 0 ? a.token[s] : a.mask_id;
+  const int pos = a.position[s] + j;
+  const uint16_t *e = a.embed + (size_t)tok * a.h;
+  float *hr = a.hid + (size_t)m * a.h;
+  float ss = 0.0f;
+  for (int i = threadIdx.x; i < a.h; i += blockDim.x) {
+    const float x = bf16_to_f32(e[i]);
+    hr[i] = x;
+    ss += x * x;
+  }
+  ss = block_sum(ss, red);
+  const float r = 1.0f / sqrtf(ss / (float)a.h + a.eps);
+  uint16_t *ar = a.a + (size_t)m * a.h;
+  for (int i = threadIdx.x; i < a.h; i += blockDim.x) ar[i] = f32_to_bf16(bf16_to_f32(e[i]) * r * a.gain[i]);
+  for (int i = threadIdx.x; i < a.half_dim; i += blockDim.x) {
+    double sn, cs;
+    sincos((double)pos * a.inv_freq[i], &sn, &cs);
+    a.cs[(size_t)m * a.half_dim + i] = make_float2((float)cs, (float)sn);
+  }
+}
+
+__global__ __launch_bounds__(256) void k_rmsnorm(const float *x, int ldx, const float *gain, float eps, int n,
+                                                 uint16_t *out, int ldo) {
+  __shared__ float red[4];
+  const int m = blockIdx.x;
+  const float *xr = x + (size_t)m * ldx;
+  float ss = 0.0f;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) ss += xr[i] * xr[i];
+  ss = block_sum(ss, red);
+  const float r = 1.0f / sqrtf(ss / (float)n + eps);
+  uint16_t *o = out + (size_t)m * ldo;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) o[i] = f32_to_bf16(xr[i] * r * gain[i]);
+}
+
+__device__ __forceinline__ uint16_t load_as_bf16(const void *src, size_t i, bool src_f32) {
+  return src_f32 ? f32_to_bf16(((const float *)src)[i]) : ((const uint16_t *)src)[i];
+}
+
+__global__ void k_convert_rows(uint16_t *dst, const void *src, const void *src2, int rows, int cols, int src_f32,
+                               int interleave) {
+  const size_t total = (size_t)rows * cols;
+  for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (size_t)gridDim.x * blockDim.x) {
+    const int rr = (int)(e / cols), cc = (int)(e % cols);
+    const void *s = src;
+    int sr = rr;
+    if (interleave) {  // dst rows 128b .. 128b+63 = gate rows 64b.., 128b+64 .. = up rows 64b..
+      const int b = rr / 128, w = rr % 128;
+      s = w < 64 ? src : src2;
+      sr = b * 64 + (w & 63);
+    }
+    dst[e] = load_as_bf16(s, (size_t)sr * cols + cc, src_f32 != 0);
+  }
+}
+
+__global__ void k_to_f32(float *dst, const void *src, int n, int src_f32) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
+    dst[i] = src_f32 ? ((const float *)src)[i] : bf16_to_f32(((const uint16_t *)src)[i]);
+}
+
+// One workgroup per vocab row: s = amax / 448 (1 for an all-zero row),
+// code = E4M3(w / s) with IEEE float32 division, round to nearest even.
+__global__ __launch_bounds__(256) void k_fp8_mirror(const uint16_t *src, int h, uint8_t *codes, float *scale) {
+  __shared__ float red[4];
+  const int v = blockIdx.x;
+  const uint16_t *row = src + (size_t)v * h;
+  float amax = 0.0f;
+  for (int i = threadIdx.x; i < h; i += blockDim.x) amax = fmaxf(amax, fabsf(bf16_to_f32(row[i])));
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, WAVE));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = amax > 0.0f ? amax / E4M3_MAX : 1.0f;
+  if (threadIdx.x == 0) scale[v] = s;
+  uint8_t *out = codes + (size_t)v * h;
+  for (int i = threadIdx.x; i < h; i += blockDim.x) out[i] = f32_to_e4m3(bf16_to_f32(row[i]) / s);
+}
+
+__global__ void k_read_kv(const uint8_t *pool, const int32_t *bt, int L, int layer, int n_kv, int d, int eb, int row0,
+                          int n_rows, uint8_t *k_out, uint8_t *v_out) {
+  const size_t row_bytes = (size_t)n_kv * d * eb;
+  const size_t total = (size_t)n_rows * row_bytes;
+  for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (size_t)gridDim.x * blockDim.x) {
+    const int r = (int)(e / row_bytes);
+    const size_t within = e % row_bytes;
+    const int g = (int)(within / ((size_t)d * eb));
+    const size_t de = within % ((size_t)d * eb);
+    const int pos = row0 + r;
+    const int32_t blk = bt[pos >> 4];
+    const size_t tile = (size_t)DFLASH_KV_BLOCK * d * eb;
+    const size_t kb = ((((size_t)blk * L + layer) * 2 + 0) * n_kv + g) * tile + (size_t)(pos & 15) * d * eb + de;
+    const size_t vb = kb + (size_t)n_kv * tile;
+    if (k_out) k_out[e] = pool[kb];
+    if (v_out) v_out[e] = pool[vb];
+  }
+}
+
+int grid_for(size_t total, int block) {
+  size_t b = (total + block - 1) / block;
+  if (b > 65535) b = 65535;
+  return b < 1 ? 1 : (int)b;
+}
+
+}  // namespace
+
+hipError_t launch_setup(const SetupArgs &a, int M, hipStream_t s) {
+  hipLaunchKernelGGL(k_setup, dim3(M), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(const float *x, int ldx, const float *gain, float eps, int n, uint16_t *out, int ldo,
+                          int M, hipStream_t s) {
+  hipLaunchKernelGGL(k_rmsnorm, dim3(M), dim3(256), 0, s, x, ldx, gain, eps, n, out, ldo);
+  return hipGetLastError();
+}
+
+hipError_t launch_convert_rows(uint16_t *dst, const void *src, const void *src2, int rows, int cols, bool src_f32,
+                               bool interleave, hipStream_t s) {
+  hipLaunchKernelGGL(k_convert_rows, dim3(grid_for((size_t)rows * cols, 256)), dim3(256), 0, s, dst, src, src2, rows,
+                     cols, (int)src_f32, (int)interleave);
+  return hipGetLastError();
+}
+
+hipError_t launch_to_f32(float *dst, const void *src, int n, bool src_f32, hipStream_t s) {
+  hipLaunchKernelGGL(k_to_f32, dim3(grid_for(n, 256)), dim3(256), 0, s, dst, src, n, (int)src_f32);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_mirror(const uint16_t *src, int V, int h, uint8_t *codes, float *scale, hipStream_t s) {
+  hipLaunchKernelGGL(k_fp8_mirror, dim3(V), dim3(256), 0, s, src, h, codes, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_read_kv(const void *pool, const int32_t *bt, int L, int layer, int n_kv, int d, int elem_bytes,
+                          int row0, int n_rows, void *k_out, void *v_out, hipStream_t s) {
+  const size_t total = (size_t)n_rows * n_kv * d * elem_bytes;
+  hipLaunchKernelGGL(k_read_kv, dim3(grid_for(total, 256)), dim3(256), 0, s, (const uint8_t *)pool, bt, L, layer, n_kv,
+                     d, elem_bytes, row0, n_rows, (uint8_t *)k_out, (uint8_t *)v_out);
+  return hipGetLastError();
+}
+
+}  // namespace dflash

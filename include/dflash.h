@@ -1,0 +1,224 @@
+/*
+ * dflash.h - C ABI of the MI355X (gfx950) block-diffusion (DFlash) draft head.
+ *
+ * The library implements the draft head's propose pass: a block of gamma rows
+ * (the last verified token, then mask tokens) runs through the drafter layers,
+ * attending to a window of context K/V that earlier calls derived from the
+ * target model's captured hidden states, and ends in the shared-vocabulary LM
+ * head with a per-row argmax. Every step runs in HIP kernels on the device;
+ * the host side only validates arguments and keeps per-sequence bookkeeping.
+ *
+ * Sources, cited by page title and section:
+ *   [Head/atlas]    "Struct BlockDiffusionDraftHead" (spark_model::layers::dflash_head)
+ *   [Head/metrale]  "Struct BlockDiffusionDraftHead" (metrale_model_arch::dflash_head)
+ *   [DraftProposer] "Trait DraftProposer" (spark_model::speculative)
+ *
+ * Conventions for every entry point:
+ *   - Device pointers are HIP device addresses on the current device; host
+ *     pointers are ordinary process memory. Each argument says which.
+ *   - `stream` is a hipStream_t cast to uint64_t (0 = the null stream). All
+ *     device work of a call is enqueued on it; no call synchronises the host
+ *     except dflash_build, dflash_state_create and dflash_state_free.
+ *   - A negative return value is a dflash_status error; dflash_last_error()
+ *     then describes it. Every argument check runs on the host before any
+ *     kernel is enqueued, so a failed call leaves the device untouched.
+ *   - A head's scratch buffers are shared by all calls on that head: calls on
+ *     one head must be ordered on the device (use one stream, or synchronise
+ *     between streams). Host-side calls on one head are serialised by an
+ *     internal mutex. States are owned by the head that created them.
+ */
+#ifndef DFLASH_H
+#define DFLASH_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DFLASH_ABI_VERSION 1
+#define DFLASH_MAX_BATCH 64     /* widest dflash_propose_batch */
+#define DFLASH_KV_BLOCK 16      /* rows per paged KV block */
+#define DFLASH_NO_TOKEN 0xFFFFFFFFu /* id of a row whose every token is masked */
+
+typedef enum {
+  DFLASH_OK = 0,
+  DFLASH_E_INVALID = -1,   /* an argument value or state is invalid */
+  DFLASH_E_SHAPE = -2,     /* geometry mismatch (e.g. fc width != num_target_layers * target_hidden) */
+  DFLASH_E_NOMEM = -3,     /* a device or host allocation failed */
+  DFLASH_E_NO_BLOCKS = -4, /* the KV pool or the state's token budget is exhausted */
+  DFLASH_E_DECLINED = -5,  /* batch width outside 1..max_batch: fall back to per-sequence propose */
+  DFLASH_E_HIP = -6        /* a HIP runtime call failed */
+} dflash_status;
+
+typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1, DFLASH_FP8_E4M3 = 2 } dflash_dtype;
+
+typedef struct dflash_head dflash_head;   /* opaque */
+typedef struct dflash_state dflash_state; /* opaque, one per sequence */
+
+/* Geometry and build options ([Head/atlas] struct fields num_layers ...
+ * rms_norm_eps, ctx_window; all validated by dflash_build). */
+typedef struct {
+  int32_t num_layers;        /* drafter layers L (>= 1) */
+  int32_t hidden;            /* drafter hidden size h, multiple of 128 or 64 (tiny) */
+  int32_t intermediate;      /* SwiGLU width I, multiple of 64 */
+  int32_t num_q_heads;       /* query heads */
+  int32_t num_kv_heads;      /* kv heads (divides num_q_heads) */
+  int32_t head_dim;          /* 16, 32, 64 or 128; RoPE covers the whole head */
+  int32_t vocab;             /* shared vocabulary V */
+  int32_t gamma;             /* block rows per sequence (2..64) */
+  uint32_t mask_token_id;    /* id of rows 1..gamma-1 of the block (< vocab) */
+  int32_t num_target_layers; /* T: target layers in the captured hidden stack */
+  int32_t target_hidden;     /* Ht: target hidden size; fc input width = T * Ht */
+  int32_t ctx_window;        /* most ctx rows a block attends to; 0 disables ctx */
+  float rope_theta;          /* inv_freq[i] = theta^(-2i/head_dim) unless a table is given */
+  float rms_eps;             /* RMSNorm epsilon */
+  int32_t kv_block_size;     /* must be DFLASH_KV_BLOCK */
+  int32_t kv_pool_blocks;    /* physical blocks in the head's paged KV pool */
+  int32_t max_batch;         /* widest batch (1..DFLASH_MAX_BATCH) */
+  int32_t max_seq_len;       /* per-state row ceiling when its budget is unknown */
+  dflash_dtype weight_dtype;  /* F32 or BF16: dtype of the drafter tensors given at build */
+  dflash_dtype lm_head_dtype; /* BF16, or FP8_E4M3 (a mirror is built unless one is given) */
+  dflash_dtype kv_dtype;      /* BF16, or FP8_E4M3 with per-(layer, K|V, kv head) scales */
+} dflash_config;
+
+/* One drafter layer's tensors: device pointers in weight_dtype, matrices in
+ * PyTorch Linear layout [out, in], row-major. */
+typedef struct {
+  const void *in_norm;   /* [h] input RMSNorm gain */
+  const void *q;         /* [n_q * d, h] */
+  const void *k;         /* [n_kv * d, h] */
+  const void *v;         /* [n_kv * d, h] */
+  const void *o;         /* [h, n_q * d] */
+  const void *post_norm; /* [h] post-attention RMSNorm gain */
+  const void *gate;      /* [I, h] */
+  const void *up;        /* [I, h] */
+  const void *down;      /* [h, I] */
+} dflash_layer_weights;
+
+/* Weights given to dflash_build. The drafter checkpoint's tensors (fc, norms,
+ * layers) are copied into the head's own layout during the call and may be
+ * freed afterwards. The target's embedding and LM head are borrowed when they
+ * are bf16 and must outlive the head ([Head/atlas], struct description: the
+ * drafter uses the target's embed_tokens and lm_head). */
+typedef struct {
+  const void *fc;             /* device [h, T*Ht], weight_dtype ([Head/atlas] field fc) */
+  const void *hidden_norm;    /* device [h] ([Head/atlas] field hidden_norm) */
+  const void *norm;           /* device [h] final norm ([Head/atlas] field norm) */
+  const void *embed_tokens;   /* device [V, h], weight_dtype (bf16: borrowed) */
+  const void *lm_head;        /* device [V, h], weight_dtype (bf16: borrowed) */
+  const void *lm_head_fp8;    /* optional device [V, h] E4M3 codes (borrowed); NULL = build a mirror */
+  const float *lm_head_scale; /* device [V] f32 row scales of lm_head_fp8 (borrowed) */
+  const float *kv_scale;      /* host [L][2][n_kv] f32 (K then V) when kv_dtype is FP8, else NULL */
+  const float *inv_freq;      /* optional host [head_dim/2] f32 RoPE table; NULL = plain theta table */
+  const dflash_layer_weights *layers; /* host array [num_layers] */
+} dflash_weights;
+
+/* Build a head ([Head/atlas] impl, from_weights and validate_against_target).
+ * Validates the geometry (a mismatched fc width is DFLASH_E_SHAPE), stitches
+ * the fused ctx-K/V weight [L * 2 * n_kv * d, h] with rows [K0; V0; K1; V1;
+ * ...] ([Head/atlas] field fused_kv_weight), converts and repacks the drafter
+ * tensors to bf16, builds the FP8 LM-head mirror when asked ([Head/atlas]
+ * field lm_head_shared_fp8: E4M3 codes, per-row scale amax / 448), and
+ * allocates the paged KV pool and the scratch. Synchronises `stream`.
+ * On success *out owns all of it until dflash_destroy. */
+int dflash_build(const dflash_config *cfg, const dflash_weights *w, uint64_t stream, dflash_head **out);
+
+/* Free the head and everything it owns. States of the head must have been
+ * freed first (remaining ones are freed here). NULL is a no-op. */
+void dflash_destroy(dflash_head *head);
+
+/* Block size gamma ([DraftProposer] block_gamma); callers draft gamma - 1. */
+int dflash_block_gamma(const dflash_head *head);
+
+/* Widest batch one dflash_propose_batch call can carry ([DraftProposer]
+ * propose_batch_max): the build's max_batch. */
+int dflash_propose_batch_max(const dflash_head *head);
+
+/* Per-sequence state ([DraftProposer] alloc_state / alloc_state_for).
+ * budget_tokens: most ctx rows the sequence will hold; INT64_MAX = unknown
+ * (the build's max_seq_len applies and blocks are taken from the pool as
+ * rows arrive). With a known budget every block is taken now.
+ * block_ids (host, optional): explicit physical pool blocks for the
+ * sequence, in logical order; n_ids of them bound its capacity. They must be
+ * free. Returns DFLASH_E_NO_BLOCKS when the pool cannot supply the blocks. */
+int dflash_state_create(dflash_head *head, int64_t budget_tokens, const int32_t *block_ids, int32_t n_ids,
+                        dflash_state **out);
+
+/* Release a state's KV blocks and device memory ([DraftProposer] free_state).
+ * Synchronises the device before releasing. */
+int dflash_state_free(dflash_head *head, dflash_state *st);
+
+/* Ctx rows the state holds (appended and not trimmed); negative on error. */
+int dflash_state_ctx_len(const dflash_state *st);
+
+/* Append ctx rows to n states ([Head/atlas] field fused_kv_weight: the
+ * precompute module). For each state i, n_new[i] rows of the captured hidden
+ * stack (rows sum(n_new[0..i)) .. of `stack`) are projected by fc, normed by
+ * hidden_norm, and turned into every layer's K and V by one fused GEMM; K is
+ * rotated at positions ctx_len .. ctx_len + n_new[i] - 1 and both are written
+ * into the state's paged blocks. The rows become the state's pending rows.
+ *   states: host array [n]; n_new: host array [n], each >= 0;
+ *   stack: device bf16 [sum(n_new), T * Ht], row-major, shallow-to-deep
+ *          concatenation of the target layers ([DraftProposer] propose,
+ *          argument target_hidden_stack).
+ * DFLASH_E_NO_BLOCKS if a state would exceed its budget or the pool. */
+int dflash_precompute_ctx_kv(dflash_head *head, dflash_state *const *states, int32_t n, const int32_t *n_new,
+                             const void *stack, uint64_t stream);
+
+/* One propose ([DraftProposer] propose; [Head/atlas] last_confidence).
+ * The block [last_token, mask_token_id x (gamma - 1)] at RoPE positions
+ * position .. position + gamma - 1 attends to the state's ctx rows
+ * [max(0, ctx_len - ctx_window), ctx_len) and to itself; after the final norm
+ * and LM head each row takes its argmax (ties to the lowest id).
+ *   last_token < vocab; 0 <= position < 2^31 - gamma; 1 <= num_drafts <= gamma - 1.
+ *   bitmask: optional device int32 [ceil(V/32)]; bit v&31 of word v>>5 set
+ *            means token v is allowed ([DraftProposer] propose, grammar_bitmask).
+ * Outputs (device, caller-owned, valid after the stream completes):
+ *   ids      uint32 [gamma]: argmax of every block row (drafts are rows
+ *            1..num_drafts); DFLASH_NO_TOKEN when the mask allows nothing;
+ *   conf     f32 [1]: min over rows 1..num_drafts of the top-1 softmax prob;
+ *   row_prob f32 [gamma] or NULL: top-1 softmax prob of every row;
+ *   logits   f32 [gamma, V] or NULL: unmasked logits (inspection only). */
+int dflash_propose(dflash_head *head, dflash_state *st, uint32_t last_token, int64_t position, int32_t num_drafts,
+                   const int32_t *bitmask, uint32_t *ids, float *conf, float *row_prob, float *logits,
+                   uint64_t stream);
+
+/* Batched propose: ONE forward over n * gamma rows ([Head/atlas] and
+ * [DraftProposer] propose_batch). Sequence i uses states[i], last_tokens[i]
+ * and positions[i] (host arrays [n]); the result for each sequence is that of
+ * dflash_propose. 1 <= n <= max_batch, else DFLASH_E_DECLINED (the caller
+ * falls back to per-sequence calls, never a different answer).
+ *   bitmasks: optional device int32 [n, ceil(V/32)], one mask per sequence.
+ *   ids [n, gamma], conf [n], row_prob [n, gamma] or NULL,
+ *   logits [n, gamma, V] or NULL: device, caller-owned. */
+int dflash_propose_batch(dflash_head *head, dflash_state *const *states, int32_t n, const uint32_t *last_tokens,
+                         const int64_t *positions, int32_t num_drafts, const int32_t *bitmasks, uint32_t *ids,
+                         float *conf, float *row_prob, float *logits, uint64_t stream);
+
+/* Trim after verification ([DraftProposer] after_verify): keep the first
+ * num_accepted rows appended since the previous dflash_after_verify (or since
+ * the state was created) and drop the rest; the kept rows become committed.
+ * 0 <= num_accepted <= pending rows, else DFLASH_E_INVALID. Host-only: no
+ * device work; the dropped rows' slots are overwritten by later appends. */
+int dflash_after_verify(dflash_head *head, dflash_state *st, int32_t num_accepted);
+
+/* Copy cached ctx rows [row0, row0 + n_rows) of one layer out of the paged
+ * cache, in the cache's storage dtype (bf16: 2 bytes, FP8: 1 byte per value),
+ * as K [n_rows, n_kv, d] and V [n_rows, n_kv, d] into device buffers k_out and
+ * v_out (either may be NULL). Inspection of what precompute wrote. */
+int dflash_state_read_kv(dflash_head *head, const dflash_state *st, int32_t layer, int32_t row0, int32_t n_rows,
+                         void *k_out, void *v_out, uint64_t stream);
+
+/* The LM head the propose reads when lm_head_dtype is FP8: copies the E4M3
+ * codes [V, h] and row scales [V] into device buffers (either may be NULL).
+ * DFLASH_E_INVALID on a bf16 head. */
+int dflash_read_lm_head_fp8(dflash_head *head, void *codes_out, float *scale_out, uint64_t stream);
+
+/* Message of the calling thread's last error ("" if none). */
+const char *dflash_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DFLASH_H */

@@ -1,0 +1,169 @@
+"""CPU tests of the HIP-free host core (config validation, block pool,
+append / trim bookkeeping) through libdflash_host.so, and of the HIP
+library's exported C ABI (symbols only: no device calls without a GPU)."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PKG = os.path.join(ROOT, "block_diffusion_draft_03_amd")
+HOST_LIB = os.path.join(PKG, "libdflash_host.so")
+INT64_MAX = (1 << 63) - 1
+
+OK, E_INVALID, E_SHAPE, E_NOMEM, E_NO_BLOCKS, E_DECLINED, E_HIP = 0, -1, -2, -3, -4, -5, -6
+
+
+@pytest.fixture(scope="module")
+def host():
+    if not os.path.exists(HOST_LIB):
+        from block_diffusion_draft_03_amd import build
+        build.build_host_lib()
+    lib = C.CDLL(HOST_LIB)
+    vp = C.c_void_p
+    lib.dfh_last_error.restype = C.c_char_p
+    lib.dfh_validate.argtypes = [vp]
+    lib.dfh_pool_new.restype = vp
+    lib.dfh_pool_new.argtypes = [C.c_int32]
+    lib.dfh_pool_delete.argtypes = [vp]
+    lib.dfh_pool_free_count.argtypes = [vp]
+    lib.dfh_seq_new.restype = vp
+    lib.dfh_seq_new.argtypes = [vp, C.c_int64, vp, C.c_int32, C.c_int32, C.POINTER(C.c_int)]
+    lib.dfh_seq_append.argtypes = [vp, vp, C.c_int32]
+    lib.dfh_seq_trim.argtypes = [vp, C.c_int32]
+    lib.dfh_seq_ctx_len.argtypes = [vp]
+    lib.dfh_seq_pending.argtypes = [vp]
+    lib.dfh_seq_blocks.argtypes = [vp, vp, C.c_int32]
+    lib.dfh_seq_release.argtypes = [vp, vp]
+    lib.dfh_seq_delete.argtypes = [vp]
+    return lib
+
+
+def make_cfg(geo=synth.FULL, **over):
+    from block_diffusion_draft_03_amd.binding import Config, DTYPE
+    d = dict(num_layers=geo.num_layers, hidden=geo.hidden, intermediate=geo.intermediate,
+             num_q_heads=geo.num_q_heads, num_kv_heads=geo.num_kv_heads, head_dim=geo.head_dim, vocab=geo.vocab,
+             gamma=geo.gamma, mask_token_id=geo.mask_token_id, num_target_layers=geo.num_target_layers,
+             target_hidden=geo.target_hidden, ctx_window=geo.ctx_window, rope_theta=geo.rope_theta,
+             rms_eps=geo.rms_eps, kv_block_size=16, kv_pool_blocks=1024, max_batch=64, max_seq_len=8192,
+             weight_dtype=DTYPE[geo.weight_dtype], lm_head_dtype=DTYPE[geo.lm_head_dtype], kv_dtype=DTYPE[geo.kv_dtype])
+    d.update(over)
+    return Config(**d)
+
+
+def test_valid_configs(host):
+    for geo in (synth.TINY, synth.FULL, synth.FULL_FP8):
+        assert host.dfh_validate(C.byref(make_cfg(geo))) == OK, host.dfh_last_error()
+
+
+@pytest.mark.parametrize("field,value", [
+    ("num_layers", 0), ("hidden", 100), ("intermediate", 96), ("head_dim", 48), ("num_kv_heads", 3),
+    ("gamma", 1), ("gamma", 65), ("vocab", 1), ("mask_token_id", 248320), ("ctx_window", -1),
+    ("kv_block_size", 32), ("kv_pool_blocks", 0), ("max_batch", 0), ("max_batch", 65), ("max_seq_len", 0),
+    ("rope_theta", 0.5), ("rms_eps", -1.0), ("weight_dtype", 2), ("lm_head_dtype", 0), ("kv_dtype", 0),
+    ("target_hidden", 0), ("gamma", 32)])
+def test_invalid_configs(host, field, value):
+    # gamma 32 with 8 query heads per kv head gives 256 query rows per kv head
+    cfg = make_cfg(**{field: value})
+    assert host.dfh_validate(C.byref(cfg)) == E_INVALID
+    assert host.dfh_last_error().decode().startswith("config:")
+
+
+def _seq(host, pool, budget=INT64_MAX, ids=None, max_seq_len=8192):
+    st = C.c_int()
+    arr = None if ids is None else np.ascontiguousarray(ids, dtype=np.int32)
+    s = host.dfh_seq_new(pool, budget, None if arr is None else arr.ctypes.data_as(C.c_void_p),
+                         0 if arr is None else len(arr), max_seq_len, C.byref(st))
+    return s, st.value
+
+
+def _blocks(host, s):
+    out = np.zeros(4096, dtype=np.int32)
+    n = host.dfh_seq_blocks(s, out.ctypes.data_as(C.c_void_p), 4096)
+    return out[:n].tolist()
+
+
+def test_pool_lowest_free_first_and_release(host):
+    pool = host.dfh_pool_new(8)
+    a, st = _seq(host, pool, budget=40)           # 3 blocks now
+    assert st == OK and _blocks(host, a) == [0, 1, 2]
+    b, st = _seq(host, pool, budget=16)
+    assert st == OK and _blocks(host, b) == [3]
+    host.dfh_seq_release(a, pool)
+    assert host.dfh_pool_free_count(pool) == 7
+    c, st = _seq(host, pool, budget=17)           # reuses the lowest ids
+    assert st == OK and _blocks(host, c) == [0, 1]
+    for s in (a, b, c):
+        host.dfh_seq_delete(s)
+    host.dfh_pool_delete(pool)
+
+
+def test_budget_and_pool_exhaustion(host):
+    pool = host.dfh_pool_new(4)
+    s, st = _seq(host, pool, budget=100)          # needs 7 blocks
+    assert s is None and st == E_NO_BLOCKS
+    assert host.dfh_pool_free_count(pool) == 4    # nothing taken
+    g, st = _seq(host, pool)                       # grow mode, unknown budget
+    assert st == OK
+    assert host.dfh_seq_append(g, pool, 33) == OK and _blocks(host, g) == [0, 1, 2]
+    assert host.dfh_seq_append(g, pool, 40) == E_NO_BLOCKS      # pool has one block left
+    assert host.dfh_seq_ctx_len(g) == 33 and _blocks(host, g) == [0, 1, 2]
+    assert host.dfh_seq_append(g, pool, 15) == OK and _blocks(host, g) == [0, 1, 2]   # 48 rows fit
+    assert host.dfh_seq_append(g, pool, 1) == OK and _blocks(host, g) == [0, 1, 2, 3]
+    h, st = _seq(host, pool, max_seq_len=10)
+    host.dfh_seq_release(g, pool)
+    assert host.dfh_seq_append(h, pool, 10) == OK
+    assert host.dfh_seq_append(h, pool, 1) == E_NO_BLOCKS       # max_seq_len ceiling
+    host.dfh_seq_delete(g)
+    host.dfh_seq_delete(h)
+    host.dfh_pool_delete(pool)
+
+
+def test_explicit_blocks(host):
+    pool = host.dfh_pool_new(16)
+    ids = [9, 3, 14]
+    s, st = _seq(host, pool, ids=ids)
+    assert st == OK and _blocks(host, s) == ids and host.dfh_pool_free_count(pool) == 13
+    assert host.dfh_seq_append(s, pool, 48) == OK
+    assert host.dfh_seq_append(s, pool, 1) == E_NO_BLOCKS        # capacity = 3 blocks
+    t, st = _seq(host, pool, ids=[2, 3])                          # 3 is taken
+    assert t is None and st == E_NO_BLOCKS and host.dfh_pool_free_count(pool) == 13
+    host.dfh_seq_delete(s)
+    host.dfh_pool_delete(pool)
+
+
+def test_trim_semantics(host):
+    pool = host.dfh_pool_new(64)
+    s, _ = _seq(host, pool)
+    assert host.dfh_seq_append(s, pool, 20) == OK
+    assert host.dfh_seq_trim(s, 20) == OK                          # commit all
+    assert host.dfh_seq_pending(s) == 0
+    assert host.dfh_seq_append(s, pool, 16) == OK
+    assert host.dfh_seq_trim(s, 17) == E_INVALID                   # more than pending
+    assert host.dfh_seq_trim(s, -1) == E_INVALID
+    assert host.dfh_seq_ctx_len(s) == 36
+    assert host.dfh_seq_trim(s, 5) == OK
+    assert host.dfh_seq_ctx_len(s) == 25 and host.dfh_seq_pending(s) == 0
+    assert host.dfh_seq_append(s, pool, 8) == OK and host.dfh_seq_append(s, pool, 8) == OK
+    assert host.dfh_seq_pending(s) == 16                           # two appends since the verify
+    assert host.dfh_seq_trim(s, 0) == OK and host.dfh_seq_ctx_len(s) == 25
+    host.dfh_seq_delete(s)
+    host.dfh_pool_delete(pool)
+
+
+def test_hip_library_exports_every_declared_symbol():
+    """libdflash.so loads without a GPU and exports every function
+    include/dflash.h declares (no compute calls are made here)."""
+    from block_diffusion_draft_03_amd.binding import EXPORTED_SYMBOLS, load_library
+    with open(os.path.join(ROOT, "include", "dflash.h")) as f:
+        header = f.read()
+    declared = set(re.findall(r"\b(dflash_[a-z0-9_]+)\s*\(", header))
+    assert declared == set(EXPORTED_SYMBOLS)
+    lib = load_library()
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert lib.dflash_last_error() == b""
