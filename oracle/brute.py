@@ -91,7 +91,8 @@ def brute_propose(geo, weights, ctx_stack_rows, last_token, position, num_drafts
     ctxK = [[None] * c for _ in range(L)]
     ctxV = [[None] * c for _ in range(L)]
     for i in range(c):
-        feat = _rmsnorm(_matvec(fc, S[i]), gh, eps)
+        # the fused ctx K/V projection is a bf16 GEMM: its input enters as bf16
+        feat = [_store_bf16(x) for x in _rmsnorm(_matvec(fc, S[i]), gh, eps)]
         for l in range(L):
             kr = _matvec(layers[l]["k"], feat)
             vr = _matvec(layers[l]["v"], feat)

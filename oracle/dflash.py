@@ -133,13 +133,26 @@ def fp8_head_mirror(lm_head_bf16_bits):
     s_v = amax_v / 448 and q_vk = enc(w_vk / s_v). Both the scale and the
     quotient are computed in float32, the precision of the stored scale, so
     the integer codes are a deterministic function of the bf16 head. An
-    all-zero row gets scale 1.
+    all-zero row gets scale 1. Rows are independent, so they are processed
+    in blocks of 2048 on a thread pool (memory and time only).
     """
-    w = stored_to_f64(lm_head_bf16_bits).astype(np.float32)
-    amax = np.max(np.abs(w), axis=1)
-    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
-    q = w / scale[:, None]  # float32 IEEE division
-    codes = e4m3_encode(q.astype(np.float64))
+    src = np.asarray(lm_head_bf16_bits)
+    V, h = src.shape
+    codes = np.empty((V, h), dtype=np.uint8)
+    scale = np.empty(V, dtype=np.float32)
+
+    def rows(r0):
+        r1 = min(V, r0 + 2048)
+        w = stored_to_f64(src[r0:r1]).astype(np.float32)
+        amax = np.max(np.abs(w), axis=1)
+        s = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+        q = w / s[:, None]  # float32 IEEE division
+        codes[r0:r1] = e4m3_encode(q.astype(np.float64))
+        scale[r0:r1] = s
+
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(16) as ex:
+        list(ex.map(rows, range(0, V, 2048)))
     return codes, scale
 
 
@@ -215,7 +228,8 @@ class OracleHead:
             else:
                 codes, scale = fp8_head_mirror(w["lm_head"])
             self.lm_codes, self.lm_scale = codes, scale
-            self.lm = e4m3_decode(codes)  # dequantised without the row scale
+            # dequantised without the row scale (table of the 256 decoded codes)
+            self.lm = e4m3_decode(np.arange(256, dtype=np.uint8))[codes]
         else:
             self.lm = stored_to_f64(w["lm_head"])
         if self.kv_fp8:
@@ -247,13 +261,20 @@ class OracleHead:
         values pass through the cache's storage format: bf16 ([Head/metrale],
         field ``kv_cache``) or FP8 E4M3 with one f32 scale per (layer, K|V,
         kv head) ([Head/atlas], field ``kv_cache``).
+
+        The fused projection is one bf16 dense GEMM over a BF16 weight
+        ([Head/atlas], field ``fused_kv_weight``), so its input c enters as
+        bf16: c is rounded to bf16 here, and the products are exact float64
+        sums of those bf16 values. This fixes the values every cache code is
+        decided on.
         Returns lists over layers of ``[rows, n_kv, d]`` K and V.
         """
         ks, vs = [], []
         n = c_hat.shape[0]
+        c_in = bf16_round(c_hat)
         for l, lw in enumerate(self.layers):
-            k = (c_hat @ lw["k"].T).reshape(n, self.n_kv, self.d)
-            v = (c_hat @ lw["v"].T).reshape(n, self.n_kv, self.d)
+            k = (c_in @ lw["k"].T).reshape(n, self.n_kv, self.d)
+            v = (c_in @ lw["v"].T).reshape(n, self.n_kv, self.d)
             k = rope(k, positions, self.inv_freq)
             if self.kv_fp8:
                 k = fp8_roundtrip(k, self.kv_scale[l, 0][None, :, None])
