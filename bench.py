@@ -1,0 +1,289 @@
+#!/usr/bin/env python3
+"""Benchmark of the DFlash draft head's propose path on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+ctx precompute of the new rows (fc, hidden_norm, fused ctx-K/V GEMM, RoPE,
+paged scatter), the propose forward (embedding, 8 drafter layers, final norm,
+LM head, argmax / confidence) and the after-verify trim. Inputs are resident
+in HBM before the timed region starts.
+
+Prints ONE JSON line. `value` is draft blocks per second over the timed
+steps; `us_per_propose` times the forward alone. `roofline` is measured on
+the dominant kernel (LM-head stage 1) with HIP events the library records on
+its own stream during the timed steps. `cpu_baseline` times the float64 oracle
+on the host on a bounded sample of the same workload.
+
+Workloads (--workload): single_ctx1024 (default), single_ctx4096_trim,
+batch32_ctx512_4096, batch64_fp8_ctx256_4096.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "draft blocks/sec and µs/propose (γ=16, L=8, vocab 248320); % HBM roofline"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(geo, ctx_rows, lm_rows_per_launch):
+    """Bytes a propose must move at least: every weight once, the KV it reads,
+    the embedding rows; and for one LM-head launch, the head plus its rows."""
+    h, I, L = geo.hidden, geo.intermediate, geo.num_layers
+    q_dim, kv_dim = geo.num_q_heads * geo.head_dim, geo.num_kv_heads * geo.head_dim
+    layer_w = L * ((q_dim + 2 * kv_dim) * h + h * q_dim + 2 * I * h + h * I) * 2
+    fp8 = geo.lm_head_dtype == "fp8"
+    lm = geo.vocab * h * (1 if fp8 else 2) + (geo.vocab * 4 if fp8 else 0)
+    kv_elem = 1 if geo.kv_dtype == "fp8" else 2
+    kv = sum(min(c, geo.ctx_window) for c in ctx_rows) * L * 2 * kv_dim * kv_elem
+    n = len(ctx_rows)
+    embed = n * geo.gamma * h * 2
+    lm_launch = lm + lm_rows_per_launch * h * 2
+    return layer_w + lm + kv + embed, lm_launch
+
+
+def precompute_bytes(geo, rows):
+    h = geo.hidden
+    fc_in = geo.num_target_layers * geo.target_hidden
+    fkv = geo.num_layers * 2 * geo.num_kv_heads * geo.head_dim
+    kv_elem = 1 if geo.kv_dtype == "fp8" else 2
+    return (h * fc_in + fkv * h) * 2 + rows * fc_in * 2 + rows * fkv * kv_elem
+
+
+class Workload:
+    """Head, states and inputs of one workload, plus its step."""
+
+    def __init__(self, name, steps_planned):
+        import numpy as np
+        import synth
+        from block_diffusion_draft_03_amd import Head
+        self.wl = synth.WORKLOADS[name]
+        wl = self.wl
+        geo = wl.geo
+        self.geo = geo
+        log(f"[bench] {name}: generating weights")
+        self.weights = synth.make_weights(geo)
+        n = wl.n_seqs
+        self.lens = [wl.ctx_lo] * n if wl.ctx_lo == wl.ctx_hi else [int(x) for x in synth.make_ctx_lengths(n, wl.ctx_lo, wl.ctx_hi)]
+        grow = wl.new_rows * (steps_planned + 2) if wl.trim else wl.new_rows
+        blocks = sum((c + grow + 15) // 16 for c in self.lens) + 16
+        log(f"[bench] building head (pool {blocks} blocks)")
+        self.head = Head(geo, self.weights, kv_pool_blocks=blocks, max_batch=max(1, n), max_seq_len=8192)
+        self.states = []
+        for i, c in enumerate(self.lens):
+            budget = c + grow
+            ids = None
+            if wl.permute_blocks:
+                nb = (budget + 15) // 16
+                ids = synth.make_block_permutation(nb, blocks, tag=i)
+            st = self.head.state_create(budget_tokens=budget, block_ids=ids)
+            self.head.precompute([st], [c], synth.make_stack(geo, c, tag=i))
+            self.head.after_verify(st, c)
+            self.states.append(st)
+        import torch
+        dev = lambda a: torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda()
+        self.new_stack = dev(np.concatenate([synth.make_stack(geo, wl.new_rows, tag=10000 + i) for i in range(n)]))
+        self.tokens = synth.make_tokens(geo, n)
+        self.masks = None
+        if wl.mask_frac > 0:
+            self.masks = dev(np.stack([synth.make_bitmask(geo.vocab, wl.mask_frac, tag=i) for i in range(n)]))
+        self.accepted = synth.make_accepted(steps_planned + 64, wl.new_rows)
+        self.k = 0
+        torch.cuda.synchronize()
+
+    def propose(self):
+        wl = self.wl
+        if wl.n_seqs == 1:
+            st = self.states[0]
+            return self.head.propose(st, int(self.tokens[0]), st.ctx_len, self.geo.gamma - 1,
+                                     bitmask=None if self.masks is None else self.masks[0])
+        pos = [s.ctx_len for s in self.states]
+        return self.head.propose_batch(self.states, self.tokens, pos, self.geo.gamma - 1, bitmasks=self.masks)
+
+    def step(self):
+        wl = self.wl
+        n = wl.n_seqs
+        self.head.precompute(self.states, [wl.new_rows] * n, self.new_stack)
+        if wl.trim:
+            a = int(self.accepted[self.k % len(self.accepted)])
+            for st in self.states:
+                self.head.after_verify(st, a)
+            out = self.propose()
+        else:
+            out = self.propose()
+            for st in self.states:
+                self.head.after_verify(st, 0)
+        self.k += 1
+        return out
+
+
+def time_loop(fn, steps):
+    import torch
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    a.record()
+    for _ in range(steps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return a.elapsed_time(b) / steps, wall
+
+
+def cpu_baseline(wl_obj, budget_s=12.0, max_seqs=2):
+    """Time the float64 oracle on the host on a bounded sample: at most
+    max_seqs sequences of the workload, whole steps (precompute of the new
+    rows + propose + trim), for about budget_s seconds after one warm-up."""
+    import numpy as np
+    import synth
+    from oracle.dflash import OracleHead
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    wl = wl_obj.wl
+    geo = wl_obj.geo
+    log("[bench] cpu baseline: oracle setup")
+    orc = OracleHead(geo.as_dict(), wl_obj.weights)
+    idx = list(range(min(max_seqs, wl.n_seqs)))
+    states = []
+    for i in idx:
+        st = orc.new_state()
+        orc.precompute(st, synth.make_stack(geo, wl_obj.lens[i], tag=i))
+        orc.after_verify(st, wl_obj.lens[i])
+        states.append(st)
+    news = [synth.make_stack(geo, wl.new_rows, tag=10000 + i) for i in idx]
+    masks = [synth.make_bitmask(geo.vocab, wl.mask_frac, tag=i) if wl.mask_frac > 0 else None for i in idx]
+
+    def step():
+        for j, st in enumerate(states):
+            orc.precompute(st, news[j])
+            orc.propose(st, int(wl_obj.tokens[idx[j]]), st.ctx_len, geo.gamma - 1, masks[j])
+            orc.after_verify(st, 0)
+
+    step()
+    t0 = time.perf_counter()
+    k = 0
+    while True:
+        step()
+        k += 1
+        if time.perf_counter() - t0 >= budget_s or k >= 50:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(k * len(idx) / dt, 4), "unit": "blocks/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{k} steps x {len(idx)} sequence(s) of {wl.name} (precompute {wl.new_rows} rows + "
+                      f"propose + trim), float64 numpy, {dt:.1f} s"}
+
+
+def copy_calibration(mib):
+    """A plain device-to-device copy of known size, for scaling PMC byte
+    counters (FETCH_SIZE / WRITE_SIZE) against what they read for it."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_each_way": n * 4, "launches": 3}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="single_ctx1024")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the propose path is data-parallel over sequences and each GPU "
+              f"would run its own head; --gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+
+    w = Workload(args.workload, args.steps + args.warmup)
+    geo, wl = w.geo, w.wl
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        w.step()
+    torch.cuda.synchronize()
+
+    log(f"[bench] timing {args.steps} steps")
+    w.head.timing_enable(True)
+    w.head.timing_read(0)
+    w.head.timing_read(1)
+    w.head.timing_read(2)
+    ms_step, wall = time_loop(w.step, args.steps)
+    lm_ms, lm_launches = w.head.timing_read(0)
+    prop_ms, prop_n = w.head.timing_read(1)
+    pre_ms, pre_n = w.head.timing_read(2)
+    w.head.timing_enable(False)
+    # forward alone, uninstrumented
+    ms_prop, _ = time_loop(w.propose, args.steps)
+
+    ctx_rows = [s.ctx_len + (0 if wl.trim else wl.new_rows) for s in w.states]
+    rows = wl.n_seqs * geo.gamma
+    lm_rows = min(64, rows)
+    fwd_bytes, lm_bytes = algorithmic_bytes(geo, ctx_rows, lm_rows)
+    lm_avg_s = lm_ms / max(1, lm_launches) / 1e3
+    lm_gbs = lm_bytes / lm_avg_s / 1e9
+    blocks_per_s = wl.n_seqs / (ms_step / 1e3)
+    out = {
+        "metric": METRIC,
+        "value": round(blocks_per_s, 3),
+        "unit": "blocks/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if geo.lm_head_dtype == "bf16" else "bf16+fp8",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "n_seqs": wl.n_seqs, "ctx_rows": ctx_rows if wl.n_seqs <= 4 else
+                   [min(ctx_rows), max(ctx_rows)], "gamma": geo.gamma, "layers": geo.num_layers,
+                   "vocab": geo.vocab, "hidden": geo.hidden, "new_rows_per_step": wl.new_rows,
+                   "lm_head": geo.lm_head_dtype, "kv_cache": geo.kv_dtype,
+                   "grammar_mask": wl.mask_frac, "parallelism": "none"},
+        "us_per_propose": round(ms_prop * 1e3, 2),
+        "us_per_propose_in_step": round(prop_ms / max(1, prop_n) * 1e3, 2),
+        "us_per_precompute": round(pre_ms / max(1, pre_n) * 1e3, 2),
+        "propose_hbm_frac": round(fwd_bytes / (ms_prop / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+        "propose_algorithmic_bytes": fwd_bytes,
+        "roofline": {"kernel": "k_lm_head (LM-head GEMM + argmax stage 1)", "bound": "hbm",
+                     "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(lm_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": lm_bytes, "avg_launch_us": round(lm_avg_s * 1e6, 2),
+                     "launches": lm_launches},
+        "wall_s_timed": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+    for st in w.states:
+        st.free()
+    w.head.destroy()
+
+
+if __name__ == "__main__":
+    main()

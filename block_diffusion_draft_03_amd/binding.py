@@ -22,8 +22,9 @@ EXPORTED_SYMBOLS = (
     "dflash_build", "dflash_destroy", "dflash_block_gamma", "dflash_propose_batch_max",
     "dflash_state_create", "dflash_state_free", "dflash_state_ctx_len", "dflash_precompute_ctx_kv",
     "dflash_propose", "dflash_propose_batch", "dflash_after_verify", "dflash_state_read_kv",
-    "dflash_read_lm_head_fp8", "dflash_last_error",
+    "dflash_read_lm_head_fp8", "dflash_timing_enable", "dflash_timing_read", "dflash_last_error",
 )
+PHASE_LM_HEAD, PHASE_PROPOSE, PHASE_PRECOMPUTE = 0, 1, 2
 
 
 class DflashError(RuntimeError):
@@ -84,6 +85,8 @@ def load_library(path=None):
         "dflash_after_verify": ([vp, vp, i32], C.c_int),
         "dflash_state_read_kv": ([vp, vp, i32, i32, i32, vp, vp, u64], C.c_int),
         "dflash_read_lm_head_fp8": ([vp, vp, vp, u64], C.c_int),
+        "dflash_timing_enable": ([vp, C.c_int], C.c_int),
+        "dflash_timing_read": ([vp, i32, C.POINTER(C.c_double), C.POINTER(C.c_int64)], C.c_int),
         "dflash_last_error": ([], C.c_char_p),
     }
     for name, (args, res) in sig.items():
@@ -276,6 +279,16 @@ class Head:
         _check(self.lib, self.lib.dflash_read_lm_head_fp8(self.handle, _ptr(codes), _ptr(scale),
                                                           _stream_handle(stream)))
         return codes, scale
+
+    def timing_enable(self, on=True):
+        _check(self.lib, self.lib.dflash_timing_enable(self.handle, 1 if on else 0))
+
+    def timing_read(self, phase):
+        """(total milliseconds, intervals) recorded for a phase since the last read."""
+        ms = C.c_double()
+        n = C.c_int64()
+        _check(self.lib, self.lib.dflash_timing_read(self.handle, int(phase), C.byref(ms), C.byref(n)))
+        return ms.value, n.value
 
     def destroy(self):
         if getattr(self, "handle", None):

@@ -86,6 +86,33 @@ struct dflash_head {
   float *pre_u = nullptr;
   uint16_t *pre_c = nullptr;
 
+  // benchmark timing: recorded (start, stop) event pairs per phase
+  bool timing = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> timed[3];
+  std::vector<hipEvent_t> event_pool;
+
+  hipEvent_t take_event() {
+    if (!event_pool.empty()) {
+      hipEvent_t e = event_pool.back();
+      event_pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+
+  // Open an interval of `phase` on stream s; returns the stop event to
+  // record at the end, or nullptr when timing is off.
+  hipEvent_t interval_begin(int phase, hipStream_t s) {
+    if (!timing) return nullptr;
+    hipEvent_t a = take_event(), b = take_event();
+    if (!a || !b) return nullptr;
+    if (hipEventRecord(a, s) != hipSuccess) return nullptr;
+    timed[phase].push_back({a, b});
+    return b;
+  }
+
   template <class T>
   int alloc(T **p, size_t count) {
     void *q = nullptr;
@@ -303,6 +330,7 @@ int propose_impl(dflash_head *H, dflash_state *const *states, int n, const uint3
   }
   const int M = n * g.gamma;
   const int h = g.h;
+  hipEvent_t t_all = H->interval_begin(DFLASH_PHASE_PROPOSE, st);
 
   SetupArgs sa{};
   sa.embed = H->embed;
@@ -402,7 +430,9 @@ int propose_impl(dflash_head *H, dflash_state *const *states, int n, const uint3
     la.M = std::min(GEMM_MAX_ROWS, M - r0);
     la.row0 = r0;
     la.logits = logits ? logits + (size_t)r0 * g.V : nullptr;
+    hipEvent_t t_lm = H->interval_begin(DFLASH_PHASE_LM_HEAD, st);
     HIP_TRY(launch_lm_head(g.head_fp8, la, st));
+    if (t_lm) HIP_TRY(hipEventRecord(t_lm, st));
   }
   LmFinishArgs fa{};
   fa.part_mx = H->lm_mx;
@@ -416,6 +446,7 @@ int propose_impl(dflash_head *H, dflash_state *const *states, int n, const uint3
   fa.conf = conf;
   fa.row_prob = row_prob;
   HIP_TRY(launch_lm_finish(fa, n, st));
+  if (t_all) HIP_TRY(hipEventRecord(t_all, st));
   return DFLASH_OK;
 }
 
@@ -471,6 +502,12 @@ void dflash_destroy(dflash_head *head) {
     delete s;
   }
   head->states.clear();
+  for (auto &q : head->timed)
+    for (auto &p : q) {
+      (void)hipEventDestroy(p.first);
+      (void)hipEventDestroy(p.second);
+    }
+  for (hipEvent_t e : head->event_pool) (void)hipEventDestroy(e);
   free_head_memory(head);
   head->magic = DEAD_MAGIC;
   delete head;
@@ -581,6 +618,7 @@ int dflash_precompute_ctx_kv(dflash_head *head, dflash_state *const *states, int
       bts.push_back(states[i]->d_bt);
     }
   const int h = g.h;
+  hipEvent_t t_all = H->interval_begin(DFLASH_PHASE_PRECOMPUTE, st);
   for (int r0 = 0; r0 < (int)total; r0 += GEMM_MAX_ROWS) {
     const int m = std::min<int>(GEMM_MAX_ROWS, (int)total - r0);
     EpiArgs e{};
@@ -602,6 +640,7 @@ int dflash_precompute_ctx_kv(dflash_head *head, dflash_state *const *states, int
     }
     TRY(gemm_rows(H, EPI_KV_SCATTER, H->pre_c, h, m, H->w_fkv, g.fkv_dim, h, e, st));
   }
+  if (t_all) HIP_TRY(hipEventRecord(t_all, st));
   for (int i = 0; i < n; ++i) states[i]->rows.ctx_len += n_new[i];
   return DFLASH_OK;
 }
@@ -648,6 +687,44 @@ int dflash_state_read_kv(dflash_head *head, const dflash_state *st, int32_t laye
   if (n_rows == 0) return DFLASH_OK;
   HIP_TRY(launch_read_kv(head->kv_pool, st->d_bt, g.L, layer, g.n_kv, g.d, (int)head->kv_elem, row0, n_rows, k_out,
                          v_out, to_stream(stream)));
+  return DFLASH_OK;
+}
+
+int dflash_timing_enable(dflash_head *head, int enable) {
+  if (!head_ok(head)) return set_err(DFLASH_E_INVALID, "invalid head");
+  std::lock_guard<std::mutex> lk(head->mu);
+  head->timing = enable != 0;
+  if (!head->timing) {
+    for (auto &q : head->timed) {
+      for (auto &p : q) {
+        (void)hipEventSynchronize(p.second);
+        head->event_pool.push_back(p.first);
+        head->event_pool.push_back(p.second);
+      }
+      q.clear();
+    }
+  }
+  return DFLASH_OK;
+}
+
+int dflash_timing_read(dflash_head *head, int32_t phase, double *total_ms, int64_t *intervals) {
+  if (!head_ok(head)) return set_err(DFLASH_E_INVALID, "invalid head");
+  std::lock_guard<std::mutex> lk(head->mu);
+  if (phase < 0 || phase > 2 || !total_ms || !intervals) return set_err(DFLASH_E_INVALID, "bad phase or outputs");
+  double sum = 0.0;
+  int64_t n = 0;
+  for (auto &p : head->timed[phase]) {
+    HIP_TRY(hipEventSynchronize(p.second));
+    float ms = 0.0f;
+    HIP_TRY(hipEventElapsedTime(&ms, p.first, p.second));
+    sum += ms;
+    ++n;
+    head->event_pool.push_back(p.first);
+    head->event_pool.push_back(p.second);
+  }
+  head->timed[phase].clear();
+  *total_ms = sum;
+  *intervals = n;
   return DFLASH_OK;
 }
 

@@ -215,6 +215,20 @@ int dflash_state_read_kv(dflash_head *head, const dflash_state *st, int32_t laye
  * DFLASH_E_INVALID on a bf16 head. */
 int dflash_read_lm_head_fp8(dflash_head *head, void *codes_out, float *scale_out, uint64_t stream);
 
+/* Kernel timing for benchmarks. While enabled, each propose and precompute
+ * call records HIP events on its own stream around: DFLASH_PHASE_LM_HEAD,
+ * the LM-head stage-1 launches (the dominant weight stream);
+ * DFLASH_PHASE_PROPOSE, all launches of a propose; DFLASH_PHASE_PRECOMPUTE,
+ * all launches of a precompute. dflash_timing_read waits for the recorded
+ * events, returns the summed elapsed milliseconds and the number of timed
+ * intervals of one phase, and clears that phase. Disabling drops pending
+ * records. Recording adds one event pair per interval to the stream. */
+#define DFLASH_PHASE_LM_HEAD 0
+#define DFLASH_PHASE_PROPOSE 1
+#define DFLASH_PHASE_PRECOMPUTE 2
+int dflash_timing_enable(dflash_head *head, int enable);
+int dflash_timing_read(dflash_head *head, int32_t phase, double *total_ms, int64_t *intervals);
+
 /* Message of the calling thread's last error ("" if none). */
 const char *dflash_last_error(void);
 

@@ -40,6 +40,13 @@ def check_propose(gpu, ref, bitmask=None, logit_tol=2e-2, label=""):
     mism = np.flatnonzero(pinned & (ids != ref["ids"]))
     assert mism.size == 0, f"{label} ids differ on pinned rows {mism.tolist()}: gpu {ids[mism]} ref {ref['ids'][mism]}"
     assert np.abs(rp - ref["row_prob"]).max() <= CONF_TOL, f"{label} row_prob err {np.abs(rp - ref['row_prob']).max()}"
+    # p1 = 1 / sum exp(l - max): a logit error e moves log p1 by at most 2e,
+    # so the logit tolerance bounds the relative error of p1 as well
+    live = ~empty
+    if live.any():
+        lim = 2 * logit_tol * np.abs(lr[live]).max(axis=1)
+        dlog = np.abs(np.log(rp[live]) - np.log(ref["row_prob"][live]))
+        assert np.all(dlog <= lim), f"{label} log p1 err {dlog.max():.3e}"
     assert abs(conf - ref["conf"]) <= CONF_TOL, f"{label} conf gpu {conf} ref {ref['conf']}"
     agree_unpinned = int(((~pinned) & (ids == ref["ids"])).sum())
     return int(pinned.sum()), agree_unpinned, len(ids)

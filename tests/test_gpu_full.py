@@ -1,0 +1,200 @@
+"""GPU parity at the full DFlash geometry (8 layers, hidden 2048, 32q/4kv
+heads of 128, intermediate 6144, vocab 248320, block 16, 5 x 2048 hidden
+stack), in the launch configuration the benchmark times, against the float64
+oracle on the same seeded inputs:
+
+* single sequence, 1024 ctx rows, 8 new rows per step;
+* single sequence, 4096 ctx rows in a permuted block table, 16-row verify
+  appends trimmed by after_verify with num_accepted ~ U[0, 16];
+* batch of 32 sequences, ctx ~ U[512, 4096], 8 new rows each (sampled
+  sequences checked one by one against the oracle);
+* batch of 64 with the FP8 LM-head mirror, FP8 KV cache and 50% grammar
+  bitmasks (mirror codes bit-exact on sampled rows; sampled sequences).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+from oracle.dflash import OracleHead, fp8_head_mirror
+from oracle.numerics import bf16_to_f64, e4m3_decode
+from parity import check_propose, split_batch
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+torch = pytest.importorskip("torch")
+
+GEO = synth.FULL
+GEO8 = synth.FULL_FP8
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def weights():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    say("[setup] full-geometry weights")
+    return synth.make_weights(GEO8)  # same matrices as GEO, plus FP8 KV scales
+
+
+@pytest.fixture(scope="module")
+def bf16_pair(weights):
+    from block_diffusion_draft_03_amd import Head
+    say("[setup] bf16 head + oracle")
+    head = Head(GEO, weights, kv_pool_blocks=9000, max_batch=32, max_seq_len=8192)
+    orc = OracleHead(GEO.as_dict(), weights)
+    yield head, orc
+    head.destroy()
+
+
+def _fill(head, orc, n_rows, tag, block_ids=None, budget=None, oracle=True):
+    st = head.state_create(budget_tokens=budget, block_ids=block_ids)
+    os_ = orc.new_state() if oracle else None
+    stack = synth.make_stack(GEO, n_rows, tag=tag)
+    head.precompute([st], [n_rows], stack)
+    head.after_verify(st, n_rows)
+    if oracle:
+        orc.precompute(os_, stack)
+        orc.after_verify(os_, n_rows)
+    return st, os_
+
+
+def test_full_single_ctx1024(bf16_pair):
+    head, orc = bf16_pair
+    st, os_ = _fill(head, orc, 1024, tag=1)
+    pinned = total = 0
+    for step in range(2):
+        new = synth.make_stack(GEO, 8, tag=1000 + step)
+        head.precompute([st], [8], new)
+        orc.precompute(os_, new)
+        tok = int(synth.make_tokens(GEO, 1, tag=step)[0])
+        say(f"[case] single ctx1024 step {step} ctx {st.ctx_len} tok {tok}")
+        res = head.propose(st, tok, st.ctx_len, GEO.gamma - 1, logits=True)
+        torch.cuda.synchronize()
+        p, _, n = check_propose(res, orc.propose(os_, tok, os_.ctx_len, GEO.gamma - 1), label=f"step {step}")
+        pinned += p
+        total += n
+        head.after_verify(st, 0)
+        orc.after_verify(os_, 0)
+    say(f"[result] ctx1024: {pinned}/{total} rows margin-pinned, all pinned ids equal")
+    # cached K/V of sampled rows and layers
+    for layer in (0, 7):
+        k, v = head.read_kv(st, layer, 1000, 24)
+        torch.cuda.synchronize()
+        kg = bf16_to_f64(k.cpu().numpy().view(np.uint16))
+        kr = np.stack(os_.k[layer][1000:1024])
+        vg = bf16_to_f64(v.cpu().numpy().view(np.uint16))
+        vr = np.stack(os_.v[layer][1000:1024])
+        assert np.abs(kg - kr).max() <= 2e-2 * np.abs(kr).max(), layer
+        assert np.abs(vg - vr).max() <= 2e-2 * np.abs(vr).max(), layer
+    st.free()
+
+
+def test_full_single_ctx4096_permuted_trim(bf16_pair):
+    head, orc = bf16_pair
+    steps = 2
+    n_blocks = (4096 + 16 * steps) // 16
+    perm = synth.make_block_permutation(n_blocks, 9000 - 64 * 3, tag=5) + 64 * 3
+    st, os_ = _fill(head, orc, 4096, tag=2, block_ids=perm)
+    acc = synth.make_accepted(steps, 16)
+    for step in range(steps):
+        new = synth.make_stack(GEO, 16, tag=2000 + step)
+        head.precompute([st], [16], new)
+        orc.precompute(os_, new)
+        head.after_verify(st, int(acc[step]))
+        orc.after_verify(os_, int(acc[step]))
+        tok = int(synth.make_tokens(GEO, 1, tag=50 + step)[0])
+        say(f"[case] ctx4096 step {step} accepted {acc[step]} ctx {st.ctx_len}")
+        res = head.propose(st, tok, st.ctx_len, GEO.gamma - 1, logits=True)
+        torch.cuda.synchronize()
+        check_propose(res, orc.propose(os_, tok, os_.ctx_len, GEO.gamma - 1), label=f"ctx4096 step {step}")
+    st.free()
+
+
+def test_full_batch32(bf16_pair):
+    head, orc = bf16_pair
+    n = 32
+    lens = synth.make_ctx_lengths(n, 512, 4096)
+    sample = [0, 7, int(np.argmax(lens)), int(np.argmin(lens))]
+    states, ostates = [], {}
+    for i in range(n):
+        st, os_ = _fill(head, orc, int(lens[i]), tag=300 + i, oracle=i in sample)
+        states.append(st)
+        if i in sample:
+            ostates[i] = os_
+    news = [synth.make_stack(GEO, 8, tag=3000 + i) for i in range(n)]
+    head.precompute(states, [8] * n, np.concatenate(news))
+    for i in sample:
+        orc.precompute(ostates[i], news[i])
+    toks = synth.make_tokens(GEO, n, tag=77)
+    pos = [s.ctx_len for s in states]
+    say("[case] batch32 propose")
+    res = head.propose_batch(states, toks, pos, GEO.gamma - 1, logits=True)
+    torch.cuda.synchronize()
+    for i in sample:
+        say(f"[case] batch32 seq {i} ctx {pos[i]}")
+        ref = orc.propose(ostates[i], int(toks[i]), pos[i], GEO.gamma - 1)
+        check_propose(split_batch(res, i), ref, label=f"batch32 seq {i}")
+    for s in states:
+        s.free()
+
+
+def test_full_batch64_fp8(weights):
+    from block_diffusion_draft_03_amd import Head
+    say("[setup] fp8 head")
+    head = Head(GEO8, weights, kv_pool_blocks=16800, max_batch=64, max_seq_len=8192)
+    # the mirror's codes and scales, bit for bit, on sampled rows
+    codes, scale = head.read_lm_head_fp8()
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(3).choice(GEO.vocab, 2048, replace=False))
+    rows = np.concatenate([rows, [0, GEO.vocab - 1]])
+    rc, rs = fp8_head_mirror(weights["lm_head"][rows])
+    gc = codes.cpu().numpy()[rows]
+    gs = scale.cpu().numpy()[rows]
+    assert np.array_equal(gs, rs)
+    # codes may differ only in the sign of a zero
+    assert np.array_equal(e4m3_decode(gc), e4m3_decode(rc))
+    del codes, scale
+    say("[setup] fp8 oracle")
+    orc = OracleHead(GEO8.as_dict(), weights)
+    n = 64
+    lens = synth.make_ctx_lengths(n, 256, 4096, tag=1)
+    sample = [3, int(np.argmax(lens)), int(np.argmin(lens))]
+    states, ostates = [], {}
+    for i in range(n):
+        st, os_ = _fill(head, orc, int(lens[i]), tag=600 + i, oracle=i in sample)
+        states.append(st)
+        if i in sample:
+            ostates[i] = os_
+    news = [synth.make_stack(GEO, 8, tag=6000 + i) for i in range(n)]
+    head.precompute(states, [8] * n, np.concatenate(news))
+    for i in sample:
+        orc.precompute(ostates[i], news[i])
+    # FP8 cache of sampled rows: the GPU's K differs from the oracle's by the
+    # bf16 rounding of its GEMM inputs, about 2e-3 absolute (K elements are
+    # ~N(0, 0.9)); after quantisation the two may sit one E4M3 step apart
+    # plus that error. About 94% of the codes are identical.
+    k, _ = head.read_kv(states[sample[0]], 2, 0, 64)
+    torch.cuda.synchronize()
+    sk = weights["kv_scale"][2, 0].astype(np.float64)
+    kg = e4m3_decode(k.cpu().numpy()) * sk[None, :, None]
+    kr = np.stack(ostates[sample[0]].k[2][:64])
+    step = np.maximum(np.abs(kr) * 2.0 ** -3, sk[None, :, None] * 2.0 ** -9)
+    assert np.all(np.abs(kg - kr) <= step + 1e-2)
+    assert np.mean(kg == kr) > 0.9
+    masks = np.stack([synth.make_bitmask(GEO.vocab, 0.5, tag=i) for i in range(n)])
+    toks = synth.make_tokens(GEO, n, tag=88)
+    pos = [s.ctx_len for s in states]
+    say("[case] batch64 fp8 propose")
+    res = head.propose_batch(states, toks, pos, GEO.gamma - 1, bitmasks=masks, logits=True)
+    torch.cuda.synchronize()
+    for i in sample:
+        say(f"[case] batch64 fp8 seq {i} ctx {pos[i]}")
+        ref = orc.propose(ostates[i], int(toks[i]), pos[i], GEO.gamma - 1, masks[i])
+        check_propose(split_batch(res, i), ref, bitmask=masks[i], logit_tol=6e-2, label=f"fp8 seq {i}")
+    for s in states:
+        s.free()
+    head.destroy()
