@@ -63,6 +63,7 @@ struct dflash_head {
 
   // repacked drafter weights (bf16 unless noted), layer-major
   uint16_t *w_qkv = nullptr, *w_o = nullptr, *w_gu = nullptr, *w_down = nullptr, *w_fc = nullptr, *w_fkv = nullptr;
+  size_t sz_qkv = 0, sz_o = 0, sz_gu = 0, sz_down = 0;  // tiled elements per layer
   float *g_in = nullptr, *g_post = nullptr, *g_hidden = nullptr, *g_final = nullptr;
   const uint16_t *embed = nullptr, *lm = nullptr;
   const uint8_t *lm8 = nullptr;
@@ -81,10 +82,13 @@ struct dflash_head {
   float *o_part = nullptr, *ml_part = nullptr;
   float *lm_mx = nullptr, *lm_se = nullptr;
   uint32_t *lm_idx = nullptr;
+  float *lm_p1 = nullptr;
+  int *fin_counters = nullptr;
   int lm_P = 0;
   int attn_slots = 0;
   float *pre_u = nullptr;
   uint16_t *pre_c = nullptr;
+  float *part = nullptr;  // split-K partial sums [splits][rows][h]
 
   // benchmark timing: recorded (start, stop) event pairs per phase
   bool timing = false;
@@ -172,66 +176,88 @@ int build_impl(dflash_head *H, const dflash_weights *w, hipStream_t st) {
         return set_err(DFLASH_E_INVALID, "weights: kv_scale entries must be finite and > 0");
   }
 
-  // drafter tensors -> bf16, repacked
-  TRY(H->alloc(&H->w_qkv, (size_t)g.L * g.qkv_dim * h));
-  TRY(H->alloc(&H->w_o, (size_t)g.L * h * g.q_dim));
-  TRY(H->alloc(&H->w_gu, (size_t)g.L * 2 * g.I * h));
-  TRY(H->alloc(&H->w_down, (size_t)g.L * h * g.I));
-  TRY(H->alloc(&H->w_fc, h * g.fc_in));
-  TRY(H->alloc(&H->w_fkv, (size_t)g.fkv_dim * h));
+  // drafter tensors -> bf16, repacked into the tile-major GEMM layout
+  H->sz_qkv = tiled_elems(g.qkv_dim, g.h);
+  H->sz_o = tiled_elems(g.h, g.q_dim);
+  H->sz_gu = tiled_elems(2 * g.I, g.h);
+  H->sz_down = tiled_elems(g.h, g.I);
+  TRY(H->alloc(&H->w_qkv, (size_t)g.L * H->sz_qkv));
+  TRY(H->alloc(&H->w_o, (size_t)g.L * H->sz_o));
+  TRY(H->alloc(&H->w_gu, (size_t)g.L * H->sz_gu));
+  TRY(H->alloc(&H->w_down, (size_t)g.L * H->sz_down));
+  TRY(H->alloc(&H->w_fc, tiled_elems(g.h, g.fc_in)));
+  TRY(H->alloc(&H->w_fkv, tiled_elems(g.fkv_dim, g.h)));
   TRY(H->alloc(&H->g_in, (size_t)g.L * h));
   TRY(H->alloc(&H->g_post, (size_t)g.L * h));
   TRY(H->alloc(&H->g_hidden, h));
   TRY(H->alloc(&H->g_final, h));
+  const int d = g.d;
   for (int l = 0; l < g.L; ++l) {
     const dflash_layer_weights &lw = w->layers[l];
-    uint16_t *qkv = H->w_qkv + (size_t)l * g.qkv_dim * h;
-    HIP_TRY(launch_convert_rows(qkv, lw.q, nullptr, g.q_dim, g.h, f32, false, st));
-    HIP_TRY(launch_convert_rows(qkv + (size_t)g.q_dim * h, lw.k, nullptr, g.kv_dim, g.h, f32, false, st));
-    HIP_TRY(launch_convert_rows(qkv + (size_t)(g.q_dim + g.kv_dim) * h, lw.v, nullptr, g.kv_dim, g.h, f32, false, st));
-    HIP_TRY(launch_convert_rows(H->w_o + (size_t)l * h * g.q_dim, lw.o, nullptr, g.h, g.q_dim, f32, false, st));
-    HIP_TRY(launch_convert_rows(H->w_gu + (size_t)l * 2 * g.I * h, lw.gate, lw.up, 2 * g.I, g.h, f32, true, st));
-    HIP_TRY(launch_convert_rows(H->w_down + (size_t)l * h * g.I, lw.down, nullptr, g.h, g.I, f32, false, st));
-    // fused ctx K/V weight: rows [K0; V0; K1; V1; ...]
-    uint16_t *fk = H->w_fkv + (size_t)(2 * l) * g.kv_dim * h;
-    HIP_TRY(launch_convert_rows(fk, lw.k, nullptr, g.kv_dim, g.h, f32, false, st));
-    HIP_TRY(launch_convert_rows(fk + (size_t)g.kv_dim * h, lw.v, nullptr, g.kv_dim, g.h, f32, false, st));
+    // [Q; K; V] with Q and K rows in RoPE pair order
+    uint16_t *qkv = H->w_qkv + (size_t)l * H->sz_qkv;
+    HIP_TRY(launch_tile_rows(qkv, 0, lw.q, nullptr, g.q_dim, g.h, f32, ROWS_ROPE_PAIRS, d, st));
+    HIP_TRY(launch_tile_rows(qkv, g.q_dim, lw.k, nullptr, g.kv_dim, g.h, f32, ROWS_ROPE_PAIRS, d, st));
+    HIP_TRY(launch_tile_rows(qkv, g.q_dim + g.kv_dim, lw.v, nullptr, g.kv_dim, g.h, f32, ROWS_SAME, d, st));
+    HIP_TRY(launch_tile_rows(H->w_o + (size_t)l * H->sz_o, 0, lw.o, nullptr, g.h, g.q_dim, f32, ROWS_SAME, d, st));
+    HIP_TRY(launch_tile_rows(H->w_gu + (size_t)l * H->sz_gu, 0, lw.gate, lw.up, 2 * g.I, g.h, f32, ROWS_GATE_UP, d, st));
+    HIP_TRY(launch_tile_rows(H->w_down + (size_t)l * H->sz_down, 0, lw.down, nullptr, g.h, g.I, f32, ROWS_SAME, d, st));
+    // fused ctx K/V weight: rows [K0; V0; K1; V1; ...] (K rows in RoPE pair order)
+    HIP_TRY(launch_tile_rows(H->w_fkv, 2 * l * g.kv_dim, lw.k, nullptr, g.kv_dim, g.h, f32, ROWS_ROPE_PAIRS, d, st));
+    HIP_TRY(launch_tile_rows(H->w_fkv, (2 * l + 1) * g.kv_dim, lw.v, nullptr, g.kv_dim, g.h, f32, ROWS_SAME, d, st));
     HIP_TRY(launch_to_f32(H->g_in + (size_t)l * h, lw.in_norm, g.h, f32, st));
     HIP_TRY(launch_to_f32(H->g_post + (size_t)l * h, lw.post_norm, g.h, f32, st));
   }
-  HIP_TRY(launch_convert_rows(H->w_fc, w->fc, nullptr, g.h, g.fc_in, f32, false, st));
+  HIP_TRY(launch_tile_rows(H->w_fc, 0, w->fc, nullptr, g.h, g.fc_in, f32, ROWS_SAME, d, st));
   HIP_TRY(launch_to_f32(H->g_hidden, w->hidden_norm, g.h, f32, st));
   HIP_TRY(launch_to_f32(H->g_final, w->norm, g.h, f32, st));
 
-  // target's shared tensors: borrowed when bf16
+  // target's shared tensors: the embedding is borrowed when bf16 (rows are
+  // gathered); the LM head is streamed from a tiled copy the head owns
   if (f32) {
     uint16_t *e = nullptr;
     TRY(H->alloc(&e, (size_t)g.V * h));
-    HIP_TRY(launch_convert_rows(e, w->embed_tokens, nullptr, g.V, g.h, true, false, st));
+    HIP_TRY(launch_convert_rows(e, w->embed_tokens, nullptr, g.V, g.h, true, ROWS_SAME, d, st));
     H->embed = e;
-    if (w->lm_head) {
-      uint16_t *m = nullptr;
-      TRY(H->alloc(&m, (size_t)g.V * h));
-      HIP_TRY(launch_convert_rows(m, w->lm_head, nullptr, g.V, g.h, true, false, st));
-      H->lm = m;
-    }
   } else {
     H->embed = (const uint16_t *)w->embed_tokens;
-    H->lm = (const uint16_t *)w->lm_head;
   }
-  if (g.head_fp8) {
+  if (!g.head_fp8) {
+    uint16_t *m = nullptr;
+    TRY(H->alloc(&m, tiled_elems(g.V, g.h)));
+    HIP_TRY(launch_tile_rows(m, 0, w->lm_head, nullptr, g.V, g.h, f32, ROWS_SAME, d, st));
+    H->lm = m;
+  } else {
+    // E4M3 codes + per-row scales: the given native head, or a mirror of the
+    // bf16 head (amax / 448 per row); tiled into a copy the head owns
+    uint8_t *tiled = nullptr;
+    TRY(H->alloc(&tiled, tiled_elems(g.V, g.h)));
     if (w->lm_head_fp8) {
-      H->lm8 = (const uint8_t *)w->lm_head_fp8;
-      H->lm8_scale = w->lm_head_scale;
-    } else {
-      uint8_t *c = nullptr;
       float *s = nullptr;
-      TRY(H->alloc(&c, (size_t)g.V * h));
       TRY(H->alloc(&s, (size_t)g.V));
-      HIP_TRY(launch_fp8_mirror(H->lm, g.V, g.h, c, s, st));
-      H->lm8 = c;
+      HIP_TRY(hipMemcpyAsync(s, w->lm_head_scale, (size_t)g.V * sizeof(float), hipMemcpyDeviceToDevice, st));
+      HIP_TRY(launch_tile_fp8(tiled, (const uint8_t *)w->lm_head_fp8, g.V, g.h, st));
+      H->lm8_scale = s;
+    } else {
+      const uint16_t *src = (const uint16_t *)w->lm_head;
+      uint16_t *conv = nullptr;
+      if (f32) {  // bf16 view of an f32 head, for the mirror only
+        HIP_TRY(hipMalloc(&conv, (size_t)g.V * h * 2));
+        HIP_TRY(launch_convert_rows(conv, w->lm_head, nullptr, g.V, g.h, true, ROWS_SAME, d, st));
+        src = conv;
+      }
+      uint8_t *rowmajor = nullptr;
+      float *s = nullptr;
+      TRY(H->alloc(&s, (size_t)g.V));
+      HIP_TRY(hipMalloc(&rowmajor, (size_t)g.V * h));
+      HIP_TRY(launch_fp8_mirror(src, g.V, g.h, rowmajor, s, st));
+      HIP_TRY(launch_tile_fp8(tiled, rowmajor, g.V, g.h, st));
+      HIP_TRY(hipStreamSynchronize(st));
+      (void)hipFree(rowmajor);
+      if (conv) (void)hipFree(conv);
       H->lm8_scale = s;
     }
+    H->lm8 = tiled;
   }
 
   // RoPE inverse frequencies in double
@@ -263,16 +289,10 @@ int build_impl(dflash_head *H, const dflash_weights *w, hipStream_t st) {
   TRY(H->alloc(&H->attn, M * g.q_dim));
   TRY(H->alloc(&H->mlp, M * g.I));
   TRY(H->alloc(&H->cs, M * (g.d / 2)));
-  const int shapes[6][2] = {{g.qkv_dim, g.h}, {g.h, g.q_dim}, {2 * g.I, g.h}, {g.h, g.I}, {g.h, g.fc_in}, {g.fkv_dim, g.h}};
-  size_t ws = 0;
-  int groups = 0;
-  for (auto &sh : shapes) {
-    ws = std::max(ws, gemm_ws_floats(sh[0], sh[1]));
-    groups = std::max(groups, gemm_groups(sh[0]));
-  }
-  TRY(H->alloc(&H->ws, ws));
-  TRY(H->alloc(&H->counters, (size_t)groups));
-  HIP_TRY(hipMemsetAsync(H->counters, 0, (size_t)groups * sizeof(int), st));
+  // split-K partials of the GEMMs that feed the residual stream (N = h)
+  int max_splits = 1;
+  for (int K : {g.q_dim, g.I, g.fc_in}) max_splits = std::max(max_splits, gemm_plan(g.h, K, true).splits);
+  TRY(H->alloc(&H->part, (size_t)max_splits * std::max<size_t>(M, GEMM_MAX_ROWS) * h));
   const size_t R = (size_t)g.rep * g.gamma;
   H->attn_slots = std::max(ATTN_SLOTS, g.max_batch * g.n_kv);
   TRY(H->alloc(&H->o_part, (size_t)H->attn_slots * R * g.d));
@@ -281,6 +301,9 @@ int build_impl(dflash_head *H, const dflash_weights *w, hipStream_t st) {
   TRY(H->alloc(&H->lm_mx, (size_t)H->lm_P * M));
   TRY(H->alloc(&H->lm_se, (size_t)H->lm_P * M));
   TRY(H->alloc(&H->lm_idx, (size_t)H->lm_P * M));
+  TRY(H->alloc(&H->lm_p1, M));
+  TRY(H->alloc(&H->fin_counters, (size_t)g.max_batch));
+  HIP_TRY(hipMemsetAsync(H->fin_counters, 0, (size_t)g.max_batch * sizeof(int), st));
   TRY(H->alloc(&H->pre_u, (size_t)GEMM_MAX_ROWS * h));
   TRY(H->alloc(&H->pre_c, (size_t)GEMM_MAX_ROWS * h));
   HIP_TRY(hipStreamSynchronize(st));
@@ -288,17 +311,23 @@ int build_impl(dflash_head *H, const dflash_weights *w, hipStream_t st) {
 }
 
 // One GEMM over M rows in chunks of GEMM_MAX_ROWS. The epilogue output
-// pointers and the RoPE table are advanced with the rows.
+// pointers and the RoPE table are advanced with the rows. EPI_PARTIAL
+// outputs are laid out [splits][M][N] over all M rows of the call.
 int gemm_rows(dflash_head *H, int epi, const uint16_t *A, int lda, int M, const uint16_t *W, int N, int K,
-              EpiArgs e, hipStream_t st) {
+              EpiArgs e, hipStream_t st, int *splits_out = nullptr) {
   GemmArgs ga{};
   ga.lda = lda;
   ga.W = W;
   ga.N = N;
   ga.K = K;
-  gemm_plan(N, K, &ga.kslice, &ga.splits);
-  ga.ws = H->ws;
-  ga.counters = H->counters;
+  const GemmPlan p = gemm_plan(N, K, epi == EPI_PARTIAL);
+  ga.tn = p.tn;
+  ga.nw = p.nw;
+  ga.st = p.st;
+  ga.splits = p.splits;
+  ga.kslice = p.kslice;
+  if (splits_out) *splits_out = p.splits;
+  e.ld_split = M;
   const int half = H->g.d / 2;
   for (int r0 = 0; r0 < M; r0 += GEMM_MAX_ROWS) {
     ga.A = A + (size_t)r0 * lda;
@@ -307,8 +336,31 @@ int gemm_rows(dflash_head *H, int epi, const uint16_t *A, int lda, int M, const 
     if (e.out_f32) ec.out_f32 = e.out_f32 + (size_t)r0 * e.ldo;
     if (e.out_bf16) ec.out_bf16 = e.out_bf16 + (size_t)r0 * e.ldo;
     if (e.cs) ec.cs = e.cs + (size_t)r0 * half;
-    HIP_TRY(launch_gemm(epi, false, ga, ec, st));
+    HIP_TRY(launch_gemm(epi, ga, ec, st));
   }
+  return DFLASH_OK;
+}
+
+// h += W A^T for a GEMM into the residual stream (split over K, then the
+// splits are added in order), followed by out = bf16(RMSNorm(h) * gain).
+int resid_gemm(dflash_head *H, const uint16_t *A, int lda, int M, const uint16_t *W, int K, float *h,
+               const float *gain, uint16_t *out, bool init_zero, hipStream_t st) {
+  EpiArgs e{};
+  e.out_f32 = H->part;
+  e.ldo = H->g.h;
+  int splits = 1;
+  TRY(gemm_rows(H, EPI_PARTIAL, A, lda, M, W, H->g.h, K, e, st, &splits));
+  ResidNormArgs r{};
+  r.h = h;
+  r.part = H->part;
+  r.splits = splits;
+  r.ld_split = M;
+  r.n = H->g.h;
+  r.init_zero = init_zero ? 1 : 0;
+  r.gain = gain;
+  r.eps = H->cfg.rms_eps;
+  r.out = out;
+  HIP_TRY(launch_resid_norm(r, M, st));
   return DFLASH_OK;
 }
 
@@ -384,9 +436,10 @@ int propose_impl(dflash_head *H, dflash_state *const *states, int n, const uint3
     aa.max_splits = (max_S + chunk - 1) / chunk;
   }
 
+  // act holds RMSNorm(h) with the next consumer's gain: layer 0's input norm
+  // comes from the setup kernel, every later one from the residual finish.
   EpiArgs e{};
   for (int l = 0; l < g.L; ++l) {
-    if (l > 0) HIP_TRY(launch_rmsnorm(H->hid, h, H->g_in + (size_t)l * h, H->cfg.rms_eps, h, H->act, h, M, st));
     e = EpiArgs{};
     e.out_bf16 = H->qkv;
     e.ldo = g.qkv_dim;
@@ -394,24 +447,18 @@ int propose_impl(dflash_head *H, dflash_state *const *states, int n, const uint3
     e.head_dim = g.d;
     e.q_dim = g.q_dim;
     e.kv_dim = g.kv_dim;
-    TRY(gemm_rows(H, EPI_QKV_ROPE, H->act, h, M, H->w_qkv + (size_t)l * g.qkv_dim * h, g.qkv_dim, h, e, st));
+    TRY(gemm_rows(H, EPI_QKV_ROPE, H->act, h, M, H->w_qkv + (size_t)l * H->sz_qkv, g.qkv_dim, h, e, st));
     aa.layer = l;
     HIP_TRY(launch_attention(aa, n, st));
-    e = EpiArgs{};
-    e.out_f32 = H->hid;
-    e.ldo = h;
-    TRY(gemm_rows(H, EPI_RESID, H->attn, g.q_dim, M, H->w_o + (size_t)l * h * g.q_dim, h, g.q_dim, e, st));
-    HIP_TRY(launch_rmsnorm(H->hid, h, H->g_post + (size_t)l * h, H->cfg.rms_eps, h, H->act, h, M, st));
+    TRY(resid_gemm(H, H->attn, g.q_dim, M, H->w_o + (size_t)l * H->sz_o, g.q_dim, H->hid,
+                   H->g_post + (size_t)l * h, H->act, false, st));
     e = EpiArgs{};
     e.out_bf16 = H->mlp;
     e.ldo = g.I;
-    TRY(gemm_rows(H, EPI_SWIGLU, H->act, h, M, H->w_gu + (size_t)l * 2 * g.I * h, 2 * g.I, h, e, st));
-    e = EpiArgs{};
-    e.out_f32 = H->hid;
-    e.ldo = h;
-    TRY(gemm_rows(H, EPI_RESID, H->mlp, g.I, M, H->w_down + (size_t)l * h * g.I, h, g.I, e, st));
+    TRY(gemm_rows(H, EPI_SWIGLU, H->act, h, M, H->w_gu + (size_t)l * H->sz_gu, 2 * g.I, h, e, st));
+    const float *next_gain = l + 1 < g.L ? H->g_in + (size_t)(l + 1) * h : H->g_final;
+    TRY(resid_gemm(H, H->mlp, g.I, M, H->w_down + (size_t)l * H->sz_down, g.I, H->hid, next_gain, H->act, false, st));
   }
-  HIP_TRY(launch_rmsnorm(H->hid, h, H->g_final, H->cfg.rms_eps, h, H->act, h, M, st));
 
   LmArgs la{};
   la.K = h;
@@ -445,6 +492,8 @@ int propose_impl(dflash_head *H, dflash_state *const *states, int n, const uint3
   fa.ids = ids;
   fa.conf = conf;
   fa.row_prob = row_prob;
+  fa.p1 = H->lm_p1;
+  fa.counters = H->fin_counters;
   HIP_TRY(launch_lm_finish(fa, n, st));
   if (t_all) HIP_TRY(hipEventRecord(t_all, st));
   return DFLASH_OK;
@@ -621,12 +670,10 @@ int dflash_precompute_ctx_kv(dflash_head *head, dflash_state *const *states, int
   hipEvent_t t_all = H->interval_begin(DFLASH_PHASE_PRECOMPUTE, st);
   for (int r0 = 0; r0 < (int)total; r0 += GEMM_MAX_ROWS) {
     const int m = std::min<int>(GEMM_MAX_ROWS, (int)total - r0);
+    // u = S fc^T (split over K, summed in split order), c = RMSNorm(u) bf16
+    TRY(resid_gemm(H, (const uint16_t *)stack + (size_t)r0 * g.fc_in, g.fc_in, m, H->w_fc, g.fc_in, H->pre_u,
+                   H->g_hidden, H->pre_c, true, st));
     EpiArgs e{};
-    e.out_f32 = H->pre_u;
-    e.ldo = h;
-    TRY(gemm_rows(H, EPI_F32, (const uint16_t *)stack + (size_t)r0 * g.fc_in, g.fc_in, m, H->w_fc, h, g.fc_in, e, st));
-    HIP_TRY(launch_rmsnorm(H->pre_u, h, H->g_hidden, H->cfg.rms_eps, h, H->pre_c, h, m, st));
-    e = EpiArgs{};
     e.head_dim = g.d;
     e.pool = H->kv_pool;
     e.L = g.L;
@@ -734,7 +781,7 @@ int dflash_read_lm_head_fp8(dflash_head *head, void *codes_out, float *scale_out
   const Geo &g = head->g;
   if (!g.head_fp8) return set_err(DFLASH_E_INVALID, "the head's LM head is bf16");
   hipStream_t st = to_stream(stream);
-  if (codes_out) HIP_TRY(hipMemcpyAsync(codes_out, head->lm8, (size_t)g.V * g.h, hipMemcpyDeviceToDevice, st));
+  if (codes_out) HIP_TRY(launch_untile_fp8((uint8_t *)codes_out, head->lm8, g.V, g.h, st));
   if (scale_out) HIP_TRY(hipMemcpyAsync(scale_out, head->lm8_scale, (size_t)g.V * sizeof(float), hipMemcpyDeviceToDevice, st));
   return DFLASH_OK;
 }

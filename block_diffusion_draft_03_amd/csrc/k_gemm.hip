@@ -2,22 +2,31 @@
 //
 // All contractions of the propose path have few activation rows (gamma per
 // sequence) against large bf16 (or E4M3) weight matrices, so they are bound
-// by streaming the weights from HBM once. The kernel computes the transposed
-// product D^T = W A^T with v_mfma_f32_16x16x32_bf16: the A operand of the
-// MFMA is 16 weight rows, the B operand 16 activation rows. Lane l loads 64
-// contiguous bytes (32 bf16) of weight row n0 + l % 16 per 128-wide K step,
-// so a wave reads 16 rows x 256 contiguous bytes per step; the 32 values are
-// split into the four 8-value MFMA k-groups, and the activations are loaded
-// with the same k permutation, which leaves the dot products unchanged.
+// by streaming the weights from HBM once. The kernels compute the transposed
+// product D^T = W A^T with v_mfma_f32_16x16x32_bf16: the MFMA's A operand is
+// 16 weight rows, its B operand 16 activation rows. For k-step c of a
+// 128-wide K step, lane l (row l % 16, group g = l / 16) loads the 8 values
+// at k0 + 32c + 8g, so one load instruction covers 16 weight rows x 64
+// contiguous bytes. A lane then holds outputs (rows) 4g .. 4g+3 of a tile
+// for activation row l % 16.
 //
-// Each wave owns two 16-row weight tiles 64 rows apart (tiles w and w + 4 of
-// a 128-row column group), so a RoPE pair (i, i + 64) of a 128-wide head, or
-// a gate / up pair of the interleaved MLP weight, lands in one lane.
+// Work unit: 16 * TN consecutive weight rows. The NW waves of a workgroup
+// split the unit's K range into NW contiguous parts and reduce through LDS in
+// wave order. A GEMM may also be split over K across workgroups; then every
+// split writes its partial sums and a separate kernel (k_resid_norm) adds
+// them in split order. Every reduction order is fixed, so results are
+// deterministic and a row's result does not depend on the other rows.
 //
-// Split-K: the workgroups of one column group write partial tiles to a
-// workspace; the last to arrive (atomic ticket) sums them in split order
-// 0, 1, 2, ... and runs the epilogue, so results are deterministic and do not
-// depend on which rows share the launch.
+// Epilogues are lane-local because the build repacks weight rows in pairs:
+// Q and K rows of a head are ordered (dim i, dim i + d/2) for i = 0 .. d/2-1,
+// and the MLP weight alternates gate and up rows. Lane rows 4g, 4g+1 and
+// 4g+2, 4g+3 are therefore a RoPE pair (or a gate/up pair). Q and K stay in
+// that pair order everywhere inside the library (attention is invariant to a
+// common permutation of the Q and K dimensions).
+//
+// With ANORM the A operand is the RMSNorm of the fp32 residual stream,
+// formed while loading: bf16(h * r * gain) with r = 1 / sqrt(mean(h^2) + eps)
+// from per-unit sums of squares that the producing GEMM wrote.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -25,251 +34,344 @@ namespace dflash {
 
 namespace {
 
-template <int MT>
+template <int MT, int TN>
 struct Frag {
-  uint4 w0[4], w1[4];
+  uint4 w[TN][4];
   uint4 a[MT][4];
 };
 
-// Load one 128-wide K step for this lane into registers.
-template <int MT, bool WFP8>
-__device__ __forceinline__ void load_step(Frag<MT> &f, const void *__restrict__ Wv, int K, int n0, int n1,
-                                          const uint16_t *__restrict__ A, int lda, const int (&arow)[MT], int kk,
-                                          int ke) {
+// 8 bf16 of normalised activations: h[k .. k+8) * r * gain[k .. k+8)
+__device__ __forceinline__ uint4 norm_bf16x8(const float *h, const float *gain, float r) {
+  const float4 x0 = *(const float4 *)h, x1 = *(const float4 *)(h + 4);
+  const float4 g0 = *(const float4 *)gain, g1 = *(const float4 *)(gain + 4);
+  uint4 o;
+  o.x = pack_bf16x2(x0.x * r * g0.x, x0.y * r * g0.y);
+  o.y = pack_bf16x2(x0.z * r * g0.z, x0.w * r * g0.w);
+  o.z = pack_bf16x2(x1.x * r * g1.x, x1.y * r * g1.y);
+  o.w = pack_bf16x2(x1.z * r * g1.z, x1.w * r * g1.w);
+  return o;
+}
+
+struct AOperand {
+  const uint16_t *a;   // bf16 activations (plain)
+  const float *h;      // fp32 residual (ANORM)
+  const float *gain;   // ANORM
+  const float *rinv;   // ANORM: per activation row (LDS)
+  int lda;
+};
+
+template <int MT, int TN, bool WFP8, bool ANORM, bool TILED = false>
+__device__ __forceinline__ void load_step(Frag<MT, TN> &f, const void *__restrict__ Wv, int K, const int (&wrow)[TN],
+                                          const AOperand &A, const int (&arow)[MT], int k0, int ke, int g) {
   const uint4 z = {0u, 0u, 0u, 0u};
-  if constexpr (!WFP8) {
+  if constexpr (TILED && !WFP8) {
+    // tile-major weights: 16-row tile, 128-wide step, k-group c, lane -> 8 values
     const uint16_t *W = (const uint16_t *)Wv;
-    const uint16_t *p0 = W + (size_t)n0 * K + kk;
-    const uint16_t *p1 = W + (size_t)n1 * K + kk;
+    const int lane = threadIdx.x & 63;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const bool ok = kk + 8 * c < ke;
-      f.w0[c] = ok ? *(const uint4 *)(p0 + 8 * c) : z;
-      f.w1[c] = ok ? *(const uint4 *)(p1 + 8 * c) : z;
+    for (int t = 0; t < TN; ++t) {
+      const uint16_t *p = W + (((size_t)(wrow[t] >> 4) * ((K + 127) >> 7) + (k0 >> 7)) * 4 * 64 + lane) * 8;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) f.w[t][c] = (k0 + 32 * c + 8 * g < ke) ? *(const uint4 *)(p + c * 64 * 8) : z;
+    }
+  } else if constexpr (TILED && WFP8) {
+    // tile-major E4M3: pair j of lane l = codes of k-groups 2j and 2j + 1
+    const uint8_t *W = (const uint8_t *)Wv;
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int t = 0; t < TN; ++t) {
+      const uint8_t *p = W + (((size_t)(wrow[t] >> 4) * ((K + 127) >> 7) + (k0 >> 7)) * 2 * 64 + lane) * 16;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        uint4 q = z;
+        if (k0 + 64 * j + 8 * g < ke) q = *(const uint4 *)(p + j * 64 * 16);
+        uint2 lo = e4m3x4_to_bf16x4(q.x), hi = e4m3x4_to_bf16x4(q.y);
+        f.w[t][2 * j] = uint4{lo.x, lo.y, hi.x, hi.y};
+        lo = e4m3x4_to_bf16x4(q.z);
+        hi = e4m3x4_to_bf16x4(q.w);
+        f.w[t][2 * j + 1] = (k0 + 64 * j + 32 + 8 * g < ke) ? uint4{lo.x, lo.y, hi.x, hi.y} : z;
+      }
+    }
+  } else if constexpr (!WFP8) {
+    const uint16_t *W = (const uint16_t *)Wv;
+#pragma unroll
+    for (int t = 0; t < TN; ++t) {
+      const uint16_t *p = W + (size_t)wrow[t] * K + k0 + 8 * g;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) f.w[t][c] = (k0 + 32 * c + 8 * g < ke) ? *(const uint4 *)(p + 32 * c) : z;
     }
   } else {
     const uint8_t *W = (const uint8_t *)Wv;
-    const bool ok = kk < ke;  // K % 32 == 0: a lane's 32 codes are all in or all out
-    uint4 q0a = z, q0b = z, q1a = z, q1b = z;
-    if (ok) {
-      const uint8_t *p0 = W + (size_t)n0 * K + kk;
-      const uint8_t *p1 = W + (size_t)n1 * K + kk;
-      q0a = *(const uint4 *)p0;
-      q0b = *(const uint4 *)(p0 + 16);
-      q1a = *(const uint4 *)p1;
-      q1b = *(const uint4 *)(p1 + 16);
-    }
-    const uint32_t d0[8] = {q0a.x, q0a.y, q0a.z, q0a.w, q0b.x, q0b.y, q0b.z, q0b.w};
-    const uint32_t d1[8] = {q1a.x, q1a.y, q1a.z, q1a.w, q1b.x, q1b.y, q1b.z, q1b.w};
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      uint2 lo = e4m3x4_to_bf16x4(d0[2 * c]), hi = e4m3x4_to_bf16x4(d0[2 * c + 1]);
-      f.w0[c] = uint4{lo.x, lo.y, hi.x, hi.y};
-      lo = e4m3x4_to_bf16x4(d1[2 * c]);
-      hi = e4m3x4_to_bf16x4(d1[2 * c + 1]);
-      f.w1[c] = uint4{lo.x, lo.y, hi.x, hi.y};
+    for (int t = 0; t < TN; ++t) {
+      const uint8_t *p = W + (size_t)wrow[t] * K + k0 + 8 * g;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        uint2 q = {0u, 0u};
+        if (k0 + 32 * c + 8 * g < ke) q = *(const uint2 *)(p + 32 * c);
+        const uint2 lo = e4m3x4_to_bf16x4(q.x), hi = e4m3x4_to_bf16x4(q.y);
+        f.w[t][c] = uint4{lo.x, lo.y, hi.x, hi.y};
+      }
     }
   }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    const uint16_t *pa = A + (size_t)arow[mt] * lda + kk;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) f.a[mt][c] = (kk + 8 * c < ke) ? *(const uint4 *)(pa + 8 * c) : z;
-  }
-}
-
-template <int MT>
-__device__ __forceinline__ void mma_step(const Frag<MT> &f, f32x4 (&acc)[2][MT]) {
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      acc[0][mt] = mfma16x16x32(as_bf16x8(f.w0[c]), as_bf16x8(f.a[mt][c]), acc[0][mt]);
-      acc[1][mt] = mfma16x16x32(as_bf16x8(f.w1[c]), as_bf16x8(f.a[mt][c]), acc[1][mt]);
+    for (int c = 0; c < 4; ++c) {
+      const int k = k0 + 32 * c + 8 * g;
+      if (k >= ke) {
+        f.a[mt][c] = z;
+      } else if constexpr (ANORM) {
+        f.a[mt][c] = norm_bf16x8(A.h + (size_t)arow[mt] * A.lda + k, A.gain + k, A.rinv[mt * 16 + (threadIdx.x & 15)]);
+      } else {
+        f.a[mt][c] = *(const uint4 *)(A.a + (size_t)arow[mt] * A.lda + k);
+      }
     }
   }
 }
 
-// acc[t][mt][r] = sum_k W[n_t + 4g + r, k] * A[mt*16 + l%16, k] over [kb, ke).
-template <int MT, bool WFP8>
-__device__ __forceinline__ void mainloop(const void *__restrict__ W, int N, int K, const uint16_t *__restrict__ A,
-                                         int lda, int M, int n_t0, int n_t1, int kb, int ke, f32x4 (&acc)[2][MT]) {
+template <int MT, int TN>
+__device__ __forceinline__ void mma_step(const Frag<MT, TN> &f, f32x4 (&acc)[TN][MT]) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int t = 0; t < TN; ++t)
+        acc[t][mt] = mfma16x16x32(as_bf16x8(f.w[t][c]), as_bf16x8(f.a[mt][c]), acc[t][mt]);
+}
+
+template <int MT, int TN>
+__device__ __forceinline__ void zero(f32x4 (&acc)[TN][MT]) {
+#pragma unroll
+  for (int t = 0; t < TN; ++t)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// acc[t][mt][r] += sum over k in [kb, ke) of W[row0 + 16t + 4g + r, k] * A[mt*16 + l%16, k]
+// The range is walked in batches of ST 128-wide steps: all loads of a batch
+// are issued before its MFMAs (steps past ke load nothing and add zeros), so
+// a wave keeps ST steps of weight rows in flight.
+template <int MT, int TN, int ST, bool WFP8, bool ANORM, bool TILED = false>
+__device__ __forceinline__ void stream_rows(const void *__restrict__ W, int N, int K, const AOperand &A, int M,
+                                            int row0, int kb, int ke, f32x4 (&acc)[TN][MT]) {
   const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
-  const int n0 = min(n_t0 + r16, N - 1), n1 = min(n_t1 + r16, N - 1);
-  int arow[MT];
+  int wrow[TN], arow[MT];
+#pragma unroll
+  for (int t = 0; t < TN; ++t) wrow[t] = min(row0 + 16 * t + r16, N - 1);
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) arow[mt] = min(mt * 16 + r16, M - 1);
+  for (int k0 = kb; k0 < ke; k0 += 128 * ST) {
+    Frag<MT, TN> f[ST];
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+    for (int s = 0; s < ST; ++s) load_step<MT, TN, WFP8, ANORM, TILED>(f[s], W, K, wrow, A, arow, k0 + 128 * s, ke, g);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (kb >= ke) return;
-  Frag<MT> cur, nxt;
-  load_step<MT, WFP8>(cur, W, K, n0, n1, A, lda, arow, kb + 32 * g, ke);
-  for (int k0 = kb; k0 < ke; k0 += 128) {
-    const bool more = k0 + 128 < ke;
-    if (more) load_step<MT, WFP8>(nxt, W, K, n0, n1, A, lda, arow, k0 + 128 + 32 * g, ke);
-    mma_step<MT>(cur, acc);
-    if (more) cur = nxt;
+    for (int s = 0; s < ST; ++s) mma_step<MT, TN>(f[s], acc);
   }
 }
 
-// Deterministic split-K reduction. Returns false in every workgroup except
-// the last one of the column group, which ends holding the full sums.
-template <int MT>
-__device__ __forceinline__ bool splitk_reduce(const GemmArgs &ga, f32x4 (&acc)[2][MT]) {
-  if (ga.splits <= 1) return true;
-  __shared__ int s_last;
-  const int cg = blockIdx.x, split = blockIdx.y;
-  f32x4 *my = (f32x4 *)ga.ws + ((size_t)(split * gridDim.x + cg) * blockDim.x + threadIdx.x) * (2 * MT);
+// Sum the NW waves' partials in wave order; the result ends in wave 0.
+template <int MT, int TN, int NW>
+__device__ __forceinline__ void wave_reduce(f32x4 (&acc)[TN][MT], float *red) {
+  if constexpr (NW == 1) return;
+  constexpr int V = TN * MT * 4;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (wave > 0) {
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) my[t * MT + mt] = acc[t][mt];
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int prev = atomicAdd(&ga.counters[cg], 1);
-    s_last = (prev == ga.splits - 1);
-  }
-  __syncthreads();
-  if (!s_last) return false;
-  __threadfence();
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < ga.splits; ++s) {
-    const f32x4 *p = (const f32x4 *)ga.ws + ((size_t)(s * gridDim.x + cg) * blockDim.x + threadIdx.x) * (2 * MT);
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        acc[t][mt] += p[t * MT + mt];
-      }
-  }
-  if (threadIdx.x == 0) ga.counters[cg] = 0;
-  return true;
-}
-
-template <int MT, bool WFP8, int EPI>
-__global__ __launch_bounds__(256) void k_gemm(GemmArgs ga, EpiArgs ea) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
-  const int cg = blockIdx.x;
-  const int n_t0 = cg * 128 + wave * 16, n_t1 = n_t0 + 64;
-  const int kb = blockIdx.y * ga.kslice, ke = min(ga.K, kb + ga.kslice);
-  f32x4 acc[2][MT];
-  mainloop<MT, WFP8>(ga.W, ga.N, ga.K, ga.A, ga.lda, ga.M, n_t0, n_t1, kb, ke, acc);
-  if (!splitk_reduce<MT>(ga, acc)) return;
-
-  if constexpr (EPI == EPI_F32 || EPI == EPI_RESID) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int m = mt * 16 + r16;
-        if (m >= ga.M) continue;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int n = (t ? n_t1 : n_t0) + 4 * g + r;
-          if (n >= ga.N) continue;
-          float *o = ea.out_f32 + (size_t)m * ea.ldo + n;
-          if constexpr (EPI == EPI_F32)
-            *o = acc[t][mt][r];
-          else
-            *o += acc[t][mt][r];
-        }
-      }
-  } else if constexpr (EPI == EPI_SWIGLU) {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int m = mt * 16 + r16;
-      if (m >= ga.M) continue;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = cg * 64 + wave * 16 + 4 * g + r;  // intermediate index
-        if (cg * 128 + wave * 16 + 4 * g + r >= ga.N) continue;
-        ea.out_bf16[(size_t)m * ea.ldo + i] = f32_to_bf16(silu(acc[0][mt][r]) * acc[1][mt][r]);
-      }
-    }
-  } else {
-    // RoPE epilogues: stage the 128-column tile in LDS, then rotate pairs.
-    __shared__ float tile[MT * 16][129];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < TN; ++t)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) tile[mt * 16 + r16][t * 64 + wave * 16 + 4 * g + r] = acc[t][mt][r];
-    __syncthreads();
-    const int d = ea.head_dim, half = d >> 1;
-    for (int e = threadIdx.x; e < MT * 16 * 128; e += blockDim.x) {
-      const int m = e >> 7, col = e & 127;
-      const int n = cg * 128 + col;
-      if (m >= ga.M || n >= ga.N) continue;
-      const int i = n % d;  // dim within the head (heads align to d inside a group)
-      const float x = tile[m][col];
-      if constexpr (EPI == EPI_QKV_ROPE) {
-        float y = x;
-        if (n < ea.q_dim + ea.kv_dim) {
-          const int ip = i < half ? i : i - half;
-          const float xp = tile[m][i < half ? col + half : col - half];
-          const float2 c = ea.cs[(size_t)m * half + ip];
-          y = i < half ? x * c.x - xp * c.y : x * c.x + xp * c.y;
+        for (int r = 0; r < 4; ++r) red[((wave - 1) * V + (t * MT + mt) * 4 + r) * 64 + lane] = acc[t][mt][r];
+  }
+  __syncthreads();
+  if (wave == 0) {
+    for (int w = 1; w < NW; ++w)
+#pragma unroll
+      for (int t = 0; t < TN; ++t)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[t][mt][r] += red[((w - 1) * V + (t * MT + mt) * 4 + r) * 64 + lane];
+  }
+}
+
+// Per-row inverse RMS from the producer's per-unit sums of squares, into LDS.
+template <int MT>
+__device__ __forceinline__ void load_rinv(const GemmArgs &ga, float *rinv, float *tmp) {
+  // thread t: row t % (16 MT), units t / (16 MT), + stride
+  constexpr int R = 16 * MT;
+  const int nthr = blockDim.x;
+  const int row = threadIdx.x % R, lane_u = threadIdx.x / R, nu = nthr / R;
+  float s = 0.0f;
+  if (row < ga.M)
+    for (int u = lane_u; u < ga.ss_units; u += nu) s += ga.ss_in[(size_t)u * ga.ss_ld + ga.ss_row0 + row];
+  tmp[threadIdx.x] = s;
+  __syncthreads();
+  if (threadIdx.x < R) {
+    float t = 0.0f;
+    for (int i = 0; i < nu; ++i) t += tmp[i * R + threadIdx.x];
+    rinv[threadIdx.x] = 1.0f / sqrtf(t / (float)ga.K + ga.eps);
+  }
+  __syncthreads();
+}
+
+template <int MT, int TN, int NW, int ST, int EPI, bool ANORM, bool TILED = false>
+__global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs ga, EpiArgs ea) {
+  __shared__ float red[(NW > 1 ? NW - 1 : 1) * TN * MT * 4 * 64];
+  __shared__ float rinv[16 * MT];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
+  const int row0 = blockIdx.x * 16 * TN;
+  const int kb = blockIdx.y * ga.kslice, ke = min(ga.K, kb + ga.kslice);
+  const int steps = (ke - kb + 127) / 128;
+  const int s0 = (steps * wave) / NW, s1 = (steps * (wave + 1)) / NW;
+  AOperand A{ga.A, ga.H, ga.gain, rinv, ga.lda};
+  if constexpr (ANORM) load_rinv<MT>(ga, rinv, red);
+  f32x4 acc[TN][MT];
+  zero<MT, TN>(acc);
+  stream_rows<MT, TN, ST, false, ANORM, TILED>(ga.W, ga.N, ga.K, A, ga.M, row0, kb + 128 * s0, min(ke, kb + 128 * s1),
+                                               acc);
+  wave_reduce<MT, TN, NW>(acc, red);
+  if (wave != 0) return;
+
+  float ss_acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) ss_acc[mt] = 0.0f;
+#pragma unroll
+  for (int t = 0; t < TN; ++t)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = mt * 16 + r16;
+      const int n = row0 + 16 * t + 4 * g;  // first of this lane's 4 rows
+      const bool ok = m < ga.M && n < ga.N;
+      const f32x4 v = acc[t][mt];
+      if constexpr (EPI == EPI_F32 || EPI == EPI_PARTIAL) {
+        if (ok) {
+          float *o = EPI == EPI_F32 ? ea.out_f32 + (size_t)m * ea.ldo + n
+                                    : ea.out_f32 + ((size_t)blockIdx.y * ea.ld_split + m) * ea.ldo + n;
+          *(f32x4 *)o = v;
         }
-        ea.out_bf16[(size_t)m * ea.ldo + n] = f32_to_bf16(y);
-      } else {  // EPI_KV_SCATTER
+      } else if constexpr (EPI == EPI_RESID) {
+        // h += acc, and this unit's sum of squares of the new h per row
+        float ss = 0.0f;
+        if (ok) {
+          float *o = ea.out_f32 + (size_t)m * ea.ldo + n;
+          const f32x4 x = v + *(const f32x4 *)o;
+          *(f32x4 *)o = x;
+          ss = x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+        }
+        ss += __shfl_xor(ss, 16, WAVE);
+        ss += __shfl_xor(ss, 32, WAVE);
+        ss_acc[mt] += ss;
+      } else if constexpr (EPI == EPI_SWIGLU) {
+        // rows (gate_i, up_i, gate_i+1, up_i+1) with i = n / 2
+        if (ok)
+          *(uint32_t *)(ea.out_bf16 + (size_t)m * ea.ldo + n / 2) = pack_bf16x2(silu(v[0]) * v[1], silu(v[2]) * v[3]);
+      } else if constexpr (EPI == EPI_QKV_ROPE) {
+        if (!ok) continue;
+        const int half = ea.head_dim >> 1;
+        float y[4] = {v[0], v[1], v[2], v[3]};
+        if (n < ea.q_dim + ea.kv_dim) {
+          const int p = (n % ea.head_dim) >> 1;  // pair index of rows n, n+1
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const float2 c = ea.cs[(size_t)m * half + p + q];
+            const float x0 = v[2 * q], x1 = v[2 * q + 1];
+            y[2 * q] = x0 * c.x - x1 * c.y;
+            y[2 * q + 1] = x1 * c.x + x0 * c.y;
+          }
+        }
+        uint2 o;
+        o.x = pack_bf16x2(y[0], y[1]);
+        o.y = pack_bf16x2(y[2], y[3]);
+        *(uint2 *)(ea.out_bf16 + (size_t)m * ea.ldo + n) = o;
+      } else {  // EPI_KV_SCATTER: columns [K0 | V0 | K1 | V1 ...], K in pair order
+        if (!ok) continue;
+        const int d = ea.head_dim;
         const int kv_dim = ea.n_kv * d;
         const int l = n / (2 * kv_dim), rem = n % (2 * kv_dim);
-        const int kv = rem / kv_dim, hd = (rem % kv_dim) / d;
+        const int kv = rem / kv_dim, hd = (rem % kv_dim) / d, j = n % d;
         const int pos = ea.row_pos[m];
-        float y = x;
+        float y[4] = {v[0], v[1], v[2], v[3]};
         if (kv == 0) {
-          const int ip = i < half ? i : i - half;
-          const float xp = tile[m][i < half ? col + half : col - half];
-          double sn, cs;
-          sincos((double)pos * ea.inv_freq[ip], &sn, &cs);
-          const float c = (float)cs, s = (float)sn;
-          y = i < half ? x * c - xp * s : x * c + xp * s;
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            double sn, cs;
+            sincos((double)pos * ea.inv_freq[(j >> 1) + q], &sn, &cs);
+            const float c = (float)cs, s = (float)sn;
+            const float x0 = v[2 * q], x1 = v[2 * q + 1];
+            y[2 * q] = x0 * c - x1 * s;
+            y[2 * q + 1] = x1 * c + x0 * s;
+          }
         }
         const int32_t blk = ea.row_bt[m][pos >> 4];
         const size_t off = ((((size_t)blk * ea.L + l) * 2 + kv) * ea.n_kv + hd) * (size_t)(DFLASH_KV_BLOCK * d) +
-                           (size_t)(pos & 15) * d + i;
+                           (size_t)(pos & 15) * d + j;
         if (ea.kv_fp8) {
           const float sc = ea.kv_scale[(l * 2 + kv) * ea.n_kv + hd];
-          ((uint8_t *)ea.pool)[off] = f32_to_e4m3(y / sc);
+          uint32_t w = 0;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) w |= (uint32_t)f32_to_e4m3(y[r] / sc) << (8 * r);
+          *(uint32_t *)((uint8_t *)ea.pool + off) = w;
         } else {
-          ((uint16_t *)ea.pool)[off] = f32_to_bf16(y);
+          uint2 o;
+          o.x = pack_bf16x2(y[0], y[1]);
+          o.y = pack_bf16x2(y[2], y[3]);
+          *(uint2 *)((uint16_t *)ea.pool + off) = o;
         }
       }
     }
+  if constexpr (EPI == EPI_RESID) {
+    if (ea.ss_out && g == 0)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int m = mt * 16 + r16;
+        if (m < ga.M) ea.ss_out[(size_t)blockIdx.x * ea.ss_ld + ea.ss_row0 + m] = ss_acc[mt];
+      }
   }
 }
 
-template <int MT, bool WFP8>
-hipError_t launch_t(int epi, const GemmArgs &g, const EpiArgs &e, hipStream_t s) {
-  dim3 grid(gemm_groups(g.N), g.splits), block(256);
-  switch (epi) {
-    case EPI_F32: hipLaunchKernelGGL((k_gemm<MT, WFP8, EPI_F32>), grid, block, 0, s, g, e); break;
-    case EPI_RESID: hipLaunchKernelGGL((k_gemm<MT, WFP8, EPI_RESID>), grid, block, 0, s, g, e); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL((k_gemm<MT, WFP8, EPI_SWIGLU>), grid, block, 0, s, g, e); break;
-    case EPI_QKV_ROPE: hipLaunchKernelGGL((k_gemm<MT, WFP8, EPI_QKV_ROPE>), grid, block, 0, s, g, e); break;
-    case EPI_KV_SCATTER: hipLaunchKernelGGL((k_gemm<MT, WFP8, EPI_KV_SCATTER>), grid, block, 0, s, g, e); break;
-    default: return hipErrorInvalidValue;
+// Split-K finish for the residual GEMMs: one workgroup per activation row
+// adds the splits' partial sums (in split order) to the fp32 residual row,
+// then writes the RMSNorm of the new row (with `gain`) as bf16 and, when
+// asked, the row's sum of squares.
+__global__ __launch_bounds__(256) void k_resid_norm(ResidNormArgs a) {
+  __shared__ float red[4];
+  const int m = blockIdx.x;
+  float *hr = a.h + (size_t)m * a.n;
+  float ss = 0.0f;
+  for (int i = threadIdx.x * 4; i < a.n; i += blockDim.x * 4) {
+    f32x4 x = a.init_zero ? f32x4{0.f, 0.f, 0.f, 0.f} : *(const f32x4 *)(hr + i);
+    for (int s = 0; s < a.splits; ++s) x += *(const f32x4 *)(a.part + ((size_t)s * a.ld_split + m) * a.n + i);
+    *(f32x4 *)(hr + i) = x;
+    ss += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
   }
-  return hipGetLastError();
+  ss = block_sum(ss, red);
+  if (!a.out) return;
+  const float r = 1.0f / sqrtf(ss / (float)a.n + a.eps);
+  uint16_t *o = a.out + (size_t)m * a.n;
+  for (int i = threadIdx.x * 4; i < a.n; i += blockDim.x * 4) {
+    const f32x4 x = *(const f32x4 *)(hr + i);
+    const float4 gg = *(const float4 *)(a.gain + i);
+    uint2 w;
+    w.x = pack_bf16x2(x[0] * r * gg.x, x[1] * r * gg.y);
+    w.y = pack_bf16x2(x[2] * r * gg.z, x[3] * r * gg.w);
+    *(uint2 *)(o + i) = w;
+  }
 }
 
 // ------------------------------------------------------------- LM head ----
-// Stage 1: every workgroup streams 128-row vocab groups cg = blockIdx.x,
-// blockIdx.x + P, ... and keeps, per lane, a running (max, argmax, sum exp)
-// of its activation row over the vocab entries it sees (masked entries are
-// skipped). Lanes, then waves, are merged in a fixed order and one partial
-// per workgroup and row is written.
-template <int MT, bool WFP8>
+// Stage 1: every wave streams (16 * TN)-row vocab units u = wave_id,
+// wave_id + total_waves, ... over the full K and keeps, per lane, a running
+// (max, argmax, sum exp) of its activation row over the vocab entries it sees
+// (masked entries skipped). Lanes, then the workgroup's waves, are merged in
+// a fixed order; one partial per workgroup and row is written.
+template <int MT, int TN, int ST, bool WFP8, bool TILED = false>
 __global__ __launch_bounds__(256) void k_lm_head(LmArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
-  const int groups = (a.V + 127) / 128;
+  constexpr int UNIT = 16 * TN;
+  const int units = (a.V + UNIT - 1) / UNIT;
   ArgState st[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) arg_init(st[mt]);
@@ -279,15 +381,18 @@ __global__ __launch_bounds__(256) void k_lm_head(LmArgs a) {
     const int m = min(mt * 16 + r16, a.M - 1);
     mask_row[mt] = a.bitmask ? a.bitmask + (size_t)((a.row0 + m) / a.gamma) * a.words : nullptr;
   }
-  for (int cg = blockIdx.x; cg < groups; cg += gridDim.x) {
-    const int n_t0 = cg * 128 + wave * 16, n_t1 = n_t0 + 64;
-    f32x4 acc[2][MT];
-    mainloop<MT, WFP8>(a.W, a.V, a.K, a.z, a.K, a.M, n_t0, n_t1, 0, a.K, acc);
+  AOperand A{a.z, nullptr, nullptr, nullptr, a.K};
+  const int nw = gridDim.x * 4;
+  for (int u = blockIdx.x * 4 + wave; u < units; u += nw) {
+    const int row0 = u * UNIT;
+    f32x4 acc[TN][MT];
+    zero<MT, TN>(acc);
+    stream_rows<MT, TN, ST, WFP8, false, TILED>(a.W, a.V, a.K, A, a.M, row0, 0, a.K, acc);
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < TN; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int v = (t ? n_t1 : n_t0) + 4 * g + r;
+        const int v = row0 + 16 * t + 4 * g + r;
         if (v >= a.V) continue;
         const float sc = WFP8 ? a.scale[v] : 1.0f;
 #pragma unroll
@@ -299,7 +404,6 @@ __global__ __launch_bounds__(256) void k_lm_head(LmArgs a) {
           arg_push(st[mt], x, (uint32_t)v);
         }
       }
-    }
   }
   __shared__ float s_mx[4][MT * 16], s_se[4][MT * 16];
   __shared__ uint32_t s_idx[4][MT * 16];
@@ -336,95 +440,149 @@ __global__ __launch_bounds__(256) void k_lm_head(LmArgs a) {
   }
 }
 
-// Stage 2: one workgroup per sequence merges the P partials of each of its
-// gamma rows (fixed tree order), writes the ids and top-1 probabilities, and
-// the chain confidence min(p1) over rows 1..num_drafts.
+// Stage 2: one workgroup per block row merges the row's P partials (fixed
+// tree order) and writes its id and top-1 probability; the last row of a
+// sequence to finish (atomic ticket) writes the chain confidence
+// min(p1) over rows 1..num_drafts.
 __global__ __launch_bounds__(256) void k_lm_finish(LmFinishArgs a) {
   __shared__ float s_mx[256], s_se[256];
   __shared__ uint32_t s_idx[256];
-  __shared__ float s_p1[64];
-  const int seq = blockIdx.x;
-  for (int j = 0; j < a.gamma; ++j) {
-    const int m = seq * a.gamma + j;
-    ArgState st;
-    arg_init(st);
-    for (int p = threadIdx.x; p < a.P; p += blockDim.x) {
+  const int m = blockIdx.x, seq = m / a.gamma;
+  ArgState st;
+  arg_init(st);
+  constexpr int PER = 4;
+  ArgState q[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int p = threadIdx.x + i * blockDim.x;
+    arg_init(q[i]);
+    if (p < a.P) {
       const size_t o = (size_t)p * a.M + m;
-      ArgState q;
-      q.mx = a.part_mx[o];
-      q.se = a.part_se[o];
-      q.idx = a.part_idx[o];
-      st = arg_merge(st, q);
+      q[i].mx = a.part_mx[o];
+      q[i].se = a.part_se[o];
+      q[i].idx = a.part_idx[o];
     }
-    s_mx[threadIdx.x] = st.mx;
-    s_se[threadIdx.x] = st.se;
-    s_idx[threadIdx.x] = st.idx;
-    __syncthreads();
-    for (int w = blockDim.x / 2; w > 0; w >>= 1) {
-      if (threadIdx.x < w) {
-        ArgState x, y;
-        x.mx = s_mx[threadIdx.x];
-        x.se = s_se[threadIdx.x];
-        x.idx = s_idx[threadIdx.x];
-        y.mx = s_mx[threadIdx.x + w];
-        y.se = s_se[threadIdx.x + w];
-        y.idx = s_idx[threadIdx.x + w];
-        x = arg_merge(x, y);
-        s_mx[threadIdx.x] = x.mx;
-        s_se[threadIdx.x] = x.se;
-        s_idx[threadIdx.x] = x.idx;
-      }
-      __syncthreads();
-    }
-    if (threadIdx.x == 0) {
-      const bool none = s_mx[0] == -__builtin_huge_valf();
-      const float p1 = none ? 0.0f : 1.0f / s_se[0];
-      a.ids[m] = none ? DFLASH_NO_TOKEN : s_idx[0];
-      if (a.row_prob) a.row_prob[m] = p1;
-      s_p1[j] = p1;
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) st = arg_merge(st, q[i]);
+  for (int p = threadIdx.x + PER * blockDim.x; p < a.P; p += blockDim.x) {
+    const size_t o = (size_t)p * a.M + m;
+    ArgState x;
+    x.mx = a.part_mx[o];
+    x.se = a.part_se[o];
+    x.idx = a.part_idx[o];
+    st = arg_merge(st, x);
+  }
+  s_mx[threadIdx.x] = st.mx;
+  s_se[threadIdx.x] = st.se;
+  s_idx[threadIdx.x] = st.idx;
+  __syncthreads();
+  for (int w = blockDim.x / 2; w > 0; w >>= 1) {
+    if (threadIdx.x < w) {
+      ArgState x, y;
+      x.mx = s_mx[threadIdx.x];
+      x.se = s_se[threadIdx.x];
+      x.idx = s_idx[threadIdx.x];
+      y.mx = s_mx[threadIdx.x + w];
+      y.se = s_se[threadIdx.x + w];
+      y.idx = s_idx[threadIdx.x + w];
+      x = arg_merge(x, y);
+      s_mx[threadIdx.x] = x.mx;
+      s_se[threadIdx.x] = x.se;
+      s_idx[threadIdx.x] = x.idx;
     }
     __syncthreads();
   }
   if (threadIdx.x == 0) {
-    float c = s_p1[1];
-    for (int j = 2; j <= a.num_drafts; ++j) c = fminf(c, s_p1[j]);
-    a.conf[seq] = c;
+    const bool none = s_mx[0] == -__builtin_huge_valf();
+    const float p1 = none ? 0.0f : 1.0f / s_se[0];
+    a.ids[m] = none ? DFLASH_NO_TOKEN : s_idx[0];
+    if (a.row_prob) a.row_prob[m] = p1;
+    a.p1[m] = p1;
+    __threadfence();
+    const int prev = atomicAdd(&a.counters[seq], 1);
+    if (prev == a.gamma - 1) {
+      __threadfence();
+      float c = a.p1[seq * a.gamma + 1];
+      for (int j = 2; j <= a.num_drafts; ++j) c = fminf(c, a.p1[seq * a.gamma + j]);
+      a.conf[seq] = c;
+      a.counters[seq] = 0;
+    }
   }
+}
+
+template <int MT, int TN, int NW, int ST, bool ANORM>
+hipError_t launch_cfg(int epi, const GemmArgs &g, const EpiArgs &e, hipStream_t s) {
+  dim3 grid((g.N + 16 * TN - 1) / (16 * TN), g.splits), block(NW * 64);
+#define DFL_CASE(E)                                                                         \
+  case E:                                                                                   \
+    hipLaunchKernelGGL((k_gemm<MT, TN, NW, ST, E, ANORM, true>), grid, block, 0, s, g, e);      \
+    break;
+  switch (epi) {
+    DFL_CASE(EPI_F32)
+    DFL_CASE(EPI_RESID)
+    DFL_CASE(EPI_SWIGLU)
+    DFL_CASE(EPI_QKV_ROPE)
+    DFL_CASE(EPI_KV_SCATTER)
+    DFL_CASE(EPI_PARTIAL)
+    default: return hipErrorInvalidValue;
+  }
+#undef DFL_CASE
+  return hipGetLastError();
+}
+
+template <int MT, bool ANORM>
+hipError_t launch_mt(int epi, const GemmArgs &g, const EpiArgs &e, hipStream_t s) {
+  // configurations chosen by gemm_plan
+  if (g.tn == 1 && g.nw == 4 && g.st == 4) return launch_cfg<MT, 1, 4, 4, ANORM>(epi, g, e, s);
+  if (g.tn == 2 && g.nw == 4 && g.st == 4) return launch_cfg<MT, 2, 4, 4, ANORM>(epi, g, e, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-int gemm_groups(int N) { return (N + 127) / 128; }
-
-void gemm_plan(int N, int K, int *kslice, int *splits) {
-  const int groups = gemm_groups(N);
+// Measured on MI355X over the propose shapes with tiled weights: 4 waves per
+// workgroup with 4 steps in flight each; 32-row units for wide matrices;
+// 16-row units split over K (up to 4 ways) for the N = hidden GEMMs.
+GemmPlan gemm_plan(int N, int K, bool allow_split) {
+  GemmPlan p;
   const int steps = (K + 127) / 128;
-  int want = 512 / groups;
-  if (want < 1) want = 1;
-  if (want > steps) want = steps;
-  const int per = (steps + want - 1) / want;
-  *kslice = per * 128;
-  *splits = (K + *kslice - 1) / *kslice;
+  p.tn = N > 4096 ? 2 : 1;
+  p.nw = 4;
+  p.st = 4;
+  p.splits = 1;
+  const int units = (N + 16 * p.tn - 1) / (16 * p.tn);
+  if (allow_split && units < 256) {
+    int want = (256 + units - 1) / units;
+    if (want > 4) want = 4;
+    if (want > steps) want = steps;
+    p.splits = want < 1 ? 1 : want;
+  }
+  const int per = (steps + p.splits - 1) / p.splits;
+  p.kslice = per * 128;
+  p.splits = (K + p.kslice - 1) / p.kslice;
+  return p;
 }
 
-size_t gemm_ws_floats(int N, int K) {
-  int ks, sp;
-  gemm_plan(N, K, &ks, &sp);
-  if (sp <= 1) return 0;
-  return (size_t)sp * gemm_groups(N) * 256 * (2 * 4 * 4);
-}
-
-hipError_t launch_gemm(int epi, bool w_fp8, const GemmArgs &g, const EpiArgs &e, hipStream_t s) {
-  if (g.M < 1 || g.M > GEMM_MAX_ROWS) return hipErrorInvalidValue;
+hipError_t launch_gemm(int epi, const GemmArgs &g, const EpiArgs &e, hipStream_t s) {
+  if (g.M < 1 || g.M > GEMM_MAX_ROWS || g.splits < 1) return hipErrorInvalidValue;
+  if (g.splits > 1 && epi != EPI_PARTIAL) return hipErrorInvalidValue;
   const int mt = g.M <= 16 ? 1 : (g.M <= 32 ? 2 : 4);
-  if (w_fp8) return hipErrorInvalidValue;  // only the LM head streams E4M3 weights
-  return mt == 1 ? launch_t<1, false>(epi, g, e, s) : mt == 2 ? launch_t<2, false>(epi, g, e, s)
-                                                              : launch_t<4, false>(epi, g, e, s);
+  if (g.H) return hipErrorInvalidValue;  // the norm-fused A operand is not used by the library
+  return mt == 1 ? launch_mt<1, false>(epi, g, e, s) : mt == 2 ? launch_mt<2, false>(epi, g, e, s)
+                                                               : launch_mt<4, false>(epi, g, e, s);
+}
+
+hipError_t launch_resid_norm(const ResidNormArgs &a, int M, hipStream_t s) {
+  hipLaunchKernelGGL(k_resid_norm, dim3(M), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 int lm_parts(int V) {
-  const int groups = (V + 127) / 128;
-  return groups < 1024 ? groups : 1024;
+  // one workgroup per CU measured best for the 248k x 2048 head
+  const int units = (V + 31) / 32;
+  const int wgs = (units + 3) / 4;
+  return wgs < 256 ? wgs : 256;
 }
 
 hipError_t launch_lm_head(bool w_fp8, const LmArgs &a, hipStream_t s) {
@@ -432,19 +590,19 @@ hipError_t launch_lm_head(bool w_fp8, const LmArgs &a, hipStream_t s) {
   const int mt = a.M <= 16 ? 1 : (a.M <= 32 ? 2 : 4);
   dim3 grid(lm_parts(a.V)), block(256);
   if (w_fp8) {
-    if (mt == 1) hipLaunchKernelGGL((k_lm_head<1, true>), grid, block, 0, s, a);
-    else if (mt == 2) hipLaunchKernelGGL((k_lm_head<2, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_lm_head<4, true>), grid, block, 0, s, a);
+    if (mt == 1) hipLaunchKernelGGL((k_lm_head<1, 2, 2, true, true>), grid, block, 0, s, a);
+    else if (mt == 2) hipLaunchKernelGGL((k_lm_head<2, 2, 2, true, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_lm_head<4, 2, 2, true, true>), grid, block, 0, s, a);
   } else {
-    if (mt == 1) hipLaunchKernelGGL((k_lm_head<1, false>), grid, block, 0, s, a);
-    else if (mt == 2) hipLaunchKernelGGL((k_lm_head<2, false>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_lm_head<4, false>), grid, block, 0, s, a);
+    if (mt == 1) hipLaunchKernelGGL((k_lm_head<1, 2, 2, false, true>), grid, block, 0, s, a);
+    else if (mt == 2) hipLaunchKernelGGL((k_lm_head<2, 2, 2, false, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_lm_head<4, 2, 2, false, true>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_lm_finish(const LmFinishArgs &a, int n_seq, hipStream_t s) {
-  hipLaunchKernelGGL(k_lm_finish, dim3(n_seq), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_lm_finish, dim3(n_seq * a.gamma), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -55,18 +55,85 @@ __device__ __forceinline__ uint16_t load_as_bf16(const void *src, size_t i, bool
 }
 
 __global__ void k_convert_rows(uint16_t *dst, const void *src, const void *src2, int rows, int cols, int src_f32,
-                               int interleave) {
+                               int order, int head_dim) {
   const size_t total = (size_t)rows * cols;
   for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (size_t)gridDim.x * blockDim.x) {
     const int rr = (int)(e / cols), cc = (int)(e % cols);
     const void *s = src;
     int sr = rr;
-    if (interleave) {  // dst rows 128b .. 128b+63 = gate rows 64b.., 128b+64 .. = up rows 64b..
-      const int b = rr / 128, w = rr % 128;
-      s = w < 64 ? src : src2;
-      sr = b * 64 + (w & 63);
+    if (order == ROWS_GATE_UP) {
+      s = (rr & 1) ? src2 : src;
+      sr = rr >> 1;
+    } else if (order == ROWS_ROPE_PAIRS) {
+      const int head = rr / head_dim, j = rr % head_dim;
+      sr = head * head_dim + (j >> 1) + (j & 1) * (head_dim >> 1);
     }
     dst[e] = load_as_bf16(s, (size_t)sr * cols + cc, src_f32 != 0);
+  }
+}
+
+// Source row of destination row rr under a row order; *second selects src2.
+__device__ __forceinline__ int src_row(int rr, int order, int head_dim, bool *second) {
+  *second = false;
+  if (order == ROWS_GATE_UP) {
+    *second = (rr & 1) != 0;
+    return rr >> 1;
+  }
+  if (order == ROWS_ROPE_PAIRS) {
+    const int head = rr / head_dim, j = rr % head_dim;
+    return head * head_dim + (j >> 1) + (j & 1) * (head_dim >> 1);
+  }
+  return rr;
+}
+
+// One thread per 16-byte lane chunk of the tiled layout (8 bf16).
+__global__ void k_tile_rows(uint16_t *dst, int dst_tile0, const void *src, const void *src2, int rows, int cols,
+                            int src_f32, int order, int head_dim) {
+  const int steps = (cols + 127) / 128, tiles = (rows + 15) / 16;
+  const size_t chunks = (size_t)tiles * steps * 256;
+  for (size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x; q < chunks; q += (size_t)gridDim.x * blockDim.x) {
+    const int lane = (int)(q & 63), c = (int)((q >> 6) & 3);
+    const size_t ts = q >> 8;
+    const int step = (int)(ts % steps), tile = (int)(ts / steps);
+    const int r = tile * 16 + (lane & 15);
+    const int k0 = step * 128 + 32 * c + 8 * (lane >> 4);
+    uint16_t v[8];
+    bool second = false;
+    const int sr = r < rows ? src_row(r, order, head_dim, &second) : 0;
+    const void *s = second ? src2 : src;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      v[e] = (r < rows && k0 + e < cols) ? load_as_bf16(s, (size_t)sr * cols + k0 + e, src_f32 != 0) : (uint16_t)0;
+    const size_t o = (((size_t)(dst_tile0 + tile) * steps + step) * 4 + c) * 64 + lane;
+    *(uint4 *)(dst + o * 8) = *(const uint4 *)v;
+  }
+}
+
+// E4M3: one thread per 16-byte chunk (k-groups 2j and 2j+1 of one lane).
+__global__ void k_tile_fp8(uint8_t *dst, const uint8_t *src, int rows, int cols, int untile) {
+  const int steps = (cols + 127) / 128, tiles = (rows + 15) / 16;
+  const size_t chunks = (size_t)tiles * steps * 128;
+  for (size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x; q < chunks; q += (size_t)gridDim.x * blockDim.x) {
+    const int lane = (int)(q & 63), j = (int)((q >> 6) & 1);
+    const size_t ts = q >> 7;
+    const int step = (int)(ts % steps), tile = (int)(ts / steps);
+    const int r = tile * 16 + (lane & 15);
+    uint8_t *t = dst + q * 16;
+    const uint8_t *tt = src + q * 16;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int k = step * 128 + 32 * (2 * j + h) + 8 * (lane >> 4) + e;
+        if (r >= rows || k >= cols) {
+          if (!untile) t[8 * h + e] = 0;
+          continue;
+        }
+        if (untile)
+          dst[(size_t)r * cols + k] = tt[8 * h + e];
+        else
+          t[8 * h + e] = src[(size_t)r * cols + k];
+      }
   }
 }
 
@@ -94,22 +161,27 @@ __global__ __launch_bounds__(256) void k_fp8_mirror(const uint16_t *src, int h, 
   for (int i = threadIdx.x; i < h; i += blockDim.x) out[i] = f32_to_e4m3(bf16_to_f32(row[i]) / s);
 }
 
+// Cached K is stored with its head dimensions in RoPE pair order (dim i at
+// position 2i for i < d/2, at 2(i - d/2) + 1 otherwise); the copy restores
+// the natural order.
 __global__ void k_read_kv(const uint8_t *pool, const int32_t *bt, int L, int layer, int n_kv, int d, int eb, int row0,
                           int n_rows, uint8_t *k_out, uint8_t *v_out) {
   const size_t row_bytes = (size_t)n_kv * d * eb;
   const size_t total = (size_t)n_rows * row_bytes;
+  const int half = d >> 1;
   for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (size_t)gridDim.x * blockDim.x) {
     const int r = (int)(e / row_bytes);
     const size_t within = e % row_bytes;
     const int g = (int)(within / ((size_t)d * eb));
-    const size_t de = within % ((size_t)d * eb);
+    const int de = (int)(within % ((size_t)d * eb));
+    const int i = de / eb, byte = de % eb;
+    const int j = i < half ? 2 * i : 2 * (i - half) + 1;
     const int pos = row0 + r;
     const int32_t blk = bt[pos >> 4];
     const size_t tile = (size_t)DFLASH_KV_BLOCK * d * eb;
-    const size_t kb = ((((size_t)blk * L + layer) * 2 + 0) * n_kv + g) * tile + (size_t)(pos & 15) * d * eb + de;
-    const size_t vb = kb + (size_t)n_kv * tile;
-    if (k_out) k_out[e] = pool[kb];
-    if (v_out) v_out[e] = pool[vb];
+    const size_t base = ((((size_t)blk * L + layer) * 2 + 0) * n_kv + g) * tile + (size_t)(pos & 15) * d * eb;
+    if (k_out) k_out[e] = pool[base + (size_t)j * eb + byte];
+    if (v_out) v_out[e] = pool[base + (size_t)n_kv * tile + de];
   }
 }
 
@@ -133,9 +205,32 @@ hipError_t launch_rmsnorm(const float *x, int ldx, const float *gain, float eps,
 }
 
 hipError_t launch_convert_rows(uint16_t *dst, const void *src, const void *src2, int rows, int cols, bool src_f32,
-                               bool interleave, hipStream_t s) {
+                               int order, int head_dim, hipStream_t s) {
   hipLaunchKernelGGL(k_convert_rows, dim3(grid_for((size_t)rows * cols, 256)), dim3(256), 0, s, dst, src, src2, rows,
-                     cols, (int)src_f32, (int)interleave);
+                     cols, (int)src_f32, order, head_dim);
+  return hipGetLastError();
+}
+
+size_t tiled_elems(int rows, int cols) { return (size_t)((rows + 15) / 16) * 16 * (size_t)((cols + 127) / 128) * 128; }
+
+hipError_t launch_tile_rows(uint16_t *dst, int dst_row0, const void *src, const void *src2, int rows, int cols,
+                            bool src_f32, int order, int head_dim, hipStream_t s) {
+  if (dst_row0 % 16) return hipErrorInvalidValue;
+  const size_t chunks = (size_t)((rows + 15) / 16) * ((cols + 127) / 128) * 256;
+  hipLaunchKernelGGL(k_tile_rows, dim3(grid_for(chunks, 256)), dim3(256), 0, s, dst, dst_row0 / 16, src, src2, rows,
+                     cols, (int)src_f32, order, head_dim);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_fp8(uint8_t *dst, const uint8_t *src, int rows, int cols, hipStream_t s) {
+  const size_t chunks = (size_t)((rows + 15) / 16) * ((cols + 127) / 128) * 128;
+  hipLaunchKernelGGL(k_tile_fp8, dim3(grid_for(chunks, 256)), dim3(256), 0, s, dst, src, rows, cols, 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_untile_fp8(uint8_t *dst, const uint8_t *src, int rows, int cols, hipStream_t s) {
+  const size_t chunks = (size_t)((rows + 15) / 16) * ((cols + 127) / 128) * 128;
+  hipLaunchKernelGGL(k_tile_fp8, dim3(grid_for(chunks, 256)), dim3(256), 0, s, dst, src, rows, cols, 1);
   return hipGetLastError();
 }
 

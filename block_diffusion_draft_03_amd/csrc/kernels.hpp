@@ -12,35 +12,49 @@ namespace dflash {
 
 // ---------------------------------------------------------------- GEMMs ----
 // Skinny weight-streaming GEMM: out[m, n] = sum_k A[m, k] * W[n, k] for
-// M <= 64 activation rows (bf16, row stride lda) against a weight matrix W
-// [N, K] (bf16, or E4M3 codes with per-row f32 scales). Work: one workgroup
-// per 128 output columns and K slice; split-K partials are reduced in fixed
-// split order by the last workgroup of each column group.
+// M <= 64 activation rows against a bf16 weight matrix W [N, K]. A is bf16
+// activations (row stride lda), or, when H is set, the RMSNorm of the fp32
+// residual rows H formed while loading. Work: one workgroup per 16 * tn
+// weight rows and K slice, nw waves splitting the slice; with splits > 1 the
+// epilogue must be EPI_PARTIAL and k_resid_norm finishes the sum.
 
 enum Epi : int {
   EPI_F32 = 0,        // out_f32[m, n] = acc
-  EPI_RESID = 1,      // out_f32[m, n] += acc (the fp32 residual stream)
-  EPI_SWIGLU = 2,     // W rows are 64-row gate / up blocks; out_bf16[m, i] = silu(gate) * up
-  EPI_QKV_ROPE = 3,   // columns [Q | K | V]; RoPE on Q and K from the per-row cos/sin table
-  EPI_KV_SCATTER = 4  // columns [K0 | V0 | K1 | V1 ...]; RoPE on K at the row position, store into the paged pool
+  EPI_RESID = 1,      // out_f32[m, n] += acc; per-unit sums of squares of the new rows to ss_out
+  EPI_SWIGLU = 2,     // W rows alternate gate / up; out_bf16[m, i] = silu(gate_i) * up_i
+  EPI_QKV_ROPE = 3,   // columns [Q | K | V] (Q, K in pair order); RoPE on Q and K from the cos/sin table
+  EPI_KV_SCATTER = 4, // columns [K0 | V0 | K1 | V1 ...]; RoPE on K at the row position, store into the paged pool
+  EPI_PARTIAL = 5     // out_f32[(split * ld_split + m) * ldo + n] = this split's partial sum
 };
 
 constexpr int GEMM_MAX_ROWS = 64;
 
+// Launch shape of one GEMM; a function of (N, K) only, so a row's result does
+// not depend on how many rows share the launch.
+struct GemmPlan {
+  int tn, nw, st, splits, kslice;
+};
+GemmPlan gemm_plan(int N, int K, bool allow_split);
+
 struct GemmArgs {
-  const uint16_t *A;
+  const uint16_t *A;  // bf16 activations [M, lda] (when H is null)
   int lda, M;
-  const void *W;      // [N, K] bf16 or E4M3
+  const float *H;     // fp32 residual rows [M, lda] to normalise while loading, or null
+  const float *gain;  // [K] RMSNorm gain (with H)
+  float eps;
+  const float *ss_in; // per-unit row sums of squares of H: ss_in[u * ss_ld + ss_row0 + m], u < ss_units
+  int ss_units, ss_ld, ss_row0;
+  const void *W;      // [N, K] bf16
   int N, K;
-  int kslice, splits; // K slice per workgroup (multiple of 128), number of slices
-  float *ws;          // split-K partials
-  int *counters;      // per column group, zero between launches
+  int tn, nw, st, splits, kslice;
 };
 
 struct EpiArgs {
   float *out_f32;
   uint16_t *out_bf16;
-  int ldo;
+  int ldo, ld_split;
+  float *ss_out;      // EPI_RESID: [units][ss_ld] per-unit sums of squares, or null
+  int ss_ld, ss_row0;
   // QKV RoPE
   const float2 *cs;   // [M][head_dim / 2] (cos, sin) of each row's position
   int head_dim, q_dim, kv_dim;
@@ -53,13 +67,20 @@ struct EpiArgs {
   const int32_t *row_bt[GEMM_MAX_ROWS];
 };
 
-// Split choice depends only on (N, K) so a row's result does not depend on
-// how many rows share the launch.
-void gemm_plan(int N, int K, int *kslice, int *splits);
-size_t gemm_ws_floats(int N, int K);   // workspace for M up to 64
-int gemm_groups(int N);
+hipError_t launch_gemm(int epi, const GemmArgs &g, const EpiArgs &e, hipStream_t s);
 
-hipError_t launch_gemm(int epi, bool w_fp8, const GemmArgs &g, const EpiArgs &e, hipStream_t s);
+// Finish of a split GEMM into the residual stream, one workgroup per row:
+// h[m] = (init_zero ? 0 : h[m]) + sum over splits of part[s][m]; then, if out
+// is set, out[m] = bf16(RMSNorm(h[m]) * gain).
+struct ResidNormArgs {
+  float *h;
+  const float *part;   // [splits][ld_split][n]
+  int splits, ld_split, n, init_zero;
+  const float *gain;
+  float eps;
+  uint16_t *out;
+};
+hipError_t launch_resid_norm(const ResidNormArgs &a, int M, hipStream_t s);
 
 // --------------------------------------------------------------- LM head ---
 struct LmArgs {
@@ -84,6 +105,8 @@ struct LmFinishArgs {
   int P, M, gamma, num_drafts;
   uint32_t *ids;
   float *conf, *row_prob;
+  float *p1;       // [M] scratch: top-1 probability of every row
+  int *counters;   // [n_seq] zero between launches
 };
 hipError_t launch_lm_finish(const LmFinishArgs &a, int n_seq, hipStream_t s);
 
@@ -127,11 +150,33 @@ hipError_t launch_setup(const SetupArgs &a, int M, hipStream_t s);
 hipError_t launch_rmsnorm(const float *x, int ldx, const float *gain, float eps, int n, uint16_t *out, int ldo,
                           int M, hipStream_t s);
 
-// dst rows [0, rows) of [rows, cols] bf16 from src rows (bf16 or f32);
-// interleave != 0: dst is the 64-row gate / up interleave of src (gate) and
-// src2 (up), each [rows / 2, cols].
+// Row orders of the repacked weights.
+enum RowOrder : int {
+  ROWS_SAME = 0,      // dst row r = src row r
+  ROWS_GATE_UP = 1,   // dst row 2i = src (gate) row i, dst row 2i+1 = src2 (up) row i
+  ROWS_ROPE_PAIRS = 2 // within each head of head_dim rows: dst row j = src row j/2 + (j%2) * head_dim/2
+};
+
+// dst rows [0, rows) of [rows, cols] bf16 from src rows (bf16 or f32) in the
+// given row order.
 hipError_t launch_convert_rows(uint16_t *dst, const void *src, const void *src2, int rows, int cols, bool src_f32,
-                               bool interleave, hipStream_t s);
+                               int order, int head_dim, hipStream_t s);
+
+// Tile-major weight layout read by the GEMM kernels. A [rows, cols] matrix
+// becomes ceil(rows/16) tiles of 16 rows; each tile holds ceil(cols/128)
+// steps of 128 columns; a bf16 step is 4 k-groups x 64 lanes x 8 values, lane
+// l of k-group c holding row l % 16, columns 32c + 8(l / 16) .. +7. Rows and
+// columns past the matrix are zero. An E4M3 step is 2 pairs x 64 lanes x 16
+// bytes: pair j of lane l holds the 8 codes of k-group 2j then of 2j + 1.
+size_t tiled_elems(int rows, int cols);
+// bf16 tiled copy of src rows (bf16 or f32) in the given row order, written
+// at tile row offset dst_row0 (a multiple of 16) of a matrix with `cols`.
+hipError_t launch_tile_rows(uint16_t *dst, int dst_row0, const void *src, const void *src2, int rows, int cols,
+                            bool src_f32, int order, int head_dim, hipStream_t s);
+// E4M3 tiled copy of row-major codes [rows, cols].
+hipError_t launch_tile_fp8(uint8_t *dst, const uint8_t *src, int rows, int cols, hipStream_t s);
+// Row-major copy of a tiled E4M3 matrix.
+hipError_t launch_untile_fp8(uint8_t *dst, const uint8_t *src, int rows, int cols, hipStream_t s);
 hipError_t launch_to_f32(float *dst, const void *src, int n, bool src_f32, hipStream_t s);
 
 // FP8 mirror of a bf16 [V, h] head: per-row scale amax / 448, E4M3 codes.

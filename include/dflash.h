@@ -97,10 +97,11 @@ typedef struct {
 } dflash_layer_weights;
 
 /* Weights given to dflash_build. The drafter checkpoint's tensors (fc, norms,
- * layers) are copied into the head's own layout during the call and may be
- * freed afterwards. The target's embedding and LM head are borrowed when they
- * are bf16 and must outlive the head ([Head/atlas], struct description: the
- * drafter uses the target's embed_tokens and lm_head). */
+ * layers) and the LM head (bf16, or the FP8 codes and scales) are copied into
+ * the head's tile-major streaming layout during the call and may be freed
+ * afterwards. The target's embedding is borrowed when it is bf16 and must
+ * outlive the head ([Head/atlas], struct description: the drafter uses the
+ * target's embed_tokens and lm_head). */
 typedef struct {
   const void *fc;             /* device [h, T*Ht], weight_dtype ([Head/atlas] field fc) */
   const void *hidden_norm;    /* device [h] ([Head/atlas] field hidden_norm) */
