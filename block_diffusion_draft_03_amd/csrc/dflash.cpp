@@ -29,8 +29,10 @@ int set_err(int code, const std::string &m) {
 constexpr uint64_t HEAD_MAGIC = 0x44464c4153484844ull;   // "DFLASHHD"
 constexpr uint64_t STATE_MAGIC = 0x44464c4153485354ull;  // "DFLASHST"
 constexpr uint64_t DEAD_MAGIC = 0xdeadull;
-constexpr int ATTN_SLOTS = 1024;   // (sequence, kv head, key chunk) partials per layer, at least
-constexpr int ATTN_MIN_CHUNK = 64;
+constexpr int ATTN_SLOTS = 1024;     // (sequence, kv head, key chunk) partials per layer, at least
+constexpr int ATTN_GROUP_KEYS = 64;  // keys an attention workgroup loads at once
+constexpr int ATTN_MAX_CHUNK = 992;  // keys per chunk (block ids staged per workgroup)
+constexpr int ATTN_MAX_SPLITS = 64;  // chunks per (sequence, kv head) merged by one wave
 
 #define HIP_TRY(expr)                                                                          \
   do {                                                                                         \
@@ -294,7 +296,12 @@ int build_impl(dflash_head *H, const dflash_weights *w, hipStream_t st) {
   for (int K : {g.q_dim, g.I, g.fc_in}) max_splits = std::max(max_splits, gemm_plan(g.h, K, true).splits);
   TRY(H->alloc(&H->part, (size_t)max_splits * std::max<size_t>(M, GEMM_MAX_ROWS) * h));
   const size_t R = (size_t)g.rep * g.gamma;
-  H->attn_slots = std::max(ATTN_SLOTS, g.max_batch * g.n_kv);
+  {
+    // most chunks one (sequence, kv head) can need: the window plus the block
+    const int max_keys = (g.W > 0 ? g.W : 0) + g.gamma;
+    const int forced = std::min(ATTN_MAX_SPLITS, (max_keys + ATTN_MAX_CHUNK - 1) / ATTN_MAX_CHUNK + 1);
+    H->attn_slots = std::max(ATTN_SLOTS, g.max_batch * g.n_kv * forced);
+  }
   TRY(H->alloc(&H->o_part, (size_t)H->attn_slots * R * g.d));
   TRY(H->alloc(&H->ml_part, (size_t)H->attn_slots * R * 2));
   H->lm_P = lm_parts(g.V);
@@ -429,11 +436,19 @@ int propose_impl(dflash_head *H, dflash_state *const *states, int n, const uint3
     max_S = std::max(max_S, c - lo + g.gamma);
   }
   {
-    int splits = std::max(1, std::min((max_S + ATTN_MIN_CHUNK - 1) / ATTN_MIN_CHUNK, H->attn_slots / (n * g.n_kv)));
+    // key chunks per (sequence, kv head): one group of five 32-key tiles each
+    // (loaded at once), unless that needs more partial slots than the
+    // target; then larger chunks, at most ATTN_MAX_CHUNK keys
+    int splits = (max_S + ATTN_GROUP_KEYS - 1) / ATTN_GROUP_KEYS;
+    if (n * g.n_kv * splits > ATTN_SLOTS)
+      splits = std::max((max_S + ATTN_MAX_CHUNK - 1) / ATTN_MAX_CHUNK, ATTN_SLOTS / (n * g.n_kv));
+    splits = std::max(1, std::min(splits, ATTN_MAX_SPLITS));
     int chunk = (max_S + splits - 1) / splits;
     chunk = (chunk + 31) / 32 * 32;
     aa.chunk = chunk;
     aa.max_splits = (max_S + chunk - 1) / chunk;
+    if (n * g.n_kv * aa.max_splits > H->attn_slots || chunk > ATTN_MAX_CHUNK)
+      return set_err(DFLASH_E_INVALID, "attention partial buffer too small for this batch");
   }
 
   // act holds RMSNorm(h) with the next consumer's gain: layer 0's input norm

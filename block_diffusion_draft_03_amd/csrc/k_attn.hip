@@ -6,7 +6,8 @@
 // rows, 32 per wave. Keys are the ctx rows [win_start, ctx_len) read through
 // the block table from the paged pool, followed by the gamma block rows (K/V
 // straight from the QKV output). Every 32-key tile is staged in LDS (K
-// row-major, V transposed), with FP8 codes widened to bf16 on the way.
+// row-major, V transposed), FP8 codes widened to bf16 on the way; the global
+// loads of tile t + 1 are issued before tile t is computed.
 //
 // The products are computed transposed so every per-query quantity stays in
 // one lane: S^T = K Q^T (MFMA A = 16 keys x 32 dims, B = Q^T), giving lane l
@@ -15,8 +16,11 @@
 // keys {4g..4g+3, 16+4g..16+4g+3} and whose A operand reads V^T for the same
 // key set. Online softmax in base 2; the running max is shared across the
 // four lane groups with two shuffles, the running sum stays per lane until
-// the end. Each workgroup writes an unnormalised partial (O, max, sum) and a
-// combine kernel merges the chunks of a (sequence, kv head).
+// the end. Each workgroup writes an unnormalised partial (O, max, sum); the
+// combine kernel merges the chunks of every query row with one wave.
+//
+// Q and K carry their head dimensions in RoPE pair order (the QKV epilogue and
+// the cache use the same order), which leaves every score unchanged.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -24,7 +28,13 @@ namespace dflash {
 
 namespace {
 
-constexpr int KT = 32;  // keys per tile
+constexpr int KT = 32;          // keys per tile
+constexpr int GT = 2;           // tiles whose loads are issued together
+constexpr int MAX_BT = 64;      // block ids staged per workgroup (chunk <= 1008 keys)
+
+struct Staged {
+  uint4 k[2], v[2];
+};
 
 template <int D>
 __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
@@ -32,8 +42,11 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   constexpr int DT = D / 16;                // 16-dim output tiles
   constexpr int KP = D + 8;                 // padded LDS row of K
   constexpr int VP = KT + 8;                // padded LDS row of V^T
+  constexpr int ITEMS = KT * (D / 8);       // 8-dim chunks per tile
+  constexpr int PER = (ITEMS + 255) / 256;  // chunks per thread (<= 2)
   __shared__ uint16_t Ks[KT][KP];
   __shared__ uint16_t Vt[D][VP];
+  __shared__ int32_t s_bt[MAX_BT];
 
   const int s = blockIdx.z, g = blockIdx.y, c = blockIdx.x;
   const AttnSeq sq = a.seq[s];
@@ -46,6 +59,14 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lg = lane >> 4, r16 = lane & 15;
   const uint4 z4 = {0u, 0u, 0u, 0u};
+
+  // block ids covering this chunk's ctx rows
+  const int pos_lo = sq.win_start + key_lo;
+  const int blk_lo = pos_lo >> 4;
+  if (key_lo < S_ctx) {
+    const int blk_hi = (sq.win_start + min(key_hi, S_ctx) - 1) >> 4;
+    for (int i = threadIdx.x; i <= blk_hi - blk_lo; i += blockDim.x) s_bt[i] = sq.bt[blk_lo + i];
+  }
 
   // Q fragments (B operand of S^T = K Q^T): query column r16 of each tile.
   bf16x8 qf[2][KS];
@@ -78,45 +99,75 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  __syncthreads();  // s_bt
 
   const size_t head_stride = (size_t)DFLASH_KV_BLOCK * D;  // one (block, layer, K|V, head) tile
-  for (int t0 = key_lo; t0 < key_hi; t0 += KT) {
-    __syncthreads();
-    // Stage K and V^T for keys t0 .. t0 + 31 (8 dims per item).
-    for (int e = threadIdx.x; e < KT * (D / 8); e += blockDim.x) {
+  auto load_tile = [&](int t0, Staged &st) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = threadIdx.x + i * 256;
+      st.k[i] = z4;
+      st.v[i] = z4;
+      if (e >= ITEMS) continue;
       const int key = e / (D / 8), dc = (e % (D / 8)) * 8;
       const int kidx = t0 + key;
-      uint4 kv8 = z4, vv8 = z4;
-      if (kidx < key_hi) {
-        if (kidx < S_ctx) {
-          const int pos = sq.win_start + kidx;
-          const int32_t blk = sq.bt[pos >> 4];
-          const size_t base = (((size_t)blk * a.L + a.layer) * 2 * a.n_kv + g) * head_stride + (size_t)(pos & 15) * D + dc;
-          const size_t vofs = (size_t)a.n_kv * head_stride;
-          if (a.kv_fp8) {
-            const uint8_t *p = (const uint8_t *)a.pool;
-            const uint2 kc = *(const uint2 *)(p + base), vc = *(const uint2 *)(p + base + vofs);
-            uint2 lo = e4m3x4_to_bf16x4(kc.x), hi = e4m3x4_to_bf16x4(kc.y);
-            kv8 = uint4{lo.x, lo.y, hi.x, hi.y};
-            lo = e4m3x4_to_bf16x4(vc.x);
-            hi = e4m3x4_to_bf16x4(vc.y);
-            vv8 = uint4{lo.x, lo.y, hi.x, hi.y};
-          } else {
-            const uint16_t *p = (const uint16_t *)a.pool;
-            kv8 = *(const uint4 *)(p + base);
-            vv8 = *(const uint4 *)(p + base + vofs);
-          }
+      if (kidx >= key_hi) continue;
+      if (kidx < S_ctx) {
+        const int pos = sq.win_start + kidx;
+        const int32_t blk = s_bt[(pos >> 4) - blk_lo];
+        const size_t base = (((size_t)blk * a.L + a.layer) * 2 * a.n_kv + g) * head_stride + (size_t)(pos & 15) * D + dc;
+        const size_t vofs = (size_t)a.n_kv * head_stride;
+        if (a.kv_fp8) {
+          const uint8_t *p = (const uint8_t *)a.pool;
+          const uint2 kc = *(const uint2 *)(p + base), vc = *(const uint2 *)(p + base + vofs);
+          st.k[i] = uint4{kc.x, kc.y, 0u, 1u};  // raw codes, widened when staged
+          st.v[i] = uint4{vc.x, vc.y, 0u, 1u};
         } else {
-          const uint16_t *brow = a.qkv + (size_t)(s * a.gamma + (kidx - S_ctx)) * a.ld;
-          kv8 = *(const uint4 *)(brow + a.k_off + g * D + dc);
-          vv8 = *(const uint4 *)(brow + a.v_off + g * D + dc);
+          const uint16_t *p = (const uint16_t *)a.pool;
+          st.k[i] = *(const uint4 *)(p + base);
+          st.v[i] = *(const uint4 *)(p + base + vofs);
         }
+      } else {
+        const uint16_t *brow = a.qkv + (size_t)(s * a.gamma + (kidx - S_ctx)) * a.ld;
+        st.k[i] = *(const uint4 *)(brow + a.k_off + g * D + dc);
+        st.v[i] = *(const uint4 *)(brow + a.v_off + g * D + dc);
+      }
+    }
+  };
+  auto store_tile = [&](int t0, const Staged &st) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = threadIdx.x + i * 256;
+      if (e >= ITEMS) continue;
+      const int key = e / (D / 8), dc = (e % (D / 8)) * 8;
+      const int kidx = t0 + key;
+      uint4 kv8 = st.k[i], vv8 = st.v[i];
+      if (a.kv_fp8 && kidx < S_ctx && kidx < key_hi) {
+        uint2 lo = e4m3x4_to_bf16x4(kv8.x), hi = e4m3x4_to_bf16x4(kv8.y);
+        kv8 = uint4{lo.x, lo.y, hi.x, hi.y};
+        lo = e4m3x4_to_bf16x4(vv8.x);
+        hi = e4m3x4_to_bf16x4(vv8.y);
+        vv8 = uint4{lo.x, lo.y, hi.x, hi.y};
       }
       *(uint4 *)&Ks[key][dc] = kv8;
       const uint16_t *vh = (const uint16_t *)&vv8;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) Vt[dc + i][key] = vh[i];
+      for (int q = 0; q < 8; ++q) Vt[dc + q][key] = vh[q];
     }
+  };
+
+  // Groups of GT tiles: all global loads of a group are issued together,
+  // then its tiles are staged and computed one by one.
+  for (int g0 = key_lo; g0 < key_hi; g0 += GT * KT) {
+    Staged grp[GT];
+#pragma unroll
+    for (int t = 0; t < GT; ++t) load_tile(g0 + t * KT, grp[t]);
+#pragma unroll
+    for (int t = 0; t < GT; ++t) {
+    const int t0 = g0 + t * KT;
+    if (t0 >= key_hi) break;
+    __syncthreads();  // previous tile's readers are done
+    store_tile(t0, grp[t]);
     __syncthreads();
 
 #pragma unroll
@@ -176,6 +227,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
         o[qt][dt] = mfma16x16x32(vf, pf, o[qt][dt]);
       }
     }
+    }
   }
 
   // Unnormalised partial of this chunk: O, running max (base 2), sum.
@@ -188,9 +240,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
     l_tot += __shfl_xor(l_tot, 32, WAVE);
     if ((wave * 2 + qt) * 16 >= R || q >= R) continue;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      *(f32x4 *)(a.o_part + (part + q) * D + dt * 16 + 4 * lg) = o[qt][dt];
-    }
+    for (int dt = 0; dt < DT; ++dt) *(f32x4 *)(a.o_part + (part + q) * D + dt * 16 + 4 * lg) = o[qt][dt];
     if (lg == 0) {
       a.ml_part[(part + q) * 2 + 0] = m_run[qt];
       a.ml_part[(part + q) * 2 + 1] = l_tot;
@@ -198,49 +248,78 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   }
 }
 
-// Merge the key chunks of every (sequence, kv head, query row, dim).
+// Merge the key chunks of one query row per wave: lane s < nsplit reads
+// chunk s's (max, sum); the weights exp2(m_s - M) are shared by shuffles and
+// every lane accumulates its dimensions over the chunks in order.
+template <int D>
 __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a, int n_seq) {
-  const int R = a.rep * a.gamma, D = a.head_dim;
-  const size_t total = (size_t)n_seq * a.n_kv * R * D;
-  for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (size_t)gridDim.x * blockDim.x) {
-    const int dd = (int)(e % D);
-    const int q = (int)((e / D) % R);
-    const int g = (int)((e / ((size_t)D * R)) % a.n_kv);
-    const int s = (int)(e / ((size_t)D * R * a.n_kv));
-    const AttnSeq sq = a.seq[s];
-    const int S = sq.ctx_len - sq.win_start + a.gamma;
-    const int nsplit = (S + a.chunk - 1) / a.chunk;
-    const size_t base = (size_t)(s * a.n_kv + g) * a.max_splits;
-    float M = -__builtin_huge_valf();
-    for (int c = 0; c < nsplit; ++c) M = fmaxf(M, a.ml_part[((base + c) * R + q) * 2]);
-    float num = 0.0f, den = 0.0f;
-    for (int c = 0; c < nsplit; ++c) {
-      const size_t pr = (base + c) * R + q;
-      const float w = fast_exp2(a.ml_part[pr * 2] - M);
-      den += w * a.ml_part[pr * 2 + 1];
-      num += w * a.o_part[pr * D + dd];
-    }
-    const int hq = g * a.rep + q / a.gamma, j = q % a.gamma;
-    a.out[(size_t)(s * a.gamma + j) * a.out_ld + hq * D + dd] = f32_to_bf16(num / den);
+  constexpr int DPL = D >= 64 ? D / 64 : 1;  // dims per lane
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int R = a.rep * a.gamma;
+  const int row = blockIdx.x * 4 + wave;  // (s, g, q)
+  if (row >= n_seq * a.n_kv * R) return;
+  const int q = row % R, g = (row / R) % a.n_kv, s = row / (R * a.n_kv);
+  const AttnSeq sq = a.seq[s];
+  const int S = sq.ctx_len - sq.win_start + a.gamma;
+  const int nsplit = (S + a.chunk - 1) / a.chunk;  // <= 64
+  const size_t base = (size_t)(s * a.n_kv + g) * a.max_splits;
+  float m = -__builtin_huge_valf(), l = 0.0f;
+  if (lane < nsplit) {
+    m = a.ml_part[((base + lane) * R + q) * 2];
+    l = a.ml_part[((base + lane) * R + q) * 2 + 1];
   }
+  float M = m;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, WAVE));
+  const float w = lane < nsplit ? fast_exp2(m - M) : 0.0f;
+  const float den = wave_sum(w * l);
+  float acc[DPL];
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) acc[i] = 0.0f;
+  const bool active = D >= 64 || lane < D;
+#pragma unroll 8
+  for (int c = 0; c < nsplit; ++c) {
+    const float wc = __shfl(w, c, WAVE);
+    const float *op = a.o_part + ((base + c) * R + q) * D;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i)
+      if (active) acc[i] += wc * op[lane + 64 * i];
+  }
+  const int hq = g * a.rep + q / a.gamma, j = q % a.gamma;
+  uint16_t *out = a.out + (size_t)(s * a.gamma + j) * a.out_ld + hq * D;
+#pragma unroll
+  for (int i = 0; i < DPL; ++i)
+    if (active) out[lane + 64 * i] = f32_to_bf16(acc[i] / den);
 }
 
 }  // namespace
 
+int attn_max_chunk_blocks() { return MAX_BT; }
+
 hipError_t launch_attention(const AttnArgs &a, int n_seq, hipStream_t s) {
+  if (a.chunk % KT || (a.chunk / DFLASH_KV_BLOCK) + 2 > MAX_BT || a.max_splits > 64) return hipErrorInvalidValue;
   dim3 grid(a.max_splits, a.n_kv, n_seq), block(256);
+  const int rows = n_seq * a.n_kv * a.rep * a.gamma;
+  dim3 cgrid((rows + 3) / 4);
   switch (a.head_dim) {
-    case 16: hipLaunchKernelGGL(k_attn<16>, grid, block, 0, s, a); break;
-    case 32: hipLaunchKernelGGL(k_attn<32>, grid, block, 0, s, a); break;
-    case 64: hipLaunchKernelGGL(k_attn<64>, grid, block, 0, s, a); break;
-    case 128: hipLaunchKernelGGL(k_attn<128>, grid, block, 0, s, a); break;
+    case 16:
+      hipLaunchKernelGGL(k_attn<16>, grid, block, 0, s, a);
+      hipLaunchKernelGGL(k_attn_combine<16>, cgrid, block, 0, s, a, n_seq);
+      break;
+    case 32:
+      hipLaunchKernelGGL(k_attn<32>, grid, block, 0, s, a);
+      hipLaunchKernelGGL(k_attn_combine<32>, cgrid, block, 0, s, a, n_seq);
+      break;
+    case 64:
+      hipLaunchKernelGGL(k_attn<64>, grid, block, 0, s, a);
+      hipLaunchKernelGGL(k_attn_combine<64>, cgrid, block, 0, s, a, n_seq);
+      break;
+    case 128:
+      hipLaunchKernelGGL(k_attn<128>, grid, block, 0, s, a);
+      hipLaunchKernelGGL(k_attn_combine<128>, cgrid, block, 0, s, a, n_seq);
+      break;
     default: return hipErrorInvalidValue;
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const size_t total = (size_t)n_seq * a.n_kv * a.rep * a.gamma * a.head_dim;
-  const int blocks = (int)((total + 255) / 256);
-  hipLaunchKernelGGL(k_attn_combine, dim3(blocks), dim3(256), 0, s, a, n_seq);
   return hipGetLastError();
 }
 

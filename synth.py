@@ -107,15 +107,53 @@ def _rng(seed, *tags):
 def to_bf16_bits(x32):
     """float32 -> bf16 bit patterns (uint16), round to nearest, ties even."""
     b = np.ascontiguousarray(x32, dtype=np.float32).view(np.uint32)
-    return ((b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
+    if b.size < (1 << 22):
+        return ((b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
+    flat = b.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.uint16)
+
+    def conv(i):
+        s = slice(i, min(flat.size, i + (1 << 22)))
+        x = flat[s]
+        out[s] = (x + np.uint32(0x7FFF) + ((x >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(16) as ex:
+        list(ex.map(conv, range(0, flat.size, 1 << 22)))
+    return out.reshape(b.shape)
 
 
 def _store(x32, dtype):
     return np.ascontiguousarray(x32, dtype=np.float32) if dtype == "f32" else to_bf16_bits(x32)
 
 
+ROW_BLOCK = 4096  # rows drawn from one child stream (fixed, so values do not depend on threading)
+
+
 def _normal(seed, tag, shape, std):
-    return _rng(seed, tag).standard_normal(shape, dtype=np.float32) * np.float32(std)
+    """N(0, std) float32 of the given shape. Matrices are drawn in blocks of
+    ROW_BLOCK rows, block b from child stream (seed, tag, b), on a thread
+    pool; a vector is one block."""
+    if len(shape) == 1:
+        return _rng(seed, tag, 0).standard_normal(shape, dtype=np.float32) * np.float32(std)
+    rows, cols = shape
+    out = np.empty(shape, dtype=np.float32)
+
+    def fill(b):
+        r0 = b * ROW_BLOCK
+        r1 = min(rows, r0 + ROW_BLOCK)
+        blk = out[r0:r1]
+        _rng(seed, tag, b).standard_normal((r1 - r0, cols), dtype=np.float32, out=blk)
+        blk *= np.float32(std)
+
+    nb = (rows + ROW_BLOCK - 1) // ROW_BLOCK
+    if nb == 1:
+        fill(0)
+    else:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(min(16, nb)) as ex:
+            list(ex.map(fill, range(nb)))
+    return out
 
 
 def make_weights(geo: Geometry, seed: int = SEED_WEIGHTS, std: float = 0.02):
