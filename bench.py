@@ -50,6 +50,36 @@ def algorithmic_bytes(geo, ctx_rows, lm_rows_per_launch):
     return layer_w + lm + kv + embed, lm_launch
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lm_head_single_ctx1024_traffic.md")
+KERNEL_SOURCES = {"k_gemm.hip": os.path.join(ROOT, "block_diffusion_draft_03_amd", "csrc", "k_gemm.hip"),
+                  "common.hpp": os.path.join(ROOT, "block_diffusion_draft_03_amd", "csrc", "common.hpp")}
+
+
+def lm_head_traffic(workload):
+    """HBM bytes per LM-head dispatch from the committed rocprofv3 PMC summary
+    (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads for a
+    plain 1 GiB copy), or None when that summary was taken on another
+    workload or on kernel sources that have changed since."""
+    import hashlib
+    if workload != "single_ctx1024" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals, hashes = {}, {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            p = line.split()
+            if len(p) == 3 and p[0] == "source_sha256":
+                hashes[p[1]] = p[2]
+            elif len(p) == 2 and p[0].endswith(("_dispatch", "_gib")):
+                vals[p[0]] = float(p[1])
+    for name, path in KERNEL_SOURCES.items():
+        with open(path, "rb") as f:
+            if hashes.get(name) != hashlib.sha256(f.read()).hexdigest():
+                return None
+    fetch = vals["fetch_kib_per_dispatch"] * 1024 * (1 << 30) / (vals["copy_fetch_kib_per_gib"] * 1024)
+    write = vals["write_kib_per_dispatch"] * 1024 * (1 << 30) / (vals["copy_write_kib_per_gib"] * 1024)
+    return int(round(fetch + write))
+
+
 def precompute_bytes(geo, rows):
     h = geo.hidden
     fc_in = geo.num_target_layers * geo.target_hidden
@@ -272,7 +302,7 @@ def main():
         "propose_algorithmic_bytes": fwd_bytes,
         "roofline": {"kernel": "k_lm_head (LM-head GEMM + argmax stage 1)", "bound": "hbm",
                      "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(lm_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(lm_gbs / HBM_PEAK_GBS, 4), "traffic": lm_head_traffic(wl.name),
                      "bytes_per_launch": lm_bytes, "avg_launch_us": round(lm_avg_s * 1e6, 2),
                      "launches": lm_launches},
         "wall_s_timed": round(wall, 3),
