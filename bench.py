@@ -28,6 +28,7 @@ if ROOT not in sys.path:
 
 METRIC = "draft blocks/sec and µs/propose (γ=16, L=8, vocab 248320); % HBM roofline"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix peak of MI355X
 
 
 def log(*a):
@@ -48,6 +49,20 @@ def algorithmic_bytes(geo, ctx_rows, lm_rows_per_launch):
     embed = n * geo.gamma * h * 2
     lm_launch = lm + lm_rows_per_launch * h * 2
     return layer_w + lm + kv + embed, lm_launch
+
+
+def algorithmic_flops(geo, ctx_rows):
+    """Multiply-add flops (2 per MAC) of a propose: every projection and the LM
+    head over n * gamma rows, and attention (QK^T and PV) of each sequence's
+    gamma rows over its window plus the block; and those of the LM head."""
+    h, I, L, g = geo.hidden, geo.intermediate, geo.num_layers, geo.gamma
+    d, nq = geo.head_dim, geo.num_q_heads
+    q_dim, kv_dim = nq * d, geo.num_kv_heads * d
+    M = len(ctx_rows) * g
+    proj = 2 * M * L * ((q_dim + 2 * kv_dim) * h + h * q_dim + 2 * I * h + h * I)
+    attn = sum(4 * g * (min(c, geo.ctx_window) + g) * nq * d * L for c in ctx_rows)
+    lm = 2 * M * geo.vocab * h
+    return proj + attn + lm, lm
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lm_head_single_ctx1024_traffic.md")
@@ -272,11 +287,26 @@ def main():
 
     ctx_rows = [s.ctx_len + (0 if wl.trim else wl.new_rows) for s in w.states]
     rows = wl.n_seqs * geo.gamma
-    lm_rows = min(64, rows)
+    lm_rows = rows  # one LM-head launch covers every row
     fwd_bytes, lm_bytes = algorithmic_bytes(geo, ctx_rows, lm_rows)
+    fwd_flops, lm_flops = algorithmic_flops(geo, ctx_rows)
     lm_avg_s = lm_ms / max(1, lm_launches) / 1e3
     lm_gbs = lm_bytes / lm_avg_s / 1e9
+    lm_tflops = lm_flops / lm_avg_s / 1e12
     blocks_per_s = wl.n_seqs / (ms_step / 1e3)
+    if rows > 64:
+        # many rows: the LM head is an MFMA-bound GEMM (bf16 MFMA, also for the E4M3 head)
+        roofline = {"kernel": "k_blm_head (tiled LM-head GEMM + argmax stage 1)", "bound": "mfma",
+                    "achieved": round(lm_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(lm_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                    "flops_per_launch": lm_flops, "avg_launch_us": round(lm_avg_s * 1e6, 2),
+                    "launches": lm_launches}
+    else:
+        roofline = {"kernel": "k_lm_head (LM-head GEMM + argmax stage 1)", "bound": "hbm",
+                    "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(lm_gbs / HBM_PEAK_GBS, 4), "traffic": lm_head_traffic(wl.name),
+                    "bytes_per_launch": lm_bytes, "avg_launch_us": round(lm_avg_s * 1e6, 2),
+                    "launches": lm_launches}
     out = {
         "metric": METRIC,
         "value": round(blocks_per_s, 3),
@@ -300,11 +330,9 @@ def main():
         "us_per_precompute": round(pre_ms / max(1, pre_n) * 1e3, 2),
         "propose_hbm_frac": round(fwd_bytes / (ms_prop / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
         "propose_algorithmic_bytes": fwd_bytes,
-        "roofline": {"kernel": "k_lm_head (LM-head GEMM + argmax stage 1)", "bound": "hbm",
-                     "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(lm_gbs / HBM_PEAK_GBS, 4), "traffic": lm_head_traffic(wl.name),
-                     "bytes_per_launch": lm_bytes, "avg_launch_us": round(lm_avg_s * 1e6, 2),
-                     "launches": lm_launches},
+        "propose_mfma_frac": round(fwd_flops / (ms_prop / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "propose_algorithmic_flops": fwd_flops,
+        "roofline": roofline,
         "wall_s_timed": round(wall, 3),
     }
     if not args.no_cpu_baseline:

@@ -18,7 +18,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdflash.so")
 HOST_LIB = os.path.join(PKG, "libdflash_host.so")
 
-HIP_SOURCES = ["k_gemm.hip", "k_attn.hip", "k_misc.hip", "dflash.cpp", "host_core.cpp"]
+HIP_SOURCES = ["k_gemm.hip", "k_bgemm.hip", "k_attn.hip", "k_misc.hip", "dflash.cpp", "host_core.cpp"]
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
                # packed fp32 ops are kept out of generated code
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -95,30 +95,30 @@ __device__ __forceinline__ void arg_init(ArgState &s) {
   s.idx = 0xFFFFFFFFu;
 }
 
-// Add one value with an index larger than every index already in s.
-__device__ __forceinline__ void arg_push(ArgState &s, float x, uint32_t v) {
-  if (x > s.mx) {
-    s.se = s.se * fast_exp2((s.mx - x) * LOG2E) + 1.0f;
-    s.mx = x;
-    s.idx = v;
-  } else {
-    s.se += fast_exp2((x - s.mx) * LOG2E);
-  }
+// Add one value with an index larger than every index already in s (when
+// `take` is set). Branch-free: one exponential either way.
+__device__ __forceinline__ void arg_push(ArgState &s, float x, uint32_t v, bool take = true) {
+  const bool up = x > s.mx;
+  const float e = fast_exp2((up ? s.mx - x : x - s.mx) * LOG2E);
+  const float se = up ? s.se * e + 1.0f : s.se + e;
+  s.se = take ? se : s.se;
+  s.idx = take && up ? v : s.idx;
+  s.mx = take && up ? x : s.mx;
 }
 
-// Merge two states (any index order).
-__device__ __forceinline__ ArgState arg_merge(const ArgState &a, const ArgState &b) {
-  if (b.mx == -__builtin_huge_valf()) return a;
-  if (a.mx == -__builtin_huge_valf()) return b;
+// Merge two states (any index order); ties go to the lower index.
+__device__ __forceinline__ ArgState arg_merge(const ArgState a, const ArgState b) {
+  const float ninf = -__builtin_huge_valf();
+  const bool pick_a = a.mx > b.mx || (a.mx == b.mx && a.idx < b.idx);
   ArgState r;
-  if (a.mx > b.mx || (a.mx == b.mx && a.idx < b.idx)) {
-    r.mx = a.mx;
-    r.idx = a.idx;
-  } else {
-    r.mx = b.mx;
-    r.idx = b.idx;
-  }
+  r.mx = pick_a ? a.mx : b.mx;
+  r.idx = pick_a ? a.idx : b.idx;
   r.se = a.se * fast_exp2((a.mx - r.mx) * LOG2E) + b.se * fast_exp2((b.mx - r.mx) * LOG2E);
+  // an empty side (nothing pushed) leaves the other unchanged
+  const bool a_empty = a.mx == ninf, b_empty = b.mx == ninf;
+  r.mx = b_empty ? a.mx : a_empty ? b.mx : r.mx;
+  r.idx = b_empty ? a.idx : a_empty ? b.idx : r.idx;
+  r.se = b_empty ? a.se : a_empty ? b.se : r.se;
   return r;
 }
 

@@ -79,8 +79,6 @@ struct dflash_head {
   float *hid = nullptr;
   uint16_t *act = nullptr, *qkv = nullptr, *attn = nullptr, *mlp = nullptr;
   float2 *cs = nullptr;
-  float *ws = nullptr;
-  int *counters = nullptr;
   float *o_part = nullptr, *ml_part = nullptr;
   float *lm_mx = nullptr, *lm_se = nullptr;
   uint32_t *lm_idx = nullptr;
@@ -305,9 +303,10 @@ int build_impl(dflash_head *H, const dflash_weights *w, hipStream_t st) {
   TRY(H->alloc(&H->o_part, (size_t)H->attn_slots * R * g.d));
   TRY(H->alloc(&H->ml_part, (size_t)H->attn_slots * R * 2));
   H->lm_P = lm_parts(g.V);
-  TRY(H->alloc(&H->lm_mx, (size_t)H->lm_P * M));
-  TRY(H->alloc(&H->lm_se, (size_t)H->lm_P * M));
-  TRY(H->alloc(&H->lm_idx, (size_t)H->lm_P * M));
+  const size_t lm_slots = (size_t)std::max(H->lm_P, blm_parts(g.V)) * M;
+  TRY(H->alloc(&H->lm_mx, lm_slots));
+  TRY(H->alloc(&H->lm_se, lm_slots));
+  TRY(H->alloc(&H->lm_idx, lm_slots));
   TRY(H->alloc(&H->lm_p1, M));
   TRY(H->alloc(&H->fin_counters, (size_t)g.max_batch));
   HIP_TRY(hipMemsetAsync(H->fin_counters, 0, (size_t)g.max_batch * sizeof(int), st));
@@ -335,6 +334,13 @@ int gemm_rows(dflash_head *H, int epi, const uint16_t *A, int lda, int M, const 
   ga.kslice = p.kslice;
   if (splits_out) *splits_out = p.splits;
   e.ld_split = M;
+  if (M > GEMM_MAX_ROWS && bgemm_ok(epi, N, K)) {
+    // all rows in one tiled launch (same K order as the chunked kernel)
+    ga.A = A;
+    ga.M = M;
+    HIP_TRY(launch_bgemm(epi, ga, e, st));
+    return DFLASH_OK;
+  }
   const int half = H->g.d / 2;
   for (int r0 = 0; r0 < M; r0 += GEMM_MAX_ROWS) {
     ga.A = A + (size_t)r0 * lda;
@@ -487,7 +493,17 @@ int propose_impl(dflash_head *H, dflash_state *const *states, int n, const uint3
   la.part_mx = H->lm_mx;
   la.part_se = H->lm_se;
   la.part_idx = H->lm_idx;
-  for (int r0 = 0; r0 < M; r0 += GEMM_MAX_ROWS) {
+  const bool tiled_lm = M > GEMM_MAX_ROWS && g.V % 128 == 0 && h % 128 == 0;
+  if (tiled_lm) {
+    la.z = H->act;
+    la.M = M;
+    la.row0 = 0;
+    la.logits = logits;
+    hipEvent_t t_lm = H->interval_begin(DFLASH_PHASE_LM_HEAD, st);
+    HIP_TRY(launch_blm_head(g.head_fp8, la, st));
+    if (t_lm) HIP_TRY(hipEventRecord(t_lm, st));
+  }
+  for (int r0 = 0; !tiled_lm && r0 < M; r0 += GEMM_MAX_ROWS) {
     la.z = H->act + (size_t)r0 * h;
     la.M = std::min(GEMM_MAX_ROWS, M - r0);
     la.row0 = r0;
@@ -500,7 +516,7 @@ int propose_impl(dflash_head *H, dflash_state *const *states, int n, const uint3
   fa.part_mx = H->lm_mx;
   fa.part_se = H->lm_se;
   fa.part_idx = H->lm_idx;
-  fa.P = H->lm_P;
+  fa.P = tiled_lm ? blm_parts(g.V) : H->lm_P;
   fa.M = M;
   fa.gamma = g.gamma;
   fa.num_drafts = num_drafts;

@@ -1,0 +1,85 @@
+// gemm_epi.hpp - lane-local epilogues shared by the weight-streaming GEMM
+// kernels (few activation rows) and the tiled GEMM kernels (many rows).
+//
+// Both compute D^T = W A^T with v_mfma_f32_16x16x32_bf16, so a lane ends with
+// four consecutive output columns n .. n+3 (weight rows 4g .. 4g+3 of a
+// 16-row tile) for one activation row m. The build repacks weight rows in
+// pairs: Q and K rows of a head are ordered (dim i, dim i + d/2), and the MLP
+// weight alternates gate and up rows, so (n, n+1) and (n+2, n+3) are a RoPE
+// pair or a gate/up pair and every epilogue stays inside the lane.
+#pragma once
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace dflash {
+
+// EPI_F32:      out_f32[m, n..n+3] = v
+// EPI_PARTIAL:  out_f32[split][m][n..n+3] = v   (row stride ldo, split stride ld_split rows)
+// EPI_SWIGLU:   out_bf16[m, n/2], [m, n/2 + 1] = silu(gate) * up
+// EPI_QKV_ROPE: out_bf16[m, n..n+3] = v, rotated by row m's (cos, sin) when n is a Q or K column
+// EPI_KV_SCATTER: columns [K0 | V0 | K1 | V1 ...]; K rotated at the row's position; stored
+//               (bf16 or E4M3 with the per-head scale) into the row's pool slot
+template <int EPI>
+__device__ __forceinline__ void epilogue4(const f32x4 v, int m, int n, int split, const EpiArgs &ea) {
+  if constexpr (EPI == EPI_F32 || EPI == EPI_PARTIAL) {
+    float *o = EPI == EPI_F32 ? ea.out_f32 + (size_t)m * ea.ldo + n
+                              : ea.out_f32 + ((size_t)split * ea.ld_split + m) * ea.ldo + n;
+    *(f32x4 *)o = v;
+  } else if constexpr (EPI == EPI_SWIGLU) {
+    // rows (gate_i, up_i, gate_i+1, up_i+1) with i = n / 2
+    *(uint32_t *)(ea.out_bf16 + (size_t)m * ea.ldo + n / 2) = pack_bf16x2(silu(v[0]) * v[1], silu(v[2]) * v[3]);
+  } else if constexpr (EPI == EPI_QKV_ROPE) {
+    const int half = ea.head_dim >> 1;
+    float y[4] = {v[0], v[1], v[2], v[3]};
+    if (n < ea.q_dim + ea.kv_dim) {
+      const int p = (n % ea.head_dim) >> 1;  // pair index of rows n, n+1
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const float2 c = ea.cs[(size_t)m * half + p + q];
+        const float x0 = v[2 * q], x1 = v[2 * q + 1];
+        y[2 * q] = x0 * c.x - x1 * c.y;
+        y[2 * q + 1] = x1 * c.x + x0 * c.y;
+      }
+    }
+    uint2 o;
+    o.x = pack_bf16x2(y[0], y[1]);
+    o.y = pack_bf16x2(y[2], y[3]);
+    *(uint2 *)(ea.out_bf16 + (size_t)m * ea.ldo + n) = o;
+  } else if constexpr (EPI == EPI_KV_SCATTER) {
+    const int d = ea.head_dim;
+    const int kv_dim = ea.n_kv * d;
+    const int l = n / (2 * kv_dim), rem = n % (2 * kv_dim);
+    const int kv = rem / kv_dim, hd = (rem % kv_dim) / d, j = n % d;
+    const int pos = ea.row_pos[m];
+    float y[4] = {v[0], v[1], v[2], v[3]};
+    if (kv == 0) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        double sn, cs;
+        sincos((double)pos * ea.inv_freq[(j >> 1) + q], &sn, &cs);
+        const float c = (float)cs, s = (float)sn;
+        const float x0 = v[2 * q], x1 = v[2 * q + 1];
+        y[2 * q] = x0 * c - x1 * s;
+        y[2 * q + 1] = x1 * c + x0 * s;
+      }
+    }
+    const int32_t blk = ea.row_bt[m][pos >> 4];
+    const size_t off = ((((size_t)blk * ea.L + l) * 2 + kv) * ea.n_kv + hd) * (size_t)(DFLASH_KV_BLOCK * d) +
+                       (size_t)(pos & 15) * d + j;
+    if (ea.kv_fp8) {
+      const float sc = ea.kv_scale[(l * 2 + kv) * ea.n_kv + hd];
+      uint32_t w = 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) w |= (uint32_t)f32_to_e4m3(y[r] / sc) << (8 * r);
+      *(uint32_t *)((uint8_t *)ea.pool + off) = w;
+    } else {
+      uint2 o;
+      o.x = pack_bf16x2(y[0], y[1]);
+      o.y = pack_bf16x2(y[2], y[3]);
+      *(uint2 *)((uint16_t *)ea.pool + off) = o;
+    }
+  }
+}
+
+}  // namespace dflash

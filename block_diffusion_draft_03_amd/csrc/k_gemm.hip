@@ -1,12 +1,12 @@
 // k_gemm.hip - weight-streaming MFMA GEMMs of the DFlash head for gfx950.
 //
-// All contractions of the propose path have few activation rows (gamma per
-// sequence) against large bf16 (or E4M3) weight matrices, so they are bound
-// by streaming the weights from HBM once. The kernels compute the transposed
-// product D^T = W A^T with v_mfma_f32_16x16x32_bf16: the MFMA's A operand is
-// 16 weight rows, its B operand 16 activation rows. For k-step c of a
-// 128-wide K step, lane l (row l % 16, group g = l / 16) loads the 8 values
-// at k0 + 32c + 8g, so one load instruction covers 16 weight rows x 64
+// A propose forward has few activation rows (gamma per sequence) against
+// large bf16 (or E4M3) weight matrices, so these kernels are bound by
+// streaming the weights from HBM once. They compute the transposed product
+// D^T = W A^T with v_mfma_f32_16x16x32_bf16: the MFMA's A operand is 16
+// weight rows, its B operand 16 activation rows. For k-step c of a 128-wide
+// K step, lane l (row l % 16, group g = l / 16) loads the 8 values at
+// k0 + 32c + 8g, so one load instruction covers 16 weight rows x 64
 // contiguous bytes. A lane then holds outputs (rows) 4g .. 4g+3 of a tile
 // for activation row l % 16.
 //
@@ -15,19 +15,11 @@
 // wave order. A GEMM may also be split over K across workgroups; then every
 // split writes its partial sums and a separate kernel (k_resid_norm) adds
 // them in split order. Every reduction order is fixed, so results are
-// deterministic and a row's result does not depend on the other rows.
-//
-// Epilogues are lane-local because the build repacks weight rows in pairs:
-// Q and K rows of a head are ordered (dim i, dim i + d/2) for i = 0 .. d/2-1,
-// and the MLP weight alternates gate and up rows. Lane rows 4g, 4g+1 and
-// 4g+2, 4g+3 are therefore a RoPE pair (or a gate/up pair). Q and K stay in
-// that pair order everywhere inside the library (attention is invariant to a
-// common permutation of the Q and K dimensions).
-//
-// With ANORM the A operand is the RMSNorm of the fp32 residual stream,
-// formed while loading: bf16(h * r * gain) with r = 1 / sqrt(mean(h^2) + eps)
-// from per-unit sums of squares that the producing GEMM wrote.
+// deterministic and a row's result does not depend on the other rows. The
+// tiled kernels for many rows (k_bgemm.hip) follow the same K order, so the
+// two kernels give bit-identical results.
 #include "common.hpp"
+#include "gemm_epi.hpp"
 #include "kernels.hpp"
 
 namespace dflash {
@@ -40,29 +32,10 @@ struct Frag {
   uint4 a[MT][4];
 };
 
-// 8 bf16 of normalised activations: h[k .. k+8) * r * gain[k .. k+8)
-__device__ __forceinline__ uint4 norm_bf16x8(const float *h, const float *gain, float r) {
-  const float4 x0 = *(const float4 *)h, x1 = *(const float4 *)(h + 4);
-  const float4 g0 = *(const float4 *)gain, g1 = *(const float4 *)(gain + 4);
-  uint4 o;
-  o.x = pack_bf16x2(x0.x * r * g0.x, x0.y * r * g0.y);
-  o.y = pack_bf16x2(x0.z * r * g0.z, x0.w * r * g0.w);
-  o.z = pack_bf16x2(x1.x * r * g1.x, x1.y * r * g1.y);
-  o.w = pack_bf16x2(x1.z * r * g1.z, x1.w * r * g1.w);
-  return o;
-}
-
-struct AOperand {
-  const uint16_t *a;   // bf16 activations (plain)
-  const float *h;      // fp32 residual (ANORM)
-  const float *gain;   // ANORM
-  const float *rinv;   // ANORM: per activation row (LDS)
-  int lda;
-};
-
-template <int MT, int TN, bool WFP8, bool ANORM, bool TILED = false>
+template <int MT, int TN, bool WFP8, bool TILED = false>
 __device__ __forceinline__ void load_step(Frag<MT, TN> &f, const void *__restrict__ Wv, int K, const int (&wrow)[TN],
-                                          const AOperand &A, const int (&arow)[MT], int k0, int ke, int g) {
+                                          const uint16_t *__restrict__ A, int lda, const int (&arow)[MT], int k0,
+                                          int ke, int g) {
   const uint4 z = {0u, 0u, 0u, 0u};
   if constexpr (TILED && !WFP8) {
     // tile-major weights: 16-row tile, 128-wide step, k-group c, lane -> 8 values
@@ -119,13 +92,7 @@ __device__ __forceinline__ void load_step(Frag<MT, TN> &f, const void *__restric
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int k = k0 + 32 * c + 8 * g;
-      if (k >= ke) {
-        f.a[mt][c] = z;
-      } else if constexpr (ANORM) {
-        f.a[mt][c] = norm_bf16x8(A.h + (size_t)arow[mt] * A.lda + k, A.gain + k, A.rinv[mt * 16 + (threadIdx.x & 15)]);
-      } else {
-        f.a[mt][c] = *(const uint4 *)(A.a + (size_t)arow[mt] * A.lda + k);
-      }
+      f.a[mt][c] = k < ke ? *(const uint4 *)(A + (size_t)arow[mt] * lda + k) : z;
     }
   }
 }
@@ -153,9 +120,9 @@ __device__ __forceinline__ void zero(f32x4 (&acc)[TN][MT]) {
 // The range is walked in batches of ST 128-wide steps: all loads of a batch
 // are issued before its MFMAs (steps past ke load nothing and add zeros), so
 // a wave keeps ST steps of weight rows in flight.
-template <int MT, int TN, int ST, bool WFP8, bool ANORM, bool TILED = false>
-__device__ __forceinline__ void stream_rows(const void *__restrict__ W, int N, int K, const AOperand &A, int M,
-                                            int row0, int kb, int ke, f32x4 (&acc)[TN][MT]) {
+template <int MT, int TN, int ST, bool WFP8, bool TILED = false>
+__device__ __forceinline__ void stream_rows(const void *__restrict__ W, int N, int K, const uint16_t *__restrict__ A,
+                                            int lda, int M, int row0, int kb, int ke, f32x4 (&acc)[TN][MT]) {
   const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
   int wrow[TN], arow[MT];
 #pragma unroll
@@ -165,7 +132,7 @@ __device__ __forceinline__ void stream_rows(const void *__restrict__ W, int N, i
   for (int k0 = kb; k0 < ke; k0 += 128 * ST) {
     Frag<MT, TN> f[ST];
 #pragma unroll
-    for (int s = 0; s < ST; ++s) load_step<MT, TN, WFP8, ANORM, TILED>(f[s], W, K, wrow, A, arow, k0 + 128 * s, ke, g);
+    for (int s = 0; s < ST; ++s) load_step<MT, TN, WFP8, TILED>(f[s], W, K, wrow, A, lda, arow, k0 + 128 * s, ke, g);
 #pragma unroll
     for (int s = 0; s < ST; ++s) mma_step<MT, TN>(f[s], acc);
   }
@@ -197,139 +164,28 @@ __device__ __forceinline__ void wave_reduce(f32x4 (&acc)[TN][MT], float *red) {
   }
 }
 
-// Per-row inverse RMS from the producer's per-unit sums of squares, into LDS.
-template <int MT>
-__device__ __forceinline__ void load_rinv(const GemmArgs &ga, float *rinv, float *tmp) {
-  // thread t: row t % (16 MT), units t / (16 MT), + stride
-  constexpr int R = 16 * MT;
-  const int nthr = blockDim.x;
-  const int row = threadIdx.x % R, lane_u = threadIdx.x / R, nu = nthr / R;
-  float s = 0.0f;
-  if (row < ga.M)
-    for (int u = lane_u; u < ga.ss_units; u += nu) s += ga.ss_in[(size_t)u * ga.ss_ld + ga.ss_row0 + row];
-  tmp[threadIdx.x] = s;
-  __syncthreads();
-  if (threadIdx.x < R) {
-    float t = 0.0f;
-    for (int i = 0; i < nu; ++i) t += tmp[i * R + threadIdx.x];
-    rinv[threadIdx.x] = 1.0f / sqrtf(t / (float)ga.K + ga.eps);
-  }
-  __syncthreads();
-}
-
-template <int MT, int TN, int NW, int ST, int EPI, bool ANORM, bool TILED = false>
+template <int MT, int TN, int NW, int ST, int EPI, bool TILED = false>
 __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs ga, EpiArgs ea) {
   __shared__ float red[(NW > 1 ? NW - 1 : 1) * TN * MT * 4 * 64];
-  __shared__ float rinv[16 * MT];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
   const int row0 = blockIdx.x * 16 * TN;
   const int kb = blockIdx.y * ga.kslice, ke = min(ga.K, kb + ga.kslice);
   const int steps = (ke - kb + 127) / 128;
   const int s0 = (steps * wave) / NW, s1 = (steps * (wave + 1)) / NW;
-  AOperand A{ga.A, ga.H, ga.gain, rinv, ga.lda};
-  if constexpr (ANORM) load_rinv<MT>(ga, rinv, red);
   f32x4 acc[TN][MT];
   zero<MT, TN>(acc);
-  stream_rows<MT, TN, ST, false, ANORM, TILED>(ga.W, ga.N, ga.K, A, ga.M, row0, kb + 128 * s0, min(ke, kb + 128 * s1),
-                                               acc);
+  stream_rows<MT, TN, ST, false, TILED>(ga.W, ga.N, ga.K, ga.A, ga.lda, ga.M, row0, kb + 128 * s0,
+                                        min(ke, kb + 128 * s1), acc);
   wave_reduce<MT, TN, NW>(acc, red);
   if (wave != 0) return;
-
-  float ss_acc[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) ss_acc[mt] = 0.0f;
 #pragma unroll
   for (int t = 0; t < TN; ++t)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int m = mt * 16 + r16;
       const int n = row0 + 16 * t + 4 * g;  // first of this lane's 4 rows
-      const bool ok = m < ga.M && n < ga.N;
-      const f32x4 v = acc[t][mt];
-      if constexpr (EPI == EPI_F32 || EPI == EPI_PARTIAL) {
-        if (ok) {
-          float *o = EPI == EPI_F32 ? ea.out_f32 + (size_t)m * ea.ldo + n
-                                    : ea.out_f32 + ((size_t)blockIdx.y * ea.ld_split + m) * ea.ldo + n;
-          *(f32x4 *)o = v;
-        }
-      } else if constexpr (EPI == EPI_RESID) {
-        // h += acc, and this unit's sum of squares of the new h per row
-        float ss = 0.0f;
-        if (ok) {
-          float *o = ea.out_f32 + (size_t)m * ea.ldo + n;
-          const f32x4 x = v + *(const f32x4 *)o;
-          *(f32x4 *)o = x;
-          ss = x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
-        }
-        ss += __shfl_xor(ss, 16, WAVE);
-        ss += __shfl_xor(ss, 32, WAVE);
-        ss_acc[mt] += ss;
-      } else if constexpr (EPI == EPI_SWIGLU) {
-        // rows (gate_i, up_i, gate_i+1, up_i+1) with i = n / 2
-        if (ok)
-          *(uint32_t *)(ea.out_bf16 + (size_t)m * ea.ldo + n / 2) = pack_bf16x2(silu(v[0]) * v[1], silu(v[2]) * v[3]);
-      } else if constexpr (EPI == EPI_QKV_ROPE) {
-        if (!ok) continue;
-        const int half = ea.head_dim >> 1;
-        float y[4] = {v[0], v[1], v[2], v[3]};
-        if (n < ea.q_dim + ea.kv_dim) {
-          const int p = (n % ea.head_dim) >> 1;  // pair index of rows n, n+1
-#pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            const float2 c = ea.cs[(size_t)m * half + p + q];
-            const float x0 = v[2 * q], x1 = v[2 * q + 1];
-            y[2 * q] = x0 * c.x - x1 * c.y;
-            y[2 * q + 1] = x1 * c.x + x0 * c.y;
-          }
-        }
-        uint2 o;
-        o.x = pack_bf16x2(y[0], y[1]);
-        o.y = pack_bf16x2(y[2], y[3]);
-        *(uint2 *)(ea.out_bf16 + (size_t)m * ea.ldo + n) = o;
-      } else {  // EPI_KV_SCATTER: columns [K0 | V0 | K1 | V1 ...], K in pair order
-        if (!ok) continue;
-        const int d = ea.head_dim;
-        const int kv_dim = ea.n_kv * d;
-        const int l = n / (2 * kv_dim), rem = n % (2 * kv_dim);
-        const int kv = rem / kv_dim, hd = (rem % kv_dim) / d, j = n % d;
-        const int pos = ea.row_pos[m];
-        float y[4] = {v[0], v[1], v[2], v[3]};
-        if (kv == 0) {
-#pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            double sn, cs;
-            sincos((double)pos * ea.inv_freq[(j >> 1) + q], &sn, &cs);
-            const float c = (float)cs, s = (float)sn;
-            const float x0 = v[2 * q], x1 = v[2 * q + 1];
-            y[2 * q] = x0 * c - x1 * s;
-            y[2 * q + 1] = x1 * c + x0 * s;
-          }
-        }
-        const int32_t blk = ea.row_bt[m][pos >> 4];
-        const size_t off = ((((size_t)blk * ea.L + l) * 2 + kv) * ea.n_kv + hd) * (size_t)(DFLASH_KV_BLOCK * d) +
-                           (size_t)(pos & 15) * d + j;
-        if (ea.kv_fp8) {
-          const float sc = ea.kv_scale[(l * 2 + kv) * ea.n_kv + hd];
-          uint32_t w = 0;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) w |= (uint32_t)f32_to_e4m3(y[r] / sc) << (8 * r);
-          *(uint32_t *)((uint8_t *)ea.pool + off) = w;
-        } else {
-          uint2 o;
-          o.x = pack_bf16x2(y[0], y[1]);
-          o.y = pack_bf16x2(y[2], y[3]);
-          *(uint2 *)((uint16_t *)ea.pool + off) = o;
-        }
-      }
+      if (m < ga.M && n < ga.N) epilogue4<EPI>(acc[t][mt], m, n, blockIdx.y, ea);
     }
-  if constexpr (EPI == EPI_RESID) {
-    if (ea.ss_out && g == 0)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int m = mt * 16 + r16;
-        if (m < ga.M) ea.ss_out[(size_t)blockIdx.x * ea.ss_ld + ea.ss_row0 + m] = ss_acc[mt];
-      }
-  }
 }
 
 // Split-K finish for the residual GEMMs: one workgroup per activation row
@@ -381,13 +237,12 @@ __global__ __launch_bounds__(256) void k_lm_head(LmArgs a) {
     const int m = min(mt * 16 + r16, a.M - 1);
     mask_row[mt] = a.bitmask ? a.bitmask + (size_t)((a.row0 + m) / a.gamma) * a.words : nullptr;
   }
-  AOperand A{a.z, nullptr, nullptr, nullptr, a.K};
   const int nw = gridDim.x * 4;
   for (int u = blockIdx.x * 4 + wave; u < units; u += nw) {
     const int row0 = u * UNIT;
     f32x4 acc[TN][MT];
     zero<MT, TN>(acc);
-    stream_rows<MT, TN, ST, WFP8, false, TILED>(a.W, a.V, a.K, A, a.M, row0, 0, a.K, acc);
+    stream_rows<MT, TN, ST, WFP8, TILED>(a.W, a.V, a.K, a.z, a.K, a.M, row0, 0, a.K, acc);
 #pragma unroll
     for (int t = 0; t < TN; ++t)
 #pragma unroll
@@ -400,8 +255,8 @@ __global__ __launch_bounds__(256) void k_lm_head(LmArgs a) {
           const float x = acc[t][mt][r] * sc;
           const int m = mt * 16 + r16;
           if (a.logits && m < a.M) a.logits[(size_t)m * a.V + v] = x;
-          if (mask_row[mt] && !((((uint32_t)mask_row[mt][v >> 5]) >> (v & 31)) & 1u)) continue;
-          arg_push(st[mt], x, (uint32_t)v);
+          const bool ok = !mask_row[mt] || ((((uint32_t)mask_row[mt][v >> 5]) >> (v & 31)) & 1u);
+          arg_push(st[mt], x, (uint32_t)v, ok);
         }
       }
   }
@@ -511,16 +366,15 @@ __global__ __launch_bounds__(256) void k_lm_finish(LmFinishArgs a) {
   }
 }
 
-template <int MT, int TN, int NW, int ST, bool ANORM>
+template <int MT, int TN, int NW, int ST>
 hipError_t launch_cfg(int epi, const GemmArgs &g, const EpiArgs &e, hipStream_t s) {
   dim3 grid((g.N + 16 * TN - 1) / (16 * TN), g.splits), block(NW * 64);
 #define DFL_CASE(E)                                                                         \
   case E:                                                                                   \
-    hipLaunchKernelGGL((k_gemm<MT, TN, NW, ST, E, ANORM, true>), grid, block, 0, s, g, e);      \
+    hipLaunchKernelGGL((k_gemm<MT, TN, NW, ST, E, true>), grid, block, 0, s, g, e);      \
     break;
   switch (epi) {
     DFL_CASE(EPI_F32)
-    DFL_CASE(EPI_RESID)
     DFL_CASE(EPI_SWIGLU)
     DFL_CASE(EPI_QKV_ROPE)
     DFL_CASE(EPI_KV_SCATTER)
@@ -531,11 +385,11 @@ hipError_t launch_cfg(int epi, const GemmArgs &g, const EpiArgs &e, hipStream_t 
   return hipGetLastError();
 }
 
-template <int MT, bool ANORM>
+template <int MT>
 hipError_t launch_mt(int epi, const GemmArgs &g, const EpiArgs &e, hipStream_t s) {
   // configurations chosen by gemm_plan
-  if (g.tn == 1 && g.nw == 4 && g.st == 4) return launch_cfg<MT, 1, 4, 4, ANORM>(epi, g, e, s);
-  if (g.tn == 2 && g.nw == 4 && g.st == 4) return launch_cfg<MT, 2, 4, 4, ANORM>(epi, g, e, s);
+  if (g.tn == 1 && g.nw == 4 && g.st == 4) return launch_cfg<MT, 1, 4, 4>(epi, g, e, s);
+  if (g.tn == 2 && g.nw == 4 && g.st == 4) return launch_cfg<MT, 2, 4, 4>(epi, g, e, s);
   return hipErrorInvalidValue;
 }
 
@@ -568,9 +422,7 @@ hipError_t launch_gemm(int epi, const GemmArgs &g, const EpiArgs &e, hipStream_t
   if (g.M < 1 || g.M > GEMM_MAX_ROWS || g.splits < 1) return hipErrorInvalidValue;
   if (g.splits > 1 && epi != EPI_PARTIAL) return hipErrorInvalidValue;
   const int mt = g.M <= 16 ? 1 : (g.M <= 32 ? 2 : 4);
-  if (g.H) return hipErrorInvalidValue;  // the norm-fused A operand is not used by the library
-  return mt == 1 ? launch_mt<1, false>(epi, g, e, s) : mt == 2 ? launch_mt<2, false>(epi, g, e, s)
-                                                               : launch_mt<4, false>(epi, g, e, s);
+  return mt == 1 ? launch_mt<1>(epi, g, e, s) : mt == 2 ? launch_mt<2>(epi, g, e, s) : launch_mt<4>(epi, g, e, s);
 }
 
 hipError_t launch_resid_norm(const ResidNormArgs &a, int M, hipStream_t s) {

@@ -37,19 +37,6 @@ __global__ __launch_bounds__(256) void k_setup(SetupArgs a) {
   }
 }
 
-__global__ __launch_bounds__(256) void k_rmsnorm(const float *x, int ldx, const float *gain, float eps, int n,
-                                                 uint16_t *out, int ldo) {
-  __shared__ float red[4];
-  const int m = blockIdx.x;
-  const float *xr = x + (size_t)m * ldx;
-  float ss = 0.0f;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) ss += xr[i] * xr[i];
-  ss = block_sum(ss, red);
-  const float r = 1.0f / sqrtf(ss / (float)n + eps);
-  uint16_t *o = out + (size_t)m * ldo;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) o[i] = f32_to_bf16(xr[i] * r * gain[i]);
-}
-
 __device__ __forceinline__ uint16_t load_as_bf16(const void *src, size_t i, bool src_f32) {
   return src_f32 ? f32_to_bf16(((const float *)src)[i]) : ((const uint16_t *)src)[i];
 }
@@ -195,12 +182,6 @@ int grid_for(size_t total, int block) {
 
 hipError_t launch_setup(const SetupArgs &a, int M, hipStream_t s) {
   hipLaunchKernelGGL(k_setup, dim3(M), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_rmsnorm(const float *x, int ldx, const float *gain, float eps, int n, uint16_t *out, int ldo,
-                          int M, hipStream_t s) {
-  hipLaunchKernelGGL(k_rmsnorm, dim3(M), dim3(256), 0, s, x, ldx, gain, eps, n, out, ldo);
   return hipGetLastError();
 }
 

@@ -11,16 +11,16 @@
 namespace dflash {
 
 // ---------------------------------------------------------------- GEMMs ----
-// Skinny weight-streaming GEMM: out[m, n] = sum_k A[m, k] * W[n, k] for
-// M <= 64 activation rows against a bf16 weight matrix W [N, K]. A is bf16
-// activations (row stride lda), or, when H is set, the RMSNorm of the fp32
-// residual rows H formed while loading. Work: one workgroup per 16 * tn
-// weight rows and K slice, nw waves splitting the slice; with splits > 1 the
-// epilogue must be EPI_PARTIAL and k_resid_norm finishes the sum.
+// out[m, n] = sum_k A[m, k] * W[n, k]: bf16 activations A [M, lda] against a
+// tile-major weight matrix W [N, K]. launch_gemm is the weight-streaming
+// kernel for M <= 64 rows (one workgroup per 16 * tn weight rows and K slice,
+// nw waves splitting the slice); launch_bgemm is the LDS-tiled kernel for
+// many rows. Both follow the K order of gemm_plan, so they give identical
+// results for a row. With splits > 1 the epilogue must be EPI_PARTIAL and
+// k_resid_norm finishes the sum.
 
 enum Epi : int {
   EPI_F32 = 0,        // out_f32[m, n] = acc
-  EPI_RESID = 1,      // out_f32[m, n] += acc; per-unit sums of squares of the new rows to ss_out
   EPI_SWIGLU = 2,     // W rows alternate gate / up; out_bf16[m, i] = silu(gate_i) * up_i
   EPI_QKV_ROPE = 3,   // columns [Q | K | V] (Q, K in pair order); RoPE on Q and K from the cos/sin table
   EPI_KV_SCATTER = 4, // columns [K0 | V0 | K1 | V1 ...]; RoPE on K at the row position, store into the paged pool
@@ -30,21 +30,18 @@ enum Epi : int {
 constexpr int GEMM_MAX_ROWS = 64;
 
 // Launch shape of one GEMM; a function of (N, K) only, so a row's result does
-// not depend on how many rows share the launch.
+// not depend on how many rows share the launch. Each K slice of kslice
+// columns is summed as four consecutive parts (the nw = 4 waves of the
+// weight-streaming kernel), added in order.
 struct GemmPlan {
   int tn, nw, st, splits, kslice;
 };
 GemmPlan gemm_plan(int N, int K, bool allow_split);
 
 struct GemmArgs {
-  const uint16_t *A;  // bf16 activations [M, lda] (when H is null)
+  const uint16_t *A;  // bf16 activations [M, lda]
   int lda, M;
-  const float *H;     // fp32 residual rows [M, lda] to normalise while loading, or null
-  const float *gain;  // [K] RMSNorm gain (with H)
-  float eps;
-  const float *ss_in; // per-unit row sums of squares of H: ss_in[u * ss_ld + ss_row0 + m], u < ss_units
-  int ss_units, ss_ld, ss_row0;
-  const void *W;      // [N, K] bf16
+  const void *W;      // [N, K] bf16, tile-major
   int N, K;
   int tn, nw, st, splits, kslice;
 };
@@ -53,8 +50,6 @@ struct EpiArgs {
   float *out_f32;
   uint16_t *out_bf16;
   int ldo, ld_split;
-  float *ss_out;      // EPI_RESID: [units][ss_ld] per-unit sums of squares, or null
-  int ss_ld, ss_row0;
   // QKV RoPE
   const float2 *cs;   // [M][head_dim / 2] (cos, sin) of each row's position
   int head_dim, q_dim, kv_dim;
@@ -68,6 +63,11 @@ struct EpiArgs {
 };
 
 hipError_t launch_gemm(int epi, const GemmArgs &g, const EpiArgs &e, hipStream_t s);
+
+// The tiled kernel takes any M (one launch for all rows) when N and K are
+// multiples of 128 and the epilogue is not EPI_KV_SCATTER.
+bool bgemm_ok(int epi, int N, int K);
+hipError_t launch_bgemm(int epi, const GemmArgs &g, const EpiArgs &e, hipStream_t s);
 
 // Finish of a split GEMM into the residual stream, one workgroup per row:
 // h[m] = (init_zero ? 0 : h[m]) + sum over splits of part[s][m]; then, if out
@@ -96,8 +96,12 @@ struct LmArgs {
   float *part_mx, *part_se;
   uint32_t *part_idx;    // [P, ld_part]
 };
-int lm_parts(int V);     // P, a function of V only
+int lm_parts(int V);     // P of launch_lm_head, a function of V only
 hipError_t launch_lm_head(bool w_fp8, const LmArgs &a, hipStream_t s);
+// Tiled LM head for any M (one launch for all rows; row0 = 0, ld_part = M),
+// blm_parts(V) partials per row. Logits are bit-identical to launch_lm_head's.
+int blm_parts(int V);
+hipError_t launch_blm_head(bool w_fp8, const LmArgs &a, hipStream_t s);
 
 struct LmFinishArgs {
   const float *part_mx, *part_se;
@@ -145,10 +149,6 @@ struct SetupArgs {
   int32_t position[DFLASH_MAX_BATCH];
 };
 hipError_t launch_setup(const SetupArgs &a, int M, hipStream_t s);
-
-// out[m] = bf16(RMSNorm(x[m]) * gain), x fp32 [M, n] row stride ldx.
-hipError_t launch_rmsnorm(const float *x, int ldx, const float *gain, float eps, int n, uint16_t *out, int ldo,
-                          int M, hipStream_t s);
 
 // Row orders of the repacked weights.
 enum RowOrder : int {
