@@ -23,6 +23,9 @@ HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
                # packed fp32 ops are kept out of generated code
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                "-Wno-unused-result"]
+# Per-file flags. The tiled GEMM keeps its MFMA accumulators in ordinary VGPRs:
+# with accumulation registers the allocator rotates them every K stage.
+EXTRA_FLAGS = {"k_bgemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _hipcc():
@@ -55,8 +58,7 @@ def build_hip_lib(jobs=None):
 
     def compile_one(src):
         obj = os.path.join(BUILD, src + ".o")
-        _run([hipcc, *HIPCC_FLAGS, "-x", "hip" if src.endswith(".hip") else "hip", "-c",
-              os.path.join(CSRC, src), "-o", obj])
+        _run([hipcc, *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj])
         return obj
 
     with ThreadPoolExecutor(jobs) as ex:

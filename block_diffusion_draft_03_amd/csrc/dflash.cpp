@@ -29,10 +29,8 @@ int set_err(int code, const std::string &m) {
 constexpr uint64_t HEAD_MAGIC = 0x44464c4153484844ull;   // "DFLASHHD"
 constexpr uint64_t STATE_MAGIC = 0x44464c4153485354ull;  // "DFLASHST"
 constexpr uint64_t DEAD_MAGIC = 0xdeadull;
-constexpr int ATTN_SLOTS = 1024;     // (sequence, kv head, key chunk) partials per layer, at least
-constexpr int ATTN_GROUP_KEYS = 64;  // keys an attention workgroup loads at once
-constexpr int ATTN_MAX_CHUNK = 992;  // keys per chunk (block ids staged per workgroup)
-constexpr int ATTN_MAX_SPLITS = 64;  // chunks per (sequence, kv head) merged by one wave
+constexpr int ATTN_TARGET_WGS = 512;  // attention workgroups a launch aims for (two per CU)
+constexpr int ATTN_MAX_SPLITS = 64;   // splits per (sequence, kv head) merged by one wave
 
 #define HIP_TRY(expr)                                                                          \
   do {                                                                                         \
@@ -86,6 +84,8 @@ struct dflash_head {
   int *fin_counters = nullptr;
   int lm_P = 0;
   int attn_slots = 0;
+  uint16_t *vtb = nullptr;  // V^T of the block rows [max_batch][n_kv][d][gp], zero padded
+  int gp = 0;
   float *pre_u = nullptr;
   uint16_t *pre_c = nullptr;
   float *part = nullptr;  // split-K partial sums [splits][rows][h]
@@ -295,11 +295,14 @@ int build_impl(dflash_head *H, const dflash_weights *w, hipStream_t st) {
   TRY(H->alloc(&H->part, (size_t)max_splits * std::max<size_t>(M, GEMM_MAX_ROWS) * h));
   const size_t R = (size_t)g.rep * g.gamma;
   {
-    // most chunks one (sequence, kv head) can need: the window plus the block
-    const int max_keys = (g.W > 0 ? g.W : 0) + g.gamma;
-    const int forced = std::min(ATTN_MAX_SPLITS, (max_keys + ATTN_MAX_CHUNK - 1) / ATTN_MAX_CHUNK + 1);
-    H->attn_slots = std::max(ATTN_SLOTS, g.max_batch * g.n_kv * forced);
+    // partial slots: the split rule of attn_plan never needs more
+    const int max_tiles = (std::min(g.W, H->cfg.max_seq_len) + 15 + 31) / 32 + 1;
+    const int per_seq = std::min(ATTN_MAX_SPLITS, (max_tiles + attn_max_tiles_per_split() - 1) / attn_max_tiles_per_split() + 1);
+    H->attn_slots = std::max({ATTN_TARGET_WGS * 2, g.max_batch * g.n_kv * per_seq, g.n_kv * ATTN_MAX_SPLITS});
   }
+  H->gp = (g.gamma + 31) / 32 * 32;
+  TRY(H->alloc(&H->vtb, (size_t)g.max_batch * g.n_kv * g.d * H->gp));
+  HIP_TRY(hipMemsetAsync(H->vtb, 0, (size_t)g.max_batch * g.n_kv * g.d * H->gp * sizeof(uint16_t), st));
   TRY(H->alloc(&H->o_part, (size_t)H->attn_slots * R * g.d));
   TRY(H->alloc(&H->ml_part, (size_t)H->attn_slots * R * 2));
   H->lm_P = lm_parts(g.V);
@@ -335,9 +338,10 @@ int gemm_rows(dflash_head *H, int epi, const uint16_t *A, int lda, int M, const 
   if (splits_out) *splits_out = p.splits;
   e.ld_split = M;
   if (M > GEMM_MAX_ROWS && bgemm_ok(epi, N, K)) {
-    // all rows in one tiled launch (same K order as the chunked kernel)
+    // all rows in one tiled launch
     ga.A = A;
     ga.M = M;
+    e.row0 = 0;
     HIP_TRY(launch_bgemm(epi, ga, e, st));
     return DFLASH_OK;
   }
@@ -346,6 +350,7 @@ int gemm_rows(dflash_head *H, int epi, const uint16_t *A, int lda, int M, const 
     ga.A = A + (size_t)r0 * lda;
     ga.M = std::min(GEMM_MAX_ROWS, M - r0);
     EpiArgs ec = e;
+    ec.row0 = r0;
     if (e.out_f32) ec.out_f32 = e.out_f32 + (size_t)r0 * e.ldo;
     if (e.out_bf16) ec.out_bf16 = e.out_bf16 + (size_t)r0 * e.ldo;
     if (e.cs) ec.cs = e.cs + (size_t)r0 * half;
@@ -417,6 +422,7 @@ int propose_impl(dflash_head *H, dflash_state *const *states, int n, const uint3
 
   AttnArgs aa{};
   aa.qkv = H->qkv;
+  aa.vtb = H->vtb;
   aa.ld = g.qkv_dim;
   aa.gamma = g.gamma;
   aa.rep = g.rep;
@@ -432,29 +438,28 @@ int propose_impl(dflash_head *H, dflash_state *const *states, int n, const uint3
   aa.ml_part = H->ml_part;
   aa.out = H->attn;
   aa.out_ld = g.q_dim;
-  int max_S = 0;
-  for (int i = 0; i < n; ++i) {
-    const int c = states[i]->rows.ctx_len;
-    const int lo = g.W > 0 ? std::max(0, c - g.W) : c;
-    aa.seq[i].ctx_len = c;
-    aa.seq[i].win_start = lo;
-    aa.seq[i].bt = states[i]->d_bt;
-    max_S = std::max(max_S, c - lo + g.gamma);
-  }
   {
-    // key chunks per (sequence, kv head): one group of five 32-key tiles each
-    // (loaded at once), unless that needs more partial slots than the
-    // target; then larger chunks, at most ATTN_MAX_CHUNK keys
-    int splits = (max_S + ATTN_GROUP_KEYS - 1) / ATTN_GROUP_KEYS;
-    if (n * g.n_kv * splits > ATTN_SLOTS)
-      splits = std::max((max_S + ATTN_MAX_CHUNK - 1) / ATTN_MAX_CHUNK, ATTN_SLOTS / (n * g.n_kv));
-    splits = std::max(1, std::min(splits, ATTN_MAX_SPLITS));
-    int chunk = (max_S + splits - 1) / splits;
-    chunk = (chunk + 31) / 32 * 32;
-    aa.chunk = chunk;
-    aa.max_splits = (max_S + chunk - 1) / chunk;
-    if (n * g.n_kv * aa.max_splits > H->attn_slots || chunk > ATTN_MAX_CHUNK)
-      return set_err(DFLASH_E_INVALID, "attention partial buffer too small for this batch");
+    // ctx tiles of 32 positions from the block-aligned window start; the
+    // splits give about ATTN_TARGET_WGS workgroups per launch
+    int max_T = 0;
+    for (int i = 0; i < n; ++i) {
+      const int c = states[i]->rows.ctx_len;
+      const int lo = g.W > 0 ? std::max(0, c - g.W) : c;
+      aa.seq[i].ctx_len = c;
+      aa.seq[i].win_start = lo;
+      aa.seq[i].bt = states[i]->d_bt;
+      if (lo < c) max_T = std::max(max_T, (c - lo / 16 * 16 + 31) / 32);
+    }
+    const int max_tps = attn_max_tiles_per_split();
+    const int target = std::max(1, ATTN_TARGET_WGS / (n * g.n_kv));
+    int tps = std::min(max_tps, std::max(1, (max_T + target - 1) / target));
+    tps = std::max(tps, (max_T + ATTN_MAX_SPLITS - 1) / ATTN_MAX_SPLITS);
+    const int cap = std::max(1, H->attn_slots / (n * g.n_kv));
+    tps = std::max(tps, (max_T + cap - 1) / cap);
+    if (tps > max_tps) return set_err(DFLASH_E_INVALID, "context window too long for the attention splits");
+    aa.tps = tps;
+    aa.max_splits = std::max(1, (max_T + tps - 1) / tps);
+    if (n * g.n_kv * aa.max_splits > H->attn_slots) return set_err(DFLASH_E_INVALID, "attention partial buffer too small");
   }
 
   // act holds RMSNorm(h) with the next consumer's gain: layer 0's input norm
@@ -468,6 +473,9 @@ int propose_impl(dflash_head *H, dflash_state *const *states, int n, const uint3
     e.head_dim = g.d;
     e.q_dim = g.q_dim;
     e.kv_dim = g.kv_dim;
+    e.vtb = H->vtb;
+    e.gamma = g.gamma;
+    e.gp = H->gp;
     TRY(gemm_rows(H, EPI_QKV_ROPE, H->act, h, M, H->w_qkv + (size_t)l * H->sz_qkv, g.qkv_dim, h, e, st));
     aa.layer = l;
     HIP_TRY(launch_attention(aa, n, st));

@@ -46,6 +46,14 @@ __device__ __forceinline__ void epilogue4(const f32x4 v, int m, int n, int split
     o.x = pack_bf16x2(y[0], y[1]);
     o.y = pack_bf16x2(y[2], y[3]);
     *(uint2 *)(ea.out_bf16 + (size_t)m * ea.ldo + n) = o;
+    if (n >= ea.q_dim + ea.kv_dim && ea.vtb) {
+      // V of the block rows, transposed per kv head for the attention kernel
+      const int vn = n - ea.q_dim - ea.kv_dim, hd = vn / ea.head_dim, dim = vn % ea.head_dim;
+      const int seq = (ea.row0 + m) / ea.gamma, j = (ea.row0 + m) % ea.gamma;
+      uint16_t *vt = ea.vtb + ((size_t)(seq * (ea.kv_dim / ea.head_dim) + hd) * ea.head_dim + dim) * ea.gp + j;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) vt[(size_t)r * ea.gp] = f32_to_bf16(y[r]);
+    }
   } else if constexpr (EPI == EPI_KV_SCATTER) {
     const int d = ea.head_dim;
     const int kv_dim = ea.n_kv * d;
@@ -64,20 +72,30 @@ __device__ __forceinline__ void epilogue4(const f32x4 v, int m, int n, int split
         y[2 * q + 1] = x1 * c + x0 * s;
       }
     }
+    // K tile [16 slots][d]; V tile transposed, [d][16 slots]
     const int32_t blk = ea.row_bt[m][pos >> 4];
-    const size_t off = ((((size_t)blk * ea.L + l) * 2 + kv) * ea.n_kv + hd) * (size_t)(DFLASH_KV_BLOCK * d) +
-                       (size_t)(pos & 15) * d + j;
+    const size_t tile = ((((size_t)blk * ea.L + l) * 2 + kv) * ea.n_kv + hd) * (size_t)(DFLASH_KV_BLOCK * d);
+    const int slot = pos & 15;
     if (ea.kv_fp8) {
       const float sc = ea.kv_scale[(l * 2 + kv) * ea.n_kv + hd];
-      uint32_t w = 0;
+      uint8_t *p = (uint8_t *)ea.pool + tile;
+      if (kv == 0) {
+        uint32_t w = 0;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) w |= (uint32_t)f32_to_e4m3(y[r] / sc) << (8 * r);
-      *(uint32_t *)((uint8_t *)ea.pool + off) = w;
+        for (int r = 0; r < 4; ++r) w |= (uint32_t)f32_to_e4m3(y[r] / sc) << (8 * r);
+        *(uint32_t *)(p + (size_t)slot * d + j) = w;
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p[(size_t)(j + r) * DFLASH_KV_BLOCK + slot] = f32_to_e4m3(y[r] / sc);
+      }
     } else {
-      uint2 o;
-      o.x = pack_bf16x2(y[0], y[1]);
-      o.y = pack_bf16x2(y[2], y[3]);
-      *(uint2 *)((uint16_t *)ea.pool + off) = o;
+      uint16_t *p = (uint16_t *)ea.pool + tile;
+      if (kv == 0) {
+        *(uint2 *)(p + (size_t)slot * d + j) = uint2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p[(size_t)(j + r) * DFLASH_KV_BLOCK + slot] = f32_to_bf16(y[r]);
+      }
     }
   }
 }

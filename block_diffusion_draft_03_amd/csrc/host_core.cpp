@@ -41,6 +41,7 @@ int validate_config(const dflash_config &c, Geo *g, std::string *err) {
   if (c.lm_head_dtype != DFLASH_BF16 && c.lm_head_dtype != DFLASH_FP8_E4M3)
     return bad("lm_head_dtype must be BF16 or FP8_E4M3");
   if (c.kv_dtype != DFLASH_BF16 && c.kv_dtype != DFLASH_FP8_E4M3) return bad("kv_dtype must be BF16 or FP8_E4M3");
+  if (c.kv_dtype == DFLASH_FP8_E4M3 && c.head_dim < 64) return bad("an FP8_E4M3 KV cache needs head_dim >= 64");
   if (g) {
     g->L = c.num_layers;
     g->h = c.hidden;

@@ -34,77 +34,141 @@ constexpr int BM = 128;                // activation rows per workgroup
 constexpr int NT = BN / 16;            // weight tiles
 constexpr int MTL = BM / 16;           // activation tiles
 constexpr int WN = NT / 2, WM = MTL / 2;  // tiles per wave (2 x 2 waves)
-constexpr int SW = NT * 2 * 64;        // uint4 of weights per stage
-constexpr int SA = MTL * 2 * 64;       // uint4 of activations per stage
 constexpr int NTHR = 256;
+constexpr int NSTAGE_GEMM = 3;         // LDS ring depth (stages in flight + the one multiplied)
+constexpr int NSTAGE_LM = 2;
 constexpr int LM_TILES = 8;            // vocab tiles of 128 per LM-head workgroup
 
-// Global loads of the stage that starts at absolute column k (a multiple of 64).
-template <bool WFP8>
-__device__ __forceinline__ void gload(uint4 (&rw)[SW / NTHR], uint4 (&ra)[SA / NTHR], const void *__restrict__ W,
-                                      int steps_w, int tile0,
-                                      const uint16_t *__restrict__ A, int lda, int M, int m0, int k) {
-  const int step = k >> 7, half = (k >> 6) & 1;
-  if constexpr (!WFP8) {
-    const uint4 *Wq = (const uint4 *)W;
-#pragma unroll
-    for (int i = 0; i < SW / NTHR; ++i) {
-      const int j = threadIdx.x + NTHR * i;
-      const int t = j >> 7, c = (j >> 6) & 1, lane = j & 63;
-      rw[i] = Wq[(((size_t)(tile0 + t) * steps_w + step) * 4 + half * 2 + c) * 64 + lane];
-    }
-  } else {
-    // one E4M3 pair (k-groups 2 half, 2 half + 1) per (tile, lane)
-    const uint4 *Wq = (const uint4 *)W;
-#pragma unroll
-    for (int i = 0; i < SW / NTHR / 2; ++i) {
-      const int j = threadIdx.x + NTHR * i;
-      const int t = j >> 6, lane = j & 63;
-      const uint4 q = Wq[(((size_t)(tile0 + t) * steps_w + step) * 2 + half) * 64 + lane];
-      uint2 lo = e4m3x4_to_bf16x4(q.x), hi = e4m3x4_to_bf16x4(q.y);
-      rw[2 * i] = uint4{lo.x, lo.y, hi.x, hi.y};
-      lo = e4m3x4_to_bf16x4(q.z);
-      hi = e4m3x4_to_bf16x4(q.w);
-      rw[2 * i + 1] = uint4{lo.x, lo.y, hi.x, hi.y};
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < SA / NTHR; ++i) {
-    const int j = threadIdx.x + NTHR * i;
-    const int lane = j & 63, rest = j >> 6, c = rest & 1, mt = rest >> 1;
-    const int m = min(m0 + mt * 16 + (lane & 15), M - 1);
-    ra[i] = *(const uint4 *)(A + (size_t)m * lda + k + 32 * c + 8 * (lane >> 4));
-  }
+typedef __attribute__((address_space(3))) uint4 lds_uint4;
+typedef int int4v __attribute__((ext_vector_type(4)));
+
+// Buffer resource of a global array of `bytes` bytes (offsets past the end
+// read as zero).
+__device__ __forceinline__ int4v make_rsrc(const void *base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  int4v r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xFFFF);
+  r.z = (int)bytes;
+  r.w = 0x00020000;
+  return r;
 }
 
-// LDS image of a stage: [tile][c][lane] weight fragments, then
-// [act tile][c][lane] activation fragments.
+// One wave-wide direct-to-LDS load: lane l's 16 bytes at buffer offset
+// voff + soff land at LDS byte address lds + 16 l (lds wave-uniform). Issued
+// as assembly so that the only waits on it are the pipeline's explicit vmcnt
+// waits (the compiler would drain every such load before any LDS read); m0
+// is restored afterwards.
+__device__ __forceinline__ void dma16(int4v r, uint32_t voff, uint32_t soff, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %4\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(r), "s"(soff), "s"(lds)
+      : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const uint4 *p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(const lds_uint4 *)p);
+}
+
+// A stage is a list of 1 KB fragments (64 lanes x 16 bytes): the weight
+// fragments [tile][c] (bf16) or [tile] (E4M3: the 16 codes of k-groups c = 0
+// and 1 of each lane), then the activation fragments [act tile][c]. Wave w
+// loads the weight and activation fragments of tiles 2w and 2w + 1.
 template <bool WFP8>
-__device__ __forceinline__ void lstore(const uint4 (&rw)[SW / NTHR], const uint4 (&ra)[SA / NTHR], uint4 *buf) {
-  if constexpr (!WFP8) {
+struct StageShape {
+  static constexpr int WF = WFP8 ? NT : NT * 2;
+  static constexpr int AF = MTL * 2;
+  static constexpr int F = WF + AF;
+  static constexpr int PER = F / 4;    // fragment loads per wave
+};
+
+// Per-lane offsets of a wave's loads, fixed for the whole K loop.
+struct LoadPlan {
+  int4v rw, ra;          // weight and activation buffers
+  uint32_t w_tile[2];    // byte offset of the wave's two weight tiles (step 0)
+  uint32_t w_step;       // bytes per 128-wide step of one tile
+  uint32_t va[2][2];     // activation fragment (tile 2w + i, k-group c): lane offset at column 0
+};
+
+template <bool WFP8>
+__device__ __forceinline__ LoadPlan make_plan(const void *W, size_t w_bytes, int steps_w, int tile0, const uint16_t *A,
+                                              int lda, int M, int m0, int wave, int lane) {
+  LoadPlan p;
+  p.rw = make_rsrc(W, (uint32_t)w_bytes);
+  p.ra = make_rsrc(A, (uint32_t)((size_t)M * lda * 2));
+  p.w_step = WFP8 ? 2048u : 4096u;
 #pragma unroll
-    for (int i = 0; i < SW / NTHR; ++i) buf[threadIdx.x + NTHR * i] = rw[i];
-  } else {
+  for (int i = 0; i < 2; ++i) p.w_tile[i] = (uint32_t)(tile0 + 2 * wave + i) * (uint32_t)steps_w * p.w_step;
 #pragma unroll
-    for (int i = 0; i < SW / NTHR / 2; ++i) {
-      const int j = threadIdx.x + NTHR * i;
-      const int t = j >> 6, lane = j & 63;
-      buf[(t * 2 + 0) * 64 + lane] = rw[2 * i];
-      buf[(t * 2 + 1) * 64 + lane] = rw[2 * i + 1];
+  for (int i = 0; i < 2; ++i) {
+    const int m = min(m0 + (2 * wave + i) * 16 + (lane & 15), M - 1);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) p.va[i][c] = (uint32_t)(((size_t)m * lda + 32 * c + 8 * (lane >> 4)) * 2);
+  }
+  return p;
+}
+
+// Direct-to-LDS loads of the stage at absolute column k (a multiple of 64)
+// into the slot at LDS byte address `slot`.
+template <bool WFP8>
+__device__ __forceinline__ void issue_stage(uint32_t slot, const LoadPlan &p, int wave, int lane, int k) {
+  using S = StageShape<WFP8>;
+  const uint32_t step_off = (uint32_t)(k >> 7) * p.w_step + (uint32_t)((k >> 6) & 1) * (p.w_step / 2);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int t = 2 * wave + i;
+    if constexpr (!WFP8) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) dma16(p.rw, lane * 16 + c * 1024, p.w_tile[i] + step_off, slot + (t * 2 + c) * 1024);
+    } else {
+      dma16(p.rw, lane * 16, p.w_tile[i] + step_off, slot + t * 1024);
     }
   }
 #pragma unroll
-  for (int i = 0; i < SA / NTHR; ++i) buf[SW + threadIdx.x + NTHR * i] = ra[i];
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      dma16(p.ra, p.va[i][c], (uint32_t)k * 2, slot + (S::WF + (2 * wave + i) * 2 + c) * 1024);
 }
 
-__device__ __forceinline__ void mma_stage(const uint4 *buf, int wn, int wm, int lane, f32x4 (&acc)[WN][WM]) {
+// Wait until at most `later` stages of this wave's loads are outstanding.
+template <bool WFP8>
+__device__ __forceinline__ void wait_stages(int later) {
+  constexpr int P = StageShape<WFP8>::PER;
+  // s_waitcnt vmcnt(n) with expcnt / lgkmcnt left at their maximum
+#define DFL_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0xF70)
+  if (later >= 3) DFL_VMCNT(3 * P);
+  else if (later == 2) DFL_VMCNT(2 * P);
+  else if (later == 1) DFL_VMCNT(P);
+  else DFL_VMCNT(0);
+#undef DFL_VMCNT
+}
+
+__device__ __forceinline__ void bf16_frags_of_e4m3(const uint4 q, uint4 &c0, uint4 &c1) {
+  uint2 lo = e4m3x4_to_bf16x4(q.x), hi = e4m3x4_to_bf16x4(q.y);
+  c0 = uint4{lo.x, lo.y, hi.x, hi.y};
+  lo = e4m3x4_to_bf16x4(q.z);
+  hi = e4m3x4_to_bf16x4(q.w);
+  c1 = uint4{lo.x, lo.y, hi.x, hi.y};
+}
+
+template <bool WFP8>
+__device__ __forceinline__ void mma_stage(const uint4 *slot, int wn, int wm, int lane, f32x4 (&acc)[WN][WM]) {
+  using S = StageShape<WFP8>;
+  uint4 w8[WN][2];
+  if constexpr (WFP8) {
+#pragma unroll
+    for (int i = 0; i < WN; ++i) bf16_frags_of_e4m3(slot[(wn * WN + i) * 64 + lane], w8[i][0], w8[i][1]);
+  }
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     uint4 wf[WN], af[WM];
 #pragma unroll
-    for (int i = 0; i < WN; ++i) wf[i] = buf[((wn * WN + i) * 2 + c) * 64 + lane];
+    for (int i = 0; i < WN; ++i) wf[i] = WFP8 ? w8[i][c] : slot[((wn * WN + i) * 2 + c) * 64 + lane];
 #pragma unroll
-    for (int j = 0; j < WM; ++j) af[j] = buf[SW + ((wm * WM + j) * 2 + c) * 64 + lane];
+    for (int j = 0; j < WM; ++j) af[j] = slot[(S::WF + (wm * WM + j) * 2 + c) * 64 + lane];
 #pragma unroll
     for (int i = 0; i < WN; ++i)
 #pragma unroll
@@ -128,31 +192,46 @@ __device__ __forceinline__ bool place(int b, int n_nb, int n_mb, int &nb, int &m
   return nb < n_nb;
 }
 
+// Barrier between the waves of the workgroup with no memory fence: the
+// direct-to-LDS loads of later stages stay in flight across it (each wave has
+// already waited for its own loads of the stage about to be read). The empty
+// asm statements keep the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // acc += W[tile0 .. tile0 + 8 tiles) x A[m0 .. m0 + 128) over columns
-// [kb, kb + 128 * S), summed sequentially.
-template <bool WFP8>
-__device__ __forceinline__ void block_product(const void *W, int steps_w, int tile0, const uint16_t *A, int lda, int M,
-                                              int m0, int kb, int S, uint4 (*lds)[SW + SA], f32x4 (&acc)[WN][WM]) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+// [kb, kb + 128 * S), summed sequentially. NSTAGE - 1 stages are in flight
+// ahead of the one being multiplied (ring of NSTAGE slots in `lds`); one
+// barrier per stage. Every iteration issues one stage (the last ones reload
+// the final stage into a slot nobody reads), so the wait count is constant.
+template <bool WFP8, int NSTAGE>
+__device__ __forceinline__ void block_product(const LoadPlan &p, int kb, int S, uint4 *lds, f32x4 (&acc)[WN][WM]) {
+  constexpr int SLOT = StageShape<WFP8>::F * 64;
+  constexpr uint32_t SLOT_BYTES = SLOT * 16;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int wn = wave & 1, wm = wave >> 1;
   const int NS = 2 * S;
-  uint4 rw[SW / NTHR], ra[SA / NTHR];
-  gload<WFP8>(rw, ra, W, steps_w, tile0, A, lda, M, m0, kb);
-  lstore<WFP8>(rw, ra, lds[0]);
-  __syncthreads();
-  for (int st = 0; st + 1 < NS; ++st) {
-    gload<WFP8>(rw, ra, W, steps_w, tile0, A, lda, M, m0, kb + 64 * (st + 1));
-    mma_stage(lds[st & 1], wn, wm, lane, acc);
-    lstore<WFP8>(rw, ra, lds[(st + 1) & 1]);
-    __syncthreads();
+  const uint32_t base = lds_addr(lds);
+#pragma unroll
+  for (int s = 0; s < NSTAGE - 1; ++s) issue_stage<WFP8>(base + s * SLOT_BYTES, p, wave, lane, kb + 64 * min(s, NS - 1));
+#pragma unroll 1
+  for (int s = 0; s < NS; ++s) {
+    wait_stages<WFP8>(NSTAGE - 2);
+    stage_barrier();
+    const int sn = s + NSTAGE - 1;
+    issue_stage<WFP8>(base + (sn % NSTAGE) * SLOT_BYTES, p, wave, lane, kb + 64 * min(sn, NS - 1));
+    mma_stage<WFP8>(lds + (s % NSTAGE) * SLOT, wn, wm, lane, acc);
   }
-  mma_stage(lds[(NS - 1) & 1], wn, wm, lane, acc);
+  wait_stages<WFP8>(0);
   __syncthreads();
 }
 
-template <int EPI>
-__global__ __launch_bounds__(NTHR, 2) void k_bgemm(GemmArgs ga, EpiArgs ea, int n_nb, int n_mb) {
-  __shared__ uint4 lds[2][SW + SA];
+template <int EPI, int NSTAGE>
+__global__ __launch_bounds__(NTHR) void k_bgemm(GemmArgs ga, EpiArgs ea, int n_nb, int n_mb) {
+  __shared__ uint4 lds[NSTAGE * StageShape<false>::F * 64];
   int nb, mb;
   if (!place(blockIdx.x, n_nb, n_mb, nb, mb)) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
@@ -161,7 +240,9 @@ __global__ __launch_bounds__(NTHR, 2) void k_bgemm(GemmArgs ga, EpiArgs ea, int 
   const int kb = split * ga.kslice, ke = min(ga.K, kb + ga.kslice);
   f32x4 acc[WN][WM];
   zero_acc(acc);
-  block_product<false>(ga.W, ga.K >> 7, nb * NT, ga.A, ga.lda, ga.M, mb * BM, kb, (ke - kb) >> 7, lds, acc);
+  const LoadPlan p = make_plan<false>(ga.W, (size_t)ga.N * ga.K * 2, ga.K >> 7, nb * NT, ga.A, ga.lda, ga.M, mb * BM,
+                                      __builtin_amdgcn_readfirstlane(wave), lane);
+  block_product<false, NSTAGE>(p, kb, (ke - kb) >> 7, lds, acc);
 #pragma unroll
   for (int i = 0; i < WN; ++i)
 #pragma unroll
@@ -177,9 +258,9 @@ __global__ __launch_bounds__(NTHR, 2) void k_bgemm(GemmArgs ga, EpiArgs ea, int 
 // running (max, argmax, sum exp) over the unmasked entries; lanes, then the
 // two waves sharing a row, are merged in a fixed order and one partial per
 // (p, row) is written.
-template <bool WFP8>
-__global__ __launch_bounds__(NTHR, 2) void k_blm_head(LmArgs a, int n_p, int n_mb) {
-  __shared__ uint4 lds[2][SW + SA];
+template <bool WFP8, int NSTAGE>
+__global__ __launch_bounds__(NTHR) void k_blm_head(LmArgs a, int n_p, int n_mb) {
+  __shared__ uint4 lds[NSTAGE * StageShape<WFP8>::F * 64];
   __shared__ float s_mx[2][BM], s_se[2][BM];
   __shared__ uint32_t s_idx[2][BM];
   int p, mb;
@@ -199,7 +280,9 @@ __global__ __launch_bounds__(NTHR, 2) void k_blm_head(LmArgs a, int n_p, int n_m
   for (int vb = p * LM_TILES; vb < min(n_vb, (p + 1) * LM_TILES); ++vb) {
     f32x4 acc[WN][WM];
     zero_acc(acc);
-    block_product<WFP8>(a.W, steps_w, vb * NT, a.z, a.K, a.M, mb * BM, 0, steps_w, lds, acc);
+    const LoadPlan pl = make_plan<WFP8>(a.W, (size_t)a.V * a.K * (WFP8 ? 1 : 2), steps_w, vb * NT, a.z, a.K, a.M,
+                                        mb * BM, __builtin_amdgcn_readfirstlane(wave), lane);
+    block_product<WFP8, NSTAGE>(pl, 0, steps_w, lds, acc);
 #pragma unroll
     for (int i = 0; i < WN; ++i)
 #pragma unroll
@@ -251,7 +334,7 @@ template <int EPI>
 hipError_t launch_epi(const GemmArgs &g, const EpiArgs &e, hipStream_t s) {
   const int n_nb = g.N / BN, n_mb = (g.M + BM - 1) / BM;
   dim3 grid(((n_nb + 7) / 8) * 8 * n_mb, g.splits);
-  hipLaunchKernelGGL((k_bgemm<EPI>), grid, dim3(NTHR), 0, s, g, e, n_nb, n_mb);
+  hipLaunchKernelGGL((k_bgemm<EPI, NSTAGE_GEMM>), grid, dim3(NTHR), 0, s, g, e, n_nb, n_mb);
   return hipGetLastError();
 }
 
@@ -279,8 +362,8 @@ hipError_t launch_blm_head(bool w_fp8, const LmArgs &a, hipStream_t s) {
   if (a.M < 1 || a.V % BN != 0 || a.K % 128 != 0 || a.row0 != 0) return hipErrorInvalidValue;
   const int n_p = blm_parts(a.V), n_mb = (a.M + BM - 1) / BM;
   dim3 grid(((n_p + 7) / 8) * 8 * n_mb);
-  if (w_fp8) hipLaunchKernelGGL((k_blm_head<true>), grid, dim3(NTHR), 0, s, a, n_p, n_mb);
-  else hipLaunchKernelGGL((k_blm_head<false>), grid, dim3(NTHR), 0, s, a, n_p, n_mb);
+  if (w_fp8) hipLaunchKernelGGL((k_blm_head<true, NSTAGE_LM>), grid, dim3(NTHR), 0, s, a, n_p, n_mb);
+  else hipLaunchKernelGGL((k_blm_head<false, NSTAGE_LM>), grid, dim3(NTHR), 0, s, a, n_p, n_mb);
   return hipGetLastError();
 }
 

@@ -166,9 +166,11 @@ __global__ void k_read_kv(const uint8_t *pool, const int32_t *bt, int L, int lay
     const int pos = row0 + r;
     const int32_t blk = bt[pos >> 4];
     const size_t tile = (size_t)DFLASH_KV_BLOCK * d * eb;
-    const size_t base = ((((size_t)blk * L + layer) * 2 + 0) * n_kv + g) * tile + (size_t)(pos & 15) * d * eb;
-    if (k_out) k_out[e] = pool[base + (size_t)j * eb + byte];
-    if (v_out) v_out[e] = pool[base + (size_t)n_kv * tile + de];
+    const size_t kbase = ((((size_t)blk * L + layer) * 2 + 0) * n_kv + g) * tile;
+    const size_t vbase = ((((size_t)blk * L + layer) * 2 + 1) * n_kv + g) * tile;
+    // K tile [16][d] (dims in RoPE pair order), V tile transposed [d][16]
+    if (k_out) k_out[e] = pool[kbase + ((size_t)(pos & 15) * d + j) * eb + byte];
+    if (v_out) v_out[e] = pool[vbase + ((size_t)i * DFLASH_KV_BLOCK + (pos & 15)) * eb + byte];
   }
 }
 

@@ -53,6 +53,8 @@ struct EpiArgs {
   // QKV RoPE
   const float2 *cs;   // [M][head_dim / 2] (cos, sin) of each row's position
   int head_dim, q_dim, kv_dim;
+  uint16_t *vtb;      // QKV: V^T of the block rows, [seq][n_kv][head_dim][gp] (gp = gamma rounded up to 32)
+  int gamma, gp, row0;  // row0: row of the call that this launch's row 0 is
   // KV scatter
   void *pool;
   int L, n_kv, kv_fp8;
@@ -122,17 +124,19 @@ struct AttnSeq {
 
 struct AttnArgs {
   const uint16_t *qkv;   // [n_seq * gamma, ld] rows [Q | K | V], RoPE applied
+  const uint16_t *vtb;   // V^T of the block rows, [n_seq][n_kv][head_dim][roundup(gamma, 32)], zero padded
   int ld, gamma, rep, n_kv, head_dim, k_off, v_off;
-  const void *pool;
+  const void *pool;      // [block][L][K|V][n_kv] tiles: K [16][head_dim], V^T [head_dim][16]
   int L, layer, kv_fp8;
   const float *kv_scale;
-  int chunk, max_splits;
+  int tps, max_splits;   // ctx tiles (32 positions) per split; splits per (sequence, kv head)
   float *o_part, *ml_part;
   uint16_t *out;         // [n_seq * gamma, n_q * head_dim] bf16
   int out_ld;
   AttnSeq seq[DFLASH_MAX_BATCH];
 };
 hipError_t launch_attention(const AttnArgs &a, int n_seq, hipStream_t s);
+int attn_max_tiles_per_split();
 
 // ------------------------------------------------------------------ misc ---
 struct SetupArgs {

@@ -73,6 +73,14 @@ def test_invalid_configs(host, field, value):
     assert host.dfh_last_error().decode().startswith("config:")
 
 
+def test_fp8_kv_needs_wide_heads(host):
+    # E4M3 K rows are read 16 dims per lane group, so head_dim must be >= 64
+    cfg = make_cfg(head_dim=32, kv_dtype=2)
+    assert host.dfh_validate(C.byref(cfg)) == E_INVALID
+    assert "head_dim" in host.dfh_last_error().decode()
+    assert host.dfh_validate(C.byref(make_cfg(head_dim=64, kv_dtype=2))) == OK
+
+
 def _seq(host, pool, budget=INT64_MAX, ids=None, max_seq_len=8192):
     st = C.c_int()
     arr = None if ids is None else np.ascontiguousarray(ids, dtype=np.int32)
