@@ -31,6 +31,7 @@ constexpr uint64_t STATE_MAGIC = 0x44464c4153485354ull;  // "DFLASHST"
 constexpr uint64_t DEAD_MAGIC = 0xdeadull;
 constexpr int ATTN_TARGET_WGS = 512;  // attention workgroups a launch aims for (two per CU)
 constexpr int ATTN_MAX_SPLITS = 64;   // splits per (sequence, kv head) merged by one wave
+constexpr int ATTN_PREF_SPLITS = 16;  // preferred bound: the merge reads every split's partial
 
 #define HIP_TRY(expr)                                                                          \
   do {                                                                                         \
@@ -451,7 +452,7 @@ int propose_impl(dflash_head *H, dflash_state *const *states, int n, const uint3
       if (lo < c) max_T = std::max(max_T, (c - lo / 16 * 16 + 31) / 32);
     }
     const int max_tps = attn_max_tiles_per_split();
-    const int target = std::max(1, ATTN_TARGET_WGS / (n * g.n_kv));
+    const int target = std::max(1, std::min(ATTN_PREF_SPLITS, ATTN_TARGET_WGS / (n * g.n_kv)));
     int tps = std::min(max_tps, std::max(1, (max_T + target - 1) / target));
     tps = std::max(tps, (max_T + ATTN_MAX_SPLITS - 1) / ATTN_MAX_SPLITS);
     const int cap = std::max(1, H->attn_slots / (n * g.n_kv));

@@ -50,9 +50,10 @@ __device__ __forceinline__ void epilogue4(const f32x4 v, int m, int n, int split
       // V of the block rows, transposed per kv head for the attention kernel
       const int vn = n - ea.q_dim - ea.kv_dim, hd = vn / ea.head_dim, dim = vn % ea.head_dim;
       const int seq = (ea.row0 + m) / ea.gamma, j = (ea.row0 + m) % ea.gamma;
-      uint16_t *vt = ea.vtb + ((size_t)(seq * (ea.kv_dim / ea.head_dim) + hd) * ea.head_dim + dim) * ea.gp + j;
+      const int n_kv = ea.kv_dim / ea.head_dim, nb16 = ea.gp / 16;
+      uint16_t *vt = ea.vtb + (((size_t)(seq * n_kv + hd) * nb16 + j / 16) * ea.head_dim + dim) * 16 + (j & 15);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) vt[(size_t)r * ea.gp] = f32_to_bf16(y[r]);
+      for (int r = 0; r < 4; ++r) vt[(size_t)r * 16] = f32_to_bf16(y[r]);
     }
   } else if constexpr (EPI == EPI_KV_SCATTER) {
     const int d = ea.head_dim;

@@ -10,11 +10,12 @@
 // A split owns a run of ctx tiles; the last split also owns the block tiles.
 //
 // The pool stores K row-major and V transposed ([dim][16 slots]) per block,
-// so every MFMA fragment of a tile is one contiguous 16-byte piece per lane
-// in global memory and is copied straight into LDS in fragment order with
-// direct-to-LDS loads (one 1 KB fragment per wave instruction, no register
-// staging). Ctx tiles stream through a ring of NSTAGE LDS slots with
-// NSTAGE - 1 tiles in flight.
+// so every 16-byte piece of an MFMA fragment is contiguous in global memory.
+// Direct-to-LDS loads copy one 1 KB fragment per wave instruction (no
+// register staging); the four lanes of each quad load 64 contiguous bytes (one
+// K row segment, or two V^T rows), and an XOR swizzle of the piece order
+// keeps the fragment reads from LDS free of bank conflicts. Ctx tiles stream
+// through a ring of NSTAGE LDS slots with NSTAGE - 1 tiles in flight.
 //
 // Products are transposed so every per-query quantity stays in one lane:
 // S^T = K Q^T (MFMA A = 16 keys x 32 dims, B = Q^T). The 16 MFMA rows of key
@@ -22,10 +23,11 @@
 // the scores of keys 8g .. 8g+7 for its query; those are exactly the B
 // operand of O^T = V^T P^T, whose A operand (16 dims x keys 8g .. 8g+7) is a
 // 16-byte piece of V^T. Online softmax in base 2; the FP8 V scale of ctx keys
-// is folded into P. With head_dim >= 64 the K fragments of k-steps 2j and
-// 2j+1 take dims 64j + 16g .. +15 of lane group g (one 16-byte piece of an
-// E4M3 row), and Q uses the same dim order. Q and K also carry their head
-// dims in RoPE pair order; every score is unchanged by these permutations.
+// is folded into P. With an E4M3 cache the K fragments of k-steps 2j and 2j+1
+// take dims 64j + 16g .. +15 of lane group g (one 16-byte piece of an E4M3
+// row), and Q (and the block tile's K) use the same dim order. Q and K also
+// carry their head dims in RoPE pair order; every score is unchanged by these
+// permutations.
 //
 // Each split writes an unnormalised partial (O, max, sum) that the combine
 // kernel merges (one wave per query row); with a single split the output is
@@ -85,87 +87,133 @@ struct Geom {
 };
 
 // First dim of the 8 that lane group gq holds in k-step ks.
-template <int D>
+template <bool PAIRED>
 __device__ __forceinline__ int kdim(int ks, int gq) {
-  if constexpr (D >= 64) return (ks & ~1) * 32 + 16 * gq + 8 * (ks & 1);
-  else return 8 * gq;
+  if constexpr (PAIRED) return (ks & ~1) * 32 + 16 * gq + 8 * (ks & 1);
+  else return 32 * ks + 8 * gq;
+}
+
+// LDS piece (16 bytes) of fragment row r (0..15), lane group gq, in a K
+// fragment: the quad of row r holds its four pieces, swizzled.
+__device__ __forceinline__ int k_piece(int r, int gq) { return 4 * r + (gq ^ ((r >> 2) & 3)); }
+// The K row / lane group loaded by DMA lane L (inverse of k_piece).
+__device__ __forceinline__ int k_row_of(int L) { return L >> 2; }
+__device__ __forceinline__ int k_gq_of(int L) { return (L & 3) ^ ((L >> 4) & 3); }
+
+// LDS piece of a bf16 V^T fragment for dim d (0..15) and lane group gq (keys
+// 8gq .. 8gq+7: block gq / 2, half gq % 2): the quad of dims (2k, 2k+1)
+// holds both halves of both rows.
+__device__ __forceinline__ int v_piece(int d, int gq) { return (gq >> 1) * 32 + 2 * d + ((gq & 1) ^ ((d >> 3) & 1)); }
+__device__ __forceinline__ void v_of(int L, int &blk, int &d, int &half) {
+  blk = L >> 5;
+  d = (L & 31) >> 1;
+  half = (L & 1) ^ ((d >> 3) & 1);
 }
 
 // Key within the tile held by MFMA row r of sub-tile u.
 __device__ __forceinline__ int key_of(int u, int r) { return (r >> 2) * 8 + 4 * u + (r & 3); }
 
+// This wave's share of the loads of a ctx tile, fixed for the whole kernel:
+// item j is fragment dst[j] of the slot, read from the K (kv = 0) or V^T
+// (kv = 1) tile of block A or B (per lane) at lane byte offset off[j].
+template <int D, bool FP8>
+struct IssuePlan {
+  static constexpr int PW = Geom<D, FP8>::PW;
+  uint32_t off[PW], dst[PW];
+  int kv[PW];
+  bool selB[PW], act[PW];
+};
+
+template <int D, bool FP8>
+__device__ __forceinline__ IssuePlan<D, FP8> make_issue_plan(int wave, int lane) {
+  using G = Geom<D, FP8>;
+  IssuePlan<D, FP8> p;
+  constexpr int EB = FP8 ? 1 : 2;
+#pragma unroll
+  for (int j = 0; j < G::PW; ++j) {
+    const int i = (wave + 4 * j) % G::CF;  // duplicates reload an item with the same bytes
+    p.dst[j] = i * 1024;
+    p.act[j] = true;
+    if (i < (FP8 ? G::KS : 2 * G::KS)) {
+      // K: this lane loads row k_row_of(lane), lane group k_gq_of(lane)
+      const int r = k_row_of(lane), gq = k_gq_of(lane);
+      int u, dim;
+      if constexpr (FP8) {
+        u = i / (G::KS / 2);
+        dim = kdim<true>(2 * (i % (G::KS / 2)), gq);
+      } else {
+        u = i / G::KS;
+        dim = kdim<false>(i % G::KS, gq);
+        p.act[j] = dim < D;
+      }
+      const int kt = key_of(u, r);
+      p.kv[j] = 0;
+      p.selB[j] = kt >= 16;
+      p.off[j] = ((kt & 15) * D + (dim < D ? dim : 0)) * EB;
+    } else {
+      int dim, slot0;
+      if constexpr (FP8) {
+        dim = (2 * (i - G::KS) + (lane >> 5)) * 16 + (lane & 15);
+        p.selB[j] = (lane >> 4) & 1;
+        slot0 = 0;
+      } else {
+        int blk, d, half;
+        v_of(lane, blk, d, half);
+        dim = (i - 2 * G::KS) * 16 + d;
+        p.selB[j] = blk;
+        slot0 = 8 * half;
+      }
+      p.kv[j] = 1;
+      p.off[j] = (dim * 16 + slot0) * EB;
+    }
+  }
+  return p;
+}
+
 struct TileSrc {
   const uint8_t *pool;
   size_t head_bytes;   // bytes of one (block, layer, K|V, kv head) tile
   int L, layer, n_kv, g;
-  int32_t bA, bB;      // the tile's two KV blocks
 };
 
-// Issue this wave's direct-to-LDS loads of one ctx tile into `slot`.
+// Issue this wave's direct-to-LDS loads of the ctx tile on blocks (bA, bB).
 template <int D, bool FP8>
-__device__ __forceinline__ void issue_ctx(const TileSrc &t, uint32_t slot, int wave, int lane) {
-  using G = Geom<D, FP8>;
-  const int r = lane & 15, gq = lane >> 4;
-  constexpr int EB = FP8 ? 1 : 2;
+__device__ __forceinline__ void issue_ctx(const TileSrc &t, const IssuePlan<D, FP8> &p, int32_t bA, int32_t bB,
+                                          uint32_t slot) {
+  const size_t stride = (size_t)t.n_kv * t.head_bytes;  // K -> V of one (block, layer)
+  const uint8_t *kA = t.pool + (((size_t)bA * t.L + t.layer) * 2 * t.n_kv + t.g) * t.head_bytes;
+  const uint8_t *kB = t.pool + (((size_t)bB * t.L + t.layer) * 2 * t.n_kv + t.g) * t.head_bytes;
 #pragma unroll
-  for (int j = 0; j < G::PW; ++j) {
-    const int i = (wave + 4 * j) % G::CF;  // wave-uniform; duplicates reload an item with the same bytes
-    const uint8_t *src;
-    bool active = true;
-    if (i < (FP8 ? G::KS : 2 * G::KS)) {
-      int u, dim;
-      if constexpr (FP8) {
-        u = i / (G::KS / 2);
-        dim = kdim<D>(2 * (i % (G::KS / 2)), gq);
-      } else {
-        u = i / G::KS;
-        dim = kdim<D>(i % G::KS, gq);
-        active = dim < D;
-      }
-      const int kt = key_of(u, r);
-      const int32_t blk = kt < 16 ? t.bA : t.bB;
-      src = t.pool + ((((size_t)blk * t.L + t.layer) * 2 + 0) * t.n_kv + t.g) * t.head_bytes +
-            ((size_t)(kt & 15) * D + dim) * EB;
-    } else {
-      int dim, slot0;
-      int32_t blk;
-      if constexpr (FP8) {
-        const int dt = 2 * (i - G::KS) + (lane >> 5);
-        dim = dt * 16 + r;
-        blk = ((lane >> 4) & 1) ? t.bB : t.bA;
-        slot0 = 0;
-      } else {
-        dim = (i - 2 * G::KS) * 16 + r;
-        blk = gq < 2 ? t.bA : t.bB;
-        slot0 = 8 * (gq & 1);
-      }
-      src = t.pool + ((((size_t)blk * t.L + t.layer) * 2 + 1) * t.n_kv + t.g) * t.head_bytes +
-            ((size_t)dim * 16 + slot0) * EB;
-    }
-    if (active) dma16(src, slot + i * 1024);
+  for (int j = 0; j < IssuePlan<D, FP8>::PW; ++j) {
+    const uint8_t *base = (p.selB[j] ? kB : kA) + (p.kv[j] ? stride : 0);
+    if (p.act[j]) dma16(base + p.off[j], slot + p.dst[j]);
   }
 }
 
-// Issue this wave's loads of block tile bt (keys 32 bt .. of the gamma rows).
-template <int D>
+// Issue this wave's loads of block tile bt (keys 32 bt .. of the gamma rows):
+// K from the QKV rows (dims in the kernel's K order), V^T from the block
+// copy [seq][kv][16-key block][dim][16].
+template <int D, bool PAIRED>
 __device__ __forceinline__ void issue_block(const AttnArgs &a, int s, int g, int bt, uint32_t slot, int wave,
                                             int lane) {
   using G = Geom<D, false>;
-  const int r = lane & 15, gq = lane >> 4;
-  const int GP = (a.gamma + 31) & ~31;
+  const int nb16 = ((a.gamma + 31) & ~31) / 16;
 #pragma unroll
   for (int j = 0; j < G::PB; ++j) {
     const int i = (wave + 4 * j) % G::BF;
     const uint16_t *src;
     bool active = true;
     if (i < 2 * G::KS) {
-      const int u = i / G::KS, dim = kdim<D>(i % G::KS, gq);
+      const int r = k_row_of(lane), gq = k_gq_of(lane);
+      const int u = i / G::KS, dim = kdim<PAIRED>(i % G::KS, gq);
       active = dim < D;
       const int tok = min(32 * bt + key_of(u, r), a.gamma - 1);
-      src = a.qkv + (size_t)(s * a.gamma + tok) * a.ld + a.k_off + g * D + dim;
+      src = a.qkv + (size_t)(s * a.gamma + tok) * a.ld + a.k_off + g * D + (active ? dim : 0);
     } else {
-      const int dim = (i - 2 * G::KS) * 16 + r;
-      src = a.vtb + ((size_t)(s * a.n_kv + g) * D + dim) * GP + 32 * bt + 8 * gq;
+      int blk, d, half;
+      v_of(lane, blk, d, half);
+      const int dim = (i - 2 * G::KS) * 16 + d;
+      src = a.vtb + ((((size_t)(s * a.n_kv + g) * nb16 + 2 * bt + blk) * D + dim) * 16 + 8 * half);
     }
     if (active) dma16(src, slot + i * 1024);
   }
@@ -186,7 +234,7 @@ struct WaveState {
 // the tile takes part; sc scales the raw scores into base-2 units; vs is
 // folded into P (E4M3 V of ctx keys).
 template <int D, bool FP8CTX, class Valid>
-__device__ __forceinline__ void tile_step(const uint4 *slot, const bf16x8 (&qf)[2][Geom<D, false>::KS], int nqt,
+__device__ __forceinline__ void tile_step(const uint4 *slot, const bf16x8 (&qf)[2][Geom<D, false>::KS], bool full,
                                           Valid valid, float sc, float vs, WaveState<D> &w, int lane) {
   using G = Geom<D, FP8CTX>;
   const int gq = lane >> 4;
@@ -195,18 +243,18 @@ __device__ __forceinline__ void tile_step(const uint4 *slot, const bf16x8 (&qf)[
   for (int u = 0; u < 2; ++u)
 #pragma unroll
     for (int ks = 0; ks < G::KS; ++ks) {
+      const int piece = k_piece(lane & 15, gq);
       if constexpr (FP8CTX) {
-        const uint8_t *p = (const uint8_t *)(slot + (u * (G::KS / 2) + ks / 2) * 64 + lane) + 8 * (ks & 1);
+        const uint8_t *p = (const uint8_t *)(slot + (u * (G::KS / 2) + ks / 2) * 64 + piece) + 8 * (ks & 1);
         kf[u][ks] = as_bf16x8(e4m3x8_to_bf16x8(*(const uint2 *)p));
       } else {
-        kf[u][ks] = as_bf16x8(slot[(u * G::KS + ks) * 64 + lane]);
+        kf[u][ks] = as_bf16x8(slot[(u * G::KS + ks) * 64 + piece]);
       }
     }
   uint4 pk[2];
   float alpha[2];
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
-    if (qt >= nqt) continue;
     f32x4 sacc[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -214,25 +262,31 @@ __device__ __forceinline__ void tile_step(const uint4 *slot, const bf16x8 (&qf)[
 #pragma unroll
       for (int ks = 0; ks < G::KS; ++ks) sacc[u] = mfma16x16x32(kf[u][ks], qf[qt][ks], sacc[u]);
     }
+    // raw scores; sc > 0, so the max commutes with the scaling
     float x[2][4];
-    float tmax = -__builtin_huge_valf();
+    if (!full) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        x[u][r] = valid(8 * gq + 4 * u + r) ? sacc[u][r] * sc : -__builtin_huge_valf();
-        tmax = fmaxf(tmax, x[u][r]);
-      }
+        for (int r = 0; r < 4; ++r) x[u][r] = valid(8 * gq + 4 * u + r) ? sacc[u][r] : -__builtin_huge_valf();
+    } else {
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[u][r] = sacc[u][r];
+    }
+    float tmax = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
+                       fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, WAVE));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, WAVE));
-    const float m_new = fmaxf(w.m[qt], tmax);
+    const float m_new = fmaxf(w.m[qt], tmax * sc);
     alpha[qt] = fast_exp2(w.m[qt] - m_new);
     float p[2][4], psum = 0.0f;
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float e = fast_exp2(x[u][r] - m_new);
+        const float e = fast_exp2(fmaf(x[u][r], sc, -m_new));
         psum += e;
         p[u][r] = e * vs;
       }
@@ -243,6 +297,13 @@ __device__ __forceinline__ void tile_step(const uint4 *slot, const bf16x8 (&qf)[
     pk[qt].z = pack_bf16x2(p[1][0], p[1][1]);
     pk[qt].w = pack_bf16x2(p[1][2], p[1][3]);
   }
+  // rescale O only when some lane's running max moved (alpha == 1 is exact)
+  if (__any(alpha[0] != 1.0f || alpha[1] != 1.0f)) {
+#pragma unroll
+    for (int dt = 0; dt < G::DT; ++dt)
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) w.o[qt][dt] *= alpha[qt];
+  }
 #pragma unroll
   for (int dt = 0; dt < G::DT; ++dt) {
     bf16x8 vf;
@@ -251,21 +312,17 @@ __device__ __forceinline__ void tile_step(const uint4 *slot, const bf16x8 (&qf)[
       const uint8_t *p = base + (((dt & 1) * 32 + (gq >> 1) * 16 + (lane & 15)) * 16) + 8 * (gq & 1);
       vf = as_bf16x8(e4m3x8_to_bf16x8(*(const uint2 *)p));
     } else {
-      vf = as_bf16x8(slot[(2 * G::KS + dt) * 64 + lane]);
+      vf = as_bf16x8(slot[(2 * G::KS + dt) * 64 + v_piece(lane & 15, gq)]);
     }
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      if (qt >= nqt) continue;
-      w.o[qt][dt] = mfma16x16x32(vf, as_bf16x8(pk[qt]), w.o[qt][dt] * alpha[qt]);
-    }
+    for (int qt = 0; qt < 2; ++qt) w.o[qt][dt] = mfma16x16x32(vf, as_bf16x8(pk[qt]), w.o[qt][dt]);
   }
 }
 
-template <int D, bool FP8>
+template <int D, bool FP8, int NS = Geom<D, FP8>::NSTAGE>
 __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   using G = Geom<D, FP8>;
   using GB = Geom<D, false>;
-  constexpr int NS = G::NSTAGE;
   __shared__ uint4 ring[NS][G::CF * 64];
   __shared__ uint4 blkt[GB::BF * 64];
   __shared__ int32_t s_bt[2 * MAX_TPS];
@@ -296,7 +353,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   }
 
   // Q fragments (B operand of S^T): query column r16 of this wave's tiles
-  const int nqt = min(2, max(0, (R - wave * 32 + 15) / 16));
+  // (rows past R repeat row R - 1 and are not written)
   bf16x8 qf[2][GB::KS];
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
@@ -305,7 +362,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     const uint16_t *qrow = a.qkv + (size_t)(s * a.gamma + j) * a.ld + hq * D;
 #pragma unroll
     for (int ks = 0; ks < GB::KS; ++ks) {
-      const int dd = kdim<D>(ks, gq);
+      const int dd = kdim<FP8>(ks, gq);
       qf[qt][ks] = as_bf16x8(dd < D ? *(const uint4 *)(qrow + dd) : uint4{0u, 0u, 0u, 0u});
     }
   }
@@ -337,13 +394,14 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   src.g = g;
   const uint32_t ring0 = lds_addr(&ring[0][0]), blk0 = lds_addr(blkt);
   constexpr uint32_t SLOT_BYTES = G::CF * 1024;
+  const IssuePlan<D, FP8> plan = make_issue_plan<D, FP8>(wave, lane);
   auto issue_tile = [&](int t, int slot_idx) {
-    src.bA = s_bt[2 * t];
-    src.bB = s_bt[2 * t + 1];
-    issue_ctx<D, FP8>(src, ring0 + slot_idx * SLOT_BYTES, wave, lane);
+    const int32_t bA = __builtin_amdgcn_readfirstlane(s_bt[2 * t]);
+    const int32_t bB = __builtin_amdgcn_readfirstlane(s_bt[2 * t + 1]);
+    issue_ctx<D, FP8>(src, plan, bA, bB, ring0 + slot_idx * SLOT_BYTES);
   };
 
-  if (last) issue_block<D>(a, s, g, 0, blk0, wave, lane);
+  if (last) issue_block<D, FP8>(a, s, g, 0, blk0, wave, lane);
   if (nt > 0)
 #pragma unroll
     for (int j = 0; j < NS - 1; ++j) issue_tile(min(j, nt - 1), j);
@@ -355,12 +413,12 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
         else wait_vm<0>();
       } else {
         lds_barrier();  // everyone is done with the previous block tile
-        issue_block<D>(a, s, g, bt, blk0, wave, lane);
+        issue_block<D, FP8>(a, s, g, bt, blk0, wave, lane);
         wait_vm<0>();
       }
       lds_barrier();
       const int nvalid = min(KT, a.gamma - 32 * bt);
-      tile_step<D, false>(blkt, qf, nqt, [&](int kt) { return kt < nvalid; }, sc_blk, 1.0f, w, lane);
+      tile_step<D, false>(blkt, qf, nvalid >= KT, [&](int kt) { return kt < nvalid; }, sc_blk, 1.0f, w, lane);
     }
   }
 
@@ -372,8 +430,8 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     issue_tile(min(t + NS - 1, nt - 1), (t + NS - 1) % NS);
     const int pos0 = pos_base + t * KT;
     const int lo = sq.win_start - pos0, hi = sq.ctx_len - pos0;
-    tile_step<D, FP8>(&ring[t % NS][0], qf, nqt, [&](int kt) { return kt >= lo && kt < hi; }, sc_ctx,
-                      FP8 ? vscale : 1.0f, w, lane);
+    tile_step<D, FP8>(&ring[t % NS][0], qf, lo <= 0 && hi >= KT, [&](int kt) { return kt >= lo && kt < hi; },
+                      sc_ctx, FP8 ? vscale : 1.0f, w, lane);
   }
   wait_vm<0>();
 
@@ -384,7 +442,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     l_tot += __shfl_xor(l_tot, 16, WAVE);
     l_tot += __shfl_xor(l_tot, 32, WAVE);
     const int q = (wave * 2 + qt) * 16 + r16;
-    if (qt >= nqt || q >= R) continue;
+    if (q >= R) continue;
     if (a.max_splits == 1) {
       const int hq = g * a.rep + q / a.gamma, j = q % a.gamma;
       uint16_t *out = a.out + (size_t)(s * a.gamma + j) * a.out_ld + hq * D;
@@ -433,7 +491,7 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a, int n_seq) {
 #pragma unroll
   for (int i = 0; i < DPL; ++i) acc[i] = 0.0f;
   const bool active = D >= 64 || lane < D;
-#pragma unroll 8
+#pragma unroll 16
   for (int c = 0; c < nsplit; ++c) {
     const float wc = __shfl(w, c, WAVE);
     const float *op = a.o_part + ((base + c) * R + q) * D;

@@ -53,7 +53,7 @@ struct EpiArgs {
   // QKV RoPE
   const float2 *cs;   // [M][head_dim / 2] (cos, sin) of each row's position
   int head_dim, q_dim, kv_dim;
-  uint16_t *vtb;      // QKV: V^T of the block rows, [seq][n_kv][head_dim][gp] (gp = gamma rounded up to 32)
+  uint16_t *vtb;      // QKV: V^T of the block rows, [seq][n_kv][gp / 16][head_dim][16] (gp = gamma rounded up to 32)
   int gamma, gp, row0;  // row0: row of the call that this launch's row 0 is
   // KV scatter
   void *pool;
@@ -124,7 +124,7 @@ struct AttnSeq {
 
 struct AttnArgs {
   const uint16_t *qkv;   // [n_seq * gamma, ld] rows [Q | K | V], RoPE applied
-  const uint16_t *vtb;   // V^T of the block rows, [n_seq][n_kv][head_dim][roundup(gamma, 32)], zero padded
+  const uint16_t *vtb;   // V^T of the block rows, [n_seq][n_kv][roundup(gamma, 32) / 16][head_dim][16], zero padded
   int ld, gamma, rep, n_kv, head_dim, k_off, v_off;
   const void *pool;      // [block][L][K|V][n_kv] tiles: K [16][head_dim], V^T [head_dim][16]
   int L, layer, kv_fp8;
