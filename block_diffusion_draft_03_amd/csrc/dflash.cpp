@@ -85,6 +85,8 @@ struct dflash_head {
   int *fin_counters = nullptr;
   int lm_P = 0;
   int attn_slots = 0;
+  float *ss = nullptr;        // per-unit row sums of squares [h / 16][M] (few-row path)
+  int *tile_ctr = nullptr;    // split counters of the residual GEMMs [h / 16], zero between launches
   uint16_t *vtb = nullptr;  // V^T of the block rows [max_batch][n_kv][d][gp], zero padded
   int gp = 0;
   float *pre_u = nullptr;
@@ -301,6 +303,9 @@ int build_impl(dflash_head *H, const dflash_weights *w, hipStream_t st) {
     const int per_seq = std::min(ATTN_MAX_SPLITS, (max_tiles + attn_max_tiles_per_split() - 1) / attn_max_tiles_per_split() + 1);
     H->attn_slots = std::max({ATTN_TARGET_WGS * 2, g.max_batch * g.n_kv * per_seq, g.n_kv * ATTN_MAX_SPLITS});
   }
+  TRY(H->alloc(&H->ss, (size_t)((g.h + 15) / 16) * GEMM_MAX_ROWS));
+  TRY(H->alloc(&H->tile_ctr, (size_t)((g.h + 15) / 16)));
+  HIP_TRY(hipMemsetAsync(H->tile_ctr, 0, (size_t)((g.h + 15) / 16) * sizeof(int), st));
   H->gp = (g.gamma + 31) / 32 * 32;
   TRY(H->alloc(&H->vtb, (size_t)g.max_batch * g.n_kv * g.d * H->gp));
   HIP_TRY(hipMemsetAsync(H->vtb, 0, (size_t)g.max_batch * g.n_kv * g.d * H->gp * sizeof(uint16_t), st));
@@ -324,7 +329,7 @@ int build_impl(dflash_head *H, const dflash_weights *w, hipStream_t st) {
 // pointers and the RoPE table are advanced with the rows. EPI_PARTIAL
 // outputs are laid out [splits][M][N] over all M rows of the call.
 int gemm_rows(dflash_head *H, int epi, const uint16_t *A, int lda, int M, const uint16_t *W, int N, int K,
-              EpiArgs e, hipStream_t st, int *splits_out = nullptr) {
+              EpiArgs e, hipStream_t st, int *splits_out = nullptr, RowScale rs = RowScale{}) {
   GemmArgs ga{};
   ga.lda = lda;
   ga.W = W;
@@ -338,7 +343,7 @@ int gemm_rows(dflash_head *H, int epi, const uint16_t *A, int lda, int M, const 
   ga.kslice = p.kslice;
   if (splits_out) *splits_out = p.splits;
   e.ld_split = M;
-  if (M > GEMM_MAX_ROWS && bgemm_ok(epi, N, K)) {
+  if (M > GEMM_MAX_ROWS && bgemm_ok(epi, N, K) && !rs.ss && !e.tile_ctr) {
     // all rows in one tiled launch
     ga.A = A;
     ga.M = M;
@@ -355,6 +360,11 @@ int gemm_rows(dflash_head *H, int epi, const uint16_t *A, int lda, int M, const 
     if (e.out_f32) ec.out_f32 = e.out_f32 + (size_t)r0 * e.ldo;
     if (e.out_bf16) ec.out_bf16 = e.out_bf16 + (size_t)r0 * e.ldo;
     if (e.cs) ec.cs = e.cs + (size_t)r0 * half;
+    if (e.res_h) ec.res_h = e.res_h + (size_t)r0 * N;
+    if (e.res_act) ec.res_act = e.res_act + (size_t)r0 * N;
+    if (e.ss_out) ec.ss_out = e.ss_out + r0;
+    ga.rs = rs;
+    if (rs.ss) ga.rs.ss = rs.ss + r0;
     HIP_TRY(launch_gemm(epi, ga, ec, st));
   }
   return DFLASH_OK;
@@ -380,6 +390,27 @@ int resid_gemm(dflash_head *H, const uint16_t *A, int lda, int M, const uint16_t
   r.eps = H->cfg.rms_eps;
   r.out = out;
   HIP_TRY(launch_resid_norm(r, M, st));
+  return DFLASH_OK;
+}
+
+// h += W A^T into the residual stream for few rows: the split GEMM's last
+// split of every 16-row unit adds the splits in order, writes bf16(h * gain)
+// and the unit's per-row sums of squares (H->ss); the consumer applies the
+// RMSNorm row scale. Returns the units the consumer sums.
+int resid_gemm_fused(dflash_head *H, const uint16_t *A, int lda, int M, const uint16_t *W, int K, const float *gain,
+                     hipStream_t st, int *units) {
+  EpiArgs e{};
+  e.out_f32 = H->part;
+  e.ldo = H->g.h;
+  e.res_h = H->hid;
+  e.res_gain = gain;
+  e.res_act = H->act;
+  e.ss_out = H->ss;
+  e.ss_ld = M;
+  e.tile_ctr = H->tile_ctr;
+  TRY(gemm_rows(H, EPI_PARTIAL, A, lda, M, W, H->g.h, K, e, st));
+  const GemmPlan p = gemm_plan(H->g.h, K, true);
+  *units = (H->g.h + 16 * p.tn - 1) / (16 * p.tn);
   return DFLASH_OK;
 }
 
@@ -412,8 +443,12 @@ int propose_impl(dflash_head *H, dflash_state *const *states, int n, const uint3
   sa.half_dim = g.d / 2;
   sa.mask_id = g.mask_id;
   sa.inv_freq = H->inv_freq;
+  // few rows: the residual GEMMs finish their own splits and every consumer
+  // applies the RMSNorm row scale from per-unit sums of squares (H->ss)
+  const bool fused = M <= GEMM_MAX_ROWS;
   sa.hid = H->hid;
   sa.a = H->act;
+  sa.ss_out = fused ? H->ss : nullptr;
   sa.cs = H->cs;
   for (int i = 0; i < n; ++i) {
     sa.token[i] = tokens[i];
@@ -466,6 +501,8 @@ int propose_impl(dflash_head *H, dflash_state *const *states, int n, const uint3
   // act holds RMSNorm(h) with the next consumer's gain: layer 0's input norm
   // comes from the setup kernel, every later one from the residual finish.
   EpiArgs e{};
+  RowScale rs{};
+  if (fused) rs = RowScale{H->ss, 1, M, H->cfg.rms_eps};
   for (int l = 0; l < g.L; ++l) {
     e = EpiArgs{};
     e.out_bf16 = H->qkv;
@@ -477,17 +514,25 @@ int propose_impl(dflash_head *H, dflash_state *const *states, int n, const uint3
     e.vtb = H->vtb;
     e.gamma = g.gamma;
     e.gp = H->gp;
-    TRY(gemm_rows(H, EPI_QKV_ROPE, H->act, h, M, H->w_qkv + (size_t)l * H->sz_qkv, g.qkv_dim, h, e, st));
+    TRY(gemm_rows(H, EPI_QKV_ROPE, H->act, h, M, H->w_qkv + (size_t)l * H->sz_qkv, g.qkv_dim, h, e, st, nullptr, rs));
     aa.layer = l;
     HIP_TRY(launch_attention(aa, n, st));
-    TRY(resid_gemm(H, H->attn, g.q_dim, M, H->w_o + (size_t)l * H->sz_o, g.q_dim, H->hid,
-                   H->g_post + (size_t)l * h, H->act, false, st));
+    const float *post_gain = H->g_post + (size_t)l * h;
+    if (fused) {
+      TRY(resid_gemm_fused(H, H->attn, g.q_dim, M, H->w_o + (size_t)l * H->sz_o, g.q_dim, post_gain, st, &rs.units));
+    } else {
+      TRY(resid_gemm(H, H->attn, g.q_dim, M, H->w_o + (size_t)l * H->sz_o, g.q_dim, H->hid, post_gain, H->act, false, st));
+    }
     e = EpiArgs{};
     e.out_bf16 = H->mlp;
     e.ldo = g.I;
-    TRY(gemm_rows(H, EPI_SWIGLU, H->act, h, M, H->w_gu + (size_t)l * H->sz_gu, 2 * g.I, h, e, st));
+    TRY(gemm_rows(H, EPI_SWIGLU, H->act, h, M, H->w_gu + (size_t)l * H->sz_gu, 2 * g.I, h, e, st, nullptr, rs));
     const float *next_gain = l + 1 < g.L ? H->g_in + (size_t)(l + 1) * h : H->g_final;
-    TRY(resid_gemm(H, H->mlp, g.I, M, H->w_down + (size_t)l * H->sz_down, g.I, H->hid, next_gain, H->act, false, st));
+    if (fused) {
+      TRY(resid_gemm_fused(H, H->mlp, g.I, M, H->w_down + (size_t)l * H->sz_down, g.I, next_gain, st, &rs.units));
+    } else {
+      TRY(resid_gemm(H, H->mlp, g.I, M, H->w_down + (size_t)l * H->sz_down, g.I, H->hid, next_gain, H->act, false, st));
+    }
   }
 
   LmArgs la{};
@@ -502,6 +547,7 @@ int propose_impl(dflash_head *H, dflash_state *const *states, int n, const uint3
   la.part_mx = H->lm_mx;
   la.part_se = H->lm_se;
   la.part_idx = H->lm_idx;
+  la.rs = rs;
   const bool tiled_lm = M > GEMM_MAX_ROWS && g.V % 128 == 0 && h % 128 == 0;
   if (tiled_lm) {
     la.z = H->act;

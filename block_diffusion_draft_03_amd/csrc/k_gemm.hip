@@ -164,27 +164,148 @@ __device__ __forceinline__ void wave_reduce(f32x4 (&acc)[TN][MT], float *red) {
   }
 }
 
+// r[m] = 1 / sqrt(sum_u ss[u * ld + m] / n + eps) for the R = 16 MT rows of
+// the launch, into LDS: every thread sums a strided subset of the units of
+// one row, the subsets are added in a fixed order. The first RS_PRE loads of
+// every thread are issued by row_scale_issue (before the weight stream) and
+// consumed by row_scale_finish (after it).
+constexpr int RS_PRE = 8;
+
+template <int MT>
+__device__ __forceinline__ void row_scale_issue(const RowScale &rs, int M, float (&v)[RS_PRE]) {
+  constexpr int R = 16 * MT;
+  const int row = threadIdx.x % R, grp = threadIdx.x / R, ngrp = blockDim.x / R;
+#pragma unroll
+  for (int i = 0; i < RS_PRE; ++i) {
+    const int u = grp + i * ngrp;
+    v[i] = (row < M && u < rs.units) ? rs.ss[(size_t)u * rs.ld + row] : 0.0f;
+  }
+}
+
+template <int MT>
+__device__ __forceinline__ void row_scale_finish(const RowScale &rs, int M, int n, const float (&v)[RS_PRE],
+                                                 float *rinv, float *tmp) {
+  constexpr int R = 16 * MT;
+  const int row = threadIdx.x % R, grp = threadIdx.x / R, ngrp = blockDim.x / R;
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < RS_PRE; ++i) s += v[i];
+  if (row < M)
+    for (int u = grp + RS_PRE * ngrp; u < rs.units; u += ngrp) s += rs.ss[(size_t)u * rs.ld + row];
+  __syncthreads();
+  tmp[threadIdx.x] = s;
+  __syncthreads();
+  if (threadIdx.x < R) {
+    float t = 0.0f;
+    for (int i = 0; i < ngrp; ++i) t += tmp[i * R + threadIdx.x];
+    rinv[threadIdx.x] = 1.0f / sqrtf(t / (float)n + rs.eps);
+  }
+  __syncthreads();
+}
+
+template <int MT>
+__device__ __forceinline__ void load_row_scale(const RowScale &rs, int M, int n, float *rinv, float *tmp) {
+  float v[RS_PRE];
+  row_scale_issue<MT>(rs, M, v);
+  row_scale_finish<MT>(rs, M, n, v, rinv, tmp);
+}
+
+// Split finish of a residual GEMM (EPI_PARTIAL with ea.tile_ctr), wave 0 of
+// each workgroup: publish this split's partial with write-through stores,
+// count the unit's splits, and in the last one add the splits in split order
+// onto the residual, write the gain-scaled bf16 row part and the unit's per-row
+// sums of squares.
+template <int MT, int TN>
+__device__ __forceinline__ void finish_residual(const GemmArgs &ga, const EpiArgs &ea, const f32x4 (&acc)[TN][MT],
+                                                int row0) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
+  const int split = blockIdx.y, splits = gridDim.y;
+  if (splits > 1) {
+#pragma unroll
+    for (int t = 0; t < TN; ++t)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int m = mt * 16 + r16, n = row0 + 16 * t + 4 * g;
+        if (m >= ga.M || n >= ga.N) continue;
+        float *o = ea.out_f32 + ((size_t)split * ea.ld_split + m) * ea.ldo + n;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) __hip_atomic_store(o + r, acc[t][mt][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    __builtin_amdgcn_s_waitcnt(0x0F70 & ~0xF);  // vmcnt(0): the partial is written through
+    int prev = 0;
+    if (lane == 0) prev = __hip_atomic_fetch_add(&ea.tile_ctr[blockIdx.x], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    prev = __shfl(prev, 0, WAVE);
+    if (prev != splits - 1) return;
+    if (lane == 0) __hip_atomic_store(&ea.tile_ctr[blockIdx.x], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  float ss[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) ss[mt] = 0.0f;
+#pragma unroll
+  for (int t = 0; t < TN; ++t)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = mt * 16 + r16, n = row0 + 16 * t + 4 * g;
+      if (m >= ga.M || n >= ga.N) continue;
+      float *hr = ea.res_h + (size_t)m * ga.N + n;
+      f32x4 x = *(const f32x4 *)hr;
+      for (int sp = 0; sp < splits; ++sp) {
+        if (sp == split) {
+          x += acc[t][mt];
+        } else {
+          const float *o = ea.out_f32 + ((size_t)sp * ea.ld_split + m) * ea.ldo + n;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) x[r] += __hip_atomic_load(o + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      *(f32x4 *)hr = x;
+      const float4 gg = *(const float4 *)(ea.res_gain + n);
+      *(uint2 *)(ea.res_act + (size_t)m * ga.N + n) =
+          uint2{pack_bf16x2(x[0] * gg.x, x[1] * gg.y), pack_bf16x2(x[2] * gg.z, x[3] * gg.w)};
+      ss[mt] += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+    }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    float v = ss[mt];
+    v += __shfl_xor(v, 16, WAVE);
+    v += __shfl_xor(v, 32, WAVE);
+    const int m = mt * 16 + r16;
+    if (g == 0 && m < ga.M) ea.ss_out[(size_t)blockIdx.x * ea.ss_ld + m] = v;
+  }
+}
+
 template <int MT, int TN, int NW, int ST, int EPI, bool TILED = false>
 __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs ga, EpiArgs ea) {
-  __shared__ float red[(NW > 1 ? NW - 1 : 1) * TN * MT * 4 * 64];
+  __shared__ float red[(NW > 1 ? NW - 1 : 1) * TN * MT * 4 * 64 > 256 ? (NW > 1 ? NW - 1 : 1) * TN * MT * 4 * 64 : 256];
+  __shared__ float rinv[16 * MT];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
   const int row0 = blockIdx.x * 16 * TN;
   const int kb = blockIdx.y * ga.kslice, ke = min(ga.K, kb + ga.kslice);
   const int steps = (ke - kb + 127) / 128;
   const int s0 = (steps * wave) / NW, s1 = (steps * (wave + 1)) / NW;
+  float rs_v[RS_PRE];
+  if (ga.rs.ss) row_scale_issue<MT>(ga.rs, ga.M, rs_v);
   f32x4 acc[TN][MT];
   zero<MT, TN>(acc);
   stream_rows<MT, TN, ST, false, TILED>(ga.W, ga.N, ga.K, ga.A, ga.lda, ga.M, row0, kb + 128 * s0,
                                         min(ke, kb + 128 * s1), acc);
   wave_reduce<MT, TN, NW>(acc, red);
+  if (ga.rs.ss) row_scale_finish<MT>(ga.rs, ga.M, ga.K, rs_v, rinv, red);
   if (wave != 0) return;
+  if constexpr (EPI == EPI_PARTIAL) {
+    if (ea.tile_ctr) {
+      finish_residual<MT, TN>(ga, ea, acc, row0);
+      return;
+    }
+  }
 #pragma unroll
   for (int t = 0; t < TN; ++t)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int m = mt * 16 + r16;
       const int n = row0 + 16 * t + 4 * g;  // first of this lane's 4 rows
-      if (m < ga.M && n < ga.N) epilogue4<EPI>(acc[t][mt], m, n, blockIdx.y, ea);
+      const f32x4 v = ga.rs.ss ? acc[t][mt] * rinv[min(m, 16 * MT - 1)] : acc[t][mt];
+      if (m < ga.M && n < ga.N) epilogue4<EPI>(v, m, n, blockIdx.y, ea);
     }
 }
 
@@ -237,6 +358,15 @@ __global__ __launch_bounds__(256) void k_lm_head(LmArgs a) {
     const int m = min(mt * 16 + r16, a.M - 1);
     mask_row[mt] = a.bitmask ? a.bitmask + (size_t)((a.row0 + m) / a.gamma) * a.words : nullptr;
   }
+  __shared__ float rinv[16 * MT], tmp[256];
+  if (a.rs.ss) {
+    RowScale rs = a.rs;
+    rs.ss = a.rs.ss + a.row0;
+    load_row_scale<MT>(rs, a.M, a.K, rinv, tmp);
+  }
+  float rsc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) rsc[mt] = a.rs.ss ? rinv[min(mt * 16 + r16, 16 * MT - 1)] : 1.0f;
   const int nw = gridDim.x * 4;
   for (int u = blockIdx.x * 4 + wave; u < units; u += nw) {
     const int row0 = u * UNIT;
@@ -252,7 +382,7 @@ __global__ __launch_bounds__(256) void k_lm_head(LmArgs a) {
         const float sc = WFP8 ? a.scale[v] : 1.0f;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          const float x = acc[t][mt][r] * sc;
+          const float x = a.rs.ss ? acc[t][mt][r] * rsc[mt] * sc : acc[t][mt][r] * sc;
           const int m = mt * 16 + r16;
           if (a.logits && m < a.M) a.logits[(size_t)m * a.V + v] = x;
           const bool ok = !mask_row[mt] || ((((uint32_t)mask_row[mt][v >> 5]) >> (v & 31)) & 1u);

@@ -11,8 +11,9 @@ namespace {
 // One workgroup per block row m of the call: sequence s = m / gamma, row
 // j = m % gamma. Token = last verified token for j == 0, else the mask
 // token; position = position[s] + j. Writes the fp32 residual row (embedding
-// row widened), its RMSNorm with the first layer's input gain as bf16, and
-// the row's (cos, sin) RoPE table computed in double precision.
+// row widened), its RMSNorm with the first layer's input gain as bf16 (or,
+// with ss_out, the row times the gain and the row's sum of squares), and the
+// row's (cos, sin) RoPE table computed in double precision.
 __global__ __launch_bounds__(256) void k_setup(SetupArgs a) {
   __shared__ float red[4];
   const int m = blockIdx.x, s = m / a.gamma, j = m % a.gamma;
@@ -27,7 +28,8 @@ __global__ __launch_bounds__(256) void k_setup(SetupArgs a) {
     ss += x * x;
   }
   ss = block_sum(ss, red);
-  const float r = 1.0f / sqrtf(ss / (float)a.h + a.eps);
+  const float r = a.ss_out ? 1.0f : 1.0f / sqrtf(ss / (float)a.h + a.eps);
+  if (a.ss_out && threadIdx.x == 0) a.ss_out[m] = ss;
   uint16_t *ar = a.a + (size_t)m * a.h;
   for (int i = threadIdx.x; i < a.h; i += blockDim.x) ar[i] = f32_to_bf16(bf16_to_f32(e[i]) * r * a.gain[i]);
   for (int i = threadIdx.x; i < a.half_dim; i += blockDim.x) {

@@ -38,12 +38,23 @@ struct GemmPlan {
 };
 GemmPlan gemm_plan(int N, int K, bool allow_split);
 
+// Row scale of an activation that is not yet normalised: A holds
+// bf16(h * gain) and r[m] = 1 / sqrt(sum_u ss[u * ld + m] / K + eps) from the
+// producer's per-unit sums of squares of h; the GEMM multiplies row m of its
+// result by r[m] (null ss: A is already normalised).
+struct RowScale {
+  const float *ss;
+  int units, ld;
+  float eps;
+};
+
 struct GemmArgs {
   const uint16_t *A;  // bf16 activations [M, lda]
   int lda, M;
   const void *W;      // [N, K] bf16, tile-major
   int N, K;
   int tn, nw, st, splits, kslice;
+  RowScale rs;        // weight-streaming kernel only
 };
 
 struct EpiArgs {
@@ -62,6 +73,16 @@ struct EpiArgs {
   const double *inv_freq;  // device [head_dim / 2]
   int row_pos[GEMM_MAX_ROWS];
   const int32_t *row_bt[GEMM_MAX_ROWS];
+  // EPI_PARTIAL, weight-streaming kernel: when tile_ctr is set, the last
+  // split of every unit adds the splits in order to the fp32 residual res_h
+  // [M][N], writes res_act = bf16(res_h * res_gain) and the unit's per-row
+  // sum of squares to ss_out[unit * ss_ld + m] (counters start and end at 0)
+  float *res_h;
+  const float *res_gain;
+  uint16_t *res_act;
+  float *ss_out;
+  int ss_ld;
+  int *tile_ctr;
 };
 
 hipError_t launch_gemm(int epi, const GemmArgs &g, const EpiArgs &e, hipStream_t s);
@@ -97,6 +118,7 @@ struct LmArgs {
   float *logits;         // [M, V] or null, already offset to row0
   float *part_mx, *part_se;
   uint32_t *part_idx;    // [P, ld_part]
+  RowScale rs;           // weight-streaming kernel only (rows row0 + m)
 };
 int lm_parts(int V);     // P of launch_lm_head, a function of V only
 hipError_t launch_lm_head(bool w_fp8, const LmArgs &a, hipStream_t s);
@@ -147,7 +169,8 @@ struct SetupArgs {
   uint32_t mask_id;
   const double *inv_freq;   // [half_dim]
   float *hid;               // [M, h] fp32
-  uint16_t *a;              // [M, h] bf16
+  uint16_t *a;              // [M, h] bf16: RMSNorm(h) * gain, or h * gain when ss_out is set
+  float *ss_out;            // [M] sum of squares of each row (the row scale is left to the consumer), or null
   float2 *cs;               // [M, half_dim]
   uint32_t token[DFLASH_MAX_BATCH];
   int32_t position[DFLASH_MAX_BATCH];
