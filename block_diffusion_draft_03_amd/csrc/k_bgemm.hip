@@ -1,9 +1,10 @@
 // k_bgemm.hip - LDS-tiled MFMA GEMMs for many activation rows (batched
 // propose) on gfx950.
 //
-// A workgroup of 4 waves computes a 128 x 128 block of D^T = W A^T: 8 weight
-// tiles of 16 rows against 8 activation tiles of 16 rows, each wave a 64 x 64
-// quarter with v_mfma_f32_16x16x32_bf16. K advances in stages of 64 columns
+// A workgroup computes a block of D^T = W A^T with v_mfma_f32_16x16x32_bf16:
+// 128 x 128 (weight rows x activation rows) on 4 waves of 64 x 64 for the
+// layer GEMMs, 256 x 256 on 8 waves of 128 x 64 for the LM head (larger wave
+// tiles read fewer LDS bytes per MFMA). K advances in stages of 64 columns
 // (half of one 128-wide step of the tile-major weight layout). A stage's
 // operands are staged in LDS already in MFMA fragment order (the weights come
 // from HBM in that order; activation rows are scattered into it), so every
@@ -29,15 +30,24 @@ namespace dflash {
 
 namespace {
 
-constexpr int BN = 128;                // weight rows per workgroup
-constexpr int BM = 128;                // activation rows per workgroup
-constexpr int NT = BN / 16;            // weight tiles
-constexpr int MTL = BM / 16;           // activation tiles
-constexpr int WN = NT / 2, WM = MTL / 2;  // tiles per wave (2 x 2 waves)
-constexpr int NTHR = 256;
+// Workgroup tile: BN weight rows x BM activation rows on WAVES_N x WAVES_M
+// waves; every wave loads two weight tiles and two activation tiles of each
+// stage (so NT = MTL = 2 * waves).
+template <int BN_, int BM_, int WAVES_N_, int WAVES_M_>
+struct Tiling {
+  static constexpr int BN = BN_, BM = BM_;
+  static constexpr int NT = BN / 16, MTL = BM / 16;   // 16-row tiles
+  static constexpr int WAVES_N = WAVES_N_, WAVES_M = WAVES_M_;
+  static constexpr int NWAVES = WAVES_N * WAVES_M, NTHR = 64 * NWAVES;
+  static constexpr int WN = NT / WAVES_N, WM = MTL / WAVES_M;  // tiles per wave
+  static_assert(NT == 2 * NWAVES && MTL == 2 * NWAVES, "two weight and two activation tiles per wave");
+};
+using TileG = Tiling<128, 128, 2, 2>;   // layer GEMMs: 4 waves of 64 x 64
+using TileL = Tiling<256, 256, 2, 4>;   // LM head: 8 waves of 128 x 64
+
 constexpr int NSTAGE_GEMM = 3;         // LDS ring depth (stages in flight + the one multiplied)
 constexpr int NSTAGE_LM = 2;
-constexpr int LM_TILES = 8;            // vocab tiles of 128 per LM-head workgroup
+constexpr int LM_TILES = 4;            // vocab blocks per LM-head workgroup
 
 typedef __attribute__((address_space(3))) uint4 lds_uint4;
 typedef int int4v __attribute__((ext_vector_type(4)));
@@ -76,12 +86,12 @@ __device__ __forceinline__ uint32_t lds_addr(const uint4 *p) {
 // fragments [tile][c] (bf16) or [tile] (E4M3: the 16 codes of k-groups c = 0
 // and 1 of each lane), then the activation fragments [act tile][c]. Wave w
 // loads the weight and activation fragments of tiles 2w and 2w + 1.
-template <bool WFP8>
+template <bool WFP8, class TL>
 struct StageShape {
-  static constexpr int WF = WFP8 ? NT : NT * 2;
-  static constexpr int AF = MTL * 2;
+  static constexpr int WF = WFP8 ? TL::NT : TL::NT * 2;
+  static constexpr int AF = TL::MTL * 2;
   static constexpr int F = WF + AF;
-  static constexpr int PER = F / 4;    // fragment loads per wave
+  static constexpr int PER = F / TL::NWAVES;  // fragment loads per wave
 };
 
 // Per-lane offsets of a wave's loads, fixed for the whole K loop.
@@ -112,9 +122,9 @@ __device__ __forceinline__ LoadPlan make_plan(const void *W, size_t w_bytes, int
 
 // Direct-to-LDS loads of the stage at absolute column k (a multiple of 64)
 // into the slot at LDS byte address `slot`.
-template <bool WFP8>
+template <bool WFP8, class TL>
 __device__ __forceinline__ void issue_stage(uint32_t slot, const LoadPlan &p, int wave, int lane, int k) {
-  using S = StageShape<WFP8>;
+  using S = StageShape<WFP8, TL>;
   const uint32_t step_off = (uint32_t)(k >> 7) * p.w_step + (uint32_t)((k >> 6) & 1) * (p.w_step / 2);
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -134,9 +144,9 @@ __device__ __forceinline__ void issue_stage(uint32_t slot, const LoadPlan &p, in
 }
 
 // Wait until at most `later` stages of this wave's loads are outstanding.
-template <bool WFP8>
+template <bool WFP8, class TL>
 __device__ __forceinline__ void wait_stages(int later) {
-  constexpr int P = StageShape<WFP8>::PER;
+  constexpr int P = StageShape<WFP8, TL>::PER;
   // s_waitcnt vmcnt(n) with expcnt / lgkmcnt left at their maximum
 #define DFL_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0xF70)
   if (later >= 3) DFL_VMCNT(3 * P);
@@ -146,27 +156,25 @@ __device__ __forceinline__ void wait_stages(int later) {
 #undef DFL_VMCNT
 }
 
-__device__ __forceinline__ void bf16_frags_of_e4m3(const uint4 q, uint4 &c0, uint4 &c1) {
-  uint2 lo = e4m3x4_to_bf16x4(q.x), hi = e4m3x4_to_bf16x4(q.y);
-  c0 = uint4{lo.x, lo.y, hi.x, hi.y};
-  lo = e4m3x4_to_bf16x4(q.z);
-  hi = e4m3x4_to_bf16x4(q.w);
-  c1 = uint4{lo.x, lo.y, hi.x, hi.y};
-}
-
-template <bool WFP8>
-__device__ __forceinline__ void mma_stage(const uint4 *slot, int wn, int wm, int lane, f32x4 (&acc)[WN][WM]) {
-  using S = StageShape<WFP8>;
-  uint4 w8[WN][2];
-  if constexpr (WFP8) {
-#pragma unroll
-    for (int i = 0; i < WN; ++i) bf16_frags_of_e4m3(slot[(wn * WN + i) * 64 + lane], w8[i][0], w8[i][1]);
-  }
+template <bool WFP8, class TL>
+__device__ __forceinline__ void mma_stage(const uint4 *slot, int wn, int wm, int lane,
+                                          f32x4 (&acc)[TL::WN][TL::WM]) {
+  using S = StageShape<WFP8, TL>;
+  constexpr int WN = TL::WN, WM = TL::WM;
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     uint4 wf[WN], af[WM];
 #pragma unroll
-    for (int i = 0; i < WN; ++i) wf[i] = WFP8 ? w8[i][c] : slot[((wn * WN + i) * 2 + c) * 64 + lane];
+    for (int i = 0; i < WN; ++i) {
+      if constexpr (WFP8) {
+        // k-group c of the lane's E4M3 pair, widened to bf16
+        const uint2 q = *(const uint2 *)((const uint8_t *)(slot + (wn * WN + i) * 64 + lane) + 8 * c);
+        const uint2 lo = e4m3x4_to_bf16x4(q.x), hi = e4m3x4_to_bf16x4(q.y);
+        wf[i] = uint4{lo.x, lo.y, hi.x, hi.y};
+      } else {
+        wf[i] = slot[((wn * WN + i) * 2 + c) * 64 + lane];
+      }
+    }
 #pragma unroll
     for (int j = 0; j < WM; ++j) af[j] = slot[(S::WF + (wm * WM + j) * 2 + c) * 64 + lane];
 #pragma unroll
@@ -176,6 +184,7 @@ __device__ __forceinline__ void mma_stage(const uint4 *slot, int wn, int wm, int
   }
 }
 
+template <int WN, int WM>
 __device__ __forceinline__ void zero_acc(f32x4 (&acc)[WN][WM]) {
 #pragma unroll
   for (int i = 0; i < WN; ++i)
@@ -207,42 +216,46 @@ __device__ __forceinline__ void stage_barrier() {
 // ahead of the one being multiplied (ring of NSTAGE slots in `lds`); one
 // barrier per stage. Every iteration issues one stage (the last ones reload
 // the final stage into a slot nobody reads), so the wait count is constant.
-template <bool WFP8, int NSTAGE>
-__device__ __forceinline__ void block_product(const LoadPlan &p, int kb, int S, uint4 *lds, f32x4 (&acc)[WN][WM]) {
-  constexpr int SLOT = StageShape<WFP8>::F * 64;
+template <bool WFP8, int NSTAGE, class TL>
+__device__ __forceinline__ void block_product(const LoadPlan &p, int kb, int S, uint4 *lds,
+                                              f32x4 (&acc)[TL::WN][TL::WM]) {
+  constexpr int SLOT = StageShape<WFP8, TL>::F * 64;
   constexpr uint32_t SLOT_BYTES = SLOT * 16;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int wn = wave & 1, wm = wave >> 1;
+  const int wn = wave % TL::WAVES_N, wm = wave / TL::WAVES_N;
   const int NS = 2 * S;
   const uint32_t base = lds_addr(lds);
 #pragma unroll
-  for (int s = 0; s < NSTAGE - 1; ++s) issue_stage<WFP8>(base + s * SLOT_BYTES, p, wave, lane, kb + 64 * min(s, NS - 1));
+  for (int s = 0; s < NSTAGE - 1; ++s)
+    issue_stage<WFP8, TL>(base + s * SLOT_BYTES, p, wave, lane, kb + 64 * min(s, NS - 1));
 #pragma unroll 1
   for (int s = 0; s < NS; ++s) {
-    wait_stages<WFP8>(NSTAGE - 2);
+    wait_stages<WFP8, TL>(NSTAGE - 2);
     stage_barrier();
     const int sn = s + NSTAGE - 1;
-    issue_stage<WFP8>(base + (sn % NSTAGE) * SLOT_BYTES, p, wave, lane, kb + 64 * min(sn, NS - 1));
-    mma_stage<WFP8>(lds + (s % NSTAGE) * SLOT, wn, wm, lane, acc);
+    issue_stage<WFP8, TL>(base + (sn % NSTAGE) * SLOT_BYTES, p, wave, lane, kb + 64 * min(sn, NS - 1));
+    mma_stage<WFP8, TL>(lds + (s % NSTAGE) * SLOT, wn, wm, lane, acc);
   }
-  wait_stages<WFP8>(0);
+  wait_stages<WFP8, TL>(0);
   __syncthreads();
 }
 
 template <int EPI, int NSTAGE>
-__global__ __launch_bounds__(NTHR) void k_bgemm(GemmArgs ga, EpiArgs ea, int n_nb, int n_mb) {
-  __shared__ uint4 lds[NSTAGE * StageShape<false>::F * 64];
+__global__ __launch_bounds__(TileG::NTHR) void k_bgemm(GemmArgs ga, EpiArgs ea, int n_nb, int n_mb) {
+  using TL = TileG;
+  constexpr int WN = TL::WN, WM = TL::WM, BN = TL::BN, BM = TL::BM;
+  __shared__ uint4 lds[NSTAGE * StageShape<false, TL>::F * 64];
   int nb, mb;
   if (!place(blockIdx.x, n_nb, n_mb, nb, mb)) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
-  const int wn = wave & 1, wm = wave >> 1;
+  const int wn = wave % TL::WAVES_N, wm = wave / TL::WAVES_N;
   const int split = blockIdx.y;
   const int kb = split * ga.kslice, ke = min(ga.K, kb + ga.kslice);
   f32x4 acc[WN][WM];
   zero_acc(acc);
-  const LoadPlan p = make_plan<false>(ga.W, (size_t)ga.N * ga.K * 2, ga.K >> 7, nb * NT, ga.A, ga.lda, ga.M, mb * BM,
-                                      __builtin_amdgcn_readfirstlane(wave), lane);
-  block_product<false, NSTAGE>(p, kb, (ke - kb) >> 7, lds, acc);
+  const LoadPlan p = make_plan<false>(ga.W, (size_t)ga.N * ga.K * 2, ga.K >> 7, nb * TL::NT, ga.A, ga.lda, ga.M,
+                                      mb * BM, __builtin_amdgcn_readfirstlane(wave), lane);
+  block_product<false, NSTAGE, TL>(p, kb, (ke - kb) >> 7, lds, acc);
 #pragma unroll
   for (int i = 0; i < WN; ++i)
 #pragma unroll
@@ -258,15 +271,17 @@ __global__ __launch_bounds__(NTHR) void k_bgemm(GemmArgs ga, EpiArgs ea, int n_n
 // running (max, argmax, sum exp) over the unmasked entries; lanes, then the
 // two waves sharing a row, are merged in a fixed order and one partial per
 // (p, row) is written.
-template <bool WFP8, int NSTAGE>
-__global__ __launch_bounds__(NTHR) void k_blm_head(LmArgs a, int n_p, int n_mb) {
-  __shared__ uint4 lds[NSTAGE * StageShape<WFP8>::F * 64];
+template <bool WFP8, int NSTAGE, class TL>
+__global__ __launch_bounds__(TL::NTHR) void k_blm_head(LmArgs a, int n_p, int n_mb) {
+  constexpr int WN = TL::WN, WM = TL::WM, BN = TL::BN, BM = TL::BM, NT = TL::NT;
+  static_assert(TL::WAVES_N == 2, "two waves share each activation row");
+  __shared__ uint4 lds[NSTAGE * StageShape<WFP8, TL>::F * 64];
   __shared__ float s_mx[2][BM], s_se[2][BM];
   __shared__ uint32_t s_idx[2][BM];
   int p, mb;
   if (!place(blockIdx.x, n_p, n_mb, p, mb)) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
-  const int wn = wave & 1, wm = wave >> 1;
+  const int wn = wave % TL::WAVES_N, wm = wave / TL::WAVES_N;
   const int n_vb = a.V / BN;
   const int steps_w = a.K >> 7;
   ArgState st[WM];
@@ -282,7 +297,7 @@ __global__ __launch_bounds__(NTHR) void k_blm_head(LmArgs a, int n_p, int n_mb) 
     zero_acc(acc);
     const LoadPlan pl = make_plan<WFP8>(a.W, (size_t)a.V * a.K * (WFP8 ? 1 : 2), steps_w, vb * NT, a.z, a.K, a.M,
                                         mb * BM, __builtin_amdgcn_readfirstlane(wave), lane);
-    block_product<WFP8, NSTAGE>(pl, 0, steps_w, lds, acc);
+    block_product<WFP8, NSTAGE, TL>(pl, 0, steps_w, lds, acc);
 #pragma unroll
     for (int i = 0; i < WN; ++i)
 #pragma unroll
@@ -332,16 +347,16 @@ __global__ __launch_bounds__(NTHR) void k_blm_head(LmArgs a, int n_p, int n_mb) 
 
 template <int EPI>
 hipError_t launch_epi(const GemmArgs &g, const EpiArgs &e, hipStream_t s) {
-  const int n_nb = g.N / BN, n_mb = (g.M + BM - 1) / BM;
+  const int n_nb = g.N / TileG::BN, n_mb = (g.M + TileG::BM - 1) / TileG::BM;
   dim3 grid(((n_nb + 7) / 8) * 8 * n_mb, g.splits);
-  hipLaunchKernelGGL((k_bgemm<EPI, NSTAGE_GEMM>), grid, dim3(NTHR), 0, s, g, e, n_nb, n_mb);
+  hipLaunchKernelGGL((k_bgemm<EPI, NSTAGE_GEMM>), grid, dim3(TileG::NTHR), 0, s, g, e, n_nb, n_mb);
   return hipGetLastError();
 }
 
 }  // namespace
 
 bool bgemm_ok(int epi, int N, int K) {
-  return epi != EPI_KV_SCATTER && N % BN == 0 && K % 128 == 0 && N > 0 && K > 0;
+  return epi != EPI_KV_SCATTER && N % TileG::BN == 0 && K % 128 == 0 && N > 0 && K > 0;
 }
 
 hipError_t launch_bgemm(int epi, const GemmArgs &g, const EpiArgs &e, hipStream_t s) {
@@ -356,14 +371,14 @@ hipError_t launch_bgemm(int epi, const GemmArgs &g, const EpiArgs &e, hipStream_
   }
 }
 
-int blm_parts(int V) { return (V / BN + LM_TILES - 1) / LM_TILES; }
+int blm_parts(int V) { return (V / TileL::BN + LM_TILES - 1) / LM_TILES; }
 
 hipError_t launch_blm_head(bool w_fp8, const LmArgs &a, hipStream_t s) {
-  if (a.M < 1 || a.V % BN != 0 || a.K % 128 != 0 || a.row0 != 0) return hipErrorInvalidValue;
-  const int n_p = blm_parts(a.V), n_mb = (a.M + BM - 1) / BM;
+  if (a.M < 1 || a.V % TileL::BN != 0 || a.K % 128 != 0 || a.row0 != 0) return hipErrorInvalidValue;
+  const int n_p = blm_parts(a.V), n_mb = (a.M + TileL::BM - 1) / TileL::BM;
   dim3 grid(((n_p + 7) / 8) * 8 * n_mb);
-  if (w_fp8) hipLaunchKernelGGL((k_blm_head<true, NSTAGE_LM>), grid, dim3(NTHR), 0, s, a, n_p, n_mb);
-  else hipLaunchKernelGGL((k_blm_head<false, NSTAGE_LM>), grid, dim3(NTHR), 0, s, a, n_p, n_mb);
+  if (w_fp8) hipLaunchKernelGGL((k_blm_head<true, NSTAGE_LM, TileL>), grid, dim3(TileL::NTHR), 0, s, a, n_p, n_mb);
+  else hipLaunchKernelGGL((k_blm_head<false, NSTAGE_LM, TileL>), grid, dim3(TileL::NTHR), 0, s, a, n_p, n_mb);
   return hipGetLastError();
 }
 
