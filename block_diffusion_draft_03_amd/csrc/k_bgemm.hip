@@ -6,9 +6,13 @@
 // layer GEMMs, 256 x 256 on 8 waves of 128 x 64 for the LM head (larger wave
 // tiles read fewer LDS bytes per MFMA). K advances in stages of 64 columns
 // (half of one 128-wide step of the tile-major weight layout). A stage's
-// operands are staged in LDS already in MFMA fragment order (the weights come
-// from HBM in that order; activation rows are scattered into it), so every
-// fragment read is one contiguous 1 KB ds_read_b128 per wave. The next
+// weights are staged in LDS already in MFMA fragment order (they come from HBM
+// in that order), so every weight fragment read is one contiguous 1 KB
+// ds_read_b128 per wave. Activation rows are staged row-major, 128 bytes (64
+// columns) per row, each load instruction bringing whole 128-byte row segments
+// of 8 rows (rows scattered in 64-byte halves load at well under half the
+// rate); the 16-byte chunks of a row are XOR-swizzled so that the fragment
+// reads of 16 rows fall on distinct LDS banks. The next
 // stage's global loads are in flight while the current stage is multiplied;
 // two LDS buffers, one barrier per stage.
 //
@@ -82,10 +86,11 @@ __device__ __forceinline__ uint32_t lds_addr(const uint4 *p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(const lds_uint4 *)p);
 }
 
-// A stage is a list of 1 KB fragments (64 lanes x 16 bytes): the weight
+// A stage is a list of 1 KB pieces (64 lanes x 16 bytes): the weight
 // fragments [tile][c] (bf16) or [tile] (E4M3: the 16 codes of k-groups c = 0
-// and 1 of each lane), then the activation fragments [act tile][c]. Wave w
-// loads the weight and activation fragments of tiles 2w and 2w + 1.
+// and 1 of each lane), then the activation rows, 8 rows of 128 bytes per
+// piece. Wave w loads the weight fragments of tiles 2w and 2w + 1 and the
+// activation rows 32 w .. 32 w + 31.
 template <bool WFP8, class TL>
 struct StageShape {
   static constexpr int WF = WFP8 ? TL::NT : TL::NT * 2;
@@ -99,7 +104,7 @@ struct LoadPlan {
   int4v rw, ra;          // weight and activation buffers
   uint32_t w_tile[2];    // byte offset of the wave's two weight tiles (step 0)
   uint32_t w_step;       // bytes per 128-wide step of one tile
-  uint32_t va[2][2];     // activation fragment (tile 2w + i, k-group c): lane offset at column 0
+  uint32_t va[4];        // activation piece q of the wave (rows 32w + 8q ..): lane offset at column 0
 };
 
 template <bool WFP8>
@@ -112,10 +117,12 @@ __device__ __forceinline__ LoadPlan make_plan(const void *W, size_t w_bytes, int
 #pragma unroll
   for (int i = 0; i < 2; ++i) p.w_tile[i] = (uint32_t)(tile0 + 2 * wave + i) * (uint32_t)steps_w * p.w_step;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int m = min(m0 + (2 * wave + i) * 16 + (lane & 15), M - 1);
-#pragma unroll
-    for (int c = 0; c < 2; ++c) p.va[i][c] = (uint32_t)(((size_t)m * lda + 32 * c + 8 * (lane >> 4)) * 2);
+  for (int q = 0; q < 4; ++q) {
+    // lane l lands at LDS chunk l & 7 of local row `row`; it fetches the chunk that swizzles there
+    const int row = 32 * wave + 8 * q + (lane >> 3);
+    const int m = min(m0 + row, M - 1);
+    const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+    p.va[q] = (uint32_t)(((size_t)m * lda + 8 * chunk) * 2);
   }
   return p;
 }
@@ -137,10 +144,7 @@ __device__ __forceinline__ void issue_stage(uint32_t slot, const LoadPlan &p, in
     }
   }
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-      dma16(p.ra, p.va[i][c], (uint32_t)k * 2, slot + (S::WF + (2 * wave + i) * 2 + c) * 1024);
+  for (int q = 0; q < 4; ++q) dma16(p.ra, p.va[q], (uint32_t)k * 2, slot + (S::WF + 4 * wave + q) * 1024);
 }
 
 // Wait until at most `later` stages of this wave's loads are outstanding.
@@ -161,6 +165,8 @@ __device__ __forceinline__ void mma_stage(const uint4 *slot, int wn, int wm, int
                                           f32x4 (&acc)[TL::WN][TL::WM]) {
   using S = StageShape<WFP8, TL>;
   constexpr int WN = TL::WN, WM = TL::WM;
+  const int r16 = lane & 15, g = lane >> 4, swz = (r16 >> 1) & 7;
+  const uint4 *arow = slot + S::WF * 64 + (wm * WM * 16 + r16) * 8;
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     uint4 wf[WN], af[WM];
@@ -176,7 +182,7 @@ __device__ __forceinline__ void mma_stage(const uint4 *slot, int wn, int wm, int
       }
     }
 #pragma unroll
-    for (int j = 0; j < WM; ++j) af[j] = slot[(S::WF + (wm * WM + j) * 2 + c) * 64 + lane];
+    for (int j = 0; j < WM; ++j) af[j] = arow[j * 16 * 8 + ((4 * c + g) ^ swz)];
 #pragma unroll
     for (int i = 0; i < WN; ++i)
 #pragma unroll
