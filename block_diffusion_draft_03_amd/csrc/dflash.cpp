@@ -294,7 +294,10 @@ int build_impl(dflash_head *H, const dflash_weights *w, hipStream_t st) {
   TRY(H->alloc(&H->cs, M * (g.d / 2)));
   // split-K partials of the GEMMs that feed the residual stream (N = h)
   int max_splits = 1;
-  for (int K : {g.q_dim, g.I, g.fc_in}) max_splits = std::max(max_splits, gemm_plan(g.h, K, true).splits);
+  for (int K : {g.q_dim, g.I, g.fc_in}) {
+    max_splits = std::max(max_splits, gemm_plan(g.h, K, true).splits);
+    if (bgemm_ok(EPI_PARTIAL, g.h, K)) max_splits = std::max(max_splits, bgemm_splits(g.h, K, (int)M));
+  }
   TRY(H->alloc(&H->part, (size_t)max_splits * std::max<size_t>(M, GEMM_MAX_ROWS) * h));
   const size_t R = (size_t)g.rep * g.gamma;
   {
@@ -348,6 +351,11 @@ int gemm_rows(dflash_head *H, int epi, const uint16_t *A, int lda, int M, const 
     ga.A = A;
     ga.M = M;
     e.row0 = 0;
+    if (epi == EPI_PARTIAL) {
+      ga.splits = bgemm_splits(N, K, M);
+      ga.kslice = K / ga.splits;
+      if (splits_out) *splits_out = ga.splits;
+    }
     HIP_TRY(launch_bgemm(epi, ga, e, st));
     return DFLASH_OK;
   }

@@ -35,8 +35,7 @@ namespace dflash {
 namespace {
 
 // Workgroup tile: BN weight rows x BM activation rows on WAVES_N x WAVES_M
-// waves; every wave loads two weight tiles and two activation tiles of each
-// stage (so NT = MTL = 2 * waves).
+// waves, each wave multiplying WN weight tiles by WM activation tiles.
 template <int BN_, int BM_, int WAVES_N_, int WAVES_M_>
 struct Tiling {
   static constexpr int BN = BN_, BM = BM_;
@@ -44,13 +43,19 @@ struct Tiling {
   static constexpr int WAVES_N = WAVES_N_, WAVES_M = WAVES_M_;
   static constexpr int NWAVES = WAVES_N * WAVES_M, NTHR = 64 * NWAVES;
   static constexpr int WN = NT / WAVES_N, WM = MTL / WAVES_M;  // tiles per wave
-  static_assert(NT == 2 * NWAVES && MTL == 2 * NWAVES, "two weight and two activation tiles per wave");
+  static_assert(NT % WAVES_N == 0 && MTL % WAVES_M == 0 && NWAVES % 2 == 0, "tiles divide among the waves");
 };
-using TileG = Tiling<128, 128, 2, 2>;   // layer GEMMs: 4 waves of 64 x 64
-using TileL = Tiling<256, 256, 2, 4>;   // LM head: 8 waves of 128 x 64
+// Layer GEMMs: 8 waves (two per SIMD, so one wave's multiplies cover the
+// other's waits) on 128 x 128 or 256 x 128 blocks, whichever needs fewer
+// rounds of workgroups over the chip; LM head: 8 waves of 128 x 64.
+using TileG = Tiling<128, 128, 4, 2>;   // waves of 32 x 64
+using TileW = Tiling<256, 128, 4, 2>;   // waves of 64 x 64
+using TileL = Tiling<256, 256, 2, 4>;
 
-constexpr int NSTAGE_GEMM = 3;         // LDS ring depth (stages in flight + the one multiplied)
+constexpr int NSTAGE_G = 4;            // LDS ring depth (stages in flight + the one multiplied): 128 KB
+constexpr int NSTAGE_W = 3;            // 144 KB
 constexpr int NSTAGE_LM = 2;
+constexpr int NUM_CUS = 256;           // compute units of the MI355X
 constexpr int LM_TILES = 4;            // vocab blocks per LM-head workgroup
 
 typedef __attribute__((address_space(3))) uint4 lds_uint4;
@@ -89,40 +94,49 @@ __device__ __forceinline__ uint32_t lds_addr(const uint4 *p) {
 // A stage is a list of 1 KB pieces (64 lanes x 16 bytes): the weight
 // fragments [tile][c] (bf16) or [tile] (E4M3: the 16 codes of k-groups c = 0
 // and 1 of each lane), then the activation rows, 8 rows of 128 bytes per
-// piece. Wave w loads the weight fragments of tiles 2w and 2w + 1 and the
-// activation rows 32 w .. 32 w + 31.
+// piece. Pieces are dealt to the waves round-robin (piece i * NWAVES + w to
+// wave w), so every wave issues WP weight and AP activation loads per stage.
 template <bool WFP8, class TL>
 struct StageShape {
   static constexpr int WF = WFP8 ? TL::NT : TL::NT * 2;
-  static constexpr int AF = TL::MTL * 2;
+  static constexpr int AF = TL::BM / 8;
   static constexpr int F = WF + AF;
-  static constexpr int PER = F / TL::NWAVES;  // fragment loads per wave
+  static constexpr int WP = WF / TL::NWAVES, AP = AF / TL::NWAVES;
+  static constexpr int PER = WP + AP;  // loads per wave and stage
+  static_assert(WF % TL::NWAVES == 0 && AF % TL::NWAVES == 0, "pieces divide among the waves");
 };
 
 // Per-lane offsets of a wave's loads, fixed for the whole K loop.
+template <bool WFP8, class TL>
 struct LoadPlan {
-  int4v rw, ra;          // weight and activation buffers
-  uint32_t w_tile[2];    // byte offset of the wave's two weight tiles (step 0)
-  uint32_t w_step;       // bytes per 128-wide step of one tile
-  uint32_t va[4];        // activation piece q of the wave (rows 32w + 8q ..): lane offset at column 0
+  int4v rw, ra;             // weight and activation buffers
+  uint32_t w_base;          // byte offset of the block's first weight tile (step 0)
+  uint32_t w_tile;          // bytes of one 16-row weight tile over all of K
+  uint32_t w_step;          // bytes per 128-wide step of one tile
+  uint32_t wv;              // lane offset inside a weight piece
+  uint32_t va[StageShape<WFP8, TL>::AP];  // activation pieces: lane offset at column 0
 };
 
-template <bool WFP8>
-__device__ __forceinline__ LoadPlan make_plan(const void *W, size_t w_bytes, int steps_w, int tile0, const uint16_t *A,
-                                              int lda, int M, int m0, int wave, int lane) {
-  LoadPlan p;
+template <bool WFP8, class TL>
+__device__ __forceinline__ LoadPlan<WFP8, TL> make_plan(const void *W, size_t w_bytes, int steps_w, int tile0,
+                                                        const uint16_t *A, int lda, int M, int m0, int wave,
+                                                        int lane) {
+  using S = StageShape<WFP8, TL>;
+  LoadPlan<WFP8, TL> p;
   p.rw = make_rsrc(W, (uint32_t)w_bytes);
   p.ra = make_rsrc(A, (uint32_t)((size_t)M * lda * 2));
   p.w_step = WFP8 ? 2048u : 4096u;
+  p.w_tile = (uint32_t)steps_w * p.w_step;
+  p.w_base = (uint32_t)tile0 * p.w_tile;
+  // bf16 piece i * NWAVES + w is k-group (w & 1) of its tile
+  p.wv = (uint32_t)lane * 16 + (WFP8 ? 0u : (uint32_t)(wave & 1) * 1024);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) p.w_tile[i] = (uint32_t)(tile0 + 2 * wave + i) * (uint32_t)steps_w * p.w_step;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int i = 0; i < S::AP; ++i) {
     // lane l lands at LDS chunk l & 7 of local row `row`; it fetches the chunk that swizzles there
-    const int row = 32 * wave + 8 * q + (lane >> 3);
+    const int row = 8 * (i * TL::NWAVES + wave) + (lane >> 3);
     const int m = min(m0 + row, M - 1);
     const int chunk = (lane & 7) ^ ((row >> 1) & 7);
-    p.va[q] = (uint32_t)(((size_t)m * lda + 8 * chunk) * 2);
+    p.va[i] = (uint32_t)(((size_t)m * lda + 8 * chunk) * 2);
   }
   return p;
 }
@@ -130,21 +144,18 @@ __device__ __forceinline__ LoadPlan make_plan(const void *W, size_t w_bytes, int
 // Direct-to-LDS loads of the stage at absolute column k (a multiple of 64)
 // into the slot at LDS byte address `slot`.
 template <bool WFP8, class TL>
-__device__ __forceinline__ void issue_stage(uint32_t slot, const LoadPlan &p, int wave, int lane, int k) {
+__device__ __forceinline__ void issue_stage(uint32_t slot, const LoadPlan<WFP8, TL> &p, int wave, int k) {
   using S = StageShape<WFP8, TL>;
   const uint32_t step_off = (uint32_t)(k >> 7) * p.w_step + (uint32_t)((k >> 6) & 1) * (p.w_step / 2);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int t = 2 * wave + i;
-    if constexpr (!WFP8) {
-#pragma unroll
-      for (int c = 0; c < 2; ++c) dma16(p.rw, lane * 16 + c * 1024, p.w_tile[i] + step_off, slot + (t * 2 + c) * 1024);
-    } else {
-      dma16(p.rw, lane * 16, p.w_tile[i] + step_off, slot + t * 1024);
-    }
+  for (int i = 0; i < S::WP; ++i) {
+    const int piece = i * TL::NWAVES + wave;
+    const int tile = WFP8 ? piece : piece >> 1;
+    dma16(p.rw, p.wv, p.w_base + (uint32_t)tile * p.w_tile + step_off, slot + piece * 1024);
   }
 #pragma unroll
-  for (int q = 0; q < 4; ++q) dma16(p.ra, p.va[q], (uint32_t)k * 2, slot + (S::WF + 4 * wave + q) * 1024);
+  for (int i = 0; i < S::AP; ++i)
+    dma16(p.ra, p.va[i], (uint32_t)k * 2, slot + (S::WF + i * TL::NWAVES + wave) * 1024);
 }
 
 // Wait until at most `later` stages of this wave's loads are outstanding.
@@ -190,6 +201,36 @@ __device__ __forceinline__ void mma_stage(const uint4 *slot, int wn, int wm, int
   }
 }
 
+// Fragments of one stage held in registers (bf16 weights): [k-group][tile].
+template <class TL>
+struct StageFrags {
+  uint4 w[2][TL::WN], a[2][TL::WM];
+};
+
+template <class TL>
+__device__ __forceinline__ void read_frags(const uint4 *slot, int wn, int wm, int lane, StageFrags<TL> &f) {
+  using S = StageShape<false, TL>;
+  const int r16 = lane & 15, g = lane >> 4, swz = (r16 >> 1) & 7;
+  const uint4 *arow = slot + S::WF * 64 + (wm * TL::WM * 16 + r16) * 8;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+#pragma unroll
+    for (int i = 0; i < TL::WN; ++i) f.w[c][i] = slot[((wn * TL::WN + i) * 2 + c) * 64 + lane];
+#pragma unroll
+    for (int j = 0; j < TL::WM; ++j) f.a[c][j] = arow[j * 16 * 8 + ((4 * c + g) ^ swz)];
+  }
+}
+
+template <class TL>
+__device__ __forceinline__ void mma_frags(const StageFrags<TL> &f, f32x4 (&acc)[TL::WN][TL::WM]) {
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int i = 0; i < TL::WN; ++i)
+#pragma unroll
+      for (int j = 0; j < TL::WM; ++j) acc[i][j] = mfma16x16x32(as_bf16x8(f.w[c][i]), as_bf16x8(f.a[c][j]), acc[i][j]);
+}
+
 template <int WN, int WM>
 __device__ __forceinline__ void zero_acc(f32x4 (&acc)[WN][WM]) {
 #pragma unroll
@@ -223,7 +264,7 @@ __device__ __forceinline__ void stage_barrier() {
 // barrier per stage. Every iteration issues one stage (the last ones reload
 // the final stage into a slot nobody reads), so the wait count is constant.
 template <bool WFP8, int NSTAGE, class TL>
-__device__ __forceinline__ void block_product(const LoadPlan &p, int kb, int S, uint4 *lds,
+__device__ __forceinline__ void block_product(const LoadPlan<WFP8, TL> &p, int kb, int S, uint4 *lds,
                                               f32x4 (&acc)[TL::WN][TL::WM]) {
   constexpr int SLOT = StageShape<WFP8, TL>::F * 64;
   constexpr uint32_t SLOT_BYTES = SLOT * 16;
@@ -233,22 +274,63 @@ __device__ __forceinline__ void block_product(const LoadPlan &p, int kb, int S, 
   const uint32_t base = lds_addr(lds);
 #pragma unroll
   for (int s = 0; s < NSTAGE - 1; ++s)
-    issue_stage<WFP8, TL>(base + s * SLOT_BYTES, p, wave, lane, kb + 64 * min(s, NS - 1));
+    issue_stage<WFP8, TL>(base + s * SLOT_BYTES, p, wave, kb + 64 * min(s, NS - 1));
 #pragma unroll 1
   for (int s = 0; s < NS; ++s) {
     wait_stages<WFP8, TL>(NSTAGE - 2);
     stage_barrier();
     const int sn = s + NSTAGE - 1;
-    issue_stage<WFP8, TL>(base + (sn % NSTAGE) * SLOT_BYTES, p, wave, lane, kb + 64 * min(sn, NS - 1));
+    issue_stage<WFP8, TL>(base + (sn % NSTAGE) * SLOT_BYTES, p, wave, kb + 64 * min(sn, NS - 1));
     mma_stage<WFP8, TL>(lds + (s % NSTAGE) * SLOT, wn, wm, lane, acc);
   }
   wait_stages<WFP8, TL>(0);
   __syncthreads();
 }
 
-template <int EPI, int NSTAGE>
-__global__ __launch_bounds__(TileG::NTHR) void k_bgemm(GemmArgs ga, EpiArgs ea, int n_nb, int n_mb) {
-  using TL = TileG;
+// Same product as block_product for bf16 weights, with the fragment reads
+// of stage s + 1 issued while stage s is multiplied (two register sets), so
+// the LDS reads overlap the matrix cores. Iteration s waits for stage s + 1,
+// then (after every wave has finished reading stage s, whose fragments were
+// read in iteration s - 1) refills stage s's slot with stage s + NSTAGE.
+template <int NSTAGE, class TL>
+__device__ __forceinline__ void block_product_pipelined(const LoadPlan<false, TL> &p, int kb, int S, uint4 *lds,
+                                                        f32x4 (&acc)[TL::WN][TL::WM]) {
+  constexpr int SLOT = StageShape<false, TL>::F * 64;
+  constexpr uint32_t SLOT_BYTES = SLOT * 16;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int wn = wave % TL::WAVES_N, wm = wave / TL::WAVES_N;
+  const int NS = 2 * S;  // even
+  const uint32_t base = lds_addr(lds);
+#pragma unroll
+  for (int s = 0; s < NSTAGE; ++s) issue_stage<false, TL>(base + s * SLOT_BYTES, p, wave, kb + 64 * min(s, NS - 1));
+  StageFrags<TL> f0, f1;
+  wait_stages<false, TL>(NSTAGE - 1);
+  stage_barrier();
+  read_frags<TL>(lds, wn, wm, lane, f0);
+  // sched_barrier(0) keeps the scheduler from pulling the multiplies of a
+  // stage up to its fragment reads (they have no memory dependence on the
+  // barrier), which would serialise the reads and the matrix cores again.
+  auto step = [&](int s, StageFrags<TL> &cur, StageFrags<TL> &next) {
+    __builtin_amdgcn_sched_barrier(0);
+    wait_stages<false, TL>(NSTAGE - 2);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stage s are done
+    stage_barrier();
+    issue_stage<false, TL>(base + (s % NSTAGE) * SLOT_BYTES, p, wave, kb + 64 * min(s + NSTAGE, NS - 1));
+    read_frags<TL>(lds + ((s + 1) % NSTAGE) * SLOT, wn, wm, lane, next);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_frags<TL>(cur, acc);
+  };
+#pragma unroll 1
+  for (int s = 0; s < NS; s += 2) {
+    step(s, f0, f1);
+    step(s + 1, f1, f0);
+  }
+  wait_stages<false, TL>(0);
+  __syncthreads();
+}
+
+template <int EPI, int NSTAGE, class TL>
+__global__ __launch_bounds__(TL::NTHR) void k_bgemm(GemmArgs ga, EpiArgs ea, int n_nb, int n_mb) {
   constexpr int WN = TL::WN, WM = TL::WM, BN = TL::BN, BM = TL::BM;
   __shared__ uint4 lds[NSTAGE * StageShape<false, TL>::F * 64];
   int nb, mb;
@@ -259,9 +341,9 @@ __global__ __launch_bounds__(TileG::NTHR) void k_bgemm(GemmArgs ga, EpiArgs ea, 
   const int kb = split * ga.kslice, ke = min(ga.K, kb + ga.kslice);
   f32x4 acc[WN][WM];
   zero_acc(acc);
-  const LoadPlan p = make_plan<false>(ga.W, (size_t)ga.N * ga.K * 2, ga.K >> 7, nb * TL::NT, ga.A, ga.lda, ga.M,
+  const LoadPlan<false, TL> p = make_plan<false, TL>(ga.W, (size_t)ga.N * ga.K * 2, ga.K >> 7, nb * TL::NT, ga.A, ga.lda, ga.M,
                                       mb * BM, __builtin_amdgcn_readfirstlane(wave), lane);
-  block_product<false, NSTAGE, TL>(p, kb, (ke - kb) >> 7, lds, acc);
+  block_product_pipelined<NSTAGE, TL>(p, kb, (ke - kb) >> 7, lds, acc);
 #pragma unroll
   for (int i = 0; i < WN; ++i)
 #pragma unroll
@@ -301,7 +383,7 @@ __global__ __launch_bounds__(TL::NTHR) void k_blm_head(LmArgs a, int n_p, int n_
   for (int vb = p * LM_TILES; vb < min(n_vb, (p + 1) * LM_TILES); ++vb) {
     f32x4 acc[WN][WM];
     zero_acc(acc);
-    const LoadPlan pl = make_plan<WFP8>(a.W, (size_t)a.V * a.K * (WFP8 ? 1 : 2), steps_w, vb * NT, a.z, a.K, a.M,
+    const LoadPlan<WFP8, TL> pl = make_plan<WFP8, TL>(a.W, (size_t)a.V * a.K * (WFP8 ? 1 : 2), steps_w, vb * NT, a.z, a.K, a.M,
                                         mb * BM, __builtin_amdgcn_readfirstlane(wave), lane);
     block_product<WFP8, NSTAGE, TL>(pl, 0, steps_w, lds, acc);
 #pragma unroll
@@ -351,12 +433,31 @@ __global__ __launch_bounds__(TL::NTHR) void k_blm_head(LmArgs a, int n_p, int n_
   }
 }
 
-template <int EPI>
+template <int EPI, class TL, int NSTAGE>
 hipError_t launch_epi(const GemmArgs &g, const EpiArgs &e, hipStream_t s) {
-  const int n_nb = g.N / TileG::BN, n_mb = (g.M + TileG::BM - 1) / TileG::BM;
+  const int n_nb = g.N / TL::BN, n_mb = (g.M + TL::BM - 1) / TL::BM;
   dim3 grid(((n_nb + 7) / 8) * 8 * n_mb, g.splits);
-  hipLaunchKernelGGL((k_bgemm<EPI, NSTAGE_GEMM>), grid, dim3(TileG::NTHR), 0, s, g, e, n_nb, n_mb);
+  hipLaunchKernelGGL((k_bgemm<EPI, NSTAGE, TL>), grid, dim3(TL::NTHR), 0, s, g, e, n_nb, n_mb);
   return hipGetLastError();
+}
+
+// Workgroup rounds over the chip of a tiling.
+int rounds(int N, int M, int BN, int BM, int splits) {
+  const long wgs = (long)(N / BN) * ((M + BM - 1) / BM) * splits;
+  return (int)((wgs + NUM_CUS - 1) / NUM_CUS);
+}
+
+// The 256-row blocks do twice the work of the 128-row ones in about 1.55
+// times the time (fewer LDS bytes per product): use them when that wins.
+bool wide_tiles(int epi, int N, int M) {
+  if (epi == EPI_PARTIAL || N % TileW::BN != 0) return false;
+  return 31 * rounds(N, M, TileW::BN, TileW::BM, 1) < 20 * rounds(N, M, TileG::BN, TileG::BM, 1);
+}
+
+template <int EPI>
+hipError_t launch_pick(const GemmArgs &g, const EpiArgs &e, hipStream_t s) {
+  if (wide_tiles(EPI, g.N, g.M)) return launch_epi<EPI, TileW, NSTAGE_W>(g, e, s);
+  return launch_epi<EPI, TileG, NSTAGE_G>(g, e, s);
 }
 
 }  // namespace
@@ -365,14 +466,22 @@ bool bgemm_ok(int epi, int N, int K) {
   return epi != EPI_KV_SCATTER && N % TileG::BN == 0 && K % 128 == 0 && N > 0 && K > 0;
 }
 
+int bgemm_splits(int N, int K, int M) {
+  // about one workgroup per compute unit; every split a multiple of 128 columns
+  const int blocks = (N / TileG::BN) * ((M + TileG::BM - 1) / TileG::BM);
+  int splits = std::max(1, std::min(4, (NUM_CUS + blocks / 2) / std::max(blocks, 1)));
+  while (splits > 1 && K % (splits * 128) != 0) --splits;
+  return splits;
+}
+
 hipError_t launch_bgemm(int epi, const GemmArgs &g, const EpiArgs &e, hipStream_t s) {
   if (g.M < 1 || !bgemm_ok(epi, g.N, g.K) || g.splits < 1 || g.kslice % 128 != 0) return hipErrorInvalidValue;
   if (g.splits > 1 && epi != EPI_PARTIAL) return hipErrorInvalidValue;
   switch (epi) {
-    case EPI_F32: return launch_epi<EPI_F32>(g, e, s);
-    case EPI_SWIGLU: return launch_epi<EPI_SWIGLU>(g, e, s);
-    case EPI_QKV_ROPE: return launch_epi<EPI_QKV_ROPE>(g, e, s);
-    case EPI_PARTIAL: return launch_epi<EPI_PARTIAL>(g, e, s);
+    case EPI_F32: return launch_pick<EPI_F32>(g, e, s);
+    case EPI_SWIGLU: return launch_pick<EPI_SWIGLU>(g, e, s);
+    case EPI_QKV_ROPE: return launch_pick<EPI_QKV_ROPE>(g, e, s);
+    case EPI_PARTIAL: return launch_pick<EPI_PARTIAL>(g, e, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -90,6 +90,8 @@ hipError_t launch_gemm(int epi, const GemmArgs &g, const EpiArgs &e, hipStream_t
 // The tiled kernel takes any M (one launch for all rows) when N and K are
 // multiples of 128 and the epilogue is not EPI_KV_SCATTER.
 bool bgemm_ok(int epi, int N, int K);
+// K splits of a tiled EPI_PARTIAL GEMM over M rows (at most 4; K a multiple of 128 * splits).
+int bgemm_splits(int N, int K, int M);
 hipError_t launch_bgemm(int epi, const GemmArgs &g, const EpiArgs &e, hipStream_t s);
 
 // Finish of a split GEMM into the residual stream, one workgroup per row:
