@@ -223,7 +223,7 @@ def cpu_baseline(wl_obj, budget_s=12.0, max_seqs=2):
     while True:
         step()
         k += 1
-        if time.perf_counter() - t0 >= budget_s or k >= 50:
+        if time.perf_counter() - t0 >= budget_s or k >= 400:
             break
     dt = time.perf_counter() - t0
     return {"value": round(k * len(idx) / dt, 4), "unit": "blocks/s", "cores": int(cores), "kind": "oracle",

@@ -16,8 +16,9 @@
 // split writes its partial sums and a separate kernel (k_resid_norm) adds
 // them in split order. Every reduction order is fixed, so results are
 // deterministic and a row's result does not depend on the other rows. The
-// tiled kernels for many rows (k_bgemm.hip) follow the same K order, so the
-// two kernels give bit-identical results.
+// tiled kernels for many rows (k_bgemm.hip) sum each K slice in one pass, so
+// their layer GEMMs agree with these to rounding; their LM head, which sums
+// K in one pass like the one here, is bit-identical.
 #include "common.hpp"
 #include "gemm_epi.hpp"
 #include "kernels.hpp"
