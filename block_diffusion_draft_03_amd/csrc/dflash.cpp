@@ -483,8 +483,12 @@ int propose_impl(dflash_head *H, dflash_state *const *states, int n, const uint3
   aa.out = H->attn;
   aa.out_ld = g.q_dim;
   {
-    // ctx tiles of 32 positions from the block-aligned window start; the
-    // splits give about ATTN_TARGET_WGS workgroups per launch
+    // ctx tiles of 32 positions from the block-aligned window start. Every
+    // sequence gets ceil(T / tps) splits of at most tps tiles (at least one,
+    // which also takes the block tile); tps is the smallest that keeps the
+    // launch within ATTN_TARGET_WGS workgroups (one round, two per CU), no
+    // smaller than a sequence's preferred bound of ATTN_PREF_SPLITS splits.
+    std::vector<int> T(n);
     int max_T = 0;
     for (int i = 0; i < n; ++i) {
       const int c = states[i]->rows.ctx_len;
@@ -492,18 +496,30 @@ int propose_impl(dflash_head *H, dflash_state *const *states, int n, const uint3
       aa.seq[i].ctx_len = c;
       aa.seq[i].win_start = lo;
       aa.seq[i].bt = states[i]->d_bt;
-      if (lo < c) max_T = std::max(max_T, (c - lo / 16 * 16 + 31) / 32);
+      T[i] = lo < c ? (c - lo / 16 * 16 + 31) / 32 : 0;
+      max_T = std::max(max_T, T[i]);
     }
     const int max_tps = attn_max_tiles_per_split();
-    const int target = std::max(1, std::min(ATTN_PREF_SPLITS, ATTN_TARGET_WGS / (n * g.n_kv)));
-    int tps = std::min(max_tps, std::max(1, (max_T + target - 1) / target));
+    auto flat_splits = [&](int tps) {
+      long f = 0;
+      for (int i = 0; i < n; ++i) f += std::max(1, (T[i] + tps - 1) / tps);
+      return f;
+    };
+    const long cap = std::min<long>(ATTN_MAX_FLAT, H->attn_slots / g.n_kv);
+    int tps = std::max(1, (max_T + ATTN_PREF_SPLITS - 1) / ATTN_PREF_SPLITS);
     tps = std::max(tps, (max_T + ATTN_MAX_SPLITS - 1) / ATTN_MAX_SPLITS);
-    const int cap = std::max(1, H->attn_slots / (n * g.n_kv));
-    tps = std::max(tps, (max_T + cap - 1) / cap);
-    if (tps > max_tps) return set_err(DFLASH_E_INVALID, "context window too long for the attention splits");
+    while (tps < max_tps && (flat_splits(tps) * g.n_kv > ATTN_TARGET_WGS || flat_splits(tps) > cap)) ++tps;
+    if (tps > max_tps || flat_splits(tps) > cap || (max_T + tps - 1) / tps > ATTN_MAX_SPLITS)
+      return set_err(DFLASH_E_INVALID, "context window too long for the attention splits");
     aa.tps = tps;
-    aa.max_splits = std::max(1, (max_T + tps - 1) / tps);
-    if (n * g.n_kv * aa.max_splits > H->attn_slots) return set_err(DFLASH_E_INVALID, "attention partial buffer too small");
+    int f = 0;
+    for (int i = 0; i < n; ++i) {
+      aa.seq[i].split0 = f;
+      aa.seq[i].nsplit = std::max(1, (T[i] + tps - 1) / tps);
+      for (int c = 0; c < aa.seq[i].nsplit; ++c) aa.split_seq[f + c] = (uint8_t)i;
+      f += aa.seq[i].nsplit;
+    }
+    aa.n_split = f;
   }
 
   // act holds RMSNorm(h) with the next consumer's gain: layer 0's input norm

@@ -1,7 +1,8 @@
 // k_attn.hip - GQA attention of the block rows over the paged ctx window and
 // the block itself, for gfx950.
 //
-// One workgroup (4 waves) per (sequence, kv head, split). The rep = n_q / n_kv
+// One workgroup (4 waves) per (split, kv head); a sequence has as many splits
+// as its own context needs, so short sequences take no idle workgroups. The rep = n_q / n_kv
 // query heads of the kv head times the gamma block rows form up to 128 query
 // rows, 32 per wave. Keys come in tiles of 32: ctx tiles are aligned to two
 // 16-row KV blocks (positions outside [win_start, ctx_len) are masked), and
@@ -327,8 +328,10 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   __shared__ uint4 blkt[GB::BF * 64];
   __shared__ int32_t s_bt[2 * MAX_TPS];
 
-  const int s = blockIdx.z, g = blockIdx.y, c = blockIdx.x;
+  const int flat = blockIdx.x, g = blockIdx.y;
+  const int s = a.split_seq[flat];
   const AttnSeq sq = a.seq[s];
+  const int c = flat - sq.split0;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int gq = lane >> 4, r16 = lane & 15;
   const int R = a.rep * a.gamma;
@@ -336,7 +339,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   const int p0 = has_ctx ? (sq.win_start >> 4) << 4 : 0;
   const int T = has_ctx ? (sq.ctx_len - p0 + KT - 1) / KT : 0;
   const int t0 = c * a.tps, nt = max(0, min(T, t0 + a.tps) - t0);
-  const bool last = c == a.max_splits - 1;
+  const bool last = c == sq.nsplit - 1;
   const int NBT = (a.gamma + KT - 1) / KT;
 
   if constexpr (D < 32) {
@@ -443,7 +446,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     l_tot += __shfl_xor(l_tot, 32, WAVE);
     const int q = (wave * 2 + qt) * 16 + r16;
     if (q >= R) continue;
-    if (a.max_splits == 1) {
+    if (sq.nsplit == 1) {
       const int hq = g * a.rep + q / a.gamma, j = q % a.gamma;
       uint16_t *out = a.out + (size_t)(s * a.gamma + j) * a.out_ld + hq * D;
       const float inv = 1.0f / l_tot;
@@ -453,7 +456,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
         *(uint2 *)(out + dt * 16 + 4 * gq) = uint2{pack_bf16x2(v[0] * inv, v[1] * inv), pack_bf16x2(v[2] * inv, v[3] * inv)};
       }
     } else {
-      const size_t part = ((size_t)(s * a.n_kv + g) * a.max_splits + c) * R + q;
+      const size_t part = ((size_t)g * a.n_split + flat) * R + q;
 #pragma unroll
       for (int dt = 0; dt < GB::DT; ++dt) *(f32x4 *)(a.o_part + part * D + dt * 16 + 4 * gq) = w.o[qt][dt];
       if (gq == 0) {
@@ -475,8 +478,9 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a, int n_seq) {
   const int row = blockIdx.x * 4 + wave;  // (s, g, q)
   if (row >= n_seq * a.n_kv * R) return;
   const int q = row % R, g = (row / R) % a.n_kv, s = row / (R * a.n_kv);
-  const int nsplit = a.max_splits;  // <= 64
-  const size_t base = (size_t)(s * a.n_kv + g) * nsplit;
+  const int nsplit = a.seq[s].nsplit;  // <= 64
+  if (nsplit == 1) return;             // written by the attention kernel
+  const size_t base = (size_t)g * a.n_split + a.seq[s].split0;
   float m = -__builtin_huge_valf(), l = 0.0f;
   if (lane < nsplit) {
     m = a.ml_part[((base + lane) * R + q) * 2];
@@ -507,10 +511,10 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a, int n_seq) {
 }
 
 template <int D, bool FP8>
-hipError_t launch_d(const AttnArgs &a, int n_seq, hipStream_t s) {
-  dim3 grid(a.max_splits, a.n_kv, n_seq), block(256);
+hipError_t launch_d(const AttnArgs &a, int n_seq, bool merge, hipStream_t s) {
+  dim3 grid(a.n_split, a.n_kv), block(256);
   hipLaunchKernelGGL((k_attn<D, FP8>), grid, block, 0, s, a);
-  if (a.max_splits > 1) {
+  if (merge) {
     const int rows = n_seq * a.n_kv * a.rep * a.gamma;
     hipLaunchKernelGGL(k_attn_combine<D>, dim3((rows + 3) / 4), block, 0, s, a, n_seq);
   }
@@ -522,21 +526,33 @@ hipError_t launch_d(const AttnArgs &a, int n_seq, hipStream_t s) {
 int attn_max_tiles_per_split() { return MAX_TPS; }
 
 hipError_t launch_attention(const AttnArgs &a, int n_seq, hipStream_t s) {
-  if (a.tps < 1 || a.tps > MAX_TPS || a.max_splits < 1 || a.max_splits > 64 || a.gamma > 64 ||
-      a.rep * a.gamma > 128)
+  if (a.tps < 1 || a.tps > MAX_TPS || a.n_split < n_seq || a.n_split > ATTN_MAX_FLAT || a.gamma > 64 ||
+      a.rep * a.gamma > 128 || n_seq < 1 || n_seq > DFLASH_MAX_BATCH)
     return hipErrorInvalidValue;
+  // the splits of the sequences are consecutive runs that cover [0, n_split)
+  bool merge = false;
+  int next = 0;
+  for (int i = 0; i < n_seq; ++i) {
+    const AttnSeq &q = a.seq[i];
+    if (q.split0 != next || q.nsplit < 1 || q.nsplit > 64) return hipErrorInvalidValue;
+    for (int c = 0; c < q.nsplit; ++c)
+      if (a.split_seq[next + c] != i) return hipErrorInvalidValue;
+    next += q.nsplit;
+    merge = merge || q.nsplit > 1;
+  }
+  if (next != a.n_split) return hipErrorInvalidValue;
   if (a.kv_fp8) {
     switch (a.head_dim) {
-      case 64: return launch_d<64, true>(a, n_seq, s);
-      case 128: return launch_d<128, true>(a, n_seq, s);
+      case 64: return launch_d<64, true>(a, n_seq, merge, s);
+      case 128: return launch_d<128, true>(a, n_seq, merge, s);
       default: return hipErrorInvalidValue;
     }
   }
   switch (a.head_dim) {
-    case 16: return launch_d<16, false>(a, n_seq, s);
-    case 32: return launch_d<32, false>(a, n_seq, s);
-    case 64: return launch_d<64, false>(a, n_seq, s);
-    case 128: return launch_d<128, false>(a, n_seq, s);
+    case 16: return launch_d<16, false>(a, n_seq, merge, s);
+    case 32: return launch_d<32, false>(a, n_seq, merge, s);
+    case 64: return launch_d<64, false>(a, n_seq, merge, s);
+    case 128: return launch_d<128, false>(a, n_seq, merge, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -144,7 +144,10 @@ hipError_t launch_lm_finish(const LmFinishArgs &a, int n_seq, hipStream_t s);
 struct AttnSeq {
   int ctx_len, win_start;
   const int32_t *bt;
+  int split0, nsplit;  // this sequence's first split (over all sequences of the launch) and split count (1..64)
 };
+
+constexpr int ATTN_MAX_FLAT = 1024;  // splits over all sequences of one launch
 
 struct AttnArgs {
   const uint16_t *qkv;   // [n_seq * gamma, ld] rows [Q | K | V], RoPE applied
@@ -153,11 +156,12 @@ struct AttnArgs {
   const void *pool;      // [block][L][K|V][n_kv] tiles: K [16][head_dim], V^T [head_dim][16]
   int L, layer, kv_fp8;
   const float *kv_scale;
-  int tps, max_splits;   // ctx tiles (32 positions) per split; splits per (sequence, kv head)
+  int tps, n_split;      // ctx tiles (32 positions) per split; splits over all sequences (per kv head)
   float *o_part, *ml_part;
   uint16_t *out;         // [n_seq * gamma, n_q * head_dim] bf16
   int out_ld;
   AttnSeq seq[DFLASH_MAX_BATCH];
+  uint8_t split_seq[ATTN_MAX_FLAT];  // sequence of each split
 };
 hipError_t launch_attention(const AttnArgs &a, int n_seq, hipStream_t s);
 int attn_max_tiles_per_split();
