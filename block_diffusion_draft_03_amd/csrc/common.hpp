@@ -9,6 +9,7 @@ namespace dflash {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int WAVE = 64;
 constexpr float LOG2E = 1.4426950408889634f;
@@ -16,8 +17,6 @@ constexpr float E4M3_MAX = 448.0f;
 
 // bf16 is stored as uint16_t bit patterns.
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // float -> bf16, round to nearest, ties to even (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
@@ -27,15 +26,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Four E4M3FN codes (one dword) -> four bf16 (two dwords). E4M3 values are
-// exactly representable in bf16, so taking the top half of the float is exact.
+// Four E4M3FN codes (one dword) -> four bf16 (two dwords), bytes 0, 1 into
+// the first dword and 2, 3 into the second. E4M3 values are exactly
+// representable in bf16; the conversion's scale of 1.0 leaves them unchanged.
 __device__ __forceinline__ uint2 e4m3x4_to_bf16x4(uint32_t w) {
-  f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-  f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
-  uint2 r;
-  r.x = (__float_as_uint(lo[0]) >> 16) | (__float_as_uint(lo[1]) & 0xFFFF0000u);
-  r.y = (__float_as_uint(hi[0]) >> 16) | (__float_as_uint(hi[1]) & 0xFFFF0000u);
-  return r;
+  const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, false);
+  const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, true);
+  return uint2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
 }
 
 __device__ __forceinline__ float e4m3_to_f32(uint8_t c) {
