@@ -220,6 +220,15 @@ __device__ __forceinline__ void issue_block(const AttnArgs &a, int s, int g, int
   }
 }
 
+// Max over lanes l, l ^ 16, l ^ 32, l ^ 48 (one query column's four lane
+// groups), by the gfx950 row swaps instead of LDS permutes.
+__device__ __forceinline__ float max_lane_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 __device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint2 q) {
   const uint2 lo = e4m3x4_to_bf16x4(q.x), hi = e4m3x4_to_bf16x4(q.y);
   return uint4{lo.x, lo.y, hi.x, hi.y};
@@ -278,8 +287,7 @@ __device__ __forceinline__ void tile_step(const uint4 *slot, const bf16x8 (&qf)[
     }
     float tmax = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
                        fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, WAVE));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, WAVE));
+    tmax = max_lane_groups(tmax);
     const float m_new = fmaxf(w.m[qt], tmax * sc);
     alpha[qt] = fast_exp2(w.m[qt] - m_new);
     float p[2][4], psum = 0.0f;
@@ -289,7 +297,7 @@ __device__ __forceinline__ void tile_step(const uint4 *slot, const bf16x8 (&qf)[
       for (int r = 0; r < 4; ++r) {
         const float e = fast_exp2(fmaf(x[u][r], sc, -m_new));
         psum += e;
-        p[u][r] = e * vs;
+        p[u][r] = FP8CTX ? e * vs : e;
       }
     w.l[qt] = w.l[qt] * alpha[qt] + psum;
     w.m[qt] = m_new;
