@@ -87,8 +87,18 @@ __device__ __forceinline__ void dma16(int4v r, uint32_t voff, uint32_t soff, uin
       : "memory");
 }
 
-__device__ __forceinline__ uint32_t lds_addr(const uint4 *p) {
-  return __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(const lds_uint4 *)p);
+// As dma16 with 4 bytes per lane (lane l's dword lands at lds + 4 l).
+__device__ __forceinline__ void dma4(int4v r, uint32_t voff, uint32_t soff, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %4\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(r), "s"(soff), "s"(lds)
+      : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(const lds_uint4 *)(const uint4 *)p);
 }
 
 // A stage is a list of 1 KB pieces (64 lanes x 16 bytes): the weight
@@ -355,49 +365,68 @@ __global__ __launch_bounds__(TL::NTHR) void k_bgemm(GemmArgs ga, EpiArgs ea, int
 }
 
 // LM head: workgroup (vocab range p, activation block mb) multiplies its
-// LM_TILES vocab blocks of 128 rows and keeps, per lane and activation row, a
+// LM_TILES vocab blocks of BN rows and keeps, per lane and activation row, a
 // running (max, argmax, sum exp) over the unmasked entries; lanes, then the
 // two waves sharing a row, are merged in a fixed order and one partial per
-// (p, row) is written.
+// (p, row) is written. The vocab block's row scales (E4M3) and the bitmask
+// words of the block's sequences are brought into LDS by direct loads issued
+// ahead of the block's product (they complete before its first stage), so the
+// epilogue reads no global memory.
 template <bool WFP8, int NSTAGE, class TL>
 __global__ __launch_bounds__(TL::NTHR) void k_blm_head(LmArgs a, int n_p, int n_mb) {
   constexpr int WN = TL::WN, WM = TL::WM, BN = TL::BN, BM = TL::BM, NT = TL::NT;
+  constexpr int MW = BN / 32;        // mask words of a vocab block
+  constexpr int MSEQ = BM / 2 + 1;   // sequences one block of rows can touch (gamma >= 2)
   static_assert(TL::WAVES_N == 2, "two waves share each activation row");
   __shared__ uint4 lds[NSTAGE * StageShape<WFP8, TL>::F * 64];
   __shared__ float s_mx[2][BM], s_se[2][BM];
   __shared__ uint32_t s_idx[2][BM];
+  __shared__ float s_scale[BN];
+  __shared__ uint32_t s_mask[((MSEQ + 7) / 8) * 8 * MW];  // [local sequence][word], whole loads of 8 sequences
   int p, mb;
   if (!place(blockIdx.x, n_p, n_mb, p, mb)) return;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63, g = lane >> 4,
+            r16 = lane & 15;
   const int wn = wave % TL::WAVES_N, wm = wave / TL::WAVES_N;
   const int n_vb = a.V / BN;
   const int steps_w = a.K >> 7;
+  const int seq0 = (mb * BM) / a.gamma;
+  const int n_s = (min(mb * BM + BM, a.M) - 1) / a.gamma - seq0 + 1;  // <= MSEQ
+  const int4v r_scale = make_rsrc(a.scale, WFP8 ? (uint32_t)a.V * 4u : 0u);
+  const int4v r_mask = make_rsrc(a.bitmask, a.bitmask ? (uint32_t)((a.M + a.gamma - 1) / a.gamma) * a.words * 4u : 0u);
+  const bool masked = a.bitmask != nullptr;
   ArgState st[WM];
-  const int32_t *mask_row[WM];
+  int sl[WM];  // local sequence of each row this lane holds
 #pragma unroll
   for (int j = 0; j < WM; ++j) {
     arg_init(st[j]);
-    const int m = min(mb * BM + (wm * WM + j) * 16 + r16, a.M - 1);
-    mask_row[j] = a.bitmask ? a.bitmask + (size_t)(m / a.gamma) * a.words : nullptr;
+    sl[j] = min(mb * BM + (wm * WM + j) * 16 + r16, a.M - 1) / a.gamma - seq0;
   }
   for (int vb = p * LM_TILES; vb < min(n_vb, (p + 1) * LM_TILES); ++vb) {
+    if (WFP8 || masked) __syncthreads();  // the previous block's epilogue is done with s_scale / s_mask
+    if (WFP8 && wave == 0) dma16(r_scale, lane * 16, (uint32_t)vb * BN * 4, lds_addr(s_scale));
+    if (masked)
+      for (int q = wave; q * 8 < n_s; q += TL::NWAVES) {
+        const int ls = min(q * 8 + (lane >> 3), n_s - 1);
+        dma4(r_mask, (uint32_t)(((seq0 + ls) * a.words + vb * MW + (lane & 7)) * 4), 0, lds_addr(s_mask + q * 64));
+      }
     f32x4 acc[WN][WM];
     zero_acc(acc);
     const LoadPlan<WFP8, TL> pl = make_plan<WFP8, TL>(a.W, (size_t)a.V * a.K * (WFP8 ? 1 : 2), steps_w, vb * NT, a.z, a.K, a.M,
-                                        mb * BM, __builtin_amdgcn_readfirstlane(wave), lane);
+                                        mb * BM, wave, lane);
     block_product<WFP8, NSTAGE, TL>(pl, 0, steps_w, lds, acc);
 #pragma unroll
     for (int i = 0; i < WN; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int v = vb * BN + (wn * WN + i) * 16 + 4 * g + r;
-        const float sc = WFP8 ? a.scale[v] : 1.0f;
+        const int vl = (wn * WN + i) * 16 + 4 * g + r, v = vb * BN + vl;
+        const float sc = WFP8 ? s_scale[vl] : 1.0f;
 #pragma unroll
         for (int j = 0; j < WM; ++j) {
           const float x = acc[i][j][r] * sc;
           const int m = mb * BM + (wm * WM + j) * 16 + r16;
           if (a.logits && m < a.M) a.logits[(size_t)m * a.V + v] = x;
-          const bool ok = !mask_row[j] || ((((uint32_t)mask_row[j][v >> 5]) >> (v & 31)) & 1u);
+          const bool ok = !masked || ((s_mask[sl[j] * MW + (vl >> 5)] >> (vl & 31)) & 1u);
           arg_push(st[j], x, (uint32_t)v, ok);
         }
       }
