@@ -1,10 +1,10 @@
 // k_attn.hip - GQA attention of the block rows over the paged ctx window and
 // the block itself, for gfx950.
 //
-// One workgroup (4 waves) per (split, kv head); a sequence has as many splits
+// One workgroup (NWAVE waves) per (split, kv head); a sequence has as many splits
 // as its own context needs, so short sequences take no idle workgroups. The rep = n_q / n_kv
 // query heads of the kv head times the gamma block rows form up to 128 query
-// rows, 32 per wave. Keys come in tiles of 32: ctx tiles are aligned to two
+// rows, 16 QT per wave. Keys come in tiles of 32: ctx tiles are aligned to two
 // 16-row KV blocks (positions outside [win_start, ctx_len) are masked), and
 // the gamma block rows form the block tile(s), whose K rows come straight
 // from the QKV output and whose V^T from the copy the QKV epilogue writes.
@@ -41,6 +41,9 @@ namespace dflash {
 namespace {
 
 constexpr int KT = 32;          // keys per tile
+constexpr int QT = 1;           // 16-row query tiles per wave
+constexpr int NWAVE = 8 / QT;   // waves per workgroup (128 query rows)
+constexpr int NTHR = 64 * NWAVE;
 constexpr int MAX_TPS = 32;     // ctx tiles per split (2 KV blocks each)
 
 typedef __attribute__((address_space(3))) uint4 lds_uint4;
@@ -82,8 +85,8 @@ struct Geom {
   // fragments (1 KB) per tile: K [u][ks] then V^T [dt]; E4M3: K [u][ks / 2], V^T [dt / 2]
   static constexpr int CF = FP8 ? KS + DT / 2 : 2 * KS + DT;  // ctx tile
   static constexpr int BF = 2 * KS + DT;                      // block tile (bf16)
-  static constexpr int PW = (CF + 3) / 4;                     // ctx-tile loads per wave
-  static constexpr int PB = (BF + 3) / 4;                     // block-tile loads per wave
+  static constexpr int PW = (CF + NWAVE - 1) / NWAVE;         // ctx-tile loads per wave
+  static constexpr int PB = (BF + NWAVE - 1) / NWAVE;         // block-tile loads per wave
   static constexpr int NSTAGE = FP8 ? 4 : 3;
 };
 
@@ -132,7 +135,7 @@ __device__ __forceinline__ IssuePlan<D, FP8> make_issue_plan(int wave, int lane)
   constexpr int EB = FP8 ? 1 : 2;
 #pragma unroll
   for (int j = 0; j < G::PW; ++j) {
-    const int i = (wave + 4 * j) % G::CF;  // duplicates reload an item with the same bytes
+    const int i = (wave + NWAVE * j) % G::CF;  // duplicates reload an item with the same bytes
     p.dst[j] = i * 1024;
     p.act[j] = true;
     if (i < (FP8 ? G::KS : 2 * G::KS)) {
@@ -201,7 +204,7 @@ __device__ __forceinline__ void issue_block(const AttnArgs &a, int s, int g, int
   const int nb16 = ((a.gamma + 31) & ~31) / 16;
 #pragma unroll
   for (int j = 0; j < G::PB; ++j) {
-    const int i = (wave + 4 * j) % G::BF;
+    const int i = (wave + NWAVE * j) % G::BF;
     const uint16_t *src;
     bool active = true;
     if (i < 2 * G::KS) {
@@ -236,15 +239,15 @@ __device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint2 q) {
 
 template <int D>
 struct WaveState {
-  f32x4 o[2][Geom<D, false>::DT];
-  float m[2], l[2];
+  f32x4 o[QT][Geom<D, false>::DT];
+  float m[QT], l[QT];
 };
 
 // One tile for this wave's two query tiles. `valid` says whether key kt of
 // the tile takes part; sc scales the raw scores into base-2 units; vs is
 // folded into P (E4M3 V of ctx keys).
 template <int D, bool FP8CTX, class Valid>
-__device__ __forceinline__ void tile_step(const uint4 *slot, const bf16x8 (&qf)[2][Geom<D, false>::KS], bool full,
+__device__ __forceinline__ void tile_step(const uint4 *slot, const bf16x8 (&qf)[QT][Geom<D, false>::KS], bool full,
                                           Valid valid, float sc, float vs, WaveState<D> &w, int lane) {
   using G = Geom<D, FP8CTX>;
   const int gq = lane >> 4;
@@ -261,10 +264,10 @@ __device__ __forceinline__ void tile_step(const uint4 *slot, const bf16x8 (&qf)[
         kf[u][ks] = as_bf16x8(slot[(u * G::KS + ks) * 64 + piece]);
       }
     }
-  uint4 pk[2];
-  float alpha[2];
+  uint4 pk[QT];
+  float alpha[QT];
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
+  for (int qt = 0; qt < QT; ++qt) {
     f32x4 sacc[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -307,11 +310,14 @@ __device__ __forceinline__ void tile_step(const uint4 *slot, const bf16x8 (&qf)[
     pk[qt].w = pack_bf16x2(p[1][2], p[1][3]);
   }
   // rescale O only when some lane's running max moved (alpha == 1 is exact)
-  if (__any(alpha[0] != 1.0f || alpha[1] != 1.0f)) {
+  bool moved = false;
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) moved = moved || alpha[qt] != 1.0f;
+  if (__any(moved)) {
 #pragma unroll
     for (int dt = 0; dt < G::DT; ++dt)
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) w.o[qt][dt] *= alpha[qt];
+      for (int qt = 0; qt < QT; ++qt) w.o[qt][dt] *= alpha[qt];
   }
 #pragma unroll
   for (int dt = 0; dt < G::DT; ++dt) {
@@ -324,12 +330,12 @@ __device__ __forceinline__ void tile_step(const uint4 *slot, const bf16x8 (&qf)[
       vf = as_bf16x8(slot[(2 * G::KS + dt) * 64 + v_piece(lane & 15, gq)]);
     }
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) w.o[qt][dt] = mfma16x16x32(vf, as_bf16x8(pk[qt]), w.o[qt][dt]);
+    for (int qt = 0; qt < QT; ++qt) w.o[qt][dt] = mfma16x16x32(vf, as_bf16x8(pk[qt]), w.o[qt][dt]);
   }
 }
 
 template <int D, bool FP8, int NS = Geom<D, FP8>::NSTAGE>
-__global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
+__global__ __launch_bounds__(NTHR, 2) void k_attn(AttnArgs a) {
   using G = Geom<D, FP8>;
   using GB = Geom<D, false>;
   __shared__ uint4 ring[NS][G::CF * 64];
@@ -353,22 +359,22 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   if constexpr (D < 32) {
     // lanes whose dims are past head_dim load nothing: their LDS stays zero
     uint4 *z = &ring[0][0];
-    for (int i = threadIdx.x; i < NS * G::CF * 64; i += 256) z[i] = uint4{0u, 0u, 0u, 0u};
-    for (int i = threadIdx.x; i < GB::BF * 64; i += 256) blkt[i] = uint4{0u, 0u, 0u, 0u};
+    for (int i = threadIdx.x; i < NS * G::CF * 64; i += NTHR) z[i] = uint4{0u, 0u, 0u, 0u};
+    for (int i = threadIdx.x; i < GB::BF * 64; i += NTHR) blkt[i] = uint4{0u, 0u, 0u, 0u};
   }
   {
     // block ids of this split's tiles; blocks past the sequence reuse its
     // last block (their keys are masked)
     const int nbv = (sq.ctx_len + 15) >> 4;
-    for (int i = threadIdx.x; i < 2 * nt; i += 256) s_bt[i] = sq.bt[min((p0 >> 4) + 2 * t0 + i, nbv - 1)];
+    for (int i = threadIdx.x; i < 2 * nt; i += NTHR) s_bt[i] = sq.bt[min((p0 >> 4) + 2 * t0 + i, nbv - 1)];
   }
 
   // Q fragments (B operand of S^T): query column r16 of this wave's tiles
   // (rows past R repeat row R - 1 and are not written)
-  bf16x8 qf[2][GB::KS];
+  bf16x8 qf[QT][GB::KS];
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    const int q = min((wave * 2 + qt) * 16 + r16, R - 1);
+  for (int qt = 0; qt < QT; ++qt) {
+    const int q = min((wave * QT + qt) * 16 + r16, R - 1);
     const int hq = g * a.rep + q / a.gamma, j = q % a.gamma;
     const uint16_t *qrow = a.qkv + (size_t)(s * a.gamma + j) * a.ld + hq * D;
 #pragma unroll
@@ -388,7 +394,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
 
   WaveState<D> w;
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
+  for (int qt = 0; qt < QT; ++qt) {
     w.m[qt] = -__builtin_huge_valf();
     w.l[qt] = 0.0f;
 #pragma unroll
@@ -448,11 +454,11 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
 
   // partial (O, max, sum) of this split, or the output with one split
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
+  for (int qt = 0; qt < QT; ++qt) {
     float l_tot = w.l[qt];
     l_tot += __shfl_xor(l_tot, 16, WAVE);
     l_tot += __shfl_xor(l_tot, 32, WAVE);
-    const int q = (wave * 2 + qt) * 16 + r16;
+    const int q = (wave * QT + qt) * 16 + r16;
     if (q >= R) continue;
     if (sq.nsplit == 1) {
       const int hq = g * a.rep + q / a.gamma, j = q % a.gamma;
@@ -520,11 +526,11 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a, int n_seq) {
 
 template <int D, bool FP8>
 hipError_t launch_d(const AttnArgs &a, int n_seq, bool merge, hipStream_t s) {
-  dim3 grid(a.n_split, a.n_kv), block(256);
-  hipLaunchKernelGGL((k_attn<D, FP8>), grid, block, 0, s, a);
+  dim3 grid(a.n_split, a.n_kv);
+  hipLaunchKernelGGL((k_attn<D, FP8>), grid, dim3(NTHR), 0, s, a);
   if (merge) {
     const int rows = n_seq * a.n_kv * a.rep * a.gamma;
-    hipLaunchKernelGGL(k_attn_combine<D>, dim3((rows + 3) / 4), block, 0, s, a, n_seq);
+    hipLaunchKernelGGL(k_attn_combine<D>, dim3((rows + 3) / 4), dim3(256), 0, s, a, n_seq);
   }
   return hipGetLastError();
 }
