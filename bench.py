@@ -29,6 +29,7 @@ if ROOT not in sys.path:
 METRIC = "draft blocks/sec and µs/propose (γ=16, L=8, vocab 248320); % HBM roofline"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix peak of MI355X
+PREFILL_ROWS = 4096  # rows of the prompt-scale precompute timed beside the step
 
 
 def log(*a):
@@ -119,7 +120,7 @@ class Workload:
         n = wl.n_seqs
         self.lens = [wl.ctx_lo] * n if wl.ctx_lo == wl.ctx_hi else [int(x) for x in synth.make_ctx_lengths(n, wl.ctx_lo, wl.ctx_hi)]
         grow = wl.new_rows * (steps_planned + 2) if wl.trim else wl.new_rows
-        blocks = sum((c + grow + 15) // 16 for c in self.lens) + 16
+        blocks = sum((c + grow + 15) // 16 for c in self.lens) + 16 + PREFILL_ROWS // 16
         log(f"[bench] building head (pool {blocks} blocks)")
         self.head = Head(geo, self.weights, kv_pool_blocks=blocks, max_batch=max(1, n), max_seq_len=8192)
         self.states = []
@@ -168,6 +169,31 @@ class Workload:
                 self.head.after_verify(st, 0)
         self.k += 1
         return out
+
+
+def time_prefill(w, reps=3):
+    """Microseconds of one prompt-scale precompute (PREFILL_ROWS rows into a
+    fresh state), from the library's HIP events on its stream, and its flops."""
+    import torch
+    import synth
+    geo = w.geo
+    stack = synth.make_stack(geo, PREFILL_ROWS, tag=777)
+    st = w.head.state_create(budget_tokens=PREFILL_ROWS)
+    w.head.precompute([st], [PREFILL_ROWS], stack)  # warm
+    st.free()
+    torch.cuda.synchronize()
+    w.head.timing_enable(True)
+    w.head.timing_read(2)
+    for _ in range(reps):
+        st = w.head.state_create(budget_tokens=PREFILL_ROWS)
+        w.head.precompute([st], [PREFILL_ROWS], stack)
+        torch.cuda.synchronize()
+        st.free()
+    ms, n = w.head.timing_read(2)
+    w.head.timing_enable(False)
+    fkv = geo.num_layers * 2 * geo.num_kv_heads * geo.head_dim
+    flops = 2 * PREFILL_ROWS * geo.hidden * (geo.num_target_layers * geo.target_hidden + fkv)
+    return ms / max(1, n) * 1e3, flops
 
 
 def time_loop(fn, steps):
@@ -284,6 +310,7 @@ def main():
     w.head.timing_enable(False)
     # forward alone, uninstrumented
     ms_prop, _ = time_loop(w.propose, args.steps)
+    us_prefill, prefill_flops = time_prefill(w)
 
     ctx_rows = [s.ctx_len + (0 if wl.trim else wl.new_rows) for s in w.states]
     rows = wl.n_seqs * geo.gamma
@@ -333,6 +360,9 @@ def main():
         "propose_mfma_frac": round(fwd_flops / (ms_prop / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "propose_algorithmic_flops": fwd_flops,
         "roofline": roofline,
+        "prefill_rows": PREFILL_ROWS,
+        "us_per_prefill": round(us_prefill, 2),
+        "prefill_mfma_frac": round(prefill_flops / (us_prefill / 1e6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "wall_s_timed": round(wall, 3),
     }
     if not args.no_cpu_baseline:

@@ -31,7 +31,8 @@ constexpr uint64_t STATE_MAGIC = 0x44464c4153485354ull;  // "DFLASHST"
 constexpr uint64_t DEAD_MAGIC = 0xdeadull;
 constexpr int ATTN_TARGET_WGS = 512;  // attention workgroups a launch aims for (two per CU)
 constexpr int ATTN_MAX_SPLITS = 64;   // splits per (sequence, kv head) merged by one wave
-constexpr int ATTN_PREF_SPLITS = 16;  // preferred bound: the merge reads every split's partial
+constexpr int ATTN_PREF_SPLITS = 16;
+constexpr int PREFILL_ROWS = 1024;    // rows of one tiled precompute pass  // preferred bound: the merge reads every split's partial
 
 #define HIP_TRY(expr)                                                                          \
   do {                                                                                         \
@@ -91,6 +92,13 @@ struct dflash_head {
   int gp = 0;
   float *pre_u = nullptr;
   uint16_t *pre_c = nullptr;
+  // tiled precompute of many rows: row positions and block tables, double
+  // buffered (pinned staging + device copy; ev[i] marks staging i free)
+  bool tiled_prefill = false;
+  int32_t *h_pos = nullptr, *d_pos = nullptr;
+  const int32_t **h_bts = nullptr, **d_bts = nullptr;
+  hipEvent_t pre_ev[2] = {nullptr, nullptr};
+  bool pre_ev_used[2] = {false, false};
   float *part = nullptr;  // split-K partial sums [splits][rows][h]
 
   // benchmark timing: recorded (start, stop) event pairs per phase
@@ -140,6 +148,15 @@ bool state_ok(const dflash_head *h, const dflash_state *s) { return s && s->magi
 void free_head_memory(dflash_head *h) {
   for (void *p : h->dev_allocs) (void)hipFree(p);
   h->dev_allocs.clear();
+  if (h->h_pos) (void)hipHostFree(h->h_pos);
+  if (h->h_bts) (void)hipHostFree((void *)h->h_bts);
+  h->h_pos = nullptr;
+  h->h_bts = nullptr;
+  for (hipEvent_t &e : h->pre_ev)
+    if (e) {
+      (void)hipEventDestroy(e);
+      e = nullptr;
+    }
 }
 
 void free_state_memory(dflash_state *s) {
@@ -298,7 +315,11 @@ int build_impl(dflash_head *H, const dflash_weights *w, hipStream_t st) {
     max_splits = std::max(max_splits, gemm_plan(g.h, K, true).splits);
     if (bgemm_ok(EPI_PARTIAL, g.h, K)) max_splits = std::max(max_splits, bgemm_splits(g.h, K, (int)M));
   }
-  TRY(H->alloc(&H->part, (size_t)max_splits * std::max<size_t>(M, GEMM_MAX_ROWS) * h));
+  // precompute passes of PREFILL_ROWS rows run through the tiled kernels
+  H->tiled_prefill = bgemm_ok(EPI_PARTIAL, g.h, g.fc_in) && bgemm_ok(EPI_KV_SCATTER, g.fkv_dim, g.h);
+  const size_t pre_rows = H->tiled_prefill ? PREFILL_ROWS : GEMM_MAX_ROWS;
+  if (H->tiled_prefill) max_splits = std::max(max_splits, bgemm_splits(g.h, g.fc_in, PREFILL_ROWS));
+  TRY(H->alloc(&H->part, (size_t)max_splits * std::max({M, (size_t)GEMM_MAX_ROWS, pre_rows}) * h));
   const size_t R = (size_t)g.rep * g.gamma;
   {
     // partial slots: the split rule of attn_plan never needs more
@@ -322,8 +343,15 @@ int build_impl(dflash_head *H, const dflash_weights *w, hipStream_t st) {
   TRY(H->alloc(&H->lm_p1, M));
   TRY(H->alloc(&H->fin_counters, (size_t)g.max_batch));
   HIP_TRY(hipMemsetAsync(H->fin_counters, 0, (size_t)g.max_batch * sizeof(int), st));
-  TRY(H->alloc(&H->pre_u, (size_t)GEMM_MAX_ROWS * h));
-  TRY(H->alloc(&H->pre_c, (size_t)GEMM_MAX_ROWS * h));
+  TRY(H->alloc(&H->pre_u, pre_rows * h));
+  TRY(H->alloc(&H->pre_c, pre_rows * h));
+  if (H->tiled_prefill) {
+    TRY(H->alloc(&H->d_pos, 2 * (size_t)PREFILL_ROWS));
+    TRY(H->alloc(&H->d_bts, 2 * (size_t)PREFILL_ROWS));
+    HIP_TRY(hipHostMalloc((void **)&H->h_pos, 2 * PREFILL_ROWS * sizeof(int32_t), hipHostMallocDefault));
+    HIP_TRY(hipHostMalloc((void **)&H->h_bts, 2 * PREFILL_ROWS * sizeof(const int32_t *), hipHostMallocDefault));
+    for (hipEvent_t &e : H->pre_ev) HIP_TRY(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+  }
   HIP_TRY(hipStreamSynchronize(st));
   return DFLASH_OK;
 }
@@ -778,6 +806,43 @@ int dflash_precompute_ctx_kv(dflash_head *head, dflash_state *const *states, int
     }
   const int h = g.h;
   hipEvent_t t_all = H->interval_begin(DFLASH_PHASE_PRECOMPUTE, st);
+  if (H->tiled_prefill && total > GEMM_MAX_ROWS) {
+    // passes of up to PREFILL_ROWS rows through the tiled kernels; the rows'
+    // positions and block tables go to the device through pinned staging
+    for (int r0 = 0, pass = 0; r0 < (int)total; r0 += PREFILL_ROWS, ++pass) {
+      const int m = std::min<int>(PREFILL_ROWS, (int)total - r0);
+      const int b = pass & 1;
+      if (H->pre_ev_used[b]) HIP_TRY(hipEventSynchronize(H->pre_ev[b]));  // the copy that read staging b is done
+      int32_t *hp = H->h_pos + (size_t)b * PREFILL_ROWS;
+      const int32_t **hb = H->h_bts + (size_t)b * PREFILL_ROWS;
+      for (int r = 0; r < m; ++r) {
+        hp[r] = pos[r0 + r];
+        hb[r] = bts[r0 + r];
+      }
+      int32_t *dp = H->d_pos + (size_t)b * PREFILL_ROWS;
+      const int32_t **db = H->d_bts + (size_t)b * PREFILL_ROWS;
+      HIP_TRY(hipMemcpyAsync(dp, hp, m * sizeof(int32_t), hipMemcpyHostToDevice, st));
+      HIP_TRY(hipMemcpyAsync((void *)db, (const void *)hb, m * sizeof(const int32_t *), hipMemcpyHostToDevice, st));
+      HIP_TRY(hipEventRecord(H->pre_ev[b], st));
+      H->pre_ev_used[b] = true;
+      TRY(resid_gemm(H, (const uint16_t *)stack + (size_t)r0 * g.fc_in, g.fc_in, m, H->w_fc, g.fc_in, H->pre_u,
+                     H->g_hidden, H->pre_c, true, st));
+      EpiArgs e{};
+      e.head_dim = g.d;
+      e.pool = H->kv_pool;
+      e.L = g.L;
+      e.n_kv = g.n_kv;
+      e.kv_fp8 = g.kv_fp8;
+      e.kv_scale = H->kv_scale;
+      e.inv_freq = H->inv_freq;
+      e.d_row_pos = dp;
+      e.d_row_bt = db;
+      TRY(gemm_rows(H, EPI_KV_SCATTER, H->pre_c, h, m, H->w_fkv, g.fkv_dim, h, e, st));
+    }
+    if (t_all) HIP_TRY(hipEventRecord(t_all, st));
+    for (int i = 0; i < n; ++i) states[i]->rows.ctx_len += n_new[i];
+    return DFLASH_OK;
+  }
   for (int r0 = 0; r0 < (int)total; r0 += GEMM_MAX_ROWS) {
     const int m = std::min<int>(GEMM_MAX_ROWS, (int)total - r0);
     // u = S fc^T (split over K, summed in split order), c = RMSNorm(u) bf16

@@ -60,7 +60,7 @@ __device__ __forceinline__ void epilogue4(const f32x4 v, int m, int n, int split
     const int kv_dim = ea.n_kv * d;
     const int l = n / (2 * kv_dim), rem = n % (2 * kv_dim);
     const int kv = rem / kv_dim, hd = (rem % kv_dim) / d, j = n % d;
-    const int pos = ea.row_pos[m];
+    const int pos = ea.d_row_pos ? ea.d_row_pos[m] : ea.row_pos[m];
     float y[4] = {v[0], v[1], v[2], v[3]};
     if (kv == 0) {
 #pragma unroll
@@ -74,7 +74,7 @@ __device__ __forceinline__ void epilogue4(const f32x4 v, int m, int n, int split
       }
     }
     // K tile [16 slots][d]; V tile transposed, [d][16 slots]
-    const int32_t blk = ea.row_bt[m][pos >> 4];
+    const int32_t blk = (ea.d_row_pos ? ea.d_row_bt[m] : ea.row_bt[m])[pos >> 4];
     const size_t tile = ((((size_t)blk * ea.L + l) * 2 + kv) * ea.n_kv + hd) * (size_t)(DFLASH_KV_BLOCK * d);
     const int slot = pos & 15;
     if (ea.kv_fp8) {

@@ -492,7 +492,8 @@ hipError_t launch_pick(const GemmArgs &g, const EpiArgs &e, hipStream_t s) {
 }  // namespace
 
 bool bgemm_ok(int epi, int N, int K) {
-  return epi != EPI_KV_SCATTER && N % TileG::BN == 0 && K % 128 == 0 && N > 0 && K > 0;
+  return (epi == EPI_F32 || epi == EPI_SWIGLU || epi == EPI_QKV_ROPE || epi == EPI_PARTIAL || epi == EPI_KV_SCATTER) &&
+         N % TileG::BN == 0 && K % 128 == 0 && N > 0 && K > 0;
 }
 
 int bgemm_splits(int N, int K, int M) {
@@ -506,8 +507,10 @@ int bgemm_splits(int N, int K, int M) {
 hipError_t launch_bgemm(int epi, const GemmArgs &g, const EpiArgs &e, hipStream_t s) {
   if (g.M < 1 || !bgemm_ok(epi, g.N, g.K) || g.splits < 1 || g.kslice % 128 != 0) return hipErrorInvalidValue;
   if (g.splits > 1 && epi != EPI_PARTIAL) return hipErrorInvalidValue;
+  if (epi == EPI_KV_SCATTER && (!e.d_row_pos || !e.d_row_bt)) return hipErrorInvalidValue;
   switch (epi) {
     case EPI_F32: return launch_pick<EPI_F32>(g, e, s);
+    case EPI_KV_SCATTER: return launch_pick<EPI_KV_SCATTER>(g, e, s);
     case EPI_SWIGLU: return launch_pick<EPI_SWIGLU>(g, e, s);
     case EPI_QKV_ROPE: return launch_pick<EPI_QKV_ROPE>(g, e, s);
     case EPI_PARTIAL: return launch_pick<EPI_PARTIAL>(g, e, s);

@@ -73,6 +73,10 @@ struct EpiArgs {
   const double *inv_freq;  // device [head_dim / 2]
   int row_pos[GEMM_MAX_ROWS];
   const int32_t *row_bt[GEMM_MAX_ROWS];
+  // KV scatter over more rows (tiled kernel): device [M] positions and block
+  // tables of the launch's rows, used instead of row_pos / row_bt when set
+  const int32_t *d_row_pos;
+  const int32_t *const *d_row_bt;
   // EPI_PARTIAL, weight-streaming kernel: when tile_ctr is set, the last
   // split of every unit adds the splits in order to the fp32 residual res_h
   // [M][N], writes res_act = bf16(res_h * res_gain) and the unit's per-row
@@ -88,7 +92,7 @@ struct EpiArgs {
 hipError_t launch_gemm(int epi, const GemmArgs &g, const EpiArgs &e, hipStream_t s);
 
 // The tiled kernel takes any M (one launch for all rows) when N and K are
-// multiples of 128 and the epilogue is not EPI_KV_SCATTER.
+// multiples of 128 (EPI_KV_SCATTER then reads d_row_pos / d_row_bt).
 bool bgemm_ok(int epi, int N, int K);
 // K splits of a tiled EPI_PARTIAL GEMM over M rows (at most 4; K a multiple of 128 * splits).
 int bgemm_splits(int N, int K, int M);

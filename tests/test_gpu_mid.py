@@ -84,3 +84,54 @@ def test_mid_batch_and_single_match_oracle(case):
     for s in states:
         s.free()
     head.destroy()
+
+
+@pytest.mark.parametrize("case", ["d64", "d64_fp8"])
+def test_mid_prompt_scale_precompute_matches_oracle(case):
+    """Precompute of many rows in one call (passes of up to 1024 rows through
+    the tiled GEMMs: 300 rows in one pass; 1100 rows over two sequences in two
+    passes, the second a ragged 76): the cache against the oracle's K/V, then a
+    propose over it."""
+    from oracle.numerics import bf16_to_f64, e4m3_decode
+    from block_diffusion_draft_03_amd import Head
+    geo = CASES[case]
+    fp8 = geo.kv_dtype == "fp8"
+    w = synth.make_weights(geo)
+    say(f"[build] mid prefill {case}")
+    head = Head(geo, w, kv_pool_blocks=200, max_batch=2, max_seq_len=2048)
+    orc = OracleHead(geo.as_dict(), w)
+    for lens in ([300], [700, 400]):
+        say(f"[case] mid prefill {case} rows {lens}")
+        sts = [head.state_create() for _ in lens]
+        oss = [orc.new_state() for _ in lens]
+        stacks = [synth.make_stack(geo, n, tag=1200 + i + len(lens)) for i, n in enumerate(lens)]
+        head.precompute(sts, lens, np.concatenate(stacks))
+        for os_, stk in zip(oss, stacks):
+            orc.precompute(os_, stk)
+        for i, n in enumerate(lens):
+            for layer in (0, geo.num_layers - 1):
+                k, v = head.read_kv(sts[i], layer, 0, n)
+                torch.cuda.synchronize()
+                kr = np.stack(oss[i].k[layer])
+                vr = np.stack(oss[i].v[layer])
+                if fp8:
+                    sk = w["kv_scale"][layer, 0].astype(np.float64)
+                    sv = w["kv_scale"][layer, 1].astype(np.float64)
+                    kg = e4m3_decode(k.cpu().numpy()) * sk[None, :, None]
+                    vg = e4m3_decode(v.cpu().numpy()) * sv[None, :, None]
+                    # one E4M3 step (2^-3 relative) plus the bf16 rounding of the GEMM inputs
+                    assert np.all(np.abs(kg - kr) <= np.maximum(np.abs(kr) * 2.0 ** -3, sk[None, :, None] * 2.0 ** -9) + 1e-2)
+                    assert np.all(np.abs(vg - vr) <= np.maximum(np.abs(vr) * 2.0 ** -3, sv[None, :, None] * 2.0 ** -9) + 1e-2)
+                else:
+                    kg = bf16_to_f64(k.cpu().numpy().view(np.uint16))
+                    vg = bf16_to_f64(v.cpu().numpy().view(np.uint16))
+                    assert np.abs(kg - kr).max() <= 2e-2 * np.abs(kr).max()
+                    assert np.abs(vg - vr).max() <= 2e-2 * np.abs(vr).max()
+        tok = int(synth.make_tokens(geo, 1, tag=55)[0])
+        res = head.propose(sts[-1], tok, sts[-1].ctx_len, geo.gamma - 1, logits=True)
+        torch.cuda.synchronize()
+        ref = orc.propose(oss[-1], tok, oss[-1].ctx_len, geo.gamma - 1)
+        check_propose(res, ref, logit_tol=6e-2 if geo.lm_head_dtype == "fp8" else 2e-2, label=f"{case} after {lens}")
+        for st in sts:
+            st.free()
+    head.destroy()
