@@ -79,7 +79,8 @@ struct dflash_head {
   float *hid = nullptr;
   uint16_t *act = nullptr, *qkv = nullptr, *attn = nullptr, *mlp = nullptr;
   float2 *cs = nullptr;
-  float *o_part = nullptr, *ml_part = nullptr;
+  uint16_t *o_part = nullptr;
+  float *ml_part = nullptr;
   float *lm_mx = nullptr, *lm_se = nullptr;
   uint32_t *lm_idx = nullptr;
   float *lm_p1 = nullptr;

@@ -30,9 +30,9 @@
 // carry their head dims in RoPE pair order; every score is unchanged by these
 // permutations.
 //
-// Each split writes an unnormalised partial (O, max, sum) that the combine
-// kernel merges (one wave per query row); with a single split the output is
-// written directly.
+// Each split writes an unnormalised partial (O in bf16, max and sum in f32)
+// that the combine kernel merges (one wave per query row); with a single
+// split the output is written directly.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -472,7 +472,10 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(AttnArgs a) {
     } else {
       const size_t part = ((size_t)g * a.n_split + flat) * R + q;
 #pragma unroll
-      for (int dt = 0; dt < GB::DT; ++dt) *(f32x4 *)(a.o_part + part * D + dt * 16 + 4 * gq) = w.o[qt][dt];
+      for (int dt = 0; dt < GB::DT; ++dt) {
+        const f32x4 v = w.o[qt][dt];
+        *(uint2 *)(a.o_part + part * D + dt * 16 + 4 * gq) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      }
       if (gq == 0) {
         a.ml_part[part * 2 + 0] = w.m[qt];
         a.ml_part[part * 2 + 1] = l_tot;
@@ -483,7 +486,8 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(AttnArgs a) {
 
 // Merge the splits of one query row per wave: lane s reads split s's (max,
 // sum); the weights exp2(m_s - M) are shared by shuffles and every lane
-// accumulates its dimensions over the splits in order.
+// accumulates its dimensions (two adjacent ones for head_dim 128) over the
+// splits in order.
 template <int D>
 __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a, int n_seq) {
   constexpr int DPL = D >= 64 ? D / 64 : 1;  // dims per lane
@@ -505,23 +509,35 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a, int n_seq) {
   for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, WAVE));
   const float w = lane < nsplit ? fast_exp2(m - M) : 0.0f;
   const float den = wave_sum(w * l);
-  float acc[DPL];
-#pragma unroll
-  for (int i = 0; i < DPL; ++i) acc[i] = 0.0f;
-  const bool active = D >= 64 || lane < D;
-#pragma unroll 16
-  for (int c = 0; c < nsplit; ++c) {
-    const float wc = __shfl(w, c, WAVE);
-    const float *op = a.o_part + ((base + c) * R + q) * D;
-#pragma unroll
-    for (int i = 0; i < DPL; ++i)
-      if (active) acc[i] += wc * op[lane + 64 * i];
-  }
   const int hq = g * a.rep + q / a.gamma, j = q % a.gamma;
   uint16_t *out = a.out + (size_t)(s * a.gamma + j) * a.out_ld + hq * D;
+  if constexpr (D == 128) {
+    float acc0 = 0.0f, acc1 = 0.0f;
+#pragma unroll 16
+    for (int c = 0; c < nsplit; ++c) {
+      const float wc = __shfl(w, c, WAVE);
+      const uint32_t pr = *(const uint32_t *)(a.o_part + ((base + c) * R + q) * D + 2 * lane);
+      acc0 += wc * __uint_as_float(pr << 16);
+      acc1 += wc * __uint_as_float(pr & 0xFFFF0000u);
+    }
+    *(uint32_t *)(out + 2 * lane) = pack_bf16x2(acc0 / den, acc1 / den);
+  } else {
+    float acc[DPL];
 #pragma unroll
-  for (int i = 0; i < DPL; ++i)
-    if (active) out[lane + 64 * i] = f32_to_bf16(acc[i] / den);
+    for (int i = 0; i < DPL; ++i) acc[i] = 0.0f;
+    const bool active = D >= 64 || lane < D;
+#pragma unroll 16
+    for (int c = 0; c < nsplit; ++c) {
+      const float wc = __shfl(w, c, WAVE);
+      const uint16_t *op = a.o_part + ((base + c) * R + q) * D;
+#pragma unroll
+      for (int i = 0; i < DPL; ++i)
+        if (active) acc[i] += wc * bf16_to_f32(op[lane + 64 * i]);
+    }
+#pragma unroll
+    for (int i = 0; i < DPL; ++i)
+      if (active) out[lane + 64 * i] = f32_to_bf16(acc[i] / den);
+  }
 }
 
 template <int D, bool FP8>

@@ -161,7 +161,8 @@ struct AttnArgs {
   int L, layer, kv_fp8;
   const float *kv_scale;
   int tps, n_split;      // ctx tiles (32 positions) per split; splits over all sequences (per kv head)
-  float *o_part, *ml_part;
+  uint16_t *o_part;      // bf16 unnormalised O of each split [slot][R][head_dim]
+  float *ml_part;        // (max, sum) of each split's rows
   uint16_t *out;         // [n_seq * gamma, n_q * head_dim] bf16
   int out_ld;
   AttnSeq seq[DFLASH_MAX_BATCH];
