@@ -315,27 +315,61 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs ga, EpiArgs ea) {
 // then writes the RMSNorm of the new row (with `gain`) as bf16 and, when
 // asked, the row's sum of squares.
 __global__ __launch_bounds__(256) void k_resid_norm(ResidNormArgs a) {
+  constexpr int MAXC = 4;  // row chunks (of 4 values per thread) kept in registers
+  constexpr int MAXS = 4;  // splits whose loads are all issued before the sum
   __shared__ float red[4];
   const int m = blockIdx.x;
   float *hr = a.h + (size_t)m * a.n;
+  const int step = blockDim.x * 4;
+  const bool fast = a.n <= MAXC * step && a.splits <= MAXS;
   float ss = 0.0f;
-  for (int i = threadIdx.x * 4; i < a.n; i += blockDim.x * 4) {
-    f32x4 x = a.init_zero ? f32x4{0.f, 0.f, 0.f, 0.f} : *(const f32x4 *)(hr + i);
-    for (int s = 0; s < a.splits; ++s) x += *(const f32x4 *)(a.part + ((size_t)s * a.ld_split + m) * a.n + i);
-    *(f32x4 *)(hr + i) = x;
-    ss += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+  f32x4 xs[MAXC];
+  if (fast) {
+    // every load of the row is in flight at once; the sum keeps split order
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+      const int i = c * step + threadIdx.x * 4;
+      if (i < a.n) {
+        f32x4 p[MAXS];
+#pragma unroll
+        for (int s = 0; s < MAXS; ++s)
+          if (s < a.splits) p[s] = *(const f32x4 *)(a.part + ((size_t)s * a.ld_split + m) * a.n + i);
+        f32x4 x = a.init_zero ? f32x4{0.f, 0.f, 0.f, 0.f} : *(const f32x4 *)(hr + i);
+#pragma unroll
+        for (int s = 0; s < MAXS; ++s)
+          if (s < a.splits) x += p[s];
+        *(f32x4 *)(hr + i) = x;
+        ss += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+        xs[c] = x;
+      }
+    }
+  } else {
+    for (int i = threadIdx.x * 4; i < a.n; i += step) {
+      f32x4 x = a.init_zero ? f32x4{0.f, 0.f, 0.f, 0.f} : *(const f32x4 *)(hr + i);
+      for (int s = 0; s < a.splits; ++s) x += *(const f32x4 *)(a.part + ((size_t)s * a.ld_split + m) * a.n + i);
+      *(f32x4 *)(hr + i) = x;
+      ss += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+    }
   }
   ss = block_sum(ss, red);
   if (!a.out) return;
   const float r = 1.0f / sqrtf(ss / (float)a.n + a.eps);
   uint16_t *o = a.out + (size_t)m * a.n;
-  for (int i = threadIdx.x * 4; i < a.n; i += blockDim.x * 4) {
-    const f32x4 x = *(const f32x4 *)(hr + i);
+  auto put = [&](int i, const f32x4 x) {
     const float4 gg = *(const float4 *)(a.gain + i);
     uint2 w;
     w.x = pack_bf16x2(x[0] * r * gg.x, x[1] * r * gg.y);
     w.y = pack_bf16x2(x[2] * r * gg.z, x[3] * r * gg.w);
     *(uint2 *)(o + i) = w;
+  };
+  if (fast) {
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+      const int i = c * step + threadIdx.x * 4;
+      if (i < a.n) put(i, xs[c]);
+    }
+  } else {
+    for (int i = threadIdx.x * 4; i < a.n; i += step) put(i, *(const f32x4 *)(hr + i));
   }
 }
 
