@@ -163,6 +163,10 @@ int dflash_state_ctx_len(const dflash_state *st);
  *   stack: device bf16 [sum(n_new), T * Ht], row-major, shallow-to-deep
  *          concatenation of the target layers ([DraftProposer] propose,
  *          argument target_hidden_stack).
+ * A call of up to 64 rows in all streams the weights once per 64 rows; a
+ * larger call (prompt-scale prefill) runs in passes of up to 1024 rows through
+ * MFMA-tiled GEMMs. A row's cached K/V is bit-identical for any call of the
+ * same kind; the two kinds agree to rounding.
  * DFLASH_E_NO_BLOCKS if a state would exceed its budget or the pool. */
 int dflash_precompute_ctx_kv(dflash_head *head, dflash_state *const *states, int32_t n, const int32_t *n_new,
                              const void *stack, uint64_t stream);
