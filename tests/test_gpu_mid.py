@@ -1,6 +1,7 @@
 """GPU parity on mid-size geometries that the tiny and full ones leave out:
 head_dim 32 and 64 with a bf16 KV cache, head_dim 64 with an E4M3 KV cache
-and LM head, and a ctx window shorter than the context. Two layers, hidden
+and LM head, a ctx window shorter than the context, and blocks of 64 and 33
+rows (two block tiles in the attention, the second full or holding one row). Two layers, hidden
 256, vocab 2048, block of 16. A ragged batch of six sequences (0 to 300 ctx
 rows, so several 32-key tiles, partial blocks and an empty context) runs
 through the batched path (96 rows: tiled GEMMs and LM head), and one
@@ -28,6 +29,10 @@ CASES = {
     "d64": replace(MID, num_q_heads=4, head_dim=64),
     "d64_window100": replace(MID, num_q_heads=4, head_dim=64, ctx_window=100),
     "d64_fp8": replace(MID, num_q_heads=4, head_dim=64, kv_dtype="fp8", lm_head_dtype="fp8"),
+    # the largest block (two 32-row block tiles; the single-sequence forward has 64 rows) and
+    # a ragged one (the second block tile holds one row)
+    "d64_gamma64": replace(MID, num_q_heads=4, head_dim=64, gamma=64),
+    "d64_gamma33_fp8": replace(MID, num_q_heads=4, head_dim=64, gamma=33, kv_dtype="fp8", lm_head_dtype="fp8"),
 }
 LENS = [0, 17, 64, 300, 129, 45]
 
