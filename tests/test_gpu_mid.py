@@ -33,6 +33,9 @@ CASES = {
     # a ragged one (the second block tile holds one row)
     "d64_gamma64": replace(MID, num_q_heads=4, head_dim=64, gamma=64),
     "d64_gamma33_fp8": replace(MID, num_q_heads=4, head_dim=64, gamma=33, kv_dtype="fp8", lm_head_dtype="fp8"),
+    # one query head per kv head, and one kv head for all query heads
+    "d64_mha": replace(MID, num_q_heads=4, num_kv_heads=4, head_dim=64),
+    "d64_mqa": replace(MID, num_q_heads=4, num_kv_heads=1, head_dim=64),
 }
 LENS = [0, 17, 64, 300, 129, 45]
 
