@@ -15,27 +15,76 @@ namespace {
 // with ss_out, the row times the gain and the row's sum of squares), and the
 // row's (cos, sin) RoPE table computed in double precision.
 __global__ __launch_bounds__(256) void k_setup(SetupArgs a) {
+  constexpr int VPT = 8;  // embedding values per thread and chunk (one 16-byte load)
+  constexpr int MAXC = 2; // chunks kept in registers (hidden <= 4096)
   __shared__ float red[4];
   const int m = blockIdx.x, s = m / a.gamma, j = m % a.gamma;
   const uint32_t tok = j == 0 ? a.token[s] : a.mask_id;
   const int pos = a.position[s] + j;
   const uint16_t *e = a.embed + (size_t)tok * a.h;
   float *hr = a.hid + (size_t)m * a.h;
-  float ss = 0.0f;
-  for (int i = threadIdx.x; i < a.h; i += blockDim.x) {
-    const float x = bf16_to_f32(e[i]);
-    hr[i] = x;
-    ss += x * x;
-  }
-  ss = block_sum(ss, red);
-  const float r = a.ss_out ? 1.0f : 1.0f / sqrtf(ss / (float)a.h + a.eps);
-  if (a.ss_out && threadIdx.x == 0) a.ss_out[m] = ss;
   uint16_t *ar = a.a + (size_t)m * a.h;
-  for (int i = threadIdx.x; i < a.h; i += blockDim.x) ar[i] = f32_to_bf16(bf16_to_f32(e[i]) * r * a.gain[i]);
+  const int step = blockDim.x * VPT;
+  const bool fast = a.h % VPT == 0 && a.h <= MAXC * step;
+  // the row's loads go out first; the RoPE table is computed while they are in flight
+  uint4 q[MAXC];
+  if (fast) {
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+      const int i = c * step + threadIdx.x * VPT;
+      if (i < a.h) q[c] = *(const uint4 *)(e + i);
+    }
+  }
   for (int i = threadIdx.x; i < a.half_dim; i += blockDim.x) {
     double sn, cs;
     sincos((double)pos * a.inv_freq[i], &sn, &cs);
     a.cs[(size_t)m * a.half_dim + i] = make_float2((float)cs, (float)sn);
+  }
+  float ss = 0.0f;
+  if (fast) {
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+      const int i = c * step + threadIdx.x * VPT;
+      if (i < a.h) {
+        const uint32_t w[4] = {q[c].x, q[c].y, q[c].z, q[c].w};
+        float x[VPT];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          x[2 * k] = __uint_as_float(w[k] << 16);
+          x[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+        }
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) ss += x[k] * x[k];
+        *(float4 *)(hr + i) = make_float4(x[0], x[1], x[2], x[3]);
+        *(float4 *)(hr + i + 4) = make_float4(x[4], x[5], x[6], x[7]);
+      }
+    }
+  } else {
+    for (int i = threadIdx.x; i < a.h; i += blockDim.x) {
+      const float x = bf16_to_f32(e[i]);
+      hr[i] = x;
+      ss += x * x;
+    }
+  }
+  ss = block_sum(ss, red);
+  const float r = a.ss_out ? 1.0f : 1.0f / sqrtf(ss / (float)a.h + a.eps);
+  if (a.ss_out && threadIdx.x == 0) a.ss_out[m] = ss;
+  if (fast) {
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+      const int i = c * step + threadIdx.x * VPT;
+      if (i < a.h) {
+        const uint32_t w[4] = {q[c].x, q[c].y, q[c].z, q[c].w};
+        uint32_t o[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          o[k] = pack_bf16x2(__uint_as_float(w[k] << 16) * r * a.gain[i + 2 * k],
+                             __uint_as_float(w[k] & 0xFFFF0000u) * r * a.gain[i + 2 * k + 1]);
+        *(uint4 *)(ar + i) = uint4{o[0], o[1], o[2], o[3]};
+      }
+    }
+  } else {
+    for (int i = threadIdx.x; i < a.h; i += blockDim.x) ar[i] = f32_to_bf16(bf16_to_f32(e[i]) * r * a.gain[i]);
   }
 }
 
