@@ -601,7 +601,7 @@ int propose_impl(dflash_head *H, dflash_state *const *states, int n, const uint3
   la.part_se = H->lm_se;
   la.part_idx = H->lm_idx;
   la.rs = rs;
-  const bool tiled_lm = M > GEMM_MAX_ROWS && g.V % 128 == 0 && h % 128 == 0;
+  const bool tiled_lm = M > GEMM_MAX_ROWS && blm_ok(g.V, h);
   if (tiled_lm) {
     la.z = H->act;
     la.M = M;

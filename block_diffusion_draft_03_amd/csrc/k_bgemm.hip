@@ -520,6 +520,8 @@ hipError_t launch_bgemm(int epi, const GemmArgs &g, const EpiArgs &e, hipStream_
 
 int blm_parts(int V) { return (V / TileL::BN + LM_TILES - 1) / LM_TILES; }
 
+bool blm_ok(int V, int K) { return V > 0 && K > 0 && V % TileL::BN == 0 && K % 128 == 0; }
+
 hipError_t launch_blm_head(bool w_fp8, const LmArgs &a, hipStream_t s) {
   if (a.M < 1 || a.V % TileL::BN != 0 || a.K % 128 != 0 || a.row0 != 0) return hipErrorInvalidValue;
   const int n_p = blm_parts(a.V), n_mb = (a.M + TileL::BM - 1) / TileL::BM;

@@ -128,8 +128,10 @@ struct LmArgs {
 };
 int lm_parts(int V);     // P of launch_lm_head, a function of V only
 hipError_t launch_lm_head(bool w_fp8, const LmArgs &a, hipStream_t s);
-// Tiled LM head for any M (one launch for all rows; row0 = 0, ld_part = M),
-// blm_parts(V) partials per row. Logits are bit-identical to launch_lm_head's.
+// Tiled LM head for any M (one launch for all rows; row0 = 0, ld_part = M)
+// when blm_ok(V, K), blm_parts(V) partials per row. Logits are bit-identical
+// to launch_lm_head's (both sum K in one pass).
+bool blm_ok(int V, int K);
 int blm_parts(int V);
 hipError_t launch_blm_head(bool w_fp8, const LmArgs &a, hipStream_t s);
 

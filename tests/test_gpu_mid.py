@@ -36,6 +36,9 @@ CASES = {
     # one query head per kv head, and one kv head for all query heads
     "d64_mha": replace(MID, num_q_heads=4, num_kv_heads=4, head_dim=64),
     "d64_mqa": replace(MID, num_q_heads=4, num_kv_heads=1, head_dim=64),
+    # a vocabulary that the tiled LM head's 256-row blocks do not divide: the
+    # batch takes the weight-streaming LM head in 64-row chunks
+    "d64_vocab2176": replace(MID, num_q_heads=4, head_dim=64, vocab=2176, mask_token_id=2175),
 }
 LENS = [0, 17, 64, 300, 129, 45]
 
