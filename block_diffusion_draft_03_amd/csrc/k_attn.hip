@@ -484,8 +484,32 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(AttnArgs a) {
   }
 }
 
+// Reductions over all 64 lanes without LDS: quad permutes and row rotates
+// (DPP) inside each 16-lane row, then the row swaps across rows. Every lane
+// ends with the result; the order is fixed.
+template <bool MAX>
+__device__ __forceinline__ float wave_reduce_dpp(float x) {
+  auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+  auto dpp = [](float v, int ctrl) -> float {
+    switch (ctrl) {
+      case 0xB1: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+      case 0x4E: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+      case 0x124: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));
+      default: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
+    }
+  };
+  x = op(x, dpp(x, 0xB1));   // quad_perm [1, 0, 3, 2]
+  x = op(x, dpp(x, 0x4E));   // quad_perm [2, 3, 0, 1]
+  x = op(x, dpp(x, 0x124));  // row_ror 4
+  x = op(x, dpp(x, 0x128));  // row_ror 8
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return op(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // Merge the splits of one query row per wave: lane s reads split s's (max,
-// sum); the weights exp2(m_s - M) are shared by shuffles and every lane
+// sum); the weights exp2(m_s - M) are read lane by lane and every lane
 // accumulates its dimensions (two adjacent ones for head_dim 128) over the
 // splits in order.
 template <int D>
@@ -504,18 +528,16 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a, int n_seq) {
     m = a.ml_part[((base + lane) * R + q) * 2];
     l = a.ml_part[((base + lane) * R + q) * 2 + 1];
   }
-  float M = m;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, WAVE));
+  const float M = wave_reduce_dpp<true>(m);
   const float w = lane < nsplit ? fast_exp2(m - M) : 0.0f;
-  const float den = wave_sum(w * l);
+  const float den = wave_reduce_dpp<false>(w * l);
   const int hq = g * a.rep + q / a.gamma, j = q % a.gamma;
   uint16_t *out = a.out + (size_t)(s * a.gamma + j) * a.out_ld + hq * D;
   if constexpr (D == 128) {
     float acc0 = 0.0f, acc1 = 0.0f;
 #pragma unroll 16
     for (int c = 0; c < nsplit; ++c) {
-      const float wc = __shfl(w, c, WAVE);
+      const float wc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), c));
       const uint32_t pr = *(const uint32_t *)(a.o_part + ((base + c) * R + q) * D + 2 * lane);
       acc0 += wc * __uint_as_float(pr << 16);
       acc1 += wc * __uint_as_float(pr & 0xFFFF0000u);
@@ -528,7 +550,7 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a, int n_seq) {
     const bool active = D >= 64 || lane < D;
 #pragma unroll 16
     for (int c = 0; c < nsplit; ++c) {
-      const float wc = __shfl(w, c, WAVE);
+      const float wc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), c));
       const uint16_t *op = a.o_part + ((base + c) * R + q) * D;
 #pragma unroll
       for (int i = 0; i < DPL; ++i)
