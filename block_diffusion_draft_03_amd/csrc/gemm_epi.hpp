@@ -14,6 +14,39 @@
 
 namespace dflash {
 
+// (cos, sin) of the two RoPE pairs in columns n .. n+3 of row m (unused for
+// V columns): 16 contiguous bytes of the row's table, so a kernel can load
+// them before its weight stream.
+__device__ __forceinline__ float4 qkv_cs(int m, int n, const EpiArgs &ea) {
+  if (n >= ea.q_dim + ea.kv_dim) return float4{1.0f, 0.0f, 1.0f, 0.0f};
+  const int p = (n % ea.head_dim) >> 1;  // pair index of rows n, n+1 (even)
+  return *(const float4 *)(ea.cs + (size_t)m * (ea.head_dim >> 1) + p);
+}
+
+// EPI_QKV_ROPE with the row's (cos, sin) pairs cs = (c0, s0, c1, s1).
+__device__ __forceinline__ void epilogue4_qkv(const f32x4 v, int m, int n, const float4 cs, const EpiArgs &ea) {
+  float y[4] = {v[0], v[1], v[2], v[3]};
+  if (n < ea.q_dim + ea.kv_dim) {
+    y[0] = v[0] * cs.x - v[1] * cs.y;
+    y[1] = v[1] * cs.x + v[0] * cs.y;
+    y[2] = v[2] * cs.z - v[3] * cs.w;
+    y[3] = v[3] * cs.z + v[2] * cs.w;
+  }
+  uint2 o;
+  o.x = pack_bf16x2(y[0], y[1]);
+  o.y = pack_bf16x2(y[2], y[3]);
+  *(uint2 *)(ea.out_bf16 + (size_t)m * ea.ldo + n) = o;
+  if (n >= ea.q_dim + ea.kv_dim && ea.vtb) {
+    // V of the block rows, transposed per kv head for the attention kernel
+    const int vn = n - ea.q_dim - ea.kv_dim, hd = vn / ea.head_dim, dim = vn % ea.head_dim;
+    const int seq = (ea.row0 + m) / ea.gamma, j = (ea.row0 + m) % ea.gamma;
+    const int n_kv = ea.kv_dim / ea.head_dim, nb16 = ea.gp / 16;
+    uint16_t *vt = ea.vtb + (((size_t)(seq * n_kv + hd) * nb16 + j / 16) * ea.head_dim + dim) * 16 + (j & 15);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) vt[(size_t)r * 16] = f32_to_bf16(y[r]);
+  }
+}
+
 // EPI_F32:      out_f32[m, n..n+3] = v
 // EPI_PARTIAL:  out_f32[split][m][n..n+3] = v   (row stride ldo, split stride ld_split rows)
 // EPI_SWIGLU:   out_bf16[m, n/2], [m, n/2 + 1] = silu(gate) * up
@@ -30,31 +63,7 @@ __device__ __forceinline__ void epilogue4(const f32x4 v, int m, int n, int split
     // rows (gate_i, up_i, gate_i+1, up_i+1) with i = n / 2
     *(uint32_t *)(ea.out_bf16 + (size_t)m * ea.ldo + n / 2) = pack_bf16x2(silu(v[0]) * v[1], silu(v[2]) * v[3]);
   } else if constexpr (EPI == EPI_QKV_ROPE) {
-    const int half = ea.head_dim >> 1;
-    float y[4] = {v[0], v[1], v[2], v[3]};
-    if (n < ea.q_dim + ea.kv_dim) {
-      const int p = (n % ea.head_dim) >> 1;  // pair index of rows n, n+1
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const float2 c = ea.cs[(size_t)m * half + p + q];
-        const float x0 = v[2 * q], x1 = v[2 * q + 1];
-        y[2 * q] = x0 * c.x - x1 * c.y;
-        y[2 * q + 1] = x1 * c.x + x0 * c.y;
-      }
-    }
-    uint2 o;
-    o.x = pack_bf16x2(y[0], y[1]);
-    o.y = pack_bf16x2(y[2], y[3]);
-    *(uint2 *)(ea.out_bf16 + (size_t)m * ea.ldo + n) = o;
-    if (n >= ea.q_dim + ea.kv_dim && ea.vtb) {
-      // V of the block rows, transposed per kv head for the attention kernel
-      const int vn = n - ea.q_dim - ea.kv_dim, hd = vn / ea.head_dim, dim = vn % ea.head_dim;
-      const int seq = (ea.row0 + m) / ea.gamma, j = (ea.row0 + m) % ea.gamma;
-      const int n_kv = ea.kv_dim / ea.head_dim, nb16 = ea.gp / 16;
-      uint16_t *vt = ea.vtb + (((size_t)(seq * n_kv + hd) * nb16 + j / 16) * ea.head_dim + dim) * 16 + (j & 15);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) vt[(size_t)r * 16] = f32_to_bf16(y[r]);
-    }
+    epilogue4_qkv(v, m, n, qkv_cs(m, n, ea), ea);
   } else if constexpr (EPI == EPI_KV_SCATTER) {
     const int d = ea.head_dim;
     const int kv_dim = ea.n_kv * d;

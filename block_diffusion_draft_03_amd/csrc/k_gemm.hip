@@ -27,6 +27,8 @@ namespace dflash {
 
 namespace {
 
+constexpr int NUM_CUS = 256;  // compute units of the MI355X
+
 template <int MT, int TN>
 struct Frag {
   uint4 w[TN][4];
@@ -221,6 +223,17 @@ __device__ __forceinline__ void finish_residual(const GemmArgs &ga, const EpiArg
                                                 int row0) {
   const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
   const int split = blockIdx.y, splits = gridDim.y;
+  // the residual part and the gain are final before this launch: every split
+  // loads them ahead of the split count, off the critical path of the last one
+  f32x4 hx[TN][MT];
+  float4 gg[TN];
+#pragma unroll
+  for (int t = 0; t < TN; ++t) {
+    const int n = min(row0 + 16 * t + 4 * g, ga.N - 4);
+    gg[t] = *(const float4 *)(ea.res_gain + n);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) hx[t][mt] = *(const f32x4 *)(ea.res_h + (size_t)min(mt * 16 + r16, ga.M - 1) * ga.N + n);
+  }
   if (splits > 1) {
 #pragma unroll
     for (int t = 0; t < TN; ++t)
@@ -248,8 +261,7 @@ __device__ __forceinline__ void finish_residual(const GemmArgs &ga, const EpiArg
     for (int mt = 0; mt < MT; ++mt) {
       const int m = mt * 16 + r16, n = row0 + 16 * t + 4 * g;
       if (m >= ga.M || n >= ga.N) continue;
-      float *hr = ea.res_h + (size_t)m * ga.N + n;
-      f32x4 x = *(const f32x4 *)hr;
+      f32x4 x = hx[t][mt];
       for (int sp = 0; sp < splits; ++sp) {
         if (sp == split) {
           x += acc[t][mt];
@@ -259,10 +271,9 @@ __device__ __forceinline__ void finish_residual(const GemmArgs &ga, const EpiArg
           for (int r = 0; r < 4; ++r) x[r] += __hip_atomic_load(o + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
       }
-      *(f32x4 *)hr = x;
-      const float4 gg = *(const float4 *)(ea.res_gain + n);
+      *(f32x4 *)(ea.res_h + (size_t)m * ga.N + n) = x;
       *(uint2 *)(ea.res_act + (size_t)m * ga.N + n) =
-          uint2{pack_bf16x2(x[0] * gg.x, x[1] * gg.y), pack_bf16x2(x[2] * gg.z, x[3] * gg.w)};
+          uint2{pack_bf16x2(x[0] * gg[t].x, x[1] * gg[t].y), pack_bf16x2(x[2] * gg[t].z, x[3] * gg[t].w)};
       ss[mt] += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
     }
 #pragma unroll
@@ -286,6 +297,17 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs ga, EpiArgs ea) {
   const int s0 = (steps * wave) / NW, s1 = (steps * (wave + 1)) / NW;
   float rs_v[RS_PRE];
   if (ga.rs.ss) row_scale_issue<MT>(ga.rs, ga.M, rs_v);
+  // wave 0 writes the epilogue: its RoPE (cos, sin) pairs are loaded now
+  float4 cs4[TN][MT];
+  if constexpr (EPI == EPI_QKV_ROPE) {
+    if (wave == 0) {
+#pragma unroll
+      for (int t = 0; t < TN; ++t)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          cs4[t][mt] = qkv_cs(min(mt * 16 + r16, ga.M - 1), min(row0 + 16 * t + 4 * g, ga.N - 4), ea);
+    }
+  }
   f32x4 acc[TN][MT];
   zero<MT, TN>(acc);
   stream_rows<MT, TN, ST, false, TILED>(ga.W, ga.N, ga.K, ga.A, ga.lda, ga.M, row0, kb + 128 * s0,
@@ -306,7 +328,10 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs ga, EpiArgs ea) {
       const int m = mt * 16 + r16;
       const int n = row0 + 16 * t + 4 * g;  // first of this lane's 4 rows
       const f32x4 v = ga.rs.ss ? acc[t][mt] * rinv[min(m, 16 * MT - 1)] : acc[t][mt];
-      if (m < ga.M && n < ga.N) epilogue4<EPI>(v, m, n, blockIdx.y, ea);
+      if (m < ga.M && n < ga.N) {
+        if constexpr (EPI == EPI_QKV_ROPE) epilogue4_qkv(v, m, n, cs4[t][mt], ea);
+        else epilogue4<EPI>(v, m, n, blockIdx.y, ea);
+      }
     }
 }
 
@@ -550,12 +575,40 @@ hipError_t launch_cfg(int epi, const GemmArgs &g, const EpiArgs &e, hipStream_t 
   return hipGetLastError();
 }
 
+template <int MT, int TN, int ST>
+hipError_t launch_partial(const GemmArgs &g, const EpiArgs &e, hipStream_t s) {
+  dim3 grid((g.N + 16 * TN - 1) / (16 * TN), g.splits), block(4 * 64);
+  hipLaunchKernelGGL((k_gemm<MT, TN, 4, ST, EPI_PARTIAL, true>), grid, block, 0, s, g, e);
+  return hipGetLastError();
+}
+
+// Busiest CU's 16-row tiles when N rows go out in units of 16 * tn rows, one
+// unit per workgroup and NUM_CUS workgroups per round.
+int tiles_per_cu(int N, int tn) {
+  const int units = (N + 16 * tn - 1) / (16 * tn);
+  return (units + NUM_CUS - 1) / NUM_CUS * tn;
+}
+
+// The plan fixes the K order (nw, splits, kslice); the launch shape below
+// does not change it. For one 16-row group of activations (the registers
+// allow it): a split of a residual GEMM loads a wave's 5 or 6 steps in one
+// batch, and a wide matrix goes out in 48-row units when that lowers the
+// busiest CU's share (12288 rows: 256 units of 48 instead of 384 of 32, which
+// leave half the CUs with two).
 template <int MT>
 hipError_t launch_mt(int epi, const GemmArgs &g, const EpiArgs &e, hipStream_t s) {
-  // configurations chosen by gemm_plan
-  if (g.tn == 1 && g.nw == 4 && g.st == 4) return launch_cfg<MT, 1, 4, 4>(epi, g, e, s);
-  if (g.tn == 2 && g.nw == 4 && g.st == 4) return launch_cfg<MT, 2, 4, 4>(epi, g, e, s);
-  return hipErrorInvalidValue;
+  if (g.nw != 4 || g.st != 4 || (g.tn != 1 && g.tn != 2)) return hipErrorInvalidValue;
+  if constexpr (MT == 1) {
+    if (epi == EPI_PARTIAL && g.tn == 1) {
+      const int per_wave = ((g.kslice + 127) / 128 + 3) / 4;
+      if (per_wave == 6) return launch_partial<1, 1, 6>(g, e, s);
+      if (per_wave == 5) return launch_partial<1, 1, 5>(g, e, s);
+    }
+    if (epi != EPI_PARTIAL && g.tn == 2 && tiles_per_cu(g.N, 3) < tiles_per_cu(g.N, 2))
+      return launch_cfg<MT, 3, 4, 4>(epi, g, e, s);
+  }
+  if (g.tn == 1) return launch_cfg<MT, 1, 4, 4>(epi, g, e, s);
+  return launch_cfg<MT, 2, 4, 4>(epi, g, e, s);
 }
 
 }  // namespace
