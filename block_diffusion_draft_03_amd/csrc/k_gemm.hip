@@ -403,7 +403,10 @@ __global__ __launch_bounds__(256) void k_resid_norm(ResidNormArgs a) {
 // wave_id + total_waves, ... over the full K and keeps, per lane, a running
 // (max, argmax, sum exp) of its activation row over the vocab entries it sees
 // (masked entries skipped). Lanes, then the workgroup's waves, are merged in
-// a fixed order; one partial per workgroup and row is written.
+// a fixed order; one partial per workgroup and row is written. Wave ids run
+// over the workgroups first (wave w of workgroup b is w * workgroups + b), so
+// the units that do not divide evenly are dealt one per CU: every CU streams
+// within one unit of the same bytes, and a CU's rate bounds the kernel.
 template <int MT, int TN, int ST, bool WFP8, bool TILED = false>
 __global__ __launch_bounds__(256) void k_lm_head(LmArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
@@ -428,7 +431,7 @@ __global__ __launch_bounds__(256) void k_lm_head(LmArgs a) {
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) rsc[mt] = a.rs.ss ? rinv[min(mt * 16 + r16, 16 * MT - 1)] : 1.0f;
   const int nw = gridDim.x * 4;
-  for (int u = blockIdx.x * 4 + wave; u < units; u += nw) {
+  for (int u = wave * gridDim.x + blockIdx.x; u < units; u += nw) {
     const int row0 = u * UNIT;
     f32x4 acc[TN][MT];
     zero<MT, TN>(acc);
