@@ -511,10 +511,12 @@ __device__ __forceinline__ float wave_reduce_dpp(float x) {
 // Merge the splits of one query row per wave: lane s reads split s's (max,
 // sum); the weights exp2(m_s - M) are read lane by lane and every lane
 // accumulates its dimensions (two adjacent ones for head_dim 128) over the
-// splits in order.
+// splits in order. The O parts of the first PRE splits are loaded together
+// with the (max, sum) pairs, before the weights are known.
 template <int D>
 __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a, int n_seq) {
   constexpr int DPL = D >= 64 ? D / 64 : 1;  // dims per lane
+  constexpr int PRE = 16;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int R = a.rep * a.gamma;
   const int row = blockIdx.x * 4 + wave;  // (s, g, q)
@@ -523,6 +525,25 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a, int n_seq) {
   const int nsplit = a.seq[s].nsplit;  // <= 64
   if (nsplit == 1) return;             // written by the attention kernel
   const size_t base = (size_t)g * a.n_split + a.seq[s].split0;
+  const bool active = D >= 64 || lane < D;
+  // O part of split c at this lane's dimensions: lane, lane + 64, ... (two
+  // adjacent ones, 2 lane and 2 lane + 1, for head_dim 128)
+  auto o_at = [&](int c) {
+    const uint16_t *op = a.o_part + ((base + c) * R + q) * D;
+    if constexpr (D == 128) return *(const uint32_t *)(op + 2 * lane);
+    else return active ? (uint32_t)op[lane] : 0u;
+  };
+  uint32_t pre[PRE][DPL == 2 ? 1 : DPL];
+#pragma unroll
+  for (int c = 0; c < PRE; ++c) {
+    if constexpr (D == 128) {
+      pre[c][0] = c < nsplit ? o_at(c) : 0u;
+    } else {
+#pragma unroll
+      for (int i = 0; i < DPL; ++i)
+        pre[c][i] = (c < nsplit && active) ? (uint32_t)a.o_part[((base + c) * R + q) * D + lane + 64 * i] : 0u;
+    }
+  }
   float m = -__builtin_huge_valf(), l = 0.0f;
   if (lane < nsplit) {
     m = a.ml_part[((base + lane) * R + q) * 2];
@@ -535,10 +556,18 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a, int n_seq) {
   uint16_t *out = a.out + (size_t)(s * a.gamma + j) * a.out_ld + hq * D;
   if constexpr (D == 128) {
     float acc0 = 0.0f, acc1 = 0.0f;
+#pragma unroll
+    for (int c = 0; c < PRE; ++c) {
+      if (c < nsplit) {
+        const float wc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), c));
+        acc0 += wc * __uint_as_float(pre[c][0] << 16);
+        acc1 += wc * __uint_as_float(pre[c][0] & 0xFFFF0000u);
+      }
+    }
 #pragma unroll 16
-    for (int c = 0; c < nsplit; ++c) {
+    for (int c = PRE; c < nsplit; ++c) {
       const float wc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), c));
-      const uint32_t pr = *(const uint32_t *)(a.o_part + ((base + c) * R + q) * D + 2 * lane);
+      const uint32_t pr = o_at(c);
       acc0 += wc * __uint_as_float(pr << 16);
       acc1 += wc * __uint_as_float(pr & 0xFFFF0000u);
     }
@@ -547,9 +576,16 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a, int n_seq) {
     float acc[DPL];
 #pragma unroll
     for (int i = 0; i < DPL; ++i) acc[i] = 0.0f;
-    const bool active = D >= 64 || lane < D;
+#pragma unroll
+    for (int c = 0; c < PRE; ++c) {
+      if (c < nsplit) {
+        const float wc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), c));
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) acc[i] += wc * __uint_as_float(pre[c][i] << 16);
+      }
+    }
 #pragma unroll 16
-    for (int c = 0; c < nsplit; ++c) {
+    for (int c = PRE; c < nsplit; ++c) {
       const float wc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), c));
       const uint16_t *op = a.o_part + ((base + c) * R + q) * D;
 #pragma unroll
