@@ -323,7 +323,7 @@ int build_impl(dflash_head *H, const dflash_weights *w, hipStream_t st) {
   TRY(H->alloc(&H->part, (size_t)max_splits * std::max({M, (size_t)GEMM_MAX_ROWS, pre_rows}) * h));
   const size_t R = (size_t)g.rep * g.gamma;
   {
-    // partial slots: the split rule of attn_plan never needs more
+    // partial slots: the propose split rule never needs more
     const int max_tiles = (std::min(g.W, H->cfg.max_seq_len) + 15 + 31) / 32 + 1;
     const int per_seq = std::min(ATTN_MAX_SPLITS, (max_tiles + attn_max_tiles_per_split() - 1) / attn_max_tiles_per_split() + 1);
     H->attn_slots = std::max({ATTN_TARGET_WGS * 2, g.max_batch * g.n_kv * per_seq, g.n_kv * ATTN_MAX_SPLITS});
@@ -512,11 +512,14 @@ int propose_impl(dflash_head *H, dflash_state *const *states, int n, const uint3
   aa.out = H->attn;
   aa.out_ld = g.q_dim;
   {
-    // ctx tiles of 32 positions from the block-aligned window start. Every
-    // sequence gets ceil(T / tps) splits of at most tps tiles (at least one,
-    // which also takes the block tile); tps is the smallest that keeps the
-    // launch within ATTN_TARGET_WGS workgroups (one round, two per CU), no
-    // smaller than a sequence's preferred bound of ATTN_PREF_SPLITS splits.
+    // ctx tiles of 32 positions from the block-aligned window start. The
+    // last split of a sequence also takes the block tile, which counts as one
+    // more tile: a sequence with T ctx tiles gets (T + tps) / tps splits of at
+    // most tps units, so the last one is no longer than the others (at T = 32,
+    // tps = 2: sixteen splits of two ctx tiles and one of the block tile). tps
+    // is the smallest that keeps the launch within ATTN_TARGET_WGS workgroups
+    // (one round, two per CU), no smaller than a sequence's preferred bound of
+    // ATTN_PREF_SPLITS splits.
     std::vector<int> T(n);
     int max_T = 0;
     for (int i = 0; i < n; ++i) {
@@ -529,22 +532,23 @@ int propose_impl(dflash_head *H, dflash_state *const *states, int n, const uint3
       max_T = std::max(max_T, T[i]);
     }
     const int max_tps = attn_max_tiles_per_split();
+    auto splits_of = [](int t, int tps) { return (t + tps) / tps; };
     auto flat_splits = [&](int tps) {
       long f = 0;
-      for (int i = 0; i < n; ++i) f += std::max(1, (T[i] + tps - 1) / tps);
+      for (int i = 0; i < n; ++i) f += splits_of(T[i], tps);
       return f;
     };
     const long cap = std::min<long>(ATTN_MAX_FLAT, H->attn_slots / g.n_kv);
     int tps = std::max(1, (max_T + ATTN_PREF_SPLITS - 1) / ATTN_PREF_SPLITS);
-    tps = std::max(tps, (max_T + ATTN_MAX_SPLITS - 1) / ATTN_MAX_SPLITS);
+    tps = std::max(tps, (max_T + ATTN_MAX_SPLITS) / ATTN_MAX_SPLITS);
     while (tps < max_tps && (flat_splits(tps) * g.n_kv > ATTN_TARGET_WGS || flat_splits(tps) > cap)) ++tps;
-    if (tps > max_tps || flat_splits(tps) > cap || (max_T + tps - 1) / tps > ATTN_MAX_SPLITS)
+    if (tps > max_tps || flat_splits(tps) > cap || splits_of(max_T, tps) > ATTN_MAX_SPLITS)
       return set_err(DFLASH_E_INVALID, "context window too long for the attention splits");
     aa.tps = tps;
     int f = 0;
     for (int i = 0; i < n; ++i) {
       aa.seq[i].split0 = f;
-      aa.seq[i].nsplit = std::max(1, (T[i] + tps - 1) / tps);
+      aa.seq[i].nsplit = splits_of(T[i], tps);
       for (int c = 0; c < aa.seq[i].nsplit; ++c) aa.split_seq[f + c] = (uint8_t)i;
       f += aa.seq[i].nsplit;
     }
