@@ -44,7 +44,7 @@ constexpr int KT = 32;          // keys per tile
 constexpr int QT = 1;           // 16-row query tiles per wave
 constexpr int NWAVE = 8 / QT;   // waves per workgroup (128 query rows)
 constexpr int NTHR = 64 * NWAVE;
-constexpr int MAX_TPS = 32;     // ctx tiles per split (2 KV blocks each)
+constexpr int MAX_TPS = 64;     // ctx tiles per split (2 KV blocks each)
 
 typedef __attribute__((address_space(3))) uint4 lds_uint4;
 
