@@ -8,5 +8,5 @@ only for device memory and streams. Build the library first with
 it is missing.
 """
 from .binding import (  # noqa: F401
-    DflashError, Head, State, load_library, library_path, EXPORTED_SYMBOLS,
+    DflashError, Head, State, load_library, library_path, yarn_inv_freq, EXPORTED_SYMBOLS,
 )

@@ -22,7 +22,8 @@ EXPORTED_SYMBOLS = (
     "dflash_build", "dflash_destroy", "dflash_block_gamma", "dflash_propose_batch_max",
     "dflash_state_create", "dflash_state_free", "dflash_state_ctx_len", "dflash_precompute_ctx_kv",
     "dflash_propose", "dflash_propose_batch", "dflash_after_verify", "dflash_state_read_kv",
-    "dflash_read_lm_head_fp8", "dflash_timing_enable", "dflash_timing_read", "dflash_last_error",
+    "dflash_read_lm_head_fp8", "dflash_yarn_inv_freq", "dflash_timing_enable", "dflash_timing_read",
+    "dflash_last_error",
 )
 PHASE_LM_HEAD, PHASE_PROPOSE, PHASE_PRECOMPUTE = 0, 1, 2
 
@@ -85,6 +86,7 @@ def load_library(path=None):
         "dflash_after_verify": ([vp, vp, i32], C.c_int),
         "dflash_state_read_kv": ([vp, vp, i32, i32, i32, vp, vp, u64], C.c_int),
         "dflash_read_lm_head_fp8": ([vp, vp, vp, u64], C.c_int),
+        "dflash_yarn_inv_freq": ([i32, C.c_float, C.c_float, C.c_float, C.c_float, i32, vp], C.c_int),
         "dflash_timing_enable": ([vp, C.c_int], C.c_int),
         "dflash_timing_read": ([vp, i32, C.POINTER(C.c_double), C.POINTER(C.c_int64)], C.c_int),
         "dflash_last_error": ([], C.c_char_p),
@@ -141,12 +143,23 @@ class State:
             self.handle = None
 
 
+def yarn_inv_freq(head_dim, rope_theta, factor, beta_fast, beta_slow, original_max_positions):
+    """The library's YaRN-corrected RoPE table (f32 [head_dim / 2], host), to
+    pass to Head(..., inv_freq=...)."""
+    lib = load_library()
+    out = np.zeros(head_dim // 2, dtype=np.float32)
+    _check(lib, lib.dflash_yarn_inv_freq(int(head_dim), float(rope_theta), float(factor), float(beta_fast),
+                                         float(beta_slow), int(original_max_positions),
+                                         out.ctypes.data_as(C.c_void_p)))
+    return out
+
+
 class Head:
     """A built draft head. ``weights`` is the dict synth.make_weights returns
     (numpy arrays); they are uploaded, and the borrowed ones kept alive."""
 
     def __init__(self, geo, weights, kv_pool_blocks=1024, max_batch=1, max_seq_len=8192, stream=None,
-                 lm_head_fp8=None, lm_head_scale=None, device="cuda"):
+                 lm_head_fp8=None, lm_head_scale=None, inv_freq=None, device="cuda"):
         import torch
         self.lib = load_library()
         self.geo = geo
@@ -184,6 +197,13 @@ class Head:
         if geo.kv_dtype == "fp8":
             kvs = np.ascontiguousarray(weights["kv_scale"], dtype=np.float32)
             w.kv_scale = kvs.ctypes.data_as(C.c_void_p)
+        table = None
+        if inv_freq is not None:
+            # a host f32 [head_dim / 2] RoPE table (e.g. yarn_inv_freq) replaces the plain theta table
+            table = np.ascontiguousarray(inv_freq, dtype=np.float32)
+            if table.shape != (geo.head_dim // 2,):
+                raise ValueError(f"inv_freq must have head_dim / 2 = {geo.head_dim // 2} entries")
+            w.inv_freq = table.ctypes.data_as(C.c_void_p)
         w.layers = layers
         h = C.c_void_p()
         _check(self.lib, self.lib.dflash_build(C.byref(cfg), C.byref(w), _stream_handle(stream), C.byref(h)))

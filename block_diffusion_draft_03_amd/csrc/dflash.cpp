@@ -917,6 +917,14 @@ int dflash_state_read_kv(dflash_head *head, const dflash_state *st, int32_t laye
   return DFLASH_OK;
 }
 
+int dflash_yarn_inv_freq(int32_t head_dim, float rope_theta, float factor, float beta_fast, float beta_slow,
+                         int32_t original_max_positions, float *out) {
+  std::string err;
+  const int rc = yarn_inv_freq(head_dim, rope_theta, factor, beta_fast, beta_slow, original_max_positions, out, &err);
+  if (rc != DFLASH_OK) return set_err(rc, err);
+  return DFLASH_OK;
+}
+
 int dflash_timing_enable(dflash_head *head, int enable) {
   if (!head_ok(head)) return set_err(DFLASH_E_INVALID, "invalid head");
   std::lock_guard<std::mutex> lk(head->mu);

@@ -61,6 +61,12 @@ int32_t dfh_seq_blocks(void *seq, int32_t *out, int32_t cap) {
 }
 
 void dfh_seq_release(void *seq, void *pool) { seq_release((SeqRows *)seq, (BlockPool *)pool); }
+
+int dflash_yarn_inv_freq(int32_t head_dim, float rope_theta, float factor, float beta_fast, float beta_slow,
+                         int32_t original_max_positions, float *out) {
+  g_err.clear();
+  return yarn_inv_freq(head_dim, rope_theta, factor, beta_fast, beta_slow, original_max_positions, out, &g_err);
+}
 void dfh_seq_delete(void *seq) { delete (SeqRows *)seq; }
 
 }  // extern "C"

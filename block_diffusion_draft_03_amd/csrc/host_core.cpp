@@ -1,6 +1,7 @@
 // host_core.cpp - see host_core.hpp.
 #include "host_core.hpp"
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 
@@ -162,6 +163,37 @@ void seq_release(SeqRows *s, BlockPool *pool) {
   s->blocks.clear();
   s->ctx_len = 0;
   s->pending_base = 0;
+}
+
+// Pair i rotates at w_i = theta^(-2i/d); the fractional pair index whose
+// wavelength 2 pi / w fits `turns` times into the original context L is
+// d ln(L / (2 pi turns)) / (2 ln theta). Pairs up to floor(index(beta_fast))
+// keep w_i, pairs from ceil(index(beta_slow)) on take w_i / factor, and the
+// weight of the kept frequency falls linearly in i in between (YaRN's
+// "NTK-by-parts" interpolation over the pair index). Double precision,
+// rounded once to float.
+int yarn_inv_freq(int32_t head_dim, double theta, double factor, double beta_fast, double beta_slow,
+                  int32_t original_max, float *out, std::string *err) {
+  if (!out || head_dim < 2 || head_dim % 2 != 0 || !(theta > 1.0) || !(factor >= 1.0) || !(beta_slow > 0.0) ||
+      !(beta_fast > beta_slow) || original_max < 1) {
+    *err = "yarn_inv_freq: need an even head_dim >= 2, theta > 1, factor >= 1, beta_fast > beta_slow > 0, "
+           "original_max >= 1 and an output";
+    return DFLASH_E_INVALID;
+  }
+  const double d = head_dim;
+  auto pair_index = [&](double turns) {
+    return d * std::log((double)original_max / (turns * 2.0 * 3.14159265358979323846)) / (2.0 * std::log(theta));
+  };
+  const double lo = std::max(std::floor(pair_index(beta_fast)), 0.0);
+  double hi = std::min(std::ceil(pair_index(beta_slow)), d - 1.0);
+  if (hi == lo) hi += 0.001;
+  for (int32_t i = 0; i < head_dim / 2; ++i) {
+    const double w = std::pow(theta, -2.0 * i / d);
+    const double ramp = std::min(std::max((i - lo) / (hi - lo), 0.0), 1.0);
+    const double keep = 1.0 - ramp;
+    out[i] = (float)((w / factor) * (1.0 - keep) + w * keep);
+  }
+  return DFLASH_OK;
 }
 
 }  // namespace dflash

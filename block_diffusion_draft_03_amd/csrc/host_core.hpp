@@ -66,4 +66,8 @@ int seq_trim(SeqRows *s, int32_t a, std::string *err);
 // Give every block back to the pool.
 void seq_release(SeqRows *s, BlockPool *pool);
 
+// YaRN-corrected RoPE table (dflash_yarn_inv_freq): out[head_dim / 2].
+int yarn_inv_freq(int32_t head_dim, double theta, double factor, double beta_fast, double beta_slow,
+                  int32_t original_max, float *out, std::string *err);
+
 }  // namespace dflash

@@ -220,6 +220,21 @@ int dflash_state_read_kv(dflash_head *head, const dflash_state *st, int32_t laye
  * DFLASH_E_INVALID on a bf16 head. */
 int dflash_read_lm_head_fp8(dflash_head *head, void *codes_out, float *scale_out, uint64_t stream);
 
+/* YaRN-corrected RoPE table ([Head/atlas] field yarn_inv_freq: a
+ * precomputed f32 [head_dim/2] table from the drafter's rope_scaling, e.g.
+ * factor 64, beta_fast 32, beta_slow 1, original_max_position_embeddings
+ * 4096; [Head/metrale] field yarn_inv_freq). Host-only: writes head_dim / 2
+ * floats to caller-owned host memory `out`, to be passed as
+ * dflash_weights.inv_freq. Pair i keeps theta^(-2i/head_dim) when its
+ * wavelength fits more than beta_fast times into original_max_positions, is
+ * divided by `factor` when it fits fewer than beta_slow times, and blends
+ * linearly in i in between (YaRN's NTK-by-parts interpolation; no magnitude
+ * scaling). DFLASH_E_INVALID unless head_dim is even and >= 2, theta > 1,
+ * factor >= 1, beta_fast > beta_slow > 0, original_max_positions >= 1 and
+ * out is set. */
+int dflash_yarn_inv_freq(int32_t head_dim, float rope_theta, float factor, float beta_fast, float beta_slow,
+                         int32_t original_max_positions, float *out);
+
 /* Kernel timing for benchmarks. While enabled, each propose and precompute
  * call records HIP events on its own stream around: DFLASH_PHASE_LM_HEAD,
  * the LM-head stage-1 launches (the dominant weight stream);

@@ -16,6 +16,9 @@ Geometry is a plain mapping with the keys
     gamma mask_token_id num_target_layers target_hidden ctx_window
     rope_theta rms_eps kv_dtype lm_head_dtype
 
+and optionally ``inv_freq`` (a RoPE table, e.g. ``yarn_inv_freq``'s, used in
+place of the plain theta table).
+
 Weights are a mapping with ``fc hidden_norm norm embed lm_head`` and
 ``layers`` (a list of mappings with ``in_norm q k v o post_norm gate up
 down``), each a matrix in PyTorch Linear layout ``[out, in]`` or a gain
@@ -26,6 +29,8 @@ library routines, the explicit-loop twin in ``brute``); the composition of the
 steps is the reading stated in each docstring and is otherwise unpinned (the
 pages print no worked example).
 """
+import math
+
 import numpy as np
 
 from .numerics import E4M3_MAX, bf16_round, e4m3_decode, e4m3_encode, stored_to_f64
@@ -60,6 +65,47 @@ def rope_inv_freq(theta, rotary_dim):
     rope_scaling, which the synthetic workloads do not)."""
     i = np.arange(rotary_dim // 2, dtype=np.float64)
     return np.power(float(theta), -2.0 * i / rotary_dim)
+
+
+def yarn_inv_freq(theta, rotary_dim, factor, beta_fast, beta_slow, original_max):
+    """YaRN-corrected RoPE inverse frequencies, f32 [rotary_dim/2] widened to
+    float64 ([Head/atlas], field ``yarn_inv_freq``: a precomputed f32 table
+    of head_dim/2 entries, from the drafter's rope_scaling with factor 64,
+    beta_fast 32, beta_slow 1 and original_max_position_embeddings 4096;
+    [Head/metrale], field ``yarn_inv_freq``: YaRN-corrected when the config
+    has rope_scaling). The pages give the parameters, not the formula; the
+    reading taken is YaRN's "NTK-by-parts" interpolation (Peng et al.,
+    "YaRN: Efficient Context Window Extension of Large Language Models",
+    section 3.2) with its ramp laid over the pair index, the form a
+    rope_scaling block with those four keys configures:
+
+    * pair i rotates at w_i = theta^(-2i/d) (wavelength 2 pi / w_i); the
+      fractional pair index whose wavelength fits r times into the original
+      context L is i(r) = d ln(L / (2 pi r)) / (2 ln theta);
+    * pairs up to lo = floor(i(beta_fast)) (more than beta_fast turns over L)
+      keep w_i; pairs from hi = ceil(i(beta_slow)) on (fewer than beta_slow
+      turns) are interpolated to w_i / factor; in between the weight of the
+      unchanged frequency falls linearly in i from lo to hi (lo clamped to
+      >= 0, hi to <= d - 1, hi nudged by 0.001 when equal to lo);
+    * no magnitude scaling of cos / sin (the pages name none).
+
+    Computed in float64 and rounded once to float32 (the table's dtype)."""
+    d = int(rotary_dim)
+    theta = float(theta)
+    i = np.arange(d // 2, dtype=np.float64)
+    w = np.power(theta, -2.0 * i / d)
+
+    def pair_index(turns):
+        return d * math.log(original_max / (turns * 2.0 * math.pi)) / (2.0 * math.log(theta))
+
+    lo = max(math.floor(pair_index(beta_fast)), 0)
+    hi = min(math.ceil(pair_index(beta_slow)), d - 1)
+    if hi == lo:
+        hi += 0.001
+    ramp = np.clip((i - lo) / (hi - lo), 0.0, 1.0)
+    keep = 1.0 - ramp  # weight of the unchanged frequency
+    table = (w / float(factor)) * (1.0 - keep) + w * keep
+    return table.astype(np.float32).astype(np.float64)
 
 
 def rope(x, positions, inv_freq):
@@ -206,7 +252,9 @@ class OracleHead:
         self.kv_fp8 = g.get("kv_dtype", "bf16") == "fp8"
         self.head_fp8 = g.get("lm_head_dtype", "bf16") == "fp8"
         fc_in = int(g["num_target_layers"]) * int(g["target_hidden"])
-        self.inv_freq = rope_inv_freq(g["rope_theta"], self.d)
+        # a given table (e.g. yarn_inv_freq) replaces the plain one
+        self.inv_freq = (np.asarray(g["inv_freq"], dtype=np.float64) if g.get("inv_freq") is not None
+                         else rope_inv_freq(g["rope_theta"], self.d))
 
         w = weights
         self.fc = stored_to_f64(w["fc"])

@@ -39,7 +39,12 @@ CASES = {
     # a vocabulary that the tiled LM head's 256-row blocks do not divide: the
     # batch takes the weight-streaming LM head in 64-row chunks
     "d64_vocab2176": replace(MID, num_q_heads=4, head_dim=64, vocab=2176, mask_token_id=2175),
+    # the YaRN-corrected RoPE table of the drafter's rope_scaling (factor 64, beta_fast 32,
+    # beta_slow 1, 4096 original positions): at head_dim 64 and theta 1e6 pairs 0-6 keep their
+    # frequency, 7-15 blend, 16-31 are divided by 64
+    "d64_yarn": replace(MID, num_q_heads=4, head_dim=64),
 }
+YARN = {"d64_yarn": (64.0, 32.0, 1.0, 4096)}
 LENS = [0, 17, 64, 300, 129, 45]
 
 
@@ -57,13 +62,19 @@ def gpu_ready():
 
 @pytest.mark.parametrize("case", list(CASES))
 def test_mid_batch_and_single_match_oracle(case):
-    from block_diffusion_draft_03_amd import Head
+    from block_diffusion_draft_03_amd import Head, yarn_inv_freq
+    from oracle.dflash import yarn_inv_freq as oracle_yarn
     geo = CASES[case]
     fp8 = geo.lm_head_dtype == "fp8"
     w = synth.make_weights(geo)
     say(f"[build] mid {case}")
-    head = Head(geo, w, kv_pool_blocks=160, max_batch=len(LENS), max_seq_len=1024)
-    orc = OracleHead(geo.as_dict(), w)
+    table, ogeo = None, geo.as_dict()
+    if case in YARN:
+        table = yarn_inv_freq(geo.head_dim, geo.rope_theta, *YARN[case])
+        ogeo["inv_freq"] = oracle_yarn(geo.rope_theta, geo.head_dim, *YARN[case])
+        assert np.allclose(table.astype(np.float64), ogeo["inv_freq"], rtol=2.0 ** -23, atol=0.0)
+    head = Head(geo, w, kv_pool_blocks=160, max_batch=len(LENS), max_seq_len=1024, inv_freq=table)
+    orc = OracleHead(ogeo, w)
     states, ostates = [], []
     for i, n in enumerate(LENS):
         st = head.state_create()

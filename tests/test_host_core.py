@@ -40,6 +40,7 @@ def host():
     lib.dfh_seq_blocks.argtypes = [vp, vp, C.c_int32]
     lib.dfh_seq_release.argtypes = [vp, vp]
     lib.dfh_seq_delete.argtypes = [vp]
+    lib.dflash_yarn_inv_freq.argtypes = [C.c_int32, C.c_float, C.c_float, C.c_float, C.c_float, C.c_int32, vp]
     return lib
 
 
@@ -175,3 +176,21 @@ def test_hip_library_exports_every_declared_symbol():
     for name in declared:
         assert hasattr(lib, name), name
     assert lib.dflash_last_error() == b""
+
+
+@pytest.mark.parametrize("theta,d", [(1e7, 128), (1e6, 64), (1e6, 16)])
+def test_yarn_table_matches_oracle(host, theta, d):
+    """The library's YaRN table (host code, the same in libdflash.so) equals
+    the oracle's f32 table to one float32 rounding step; bad arguments are
+    refused."""
+    from oracle.dflash import yarn_inv_freq
+    out = np.zeros(d // 2, dtype=np.float32)
+    assert host.dflash_yarn_inv_freq(d, theta, 64.0, 32.0, 1.0, 4096, out.ctypes.data_as(C.c_void_p)) == OK
+    ref = yarn_inv_freq(theta, d, 64.0, 32.0, 1.0, 4096)
+    assert np.allclose(out.astype(np.float64), ref, rtol=2.0 ** -23, atol=0.0)
+    for args in ((d + 1, theta, 64.0, 32.0, 1.0, 4096), (d, 1.0, 64.0, 32.0, 1.0, 4096),
+                 (d, theta, 0.5, 32.0, 1.0, 4096), (d, theta, 64.0, 1.0, 32.0, 4096),
+                 (d, theta, 64.0, 32.0, 1.0, 0)):
+        assert host.dflash_yarn_inv_freq(*args, out.ctypes.data_as(C.c_void_p)) == E_INVALID
+    assert host.dflash_yarn_inv_freq(d, theta, 64.0, 32.0, 1.0, 4096, None) == E_INVALID
+

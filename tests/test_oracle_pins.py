@@ -357,3 +357,27 @@ def test_page_geometry_facts():
     kv = g.num_kv_heads * g.head_dim
     assert 2 * g.num_layers * kv == facts["fused_kv_rows"]["value"]
     assert g.num_target_layers * g.target_hidden == facts["fc_input_width"]["value"]
+
+
+@pytest.mark.parametrize("theta,d", [(1e7, 128), (1e6, 64), (1e6, 16)])
+def test_yarn_table_limits(theta, d):
+    """The YaRN table pinned by its limits rather than its formula: with
+    factor 1 it is the plain table; pairs whose wavelength fits more than
+    beta_fast times into the original context keep the plain frequency
+    exactly, pairs that fit fewer than beta_slow times are divided by the
+    factor exactly, the pairs between lie between the two and the table
+    falls monotonically. Each regime is present at these geometries."""
+    L, bf, bs, f = 4096, 32.0, 1.0, 64.0
+    plain64 = O.rope_inv_freq(theta, d)
+    plain = plain64.astype(np.float32).astype(np.float64)
+    assert np.allclose(O.yarn_inv_freq(theta, d, 1.0, bf, bs, L), plain, rtol=2.0 ** -23, atol=0.0)
+    y = O.yarn_inv_freq(theta, d, f, bf, bs, L)
+    turns = L / (2.0 * math.pi / plain64)  # how often each pair's wavelength fits into L
+    fast, slow = turns > bf, turns < bs
+    mid = ~fast & ~slow
+    assert fast.any() and slow.any() and mid.any()
+    assert np.array_equal(y[fast], plain[fast])
+    assert np.array_equal(y[slow], (plain64 / f).astype(np.float32).astype(np.float64)[slow])
+    assert np.all(y[mid] <= plain[mid]) and np.all(y[mid] >= (plain64 / f)[mid] * (1 - 2.0 ** -23))
+    assert np.all(np.diff(y) < 0)
+
