@@ -632,6 +632,7 @@ int propose_impl(dflash_head *H, dflash_state *const *states, int n, const uint3
   fa.M = M;
   fa.gamma = g.gamma;
   fa.num_drafts = num_drafts;
+  fa.shifted = g.shifted ? 1 : 0;
   fa.ids = ids;
   fa.conf = conf;
   fa.row_prob = row_prob;

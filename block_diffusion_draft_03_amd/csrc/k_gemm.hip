@@ -489,9 +489,10 @@ __global__ __launch_bounds__(256) void k_lm_head(LmArgs a) {
 }
 
 // Stage 2: one workgroup per block row merges the row's P partials (fixed
-// tree order) and writes its id and top-1 probability; the last row of a
-// sequence to finish (atomic ticket) writes the chain confidence
-// min(p1) over rows 1..num_drafts.
+// tree order) and writes its id and top-1 probability at the row's entry
+// (row j at entry j, or at (j + 1) % gamma with the shifted-row convention);
+// the last row of a sequence to finish (atomic ticket) writes the chain
+// confidence min(p1) over entries 1..num_drafts.
 __global__ __launch_bounds__(256) void k_lm_finish(LmFinishArgs a) {
   __shared__ float s_mx[256], s_se[256];
   __shared__ uint32_t s_idx[256];
@@ -544,9 +545,11 @@ __global__ __launch_bounds__(256) void k_lm_finish(LmFinishArgs a) {
   if (threadIdx.x == 0) {
     const bool none = s_mx[0] == -__builtin_huge_valf();
     const float p1 = none ? 0.0f : 1.0f / s_se[0];
-    a.ids[m] = none ? DFLASH_NO_TOKEN : s_idx[0];
-    if (a.row_prob) a.row_prob[m] = p1;
-    a.p1[m] = p1;
+    const int j = m - seq * a.gamma;
+    const int e = seq * a.gamma + (a.shifted ? (j + 1) % a.gamma : j);  // entry of row j
+    a.ids[e] = none ? DFLASH_NO_TOKEN : s_idx[0];
+    if (a.row_prob) a.row_prob[e] = p1;
+    a.p1[e] = p1;
     __threadfence();
     const int prev = atomicAdd(&a.counters[seq], 1);
     if (prev == a.gamma - 1) {

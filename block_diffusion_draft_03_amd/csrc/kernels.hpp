@@ -139,6 +139,7 @@ struct LmFinishArgs {
   const float *part_mx, *part_se;
   const uint32_t *part_idx;
   int P, M, gamma, num_drafts;
+  int shifted;     // row j goes to entry (j + 1) % gamma of ids, row_prob and p1
   uint32_t *ids;
   float *conf, *row_prob;
   float *p1;       // [M] scratch: top-1 probability of every row

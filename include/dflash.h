@@ -80,6 +80,11 @@ typedef struct {
   dflash_dtype weight_dtype;  /* F32 or BF16: dtype of the drafter tensors given at build */
   dflash_dtype lm_head_dtype; /* BF16, or FP8_E4M3 (a mirror is built unless one is given) */
   dflash_dtype kv_dtype;      /* BF16, or FP8_E4M3 with per-(layer, K|V, kv head) scales */
+  int32_t shifted_rows;       /* draft-row convention ([Head/atlas] field shifted_rows): 0, block row j is the
+                                 draft for position + j; 1, block row j's output is the token at position
+                                 + j + 1, so ids and row_prob come out rotated right by one (entry j + 1
+                                 holds row j, entry 0 the last row) and index j is position + j's draft
+                                 either way; the chain confidence is the min over entries 1..num_drafts */
 } dflash_config;
 
 /* One drafter layer's tensors: device pointers in weight_dtype, matrices in

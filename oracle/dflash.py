@@ -448,7 +448,7 @@ class OracleHead:
         if not 1 <= num_drafts <= self.gamma - 1:
             raise ValueError("num_drafts must be in [1, gamma - 1]")
         lg = self.forward_block(state, last_token, position)
-        return select(lg, bitmask, num_drafts)
+        return select(lg, bitmask, num_drafts, shifted=bool(self.geo.get("shifted_rows", 0)))
 
     def propose_batch(self, states, last_tokens, positions, num_drafts, bitmasks=None):
         """Batched propose: by definition the per-sequence result for each
@@ -472,11 +472,18 @@ def apply_bitmask(logits, bitmask):
     return np.where(allowed[None, :], logits, -np.inf)
 
 
-def select(logits, bitmask, num_drafts):
+def select(logits, bitmask, num_drafts, shifted=False):
     """Per-row argmax (ties to the lowest id), top-1 softmax probability
     p1 = 1 / sum_v exp(l_v - max l), and chain confidence = min p1 over the
-    draft rows 1..num_drafts ([Head/atlas], ``last_confidence``). A row with
-    every token masked gets id 0xFFFFFFFF and p1 = 0 (reading)."""
+    draft entries 1..num_drafts ([Head/atlas], ``last_confidence``). A row
+    with every token masked gets id 0xFFFFFFFF and p1 = 0 (reading).
+
+    Entry j of ``ids`` / ``row_prob`` is the draft for position + j. With the
+    z-lab convention that is row j; with the shifted-row convention
+    ([Head/atlas] and [Head/metrale], field ``shifted_rows``: row j's output is
+    the token at position j + 1, and the draft vector is rotated right by one)
+    entry j holds row j - 1 and entry 0 the last row. ``row_of_entry`` says
+    which row each entry holds."""
     lg = logits if bitmask is None else apply_bitmask(logits, bitmask)
     R = lg.shape[0]
     ids = np.empty(R, dtype=np.uint32)
@@ -490,8 +497,12 @@ def select(logits, bitmask, num_drafts):
             continue
         ids[j] = np.flatnonzero(row == mx)[0]
         p1[j] = 1.0 / np.sum(np.exp(row - mx))
+    row_of_entry = np.arange(R)
+    if shifted:
+        row_of_entry = np.roll(row_of_entry, 1)
+        ids, p1 = ids[row_of_entry], p1[row_of_entry]
     conf = float(p1[1:1 + num_drafts].min())
-    return {"ids": ids, "row_prob": p1, "conf": conf, "logits": logits}
+    return {"ids": ids, "row_prob": p1, "conf": conf, "logits": logits, "row_of_entry": row_of_entry}
 
 
 def top2_margin(logits, bitmask=None):

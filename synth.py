@@ -52,6 +52,7 @@ class Geometry:
     weight_dtype: str = "bf16"    # "f32" | "bf16"
     lm_head_dtype: str = "bf16"   # "bf16" | "fp8"
     kv_dtype: str = "bf16"        # "bf16" | "fp8"
+    shifted_rows: int = 0         # draft-row convention: 0 z-lab, 1 shifted
 
     def as_dict(self):
         return asdict(self)

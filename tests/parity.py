@@ -3,7 +3,9 @@
 * logits: per row, max_v |l_gpu - l_ref| <= tol * max_v |l_ref| (tol 2e-2 for
   a bf16 LM head, 6e-2 for an FP8 head);
 * ids: equal on every row whose oracle top-2 margin (on masked logits) is
-  larger than 0.05; a row the mask empties must be DFLASH_NO_TOKEN on both;
+  larger than 0.05; a row the mask empties must be DFLASH_NO_TOKEN on both
+  (ids and probabilities are compared entry by entry, each entry against the
+  row the draft-row convention puts there);
 * confidence and every row's top-1 probability within 1e-2 absolute.
 """
 import numpy as np
@@ -32,6 +34,8 @@ def check_propose(gpu, ref, bitmask=None, logit_tol=2e-2, label=""):
         scale = np.abs(lr).max(axis=1)
         bad = err > logit_tol * scale
         assert not bad.any(), f"{label} logits: rel err {(err / scale).max():.3e} > {logit_tol}"
+    # ids and row_prob are per entry; entry j holds row row_of_entry[j]
+    lr = lr[ref["row_of_entry"]] if "row_of_entry" in ref else lr
     empty = ref["ids"] == NO_TOKEN
     assert np.array_equal(ids[empty], ref["ids"][empty]), f"{label} emptied rows"
     with np.errstate(invalid="ignore"):

@@ -135,6 +135,32 @@ def test_tiny_trim_equals_recompute_bit_exact(tiny):
         sb.free()
 
 
+def test_tiny_shifted_rows_match_oracle():
+    """The shifted-row convention: against the oracle with the same
+    convention, and bit for bit the z-lab head's ids and probabilities
+    rotated right by one (same logits)."""
+    geo = synth.TINY
+    w = synth.make_weights(geo)
+    stack = synth.make_stack(geo, 32)
+    res = {}
+    for sh in (0, 1):
+        g = replace(geo, shifted_rows=sh)
+        head = build(g, w)
+        orc = OracleHead(g.as_dict(), w)
+        st, os_ = head.state_create(), orc.new_state()
+        head.precompute([st], [32], stack)
+        orc.precompute(os_, stack)
+        say(f"[case] tiny shifted_rows={sh}")
+        r = head.propose(st, 9, 32, 2, logits=True)
+        torch.cuda.synchronize()
+        check_propose(r, orc.propose(os_, 9, 32, 2), label=f"shifted={sh}")
+        res[sh] = {k: r[k].cpu().numpy() for k in ("ids", "row_prob", "logits")}
+        head.destroy()
+    assert np.array_equal(res[1]["logits"], res[0]["logits"])
+    assert np.array_equal(res[1]["ids"], np.roll(res[0]["ids"], 1))
+    assert np.array_equal(res[1]["row_prob"], np.roll(res[0]["row_prob"], 1))
+
+
 def test_tiny_block_permutation_bit_exact(tiny):
     geo, w, head, orc = tiny
     stack = synth.make_stack(geo, 40, tag=31)

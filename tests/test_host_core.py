@@ -66,7 +66,7 @@ def test_valid_configs(host):
     ("gamma", 1), ("gamma", 65), ("vocab", 1), ("mask_token_id", 248320), ("ctx_window", -1),
     ("kv_block_size", 32), ("kv_pool_blocks", 0), ("max_batch", 0), ("max_batch", 65), ("max_seq_len", 0),
     ("rope_theta", 0.5), ("rms_eps", -1.0), ("weight_dtype", 2), ("lm_head_dtype", 0), ("kv_dtype", 0),
-    ("target_hidden", 0), ("gamma", 32)])
+    ("target_hidden", 0), ("gamma", 32), ("shifted_rows", 2), ("shifted_rows", -1)])
 def test_invalid_configs(host, field, value):
     # gamma 32 with 8 query heads per kv head gives 256 query rows per kv head
     cfg = make_cfg(**{field: value})

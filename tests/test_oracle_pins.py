@@ -381,3 +381,25 @@ def test_yarn_table_limits(theta, d):
     assert np.all(y[mid] <= plain[mid]) and np.all(y[mid] >= (plain64 / f)[mid] * (1 - 2.0 ** -23))
     assert np.all(np.diff(y) < 0)
 
+
+def test_shifted_rows_read_out():
+    """The shifted-row convention changes only the read-out: the block's
+    logits are the same, entry 1 (the first draft) is row 0's argmax, entry 0
+    holds the last row, and the chain confidence is the least top-1 softmax
+    probability (scipy) of rows 0..num_drafts-1."""
+    from scipy.special import softmax
+    geo, w, stack = tiny_case()
+    out = {}
+    for sh in (0, 1):
+        g = dict(geo.as_dict(), shifted_rows=sh)
+        orc = O.OracleHead(g, w)
+        st = orc.new_state()
+        orc.precompute(st, stack)
+        out[sh] = orc.propose(st, 7, st.ctx_len, 2)
+    lg = out[0]["logits"]
+    assert np.array_equal(out[1]["logits"], lg)
+    assert out[1]["ids"][1] == int(np.argmax(lg[0])) and out[1]["ids"][0] == int(np.argmax(lg[-1]))
+    p1 = softmax(lg, axis=1).max(axis=1)
+    assert math.isclose(out[1]["conf"], float(p1[0:2].min()), rel_tol=1e-12)
+    assert math.isclose(out[0]["conf"], float(p1[1:3].min()), rel_tol=1e-12)
+
