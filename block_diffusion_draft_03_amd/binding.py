@@ -21,7 +21,8 @@ INT64_MAX = (1 << 63) - 1
 EXPORTED_SYMBOLS = (
     "dflash_build", "dflash_destroy", "dflash_block_gamma", "dflash_propose_batch_max",
     "dflash_state_create", "dflash_state_free", "dflash_state_ctx_len", "dflash_precompute_ctx_kv",
-    "dflash_propose", "dflash_propose_batch", "dflash_after_verify", "dflash_state_read_kv",
+    "dflash_propose", "dflash_propose_batch", "dflash_after_verify", "dflash_take_kv", "dflash_install_kv",
+    "dflash_free_kv", "dflash_state_read_kv",
     "dflash_read_lm_head_fp8", "dflash_yarn_inv_freq", "dflash_timing_enable", "dflash_timing_read",
     "dflash_last_error",
 )
@@ -85,6 +86,9 @@ def load_library(path=None):
         "dflash_propose": ([vp, vp, u32, i64, i32, vp, vp, vp, vp, vp, u64], C.c_int),
         "dflash_propose_batch": ([vp, vp, i32, vp, vp, i32, vp, vp, vp, vp, vp, u64], C.c_int),
         "dflash_after_verify": ([vp, vp, i32], C.c_int),
+        "dflash_take_kv": ([vp, vp, vp, i32, C.POINTER(i32), C.POINTER(i32), C.POINTER(i64)], C.c_int),
+        "dflash_install_kv": ([vp, vp, vp, i32, i32, i64], C.c_int),
+        "dflash_free_kv": ([vp, vp, i32], C.c_int),
         "dflash_state_read_kv": ([vp, vp, i32, i32, i32, vp, vp, u64], C.c_int),
         "dflash_read_lm_head_fp8": ([vp, vp, vp, u64], C.c_int),
         "dflash_yarn_inv_freq": ([i32, C.c_float, C.c_float, C.c_float, C.c_float, i32, vp], C.c_int),
@@ -301,6 +305,33 @@ class Head:
         _check(self.lib, self.lib.dflash_read_lm_head_fp8(self.handle, _ptr(codes), _ptr(scale),
                                                           _stream_handle(stream)))
         return codes, scale
+
+    def take_kv(self, state):
+        """Move the state's KV blocks out (carry to a later turn): (blocks
+        int32 array, rows, last_pair_key), or None when there is nothing to
+        carry."""
+        n, rows, key = C.c_int32(), C.c_int32(), C.c_int64()
+        cap = 1
+        while True:
+            buf = np.zeros(cap, dtype=np.int32)
+            rc = self.lib.dflash_take_kv(self.handle, state.handle, buf.ctypes.data_as(C.c_void_p), cap,
+                                         C.byref(n), C.byref(rows), C.byref(key))
+            if rc == 0 or n.value <= cap:
+                _check(self.lib, rc)
+                break
+            cap = n.value  # too small: retry with the count the library asked for
+        if n.value == 0:
+            return None
+        return buf[:n.value].copy(), rows.value, key.value
+
+    def install_kv(self, state, blocks, rows, last_pair_key=-1):
+        b = np.ascontiguousarray(blocks, dtype=np.int32)
+        _check(self.lib, self.lib.dflash_install_kv(self.handle, state.handle, b.ctypes.data_as(C.c_void_p), len(b),
+                                                    int(rows), int(last_pair_key)))
+
+    def free_kv(self, blocks):
+        b = np.ascontiguousarray(blocks, dtype=np.int32)
+        _check(self.lib, self.lib.dflash_free_kv(self.handle, b.ctypes.data_as(C.c_void_p), len(b)))
 
     def timing_enable(self, on=True):
         _check(self.lib, self.lib.dflash_timing_enable(self.handle, 1 if on else 0))

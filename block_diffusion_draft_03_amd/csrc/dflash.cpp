@@ -52,6 +52,7 @@ struct dflash_state {
   int32_t *h_bt = nullptr;   // pinned host copy (entries written once, then uploaded)
   int32_t cap_blocks = 0;
   int32_t uploaded = 0;      // leading entries of d_bt already uploaded
+  int64_t pair_key = -1;     // opaque key carried with installed blocks (-1: none)
 };
 
 struct dflash_head {
@@ -901,6 +902,72 @@ int dflash_after_verify(dflash_head *head, dflash_state *st, int32_t num_accepte
   std::string err;
   int rc = seq_trim(&st->rows, num_accepted, &err);
   return rc == DFLASH_OK ? rc : set_err(rc, err);
+}
+
+// Whether a live state of the head holds block b.
+static bool block_owned(const dflash_head *head, int32_t b) {
+  for (const dflash_state *s : head->states)
+    for (int32_t x : s->rows.blocks)
+      if (x == b) return true;
+  return false;
+}
+
+int dflash_take_kv(dflash_head *head, dflash_state *st, int32_t *blocks_out, int32_t cap, int32_t *n_blocks,
+                   int32_t *rows, int64_t *last_pair_key) {
+  if (!head_ok(head)) return set_err(DFLASH_E_INVALID, "invalid head");
+  std::lock_guard<std::mutex> lk(head->mu);
+  if (!state_ok(head, st)) return set_err(DFLASH_E_INVALID, "not a live state of this head");
+  if (!n_blocks || !rows || !last_pair_key) return set_err(DFLASH_E_INVALID, "n_blocks, rows and last_pair_key are required");
+  const int32_t nb = (int32_t)st->rows.blocks.size();
+  *n_blocks = nb;
+  *rows = 0;
+  *last_pair_key = -1;
+  if (nb == 0) return DFLASH_OK;  // nothing to carry
+  if (!blocks_out || cap < nb) return set_err(DFLASH_E_INVALID, "blocks_out holds fewer than the state's blocks");
+  HIP_TRY(hipDeviceSynchronize());  // no launch still reads the state's block table
+  std::vector<int32_t> taken;
+  seq_take(&st->rows, &taken, rows);
+  std::copy(taken.begin(), taken.end(), blocks_out);
+  *last_pair_key = st->pair_key;
+  st->pair_key = -1;
+  st->uploaded = 0;
+  return DFLASH_OK;
+}
+
+int dflash_install_kv(dflash_head *head, dflash_state *st, const int32_t *blocks, int32_t n_blocks, int32_t rows,
+                      int64_t last_pair_key) {
+  if (!head_ok(head)) return set_err(DFLASH_E_INVALID, "invalid head");
+  std::lock_guard<std::mutex> lk(head->mu);
+  if (!state_ok(head, st)) return set_err(DFLASH_E_INVALID, "not a live state of this head");
+  if (!blocks || n_blocks < 1) return set_err(DFLASH_E_INVALID, "install needs at least one block");
+  if (n_blocks > st->cap_blocks) return set_err(DFLASH_E_INVALID, "more blocks than the state's block table holds");
+  for (int32_t i = 0; i < n_blocks; ++i)
+    if (block_owned(head, blocks[i]))
+      return set_err(DFLASH_E_INVALID, "block " + std::to_string(blocks[i]) + " is held by a live state");
+  HIP_TRY(hipDeviceSynchronize());  // no launch still reads the state's block table
+  std::string err;
+  const int rc = seq_install(&st->rows, &head->pool, blocks, n_blocks, rows, &err);
+  if (rc != DFLASH_OK) return set_err(rc, err);
+  for (int32_t i = 0; i < n_blocks; ++i) st->h_bt[i] = blocks[i];
+  HIP_TRY(hipMemcpy(st->d_bt, st->h_bt, (size_t)n_blocks * sizeof(int32_t), hipMemcpyHostToDevice));
+  st->uploaded = n_blocks;
+  st->pair_key = last_pair_key;
+  return DFLASH_OK;
+}
+
+int dflash_free_kv(dflash_head *head, const int32_t *blocks, int32_t n_blocks) {
+  if (!head_ok(head)) return set_err(DFLASH_E_INVALID, "invalid head");
+  std::lock_guard<std::mutex> lk(head->mu);
+  if (n_blocks < 0 || (n_blocks > 0 && !blocks)) return set_err(DFLASH_E_INVALID, "bad block list");
+  std::vector<uint8_t> seen(head->pool.size(), 0);
+  for (int32_t i = 0; i < n_blocks; ++i) {
+    const int32_t b = blocks[i];
+    if (b < 0 || b >= head->pool.size() || head->pool.is_free(b) || seen[b]++)
+      return set_err(DFLASH_E_INVALID, "block " + std::to_string(b) + " is not an allocated pool block (or given twice)");
+    if (block_owned(head, b)) return set_err(DFLASH_E_INVALID, "block " + std::to_string(b) + " is held by a live state");
+  }
+  for (int32_t i = 0; i < n_blocks; ++i) head->pool.release(blocks[i]);
+  return DFLASH_OK;
 }
 
 int dflash_state_read_kv(dflash_head *head, const dflash_state *st, int32_t layer, int32_t row0, int32_t n_rows,

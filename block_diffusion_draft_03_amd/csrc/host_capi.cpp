@@ -2,6 +2,7 @@
 // Built into libdflash_host.so (g++, no HIP); not part of libdflash.so.
 #include <climits>
 #include <string>
+#include <vector>
 
 #include "host_core.hpp"
 
@@ -61,6 +62,19 @@ int32_t dfh_seq_blocks(void *seq, int32_t *out, int32_t cap) {
 }
 
 void dfh_seq_release(void *seq, void *pool) { seq_release((SeqRows *)seq, (BlockPool *)pool); }
+
+// take: blocks into out (cap entries), returns the block count; *rows the rows moved
+int32_t dfh_seq_take(void *seq, int32_t *out, int32_t cap, int32_t *rows) {
+  std::vector<int32_t> b;
+  seq_take((SeqRows *)seq, &b, rows);
+  for (size_t i = 0; i < b.size() && (int32_t)i < cap; ++i) out[i] = b[i];
+  return (int32_t)b.size();
+}
+
+int dfh_seq_install(void *seq, void *pool, const int32_t *blocks, int32_t n, int32_t rows) {
+  g_err.clear();
+  return seq_install((SeqRows *)seq, (BlockPool *)pool, blocks, n, rows, &g_err);
+}
 
 int dflash_yarn_inv_freq(int32_t head_dim, float rope_theta, float factor, float beta_fast, float beta_slow,
                          int32_t original_max_positions, float *out) {

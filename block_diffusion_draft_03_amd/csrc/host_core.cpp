@@ -167,6 +167,36 @@ void seq_release(SeqRows *s, BlockPool *pool) {
   s->pending_base = 0;
 }
 
+void seq_take(SeqRows *s, std::vector<int32_t> *blocks, int32_t *rows) {
+  *blocks = std::move(s->blocks);
+  *rows = s->ctx_len;
+  s->blocks.clear();
+  s->ctx_len = 0;
+  s->pending_base = 0;
+  s->grow = true;
+}
+
+int seq_install(SeqRows *s, BlockPool *pool, const int32_t *blocks, int32_t n, int32_t rows, std::string *err) {
+  if (s->ctx_len != 0) return fail(err, DFLASH_E_INVALID, "install needs a state that holds no rows");
+  if (!blocks || n < 1) return fail(err, DFLASH_E_INVALID, "install needs at least one block");
+  if (rows < 0 || (int64_t)rows > (int64_t)n * DFLASH_KV_BLOCK)
+    return fail(err, DFLASH_E_INVALID, "installed rows must fit the installed blocks");
+  std::vector<uint8_t> seen(pool->size(), 0);
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t b = blocks[i];
+    if (b < 0 || b >= pool->size() || pool->is_free(b))
+      return fail(err, DFLASH_E_INVALID, "block " + std::to_string(b) + " is not an allocated pool block");
+    if (seen[b]++) return fail(err, DFLASH_E_INVALID, "block " + std::to_string(b) + " is given twice");
+  }
+  for (int32_t b : s->blocks) pool->release(b);
+  s->blocks.assign(blocks, blocks + n);
+  s->ctx_len = rows;
+  s->pending_base = rows;
+  s->cap_rows = std::max<int64_t>(s->cap_rows, (int64_t)n * DFLASH_KV_BLOCK);
+  s->grow = true;
+  return DFLASH_OK;
+}
+
 // Pair i rotates at w_i = theta^(-2i/d); the fractional pair index whose
 // wavelength 2 pi / w fits `turns` times into the original context L is
 // d ln(L / (2 pi turns)) / (2 ln theta). Pairs up to floor(index(beta_fast))

@@ -66,6 +66,19 @@ int seq_trim(SeqRows *s, int32_t a, std::string *err);
 // Give every block back to the pool.
 void seq_release(SeqRows *s, BlockPool *pool);
 
+// Carry a sequence's KV to a later turn: move all its blocks and its row
+// count (ctx_len) out; the blocks stay allocated in the pool. The state is
+// left empty, taking blocks from the pool as rows arrive, with the same row
+// capacity (as a fresh state of unknown budget).
+void seq_take(SeqRows *s, std::vector<int32_t> *blocks, int32_t *rows);
+
+// Install carried blocks (allocated in the pool, distinct) holding `rows`
+// committed rows into a state that holds no rows; the state's own blocks go
+// back to the pool first. Rows must fit the blocks and the state's row
+// capacity (which grows to the installed blocks). Errors leave the state
+// and the pool unchanged.
+int seq_install(SeqRows *s, BlockPool *pool, const int32_t *blocks, int32_t n, int32_t rows, std::string *err);
+
 // YaRN-corrected RoPE table (dflash_yarn_inv_freq): out[head_dim / 2].
 int yarn_inv_freq(int32_t head_dim, double theta, double factor, double beta_fast, double beta_slow,
                   int32_t original_max, float *out, std::string *err);

@@ -213,6 +213,34 @@ int dflash_propose_batch(dflash_head *head, dflash_state *const *states, int32_t
  * device work; the dropped rows' slots are overwritten by later appends. */
 int dflash_after_verify(dflash_head *head, dflash_state *st, int32_t num_accepted);
 
+/* Carry a sequence's drafter KV across turns ([DraftProposer]
+ * take_drafter_kv, install_drafter_kv, free_drafter_kv). Host-side
+ * bookkeeping: no kernel runs and the cached values are not touched (each
+ * call first waits for the device, so no launch still reads a block table).
+ *
+ * dflash_take_kv moves all of the state's physical blocks into blocks_out
+ * (caller-owned host array of `cap` entries) and its row count into *rows;
+ * the blocks stay allocated in the head's pool and belong to the caller. The
+ * state is left empty, as a fresh state of unknown budget with the same row
+ * capacity. *n_blocks = 0 (and DFLASH_OK) when there is nothing to carry;
+ * DFLASH_E_INVALID, with *n_blocks set to the count needed and nothing
+ * moved, when cap is too small. *last_pair_key returns the key given at
+ * install (-1 when none).
+ *
+ * dflash_install_kv gives carried blocks (n_blocks >= 1 distinct allocated
+ * blocks that no live state holds, at most the state's block-table capacity)
+ * holding `rows` committed rows (0 <= rows <= 16 n_blocks) to a state that
+ * holds no rows; the state's own blocks return to the pool. A later propose
+ * sees exactly the carried rows. DFLASH_E_INVALID otherwise, nothing changed.
+ *
+ * dflash_free_kv returns carried blocks that no live state holds to the
+ * pool (a carried entry being replaced or dropped). */
+int dflash_take_kv(dflash_head *head, dflash_state *st, int32_t *blocks_out, int32_t cap, int32_t *n_blocks,
+                   int32_t *rows, int64_t *last_pair_key);
+int dflash_install_kv(dflash_head *head, dflash_state *st, const int32_t *blocks, int32_t n_blocks, int32_t rows,
+                      int64_t last_pair_key);
+int dflash_free_kv(dflash_head *head, const int32_t *blocks, int32_t n_blocks);
+
 /* Copy cached ctx rows [row0, row0 + n_rows) of one layer out of the paged
  * cache, in the cache's storage dtype (bf16: 2 bytes, FP8: 1 byte per value),
  * as K [n_rows, n_kv, d] and V [n_rows, n_kv, d] into device buffers k_out and

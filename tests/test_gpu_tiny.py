@@ -161,6 +161,47 @@ def test_tiny_shifted_rows_match_oracle():
     assert np.array_equal(res[1]["row_prob"], np.roll(res[0]["row_prob"], 1))
 
 
+def test_tiny_kv_carry_across_turns(tiny):
+    """take / install / free of a sequence's drafter KV ([DraftProposer]
+    take_drafter_kv, install_drafter_kv, free_drafter_kv): a state given the
+    carried blocks proposes bit for bit what the original state did (and
+    matches the oracle); the emptied state proposes as a fresh one; blocks a
+    live state holds are refused; freed blocks are free pool blocks again."""
+    from block_diffusion_draft_03_amd import DflashError
+    geo, w, head, orc = tiny
+    stack = synth.make_stack(geo, 40, tag=51)
+    a = head.state_create()
+    head.precompute([a], [40], stack)
+    head.after_verify(a, 40)
+    la = _logits_of(head, a)
+    blocks, rows, key = head.take_kv(a)
+    assert rows == 40 and key == -1 and len(blocks) == 3 and a.ctx_len == 0
+    assert head.take_kv(a) is None
+    b = head.state_create()
+    head.install_kv(b, blocks, rows, last_pair_key=7)
+    assert b.ctx_len == 40
+    say("[case] tiny carried KV")
+    assert np.array_equal(_logits_of(head, b), la)
+    os_ = orc.new_state()
+    orc.precompute(os_, stack)
+    res = head.propose(b, 5, 40, 3, logits=True)
+    torch.cuda.synchronize()
+    check_propose(res, orc.propose(os_, 5, 40, 3), label="carried")
+    res = head.propose(a, 5, 0, 3, logits=True)
+    torch.cuda.synchronize()
+    check_propose(res, orc.propose(orc.new_state(), 5, 0, 3), label="emptied")
+    with pytest.raises(DflashError):
+        head.install_kv(a, blocks, rows)  # b holds them
+    blocks2, rows2, key2 = head.take_kv(b)
+    assert key2 == 7 and rows2 == 40 and np.array_equal(blocks2, blocks)
+    head.free_kv(blocks2)
+    with pytest.raises(DflashError):
+        head.free_kv(blocks2)  # already free
+    c = head.state_create(block_ids=blocks2)  # explicit blocks must be free pool blocks
+    for s in (a, b, c):
+        s.free()
+
+
 def test_tiny_block_permutation_bit_exact(tiny):
     geo, w, head, orc = tiny
     stack = synth.make_stack(geo, 40, tag=31)

@@ -40,6 +40,8 @@ def host():
     lib.dfh_seq_blocks.argtypes = [vp, vp, C.c_int32]
     lib.dfh_seq_release.argtypes = [vp, vp]
     lib.dfh_seq_delete.argtypes = [vp]
+    lib.dfh_seq_take.argtypes = [vp, vp, C.c_int32, C.POINTER(C.c_int32)]
+    lib.dfh_seq_install.argtypes = [vp, vp, vp, C.c_int32, C.c_int32]
     lib.dflash_yarn_inv_freq.argtypes = [C.c_int32, C.c_float, C.c_float, C.c_float, C.c_float, C.c_int32, vp]
     return lib
 
@@ -161,6 +163,46 @@ def test_trim_semantics(host):
     assert host.dfh_seq_pending(s) == 16                           # two appends since the verify
     assert host.dfh_seq_trim(s, 0) == OK and host.dfh_seq_ctx_len(s) == 25
     host.dfh_seq_delete(s)
+    host.dfh_pool_delete(pool)
+
+
+def test_kv_carry_take_and_install(host):
+    """Carrying a sequence's KV ([DraftProposer] take_drafter_kv /
+    install_drafter_kv): take moves every block and the row count out and
+    leaves the state empty and growing; install gives them to a state with
+    no rows (whose own blocks go back to the pool) and refuses bad lists."""
+    pool = host.dfh_pool_new(64)
+    a, _ = _seq(host, pool)
+    assert host.dfh_seq_append(a, pool, 40) == OK and host.dfh_seq_trim(a, 40) == OK
+    before = host.dfh_pool_free_count(pool)
+    out, rows = np.zeros(8, dtype=np.int32), C.c_int32()
+    n = host.dfh_seq_take(a, out.ctypes.data_as(C.c_void_p), 8, C.byref(rows))
+    assert n == 3 and rows.value == 40
+    assert host.dfh_seq_ctx_len(a) == 0 and host.dfh_seq_blocks(a, None, 0) == 0
+    assert host.dfh_pool_free_count(pool) == before              # carried blocks stay allocated
+    assert host.dfh_seq_append(a, pool, 5) == OK                  # the emptied state grows again
+    carried = out[:3].copy()
+    p = lambda arr: arr.ctypes.data_as(C.c_void_p)
+    assert host.dfh_seq_install(a, pool, p(carried), 3, 40) == E_INVALID     # the state holds rows
+    b, _ = _seq(host, pool, budget=32)                             # a fresh state with 2 own blocks
+    free_before = host.dfh_pool_free_count(pool)
+    assert host.dfh_seq_install(b, pool, p(carried), 3, 49) == E_INVALID     # 49 rows > 3 blocks
+    assert host.dfh_seq_install(b, pool, p(np.array([carried[0], carried[0]], np.int32)), 2, 10) == E_INVALID
+    free_id = np.array([63], np.int32)
+    assert host.dfh_seq_install(b, pool, p(free_id), 1, 1) == E_INVALID      # not an allocated block
+    assert host.dfh_pool_free_count(pool) == free_before          # errors change nothing
+    assert host.dfh_seq_install(b, pool, p(carried), 3, 40) == OK
+    assert host.dfh_seq_ctx_len(b) == 40 and host.dfh_seq_pending(b) == 0
+    got = np.zeros(8, dtype=np.int32)
+    assert host.dfh_seq_blocks(b, p(got), 8) == 3 and np.array_equal(got[:3], carried)
+    assert host.dfh_pool_free_count(pool) == free_before + 2     # b's own two blocks returned
+    # b's row capacity grew from its 32-token budget to the 48 rows of the installed blocks
+    assert host.dfh_seq_append(b, pool, 8) == OK and host.dfh_seq_ctx_len(b) == 48
+    assert host.dfh_seq_append(b, pool, 1) == E_NO_BLOCKS
+    for s in (a, b):
+        host.dfh_seq_release(s, pool)
+        host.dfh_seq_delete(s)
+    assert host.dfh_pool_free_count(pool) == 64
     host.dfh_pool_delete(pool)
 
 
