@@ -41,7 +41,10 @@ def algorithmic_bytes(geo, ctx_rows, lm_rows_per_launch):
     the embedding rows; and for one LM-head launch, the head plus its rows."""
     h, I, L = geo.hidden, geo.intermediate, geo.num_layers
     q_dim, kv_dim = geo.num_q_heads * geo.head_dim, geo.num_kv_heads * geo.head_dim
+    rows = (q_dim + 2 * kv_dim) + h + 2 * I + h  # output rows of the layer matrices
     layer_w = L * ((q_dim + 2 * kv_dim) * h + h * q_dim + 2 * I * h + h * I) * 2
+    if getattr(geo, "layer_dtype", "bf16") == "fp8":  # E4M3 codes + one f32 scale per row
+        layer_w = layer_w // 2 + L * rows * 4
     fp8 = geo.lm_head_dtype == "fp8"
     lm = geo.vocab * h * (1 if fp8 else 2) + (geo.vocab * 4 if fp8 else 0)
     kv_elem = 1 if geo.kv_dtype == "fp8" else 2
@@ -101,7 +104,10 @@ def precompute_bytes(geo, rows):
     fc_in = geo.num_target_layers * geo.target_hidden
     fkv = geo.num_layers * 2 * geo.num_kv_heads * geo.head_dim
     kv_elem = 1 if geo.kv_dtype == "fp8" else 2
-    return (h * fc_in + fkv * h) * 2 + rows * fc_in * 2 + rows * fkv * kv_elem
+    w = (h * fc_in + fkv * h) * 2
+    if getattr(geo, "layer_dtype", "bf16") == "fp8":  # E4M3 codes + one f32 scale per row
+        w = w // 2 + (h + fkv) * 4
+    return w + rows * fc_in * 2 + rows * fkv * kv_elem
 
 
 class Workload:
@@ -345,12 +351,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if geo.lm_head_dtype == "bf16" else "bf16+fp8",
+        "dtype": "bf16" if geo.lm_head_dtype == "bf16" and geo.layer_dtype == "bf16" else "bf16+fp8",
         "data": "synthetic",
         "config": {"workload": wl.name, "n_seqs": wl.n_seqs, "ctx_rows": ctx_rows if wl.n_seqs <= 4 else
                    [min(ctx_rows), max(ctx_rows)], "gamma": geo.gamma, "layers": geo.num_layers,
                    "vocab": geo.vocab, "hidden": geo.hidden, "new_rows_per_step": wl.new_rows,
-                   "lm_head": geo.lm_head_dtype, "kv_cache": geo.kv_dtype,
+                   "lm_head": geo.lm_head_dtype, "drafter_weights": geo.layer_dtype, "kv_cache": geo.kv_dtype,
                    "grammar_mask": wl.mask_frac, "parallelism": "none"},
         "us_per_propose": round(ms_prop * 1e3, 2),
         "us_per_propose_in_step": round(prop_ms / max(1, prop_n) * 1e3, 2),

@@ -55,6 +55,13 @@ struct dflash_state {
   int64_t pair_key = -1;     // opaque key carried with installed blocks (-1: none)
 };
 
+// A repacked drafter matrix: tile-major bf16 (s null) or tile-major E4M3
+// codes with one f32 scale per output row.
+struct Wt {
+  const void *w;
+  const float *s;
+};
+
 struct dflash_head {
   uint64_t magic = HEAD_MAGIC;
   dflash_config cfg{};
@@ -67,6 +74,21 @@ struct dflash_head {
   // repacked drafter weights (bf16 unless noted), layer-major
   uint16_t *w_qkv = nullptr, *w_o = nullptr, *w_gu = nullptr, *w_down = nullptr, *w_fc = nullptr, *w_fkv = nullptr;
   size_t sz_qkv = 0, sz_o = 0, sz_gu = 0, sz_down = 0;  // tiled elements per layer
+  // FP8 drafter weights: the same matrices as tiled E4M3 codes (one byte per
+  // element, same element offsets) and f32 scales per output row, layer-major
+  uint8_t *w8_qkv = nullptr, *w8_o = nullptr, *w8_gu = nullptr, *w8_down = nullptr, *w8_fc = nullptr,
+          *w8_fkv = nullptr;
+  float *s_qkv = nullptr, *s_o = nullptr, *s_gu = nullptr, *s_down = nullptr, *s_fc = nullptr, *s_fkv = nullptr;
+
+  Wt pick(const uint16_t *b, const uint8_t *q, const float *s, size_t elem_off, size_t row_off) const {
+    return g.fp8w ? Wt{q + elem_off, s + row_off} : Wt{b + elem_off, nullptr};
+  }
+  Wt wqkv(int l) const { return pick(w_qkv, w8_qkv, s_qkv, (size_t)l * sz_qkv, (size_t)l * g.qkv_dim); }
+  Wt wo(int l) const { return pick(w_o, w8_o, s_o, (size_t)l * sz_o, (size_t)l * g.h); }
+  Wt wgu(int l) const { return pick(w_gu, w8_gu, s_gu, (size_t)l * sz_gu, (size_t)l * 2 * g.I); }
+  Wt wdown(int l) const { return pick(w_down, w8_down, s_down, (size_t)l * sz_down, (size_t)l * g.h); }
+  Wt wfc() const { return pick(w_fc, w8_fc, s_fc, 0, 0); }
+  Wt wfkv() const { return pick(w_fkv, w8_fkv, s_fkv, 0, 0); }
   float *g_in = nullptr, *g_post = nullptr, *g_hidden = nullptr, *g_final = nullptr;
   const uint16_t *embed = nullptr, *lm = nullptr;
   const uint8_t *lm8 = nullptr;
@@ -176,6 +198,74 @@ void free_state_memory(dflash_state *s) {
 
 // Repack the drafter tensors and allocate everything; called under no lock
 // on a fresh head.
+// FP8 drafter weights: every drafter matrix in the row order of its bf16
+// tiles, quantised per output row (scale = row amax / 448 of the bf16 values,
+// code = enc(w / scale), the LM-head mirror's recipe) and tiled as E4M3. The
+// fused ctx K/V rows get the same codes and scales as the layers' K/V rows.
+int build_fp8_weights(dflash_head *H, const dflash_weights *w, hipStream_t st) {
+  const Geo &g = H->g;
+  const bool f32 = g.w_f32;
+  const int h = g.h, d = g.d;
+  TRY(H->alloc(&H->w8_qkv, (size_t)g.L * H->sz_qkv));
+  TRY(H->alloc(&H->w8_o, (size_t)g.L * H->sz_o));
+  TRY(H->alloc(&H->w8_gu, (size_t)g.L * H->sz_gu));
+  TRY(H->alloc(&H->w8_down, (size_t)g.L * H->sz_down));
+  TRY(H->alloc(&H->w8_fc, tiled_elems(h, g.fc_in)));
+  TRY(H->alloc(&H->w8_fkv, tiled_elems(g.fkv_dim, h)));
+  TRY(H->alloc(&H->s_qkv, (size_t)g.L * g.qkv_dim));
+  TRY(H->alloc(&H->s_o, (size_t)g.L * h));
+  TRY(H->alloc(&H->s_gu, (size_t)g.L * 2 * g.I));
+  TRY(H->alloc(&H->s_down, (size_t)g.L * h));
+  TRY(H->alloc(&H->s_fc, (size_t)h));
+  TRY(H->alloc(&H->s_fkv, (size_t)g.fkv_dim));
+  // row-major bf16 staging of one matrix and its row-major codes (freed below)
+  const size_t most = std::max({(size_t)g.qkv_dim * h, (size_t)h * g.q_dim, (size_t)2 * g.I * h, (size_t)h * g.I,
+                                (size_t)h * g.fc_in, (size_t)g.fkv_dim * h});
+  uint16_t *tmp = nullptr;
+  uint8_t *codes = nullptr;
+  HIP_TRY(hipMalloc(&tmp, most * sizeof(uint16_t)));
+  hipError_t e = hipMalloc(&codes, most);
+  if (e != hipSuccess) {
+    (void)hipFree(tmp);
+    HIP_TRY(e);
+  }
+  int rc = DFLASH_OK;
+  auto run = [&](hipError_t x) {
+    if (rc == DFLASH_OK && x != hipSuccess) rc = set_err(DFLASH_E_HIP, std::string("FP8 weight build: ") + hipGetErrorString(x));
+  };
+  auto pack = [&](uint8_t *dst, float *scale, int rows, int cols) {
+    run(launch_fp8_mirror(tmp, rows, cols, codes, scale, st));
+    run(launch_tile_fp8(dst, codes, rows, cols, st));
+  };
+  for (int l = 0; l < g.L && rc == DFLASH_OK; ++l) {
+    const dflash_layer_weights &lw = w->layers[l];
+    run(launch_convert_rows(tmp, lw.q, nullptr, g.q_dim, h, f32, ROWS_ROPE_PAIRS, d, st));
+    run(launch_convert_rows(tmp + (size_t)g.q_dim * h, lw.k, nullptr, g.kv_dim, h, f32, ROWS_ROPE_PAIRS, d, st));
+    run(launch_convert_rows(tmp + (size_t)(g.q_dim + g.kv_dim) * h, lw.v, nullptr, g.kv_dim, h, f32, ROWS_SAME, d, st));
+    pack(H->w8_qkv + (size_t)l * H->sz_qkv, H->s_qkv + (size_t)l * g.qkv_dim, g.qkv_dim, h);
+    run(launch_convert_rows(tmp, lw.o, nullptr, h, g.q_dim, f32, ROWS_SAME, d, st));
+    pack(H->w8_o + (size_t)l * H->sz_o, H->s_o + (size_t)l * h, h, g.q_dim);
+    run(launch_convert_rows(tmp, lw.gate, lw.up, 2 * g.I, h, f32, ROWS_GATE_UP, d, st));
+    pack(H->w8_gu + (size_t)l * H->sz_gu, H->s_gu + (size_t)l * 2 * g.I, 2 * g.I, h);
+    run(launch_convert_rows(tmp, lw.down, nullptr, h, g.I, f32, ROWS_SAME, d, st));
+    pack(H->w8_down + (size_t)l * H->sz_down, H->s_down + (size_t)l * h, h, g.I);
+  }
+  for (int l = 0; l < g.L && rc == DFLASH_OK; ++l) {
+    const dflash_layer_weights &lw = w->layers[l];
+    run(launch_convert_rows(tmp + (size_t)2 * l * g.kv_dim * h, lw.k, nullptr, g.kv_dim, h, f32, ROWS_ROPE_PAIRS, d, st));
+    run(launch_convert_rows(tmp + (size_t)(2 * l + 1) * g.kv_dim * h, lw.v, nullptr, g.kv_dim, h, f32, ROWS_SAME, d, st));
+  }
+  if (rc == DFLASH_OK) pack(H->w8_fkv, H->s_fkv, g.fkv_dim, h);
+  if (rc == DFLASH_OK) run(launch_convert_rows(tmp, w->fc, nullptr, h, g.fc_in, f32, ROWS_SAME, d, st));
+  if (rc == DFLASH_OK) pack(H->w8_fc, H->s_fc, h, g.fc_in);
+  const hipError_t se = hipStreamSynchronize(st);
+  (void)hipFree(tmp);
+  (void)hipFree(codes);
+  if (rc != DFLASH_OK) return rc;
+  HIP_TRY(se);
+  return DFLASH_OK;
+}
+
 int build_impl(dflash_head *H, const dflash_weights *w, hipStream_t st) {
   const Geo &g = H->g;
   const bool f32 = g.w_f32;
@@ -203,17 +293,27 @@ int build_impl(dflash_head *H, const dflash_weights *w, hipStream_t st) {
   H->sz_o = tiled_elems(g.h, g.q_dim);
   H->sz_gu = tiled_elems(2 * g.I, g.h);
   H->sz_down = tiled_elems(g.h, g.I);
+  TRY(H->alloc(&H->g_in, (size_t)g.L * h));
+  TRY(H->alloc(&H->g_post, (size_t)g.L * h));
+  TRY(H->alloc(&H->g_hidden, h));
+  TRY(H->alloc(&H->g_final, h));
+  const int d = g.d;
+  for (int l = 0; l < g.L; ++l) {
+    const dflash_layer_weights &lw = w->layers[l];
+    HIP_TRY(launch_to_f32(H->g_in + (size_t)l * h, lw.in_norm, g.h, f32, st));
+    HIP_TRY(launch_to_f32(H->g_post + (size_t)l * h, lw.post_norm, g.h, f32, st));
+  }
+  HIP_TRY(launch_to_f32(H->g_hidden, w->hidden_norm, g.h, f32, st));
+  HIP_TRY(launch_to_f32(H->g_final, w->norm, g.h, f32, st));
+  if (g.fp8w) {
+    TRY(build_fp8_weights(H, w, st));
+  } else {
   TRY(H->alloc(&H->w_qkv, (size_t)g.L * H->sz_qkv));
   TRY(H->alloc(&H->w_o, (size_t)g.L * H->sz_o));
   TRY(H->alloc(&H->w_gu, (size_t)g.L * H->sz_gu));
   TRY(H->alloc(&H->w_down, (size_t)g.L * H->sz_down));
   TRY(H->alloc(&H->w_fc, tiled_elems(g.h, g.fc_in)));
   TRY(H->alloc(&H->w_fkv, tiled_elems(g.fkv_dim, g.h)));
-  TRY(H->alloc(&H->g_in, (size_t)g.L * h));
-  TRY(H->alloc(&H->g_post, (size_t)g.L * h));
-  TRY(H->alloc(&H->g_hidden, h));
-  TRY(H->alloc(&H->g_final, h));
-  const int d = g.d;
   for (int l = 0; l < g.L; ++l) {
     const dflash_layer_weights &lw = w->layers[l];
     // [Q; K; V] with Q and K rows in RoPE pair order
@@ -227,12 +327,9 @@ int build_impl(dflash_head *H, const dflash_weights *w, hipStream_t st) {
     // fused ctx K/V weight: rows [K0; V0; K1; V1; ...] (K rows in RoPE pair order)
     HIP_TRY(launch_tile_rows(H->w_fkv, 2 * l * g.kv_dim, lw.k, nullptr, g.kv_dim, g.h, f32, ROWS_ROPE_PAIRS, d, st));
     HIP_TRY(launch_tile_rows(H->w_fkv, (2 * l + 1) * g.kv_dim, lw.v, nullptr, g.kv_dim, g.h, f32, ROWS_SAME, d, st));
-    HIP_TRY(launch_to_f32(H->g_in + (size_t)l * h, lw.in_norm, g.h, f32, st));
-    HIP_TRY(launch_to_f32(H->g_post + (size_t)l * h, lw.post_norm, g.h, f32, st));
   }
   HIP_TRY(launch_tile_rows(H->w_fc, 0, w->fc, nullptr, g.h, g.fc_in, f32, ROWS_SAME, d, st));
-  HIP_TRY(launch_to_f32(H->g_hidden, w->hidden_norm, g.h, f32, st));
-  HIP_TRY(launch_to_f32(H->g_final, w->norm, g.h, f32, st));
+  }
 
   // target's shared tensors: the embedding is borrowed when bf16 (rows are
   // gathered); the LM head is streamed from a tiled copy the head owns
@@ -318,7 +415,7 @@ int build_impl(dflash_head *H, const dflash_weights *w, hipStream_t st) {
     if (bgemm_ok(EPI_PARTIAL, g.h, K)) max_splits = std::max(max_splits, bgemm_splits(g.h, K, (int)M));
   }
   // precompute passes of PREFILL_ROWS rows run through the tiled kernels
-  H->tiled_prefill = bgemm_ok(EPI_PARTIAL, g.h, g.fc_in) && bgemm_ok(EPI_KV_SCATTER, g.fkv_dim, g.h);
+  H->tiled_prefill = !g.fp8w && bgemm_ok(EPI_PARTIAL, g.h, g.fc_in) && bgemm_ok(EPI_KV_SCATTER, g.fkv_dim, g.h);
   const size_t pre_rows = H->tiled_prefill ? PREFILL_ROWS : GEMM_MAX_ROWS;
   if (H->tiled_prefill) max_splits = std::max(max_splits, bgemm_splits(g.h, g.fc_in, PREFILL_ROWS));
   TRY(H->alloc(&H->part, (size_t)max_splits * std::max({M, (size_t)GEMM_MAX_ROWS, pre_rows}) * h));
@@ -361,11 +458,12 @@ int build_impl(dflash_head *H, const dflash_weights *w, hipStream_t st) {
 // One GEMM over M rows in chunks of GEMM_MAX_ROWS. The epilogue output
 // pointers and the RoPE table are advanced with the rows. EPI_PARTIAL
 // outputs are laid out [splits][M][N] over all M rows of the call.
-int gemm_rows(dflash_head *H, int epi, const uint16_t *A, int lda, int M, const uint16_t *W, int N, int K,
+int gemm_rows(dflash_head *H, int epi, const uint16_t *A, int lda, int M, Wt W, int N, int K,
               EpiArgs e, hipStream_t st, int *splits_out = nullptr, RowScale rs = RowScale{}) {
   GemmArgs ga{};
   ga.lda = lda;
-  ga.W = W;
+  ga.W = W.w;
+  ga.wscale = W.s;
   ga.N = N;
   ga.K = K;
   const GemmPlan p = gemm_plan(N, K, epi == EPI_PARTIAL);
@@ -376,7 +474,7 @@ int gemm_rows(dflash_head *H, int epi, const uint16_t *A, int lda, int M, const 
   ga.kslice = p.kslice;
   if (splits_out) *splits_out = p.splits;
   e.ld_split = M;
-  if (M > GEMM_MAX_ROWS && bgemm_ok(epi, N, K) && !rs.ss && !e.tile_ctr) {
+  if (M > GEMM_MAX_ROWS && bgemm_ok(epi, N, K) && !rs.ss && !e.tile_ctr && !W.s) {
     // all rows in one tiled launch
     ga.A = A;
     ga.M = M;
@@ -410,7 +508,7 @@ int gemm_rows(dflash_head *H, int epi, const uint16_t *A, int lda, int M, const 
 
 // h += W A^T for a GEMM into the residual stream (split over K, then the
 // splits are added in order), followed by out = bf16(RMSNorm(h) * gain).
-int resid_gemm(dflash_head *H, const uint16_t *A, int lda, int M, const uint16_t *W, int K, float *h,
+int resid_gemm(dflash_head *H, const uint16_t *A, int lda, int M, Wt W, int K, float *h,
                const float *gain, uint16_t *out, bool init_zero, hipStream_t st) {
   EpiArgs e{};
   e.out_f32 = H->part;
@@ -435,7 +533,7 @@ int resid_gemm(dflash_head *H, const uint16_t *A, int lda, int M, const uint16_t
 // split of every 16-row unit adds the splits in order, writes bf16(h * gain)
 // and the unit's per-row sums of squares (H->ss); the consumer applies the
 // RMSNorm row scale. Returns the units the consumer sums.
-int resid_gemm_fused(dflash_head *H, const uint16_t *A, int lda, int M, const uint16_t *W, int K, const float *gain,
+int resid_gemm_fused(dflash_head *H, const uint16_t *A, int lda, int M, Wt W, int K, const float *gain,
                      hipStream_t st, int *units) {
   EpiArgs e{};
   e.out_f32 = H->part;
@@ -572,24 +670,24 @@ int propose_impl(dflash_head *H, dflash_state *const *states, int n, const uint3
     e.vtb = H->vtb;
     e.gamma = g.gamma;
     e.gp = H->gp;
-    TRY(gemm_rows(H, EPI_QKV_ROPE, H->act, h, M, H->w_qkv + (size_t)l * H->sz_qkv, g.qkv_dim, h, e, st, nullptr, rs));
+    TRY(gemm_rows(H, EPI_QKV_ROPE, H->act, h, M, H->wqkv(l), g.qkv_dim, h, e, st, nullptr, rs));
     aa.layer = l;
     HIP_TRY(launch_attention(aa, n, st));
     const float *post_gain = H->g_post + (size_t)l * h;
     if (fused) {
-      TRY(resid_gemm_fused(H, H->attn, g.q_dim, M, H->w_o + (size_t)l * H->sz_o, g.q_dim, post_gain, st, &rs.units));
+      TRY(resid_gemm_fused(H, H->attn, g.q_dim, M, H->wo(l), g.q_dim, post_gain, st, &rs.units));
     } else {
-      TRY(resid_gemm(H, H->attn, g.q_dim, M, H->w_o + (size_t)l * H->sz_o, g.q_dim, H->hid, post_gain, H->act, false, st));
+      TRY(resid_gemm(H, H->attn, g.q_dim, M, H->wo(l), g.q_dim, H->hid, post_gain, H->act, false, st));
     }
     e = EpiArgs{};
     e.out_bf16 = H->mlp;
     e.ldo = g.I;
-    TRY(gemm_rows(H, EPI_SWIGLU, H->act, h, M, H->w_gu + (size_t)l * H->sz_gu, 2 * g.I, h, e, st, nullptr, rs));
+    TRY(gemm_rows(H, EPI_SWIGLU, H->act, h, M, H->wgu(l), 2 * g.I, h, e, st, nullptr, rs));
     const float *next_gain = l + 1 < g.L ? H->g_in + (size_t)(l + 1) * h : H->g_final;
     if (fused) {
-      TRY(resid_gemm_fused(H, H->mlp, g.I, M, H->w_down + (size_t)l * H->sz_down, g.I, next_gain, st, &rs.units));
+      TRY(resid_gemm_fused(H, H->mlp, g.I, M, H->wdown(l), g.I, next_gain, st, &rs.units));
     } else {
-      TRY(resid_gemm(H, H->mlp, g.I, M, H->w_down + (size_t)l * H->sz_down, g.I, H->hid, next_gain, H->act, false, st));
+      TRY(resid_gemm(H, H->mlp, g.I, M, H->wdown(l), g.I, H->hid, next_gain, H->act, false, st));
     }
   }
 
@@ -832,7 +930,7 @@ int dflash_precompute_ctx_kv(dflash_head *head, dflash_state *const *states, int
       HIP_TRY(hipMemcpyAsync((void *)db, (const void *)hb, m * sizeof(const int32_t *), hipMemcpyHostToDevice, st));
       HIP_TRY(hipEventRecord(H->pre_ev[b], st));
       H->pre_ev_used[b] = true;
-      TRY(resid_gemm(H, (const uint16_t *)stack + (size_t)r0 * g.fc_in, g.fc_in, m, H->w_fc, g.fc_in, H->pre_u,
+      TRY(resid_gemm(H, (const uint16_t *)stack + (size_t)r0 * g.fc_in, g.fc_in, m, H->wfc(), g.fc_in, H->pre_u,
                      H->g_hidden, H->pre_c, true, st));
       EpiArgs e{};
       e.head_dim = g.d;
@@ -844,7 +942,7 @@ int dflash_precompute_ctx_kv(dflash_head *head, dflash_state *const *states, int
       e.inv_freq = H->inv_freq;
       e.d_row_pos = dp;
       e.d_row_bt = db;
-      TRY(gemm_rows(H, EPI_KV_SCATTER, H->pre_c, h, m, H->w_fkv, g.fkv_dim, h, e, st));
+      TRY(gemm_rows(H, EPI_KV_SCATTER, H->pre_c, h, m, H->wfkv(), g.fkv_dim, h, e, st));
     }
     if (t_all) HIP_TRY(hipEventRecord(t_all, st));
     for (int i = 0; i < n; ++i) states[i]->rows.ctx_len += n_new[i];
@@ -853,7 +951,7 @@ int dflash_precompute_ctx_kv(dflash_head *head, dflash_state *const *states, int
   for (int r0 = 0; r0 < (int)total; r0 += GEMM_MAX_ROWS) {
     const int m = std::min<int>(GEMM_MAX_ROWS, (int)total - r0);
     // u = S fc^T (split over K, summed in split order), c = RMSNorm(u) bf16
-    TRY(resid_gemm(H, (const uint16_t *)stack + (size_t)r0 * g.fc_in, g.fc_in, m, H->w_fc, g.fc_in, H->pre_u,
+    TRY(resid_gemm(H, (const uint16_t *)stack + (size_t)r0 * g.fc_in, g.fc_in, m, H->wfc(), g.fc_in, H->pre_u,
                    H->g_hidden, H->pre_c, true, st));
     EpiArgs e{};
     e.head_dim = g.d;
@@ -867,7 +965,7 @@ int dflash_precompute_ctx_kv(dflash_head *head, dflash_state *const *states, int
       e.row_pos[r] = pos[r0 + r];
       e.row_bt[r] = bts[r0 + r];
     }
-    TRY(gemm_rows(H, EPI_KV_SCATTER, H->pre_c, h, m, H->w_fkv, g.fkv_dim, h, e, st));
+    TRY(gemm_rows(H, EPI_KV_SCATTER, H->pre_c, h, m, H->wfkv(), g.fkv_dim, h, e, st));
   }
   if (t_all) HIP_TRY(hipEventRecord(t_all, st));
   for (int i = 0; i < n; ++i) states[i]->rows.ctx_len += n_new[i];

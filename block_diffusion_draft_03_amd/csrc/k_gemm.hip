@@ -286,7 +286,9 @@ __device__ __forceinline__ void finish_residual(const GemmArgs &ga, const EpiArg
   }
 }
 
-template <int MT, int TN, int NW, int ST, int EPI, bool TILED = false>
+// WFP8: W is a tiled E4M3 matrix, widened to bf16 as it is loaded; output
+// row n of the product is scaled by ga.wscale[n] before any epilogue.
+template <int MT, int TN, int NW, int ST, int EPI, bool TILED = false, bool WFP8 = false>
 __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs ga, EpiArgs ea) {
   __shared__ float red[(NW > 1 ? NW - 1 : 1) * TN * MT * 4 * 64 > 256 ? (NW > 1 ? NW - 1 : 1) * TN * MT * 4 * 64 : 256];
   __shared__ float rinv[16 * MT];
@@ -310,11 +312,23 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs ga, EpiArgs ea) {
   }
   f32x4 acc[TN][MT];
   zero<MT, TN>(acc);
-  stream_rows<MT, TN, ST, false, TILED>(ga.W, ga.N, ga.K, ga.A, ga.lda, ga.M, row0, kb + 128 * s0,
-                                        min(ke, kb + 128 * s1), acc);
+  stream_rows<MT, TN, ST, WFP8, TILED>(ga.W, ga.N, ga.K, ga.A, ga.lda, ga.M, row0, kb + 128 * s0,
+                                       min(ke, kb + 128 * s1), acc);
   wave_reduce<MT, TN, NW>(acc, red);
   if (ga.rs.ss) row_scale_finish<MT>(ga.rs, ga.M, ga.K, rs_v, rinv, red);
   if (wave != 0) return;
+  if constexpr (WFP8) {
+#pragma unroll
+    for (int t = 0; t < TN; ++t) {
+      float sc[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sc[r] = ga.wscale[min(row0 + 16 * t + 4 * g + r, ga.N - 1)];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[t][mt][r] *= sc[r];
+    }
+  }
   if constexpr (EPI == EPI_PARTIAL) {
     if (ea.tile_ctr) {
       finish_residual<MT, TN>(ga, ea, acc, row0);
@@ -565,9 +579,10 @@ __global__ __launch_bounds__(256) void k_lm_finish(LmFinishArgs a) {
 template <int MT, int TN, int NW, int ST>
 hipError_t launch_cfg(int epi, const GemmArgs &g, const EpiArgs &e, hipStream_t s) {
   dim3 grid((g.N + 16 * TN - 1) / (16 * TN), g.splits), block(NW * 64);
-#define DFL_CASE(E)                                                                         \
-  case E:                                                                                   \
-    hipLaunchKernelGGL((k_gemm<MT, TN, NW, ST, E, true>), grid, block, 0, s, g, e);      \
+#define DFL_CASE(E)                                                                           \
+  case E:                                                                                     \
+    if (g.wscale) hipLaunchKernelGGL((k_gemm<MT, TN, NW, ST, E, true, true>), grid, block, 0, s, g, e); \
+    else hipLaunchKernelGGL((k_gemm<MT, TN, NW, ST, E, true, false>), grid, block, 0, s, g, e);         \
     break;
   switch (epi) {
     DFL_CASE(EPI_F32)
@@ -584,7 +599,8 @@ hipError_t launch_cfg(int epi, const GemmArgs &g, const EpiArgs &e, hipStream_t 
 template <int MT, int TN, int ST>
 hipError_t launch_partial(const GemmArgs &g, const EpiArgs &e, hipStream_t s) {
   dim3 grid((g.N + 16 * TN - 1) / (16 * TN), g.splits), block(4 * 64);
-  hipLaunchKernelGGL((k_gemm<MT, TN, 4, ST, EPI_PARTIAL, true>), grid, block, 0, s, g, e);
+  if (g.wscale) hipLaunchKernelGGL((k_gemm<MT, TN, 4, ST, EPI_PARTIAL, true, true>), grid, block, 0, s, g, e);
+  else hipLaunchKernelGGL((k_gemm<MT, TN, 4, ST, EPI_PARTIAL, true, false>), grid, block, 0, s, g, e);
   return hipGetLastError();
 }
 

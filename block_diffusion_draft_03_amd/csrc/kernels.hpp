@@ -55,6 +55,7 @@ struct GemmArgs {
   int N, K;
   int tn, nw, st, splits, kslice;
   RowScale rs;        // weight-streaming kernel only
+  const float *wscale;  // E4M3 weights: W is tiled E4M3 and output n is scaled by wscale[n] (weight-streaming kernel only)
 };
 
 struct EpiArgs {

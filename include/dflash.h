@@ -85,6 +85,11 @@ typedef struct {
                                  + j + 1, so ids and row_prob come out rotated right by one (entry j + 1
                                  holds row j, entry 0 the last row) and index j is position + j's draft
                                  either way; the chain confidence is the min over entries 1..num_drafts */
+  int32_t fp8_weights;        /* 0: the drafter's matrices (fc, layers, fused ctx K/V) are streamed in bf16;
+                                 1: as E4M3 codes with one f32 scale per output row, built from their bf16
+                                 values (scale = row amax / 448, code = enc(w / scale), as the LM-head
+                                 mirror); weight-only, the products still run in bf16 ([Head/metrale] field
+                                 lm_head_shared_fp8: the FP8 LM head of FP8 drafter weights) */
 } dflash_config;
 
 /* One drafter layer's tensors: device pointers in weight_dtype, matrices in

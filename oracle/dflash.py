@@ -17,7 +17,8 @@ Geometry is a plain mapping with the keys
     rope_theta rms_eps kv_dtype lm_head_dtype
 
 and optionally ``inv_freq`` (a RoPE table, e.g. ``yarn_inv_freq``'s, used in
-place of the plain theta table).
+place of the plain theta table), ``shifted_rows`` (draft-row convention) and
+``layer_dtype`` ("fp8": FP8 drafter weights, ``fp8_weight``).
 
 Weights are a mapping with ``fc hidden_norm norm embed lm_head`` and
 ``layers`` (a list of mappings with ``in_norm q k v o post_norm gate up
@@ -228,6 +229,23 @@ class OracleState:
         return len(self.stack_rows)
 
 
+def fp8_weight(stored):
+    """FP8 drafter weight ([Head/metrale], field ``lm_head_shared_fp8``: the
+    LM head used with FP8 drafter weights, so the drafter's own matrices are
+    FP8 then as well; the pages give no recipe for them). Reading: the same
+    per-row absmax E4M3 quantisation as the LM-head mirror (fp8_head_mirror),
+    applied to the bf16 value of each matrix (fp32 weights are rounded to
+    bf16 first, as the library stores them) and dequantised: w~ = s_r dec(q).
+    Weight-only: activations stay as they are."""
+    x = np.asarray(stored)
+    if x.dtype != np.uint16:
+        # bf16 bit patterns of the rounded values
+        b = bf16_round(stored_to_f64(x)).astype(np.float32).view(np.uint32) >> np.uint32(16)
+        x = b.astype(np.uint16)
+    codes, scale = fp8_head_mirror(x)
+    return e4m3_decode(np.arange(256, dtype=np.uint8))[codes] * scale.astype(np.float64)[:, None]
+
+
 class OracleHead:
     """The draft head over float64 numpy arrays.
 
@@ -257,7 +275,11 @@ class OracleHead:
                          else rope_inv_freq(g["rope_theta"], self.d))
 
         w = weights
-        self.fc = stored_to_f64(w["fc"])
+        # FP8 drafter weights: every drafter matrix quantised (norm gains, the
+        # target's embedding and the LM head are not drafter matrices)
+        self.layers_fp8 = g.get("layer_dtype", "bf16") == "fp8"
+        mat = fp8_weight if self.layers_fp8 else stored_to_f64
+        self.fc = mat(w["fc"])
         if self.fc.shape != (self.h, fc_in):
             # the fc input width is num_target_layers * target_hidden
             # ([Head/atlas], fields target_hidden_size and fc; a mismatch is a
@@ -268,7 +290,7 @@ class OracleHead:
         self.embed_stored = w["embed"]  # gathered row by row; widened lazily
         self.layers = []
         for lw in w["layers"]:
-            self.layers.append({key: stored_to_f64(lw[key]) for key in
+            self.layers.append({key: (stored_to_f64 if key in ("in_norm", "post_norm") else mat)(lw[key]) for key in
                                 ("in_norm", "q", "k", "v", "o", "post_norm", "gate", "up", "down")})
         if self.head_fp8:
             if "lm_head_fp8" in w and w["lm_head_fp8"] is not None:

@@ -53,6 +53,7 @@ class Geometry:
     lm_head_dtype: str = "bf16"   # "bf16" | "fp8"
     kv_dtype: str = "bf16"        # "bf16" | "fp8"
     shifted_rows: int = 0         # draft-row convention: 0 z-lab, 1 shifted
+    layer_dtype: str = "bf16"     # drafter matrices streamed as "bf16" or "fp8" (E4M3 + row scales)
 
     def as_dict(self):
         return asdict(self)
@@ -74,6 +75,8 @@ FULL = Geometry(num_layers=8, hidden=2048, intermediate=6144, num_q_heads=32, nu
                 target_hidden=2048, ctx_window=4096, rope_theta=1e7, rms_eps=1e-6)
 
 FULL_FP8 = replace(FULL, lm_head_dtype="fp8", kv_dtype="fp8")
+# FP8 drafter weights: every drafter matrix and the LM head as E4M3 + row scales, bf16 KV
+FULL_FP8W = replace(FULL, lm_head_dtype="fp8", layer_dtype="fp8")
 
 
 @dataclass(frozen=True)
@@ -95,6 +98,7 @@ WORKLOADS = {
     "single_ctx1024": Workload("single_ctx1024", FULL, 1, 1024, 1024, 8),
     "single_ctx4096_trim": Workload("single_ctx4096_trim", FULL, 1, 4096, 4096, 16, trim=True,
                                     permute_blocks=True),
+    "single_ctx1024_fp8w": Workload("single_ctx1024_fp8w", FULL_FP8W, 1, 1024, 1024, 8),
     "batch32_ctx512_4096": Workload("batch32_ctx512_4096", FULL, 32, 512, 4096, 8),
     "batch64_fp8_ctx256_4096": Workload("batch64_fp8_ctx256_4096", FULL_FP8, 64, 256, 4096, 8,
                                         mask_frac=0.5),

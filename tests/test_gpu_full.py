@@ -9,7 +9,8 @@ oracle on the same seeded inputs:
 * batch of 32 sequences, ctx ~ U[512, 4096], 8 new rows each (sampled
   sequences checked one by one against the oracle);
 * batch of 64 with the FP8 LM-head mirror, FP8 KV cache and 50% grammar
-  bitmasks (mirror codes bit-exact on sampled rows; sampled sequences).
+  bitmasks (mirror codes bit-exact on sampled rows; sampled sequences);
+* single sequence, 1024 ctx rows, with FP8 drafter weights and LM head.
 """
 import sys
 
@@ -198,3 +199,27 @@ def test_full_batch64_fp8(weights):
     for s in states:
         s.free()
     head.destroy()
+
+
+def test_full_single_ctx1024_fp8_weights(weights):
+    """FP8 drafter weights (every drafter matrix and the LM head as E4M3 with
+    per-row scales, bf16 cache) at the benchmark's single-sequence shape."""
+    from block_diffusion_draft_03_amd import Head
+    geo = synth.FULL_FP8W
+    say("[setup] fp8-weight head + oracle")
+    head = Head(geo, weights, kv_pool_blocks=200, max_batch=1, max_seq_len=2048)
+    orc = OracleHead(geo.as_dict(), weights)
+    st, os_ = _fill(head, orc, 1024, tag=1)
+    new = synth.make_stack(GEO, 8, tag=1000)
+    head.precompute([st], [8], new)
+    orc.precompute(os_, new)
+    tok = int(synth.make_tokens(GEO, 1, tag=0)[0])
+    say(f"[case] single ctx1024 fp8 weights ctx {st.ctx_len} tok {tok}")
+    res = head.propose(st, tok, st.ctx_len, GEO.gamma - 1, logits=True)
+    torch.cuda.synchronize()
+    p, _, n = check_propose(res, orc.propose(os_, tok, os_.ctx_len, GEO.gamma - 1), logit_tol=6e-2,
+                            label="fp8 weights")
+    say(f"[result] fp8 weights: {p}/{n} rows margin-pinned, all pinned ids equal")
+    st.free()
+    head.destroy()
+

@@ -43,6 +43,9 @@ CASES = {
     # beta_slow 1, 4096 original positions): at head_dim 64 and theta 1e6 pairs 0-6 keep their
     # frequency, 7-15 blend, 16-31 are divided by 64
     "d64_yarn": replace(MID, num_q_heads=4, head_dim=64),
+    # FP8 drafter weights (every drafter matrix as E4M3 + row scales; bf16 head and cache);
+    # the batch of 96 rows takes the weight-streaming GEMMs in 64-row chunks
+    "d64_fp8w": replace(MID, num_q_heads=4, head_dim=64, layer_dtype="fp8"),
 }
 YARN = {"d64_yarn": (64.0, 32.0, 1.0, 4096)}
 LENS = [0, 17, 64, 300, 129, 45]
@@ -108,7 +111,7 @@ def test_mid_batch_and_single_match_oracle(case):
     head.destroy()
 
 
-@pytest.mark.parametrize("case", ["d64", "d64_fp8"])
+@pytest.mark.parametrize("case", ["d64", "d64_fp8", "d64_fp8w"])
 def test_mid_prompt_scale_precompute_matches_oracle(case):
     """Precompute of many rows in one call (passes of up to 1024 rows through
     the tiled GEMMs: 300 rows in one pass; 1100 rows over two sequences in two

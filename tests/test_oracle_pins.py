@@ -403,3 +403,23 @@ def test_shifted_rows_read_out():
     assert math.isclose(out[1]["conf"], float(p1[0:2].min()), rel_tol=1e-12)
     assert math.isclose(out[0]["conf"], float(p1[1:3].min()), rel_tol=1e-12)
 
+
+def test_fp8_drafter_weight_quantisation():
+    """FP8 drafter weights: each row's largest magnitude is kept exactly (it
+    maps to the code 448), every element is within half an E4M3 step of its
+    bf16 value, fp32 weights are taken at their bf16 value, and a zero row
+    stays zero."""
+    rng = np.random.default_rng(5)
+    w = (rng.standard_normal((48, 96)) * 0.02).astype(np.float32)
+    w[7] = 0.0
+    q = O.fp8_weight(w)
+    b = O.bf16_round(w.astype(np.float64))
+    amax = np.abs(b).max(axis=1)
+    assert np.allclose(np.abs(q).max(axis=1), amax, rtol=2.0 ** -23, atol=0.0)
+    s = np.where(amax > 0, amax / 448.0, 1.0)
+    # E4M3 keeps 3 mantissa bits: a half step is 2^-4 of the value (normals) or 2^-10 of the scale (subnormals)
+    assert np.all(np.abs(q - b) <= np.maximum(np.abs(b) * 2.0 ** -4, s[:, None] * 2.0 ** -10) * (1 + 2.0 ** -20))
+    assert np.array_equal(q[7], np.zeros(96))
+    bits = (b.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    assert np.array_equal(O.fp8_weight(bits), q)
+
