@@ -33,6 +33,7 @@ template <int MT, int TN>
 struct Frag {
   uint4 w[TN][4];
   uint4 a[MT][4];
+  uint4 q8[TN][2];  // tile-major E4M3: raw codes, widened into w just before the products
 };
 
 template <int MT, int TN, bool WFP8, bool TILED = false>
@@ -51,22 +52,17 @@ __device__ __forceinline__ void load_step(Frag<MT, TN> &f, const void *__restric
       for (int c = 0; c < 4; ++c) f.w[t][c] = (k0 + 32 * c + 8 * g < ke) ? *(const uint4 *)(p + c * 64 * 8) : z;
     }
   } else if constexpr (TILED && WFP8) {
-    // tile-major E4M3: pair j of lane l = codes of k-groups 2j and 2j + 1
+    // tile-major E4M3: pair j of lane l = codes of k-groups 2j and 2j + 1,
+    // kept raw (widen_e4m3 converts them after the whole batch is issued, so
+    // the loads stay in flight together); columns past K are zero codes in
+    // the tiled copy
     const uint8_t *W = (const uint8_t *)Wv;
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
       const uint8_t *p = W + (((size_t)(wrow[t] >> 4) * ((K + 127) >> 7) + (k0 >> 7)) * 2 * 64 + lane) * 16;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        uint4 q = z;
-        if (k0 + 64 * j + 8 * g < ke) q = *(const uint4 *)(p + j * 64 * 16);
-        uint2 lo = e4m3x4_to_bf16x4(q.x), hi = e4m3x4_to_bf16x4(q.y);
-        f.w[t][2 * j] = uint4{lo.x, lo.y, hi.x, hi.y};
-        lo = e4m3x4_to_bf16x4(q.z);
-        hi = e4m3x4_to_bf16x4(q.w);
-        f.w[t][2 * j + 1] = (k0 + 64 * j + 32 + 8 * g < ke) ? uint4{lo.x, lo.y, hi.x, hi.y} : z;
-      }
+      for (int j = 0; j < 2; ++j) f.q8[t][j] = (k0 + 64 * j + 8 * g < ke) ? *(const uint4 *)(p + j * 64 * 16) : z;
     }
   } else if constexpr (!WFP8) {
     const uint16_t *W = (const uint16_t *)Wv;
@@ -98,6 +94,21 @@ __device__ __forceinline__ void load_step(Frag<MT, TN> &f, const void *__restric
       f.a[mt][c] = k < ke ? *(const uint4 *)(A + (size_t)arow[mt] * lda + k) : z;
     }
   }
+}
+
+template <int MT, int TN>
+__device__ __forceinline__ void widen_e4m3(Frag<MT, TN> &f) {
+#pragma unroll
+  for (int t = 0; t < TN; ++t)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint4 q = f.q8[t][j];
+      uint2 lo = e4m3x4_to_bf16x4(q.x), hi = e4m3x4_to_bf16x4(q.y);
+      f.w[t][2 * j] = uint4{lo.x, lo.y, hi.x, hi.y};
+      lo = e4m3x4_to_bf16x4(q.z);
+      hi = e4m3x4_to_bf16x4(q.w);
+      f.w[t][2 * j + 1] = uint4{lo.x, lo.y, hi.x, hi.y};
+    }
 }
 
 template <int MT, int TN>
@@ -137,7 +148,10 @@ __device__ __forceinline__ void stream_rows(const void *__restrict__ W, int N, i
 #pragma unroll
     for (int s = 0; s < ST; ++s) load_step<MT, TN, WFP8, TILED>(f[s], W, K, wrow, A, lda, arow, k0 + 128 * s, ke, g);
 #pragma unroll
-    for (int s = 0; s < ST; ++s) mma_step<MT, TN>(f[s], acc);
+    for (int s = 0; s < ST; ++s) {
+      if constexpr (TILED && WFP8) widen_e4m3<MT, TN>(f[s]);
+      mma_step<MT, TN>(f[s], acc);
+    }
   }
 }
 
