@@ -327,8 +327,9 @@ def main():
     lm_gbs = lm_bytes / lm_avg_s / 1e9
     lm_tflops = lm_flops / lm_avg_s / 1e12
     blocks_per_s = wl.n_seqs / (ms_step / 1e3)
-    if rows > 64:
-        # many rows: the LM head is an MFMA-bound GEMM (bf16 MFMA, also for the E4M3 head)
+    if rows > (64 if geo.layer_dtype == "fp8" else 32):
+        # many rows (the library's switch to the tiled kernels): the LM head is an
+        # MFMA-bound GEMM (bf16 MFMA, also for the E4M3 head)
         roofline = {"kernel": "k_blm_head (tiled LM-head GEMM + argmax stage 1)", "bound": "mfma",
                     "achieved": round(lm_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(lm_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
