@@ -300,7 +300,7 @@ __device__ __forceinline__ void finish_residual(const GemmArgs &ga, const EpiArg
   }
 }
 
-// WFP8: W is a tiled E4M3 matrix, widened to bf16 as it is loaded; output
+// WFP8: W is a tiled E4M3 matrix, widened to bf16 in registers; output
 // row n of the product is scaled by ga.wscale[n] before any epilogue.
 template <int MT, int TN, int NW, int ST, int EPI, bool TILED = false, bool WFP8 = false>
 __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs ga, EpiArgs ea) {
