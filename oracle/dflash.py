@@ -18,7 +18,8 @@ Geometry is a plain mapping with the keys
 
 and optionally ``inv_freq`` (a RoPE table, e.g. ``yarn_inv_freq``'s, used in
 place of the plain theta table), ``shifted_rows`` (draft-row convention) and
-``layer_dtype`` ("fp8": FP8 drafter weights, ``fp8_weight``).
+``layer_dtype`` ("fp8": FP8 drafter weights, ``fp8_weight``) and
+``lm_act_dtype`` ("fp8": the FP8 LM head takes E4M3 activations, ``fp8_rows``).
 
 Weights are a mapping with ``fc hidden_norm norm embed lm_head`` and
 ``layers`` (a list of mappings with ``in_norm q k v o post_norm gate up
@@ -246,6 +247,20 @@ def fp8_weight(stored):
     return e4m3_decode(np.arange(256, dtype=np.uint8))[codes] * scale.astype(np.float64)[:, None]
 
 
+def fp8_rows(x):
+    """FP8 activations of the LM head (W8A8 head; the pages give an FP8 LM
+    head, [Head/atlas] field ``lm_head_shared_fp8``, but no activation
+    format). Reading: each activation row is quantised with the LM-head
+    mirror's recipe (fp8_head_mirror) applied to its float32 value,
+    a_m = amax_m / 448 (1 for an all-zero row) and c_mk = enc(z_mk / a_m) with
+    float32 division, and used dequantised: z~_mk = a_m dec(c_mk)."""
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    amax = np.max(np.abs(x32), axis=-1)
+    s = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    q = x32 / s[..., None]  # float32 IEEE division
+    return s.astype(np.float64)[..., None] * e4m3_decode(e4m3_encode(q.astype(np.float64)))
+
+
 class OracleHead:
     """The draft head over float64 numpy arrays.
 
@@ -269,6 +284,10 @@ class OracleHead:
         self.mask_id = int(g["mask_token_id"])
         self.kv_fp8 = g.get("kv_dtype", "bf16") == "fp8"
         self.head_fp8 = g.get("lm_head_dtype", "bf16") == "fp8"
+        # W8A8 head: the final-normed rows enter the FP8 head as E4M3 (fp8_rows)
+        self.head_a8 = g.get("lm_act_dtype", "bf16") == "fp8"
+        if self.head_a8 and not self.head_fp8:
+            raise ValueError("lm_act_dtype fp8 needs lm_head_dtype fp8")
         fc_in = int(g["num_target_layers"]) * int(g["target_hidden"])
         # a given table (e.g. yarn_inv_freq) replaces the plain one
         self.inv_freq = (np.asarray(g["inv_freq"], dtype=np.float64) if g.get("inv_freq") is not None
@@ -438,8 +457,11 @@ class OracleHead:
     def logits(self, hid):
         """Final RMSNorm then the shared LM head ([Head/atlas], fields
         ``norm``, ``lm_head_shared``). FP8 head: l_v = s_v * sum_k dec(q_vk)
-        z_k ([Head/atlas], field ``lm_head_shared_fp8``)."""
+        z_k ([Head/atlas], field ``lm_head_shared_fp8``); W8A8 head: z is
+        replaced by its per-row E4M3 value fp8_rows(z)."""
         z = rms_norm(hid, self.final_norm, self.eps)
+        if self.head_a8:
+            z = fp8_rows(z)
         l = z @ self.lm.T
         if self.head_fp8:
             l = l * self.lm_scale.astype(np.float64)[None, :]

@@ -54,6 +54,7 @@ class Geometry:
     kv_dtype: str = "bf16"        # "bf16" | "fp8"
     shifted_rows: int = 0         # draft-row convention: 0 z-lab, 1 shifted
     layer_dtype: str = "bf16"     # drafter matrices streamed as "bf16" or "fp8" (E4M3 + row scales)
+    lm_act_dtype: str = "bf16"    # rows entering the FP8 LM head: "bf16", or "fp8" (E4M3 + row scales)
 
     def as_dict(self):
         return asdict(self)
@@ -77,6 +78,8 @@ FULL = Geometry(num_layers=8, hidden=2048, intermediate=6144, num_q_heads=32, nu
 FULL_FP8 = replace(FULL, lm_head_dtype="fp8", kv_dtype="fp8")
 # FP8 drafter weights: every drafter matrix and the LM head as E4M3 + row scales, bf16 KV
 FULL_FP8W = replace(FULL, lm_head_dtype="fp8", layer_dtype="fp8")
+# W8A8 LM head: as FULL_FP8, and the final-normed rows enter the head as E4M3 + row scales
+FULL_FP8A8 = replace(FULL_FP8, lm_act_dtype="fp8")
 
 
 @dataclass(frozen=True)
@@ -102,6 +105,8 @@ WORKLOADS = {
     "batch32_ctx512_4096": Workload("batch32_ctx512_4096", FULL, 32, 512, 4096, 8),
     "batch64_fp8_ctx256_4096": Workload("batch64_fp8_ctx256_4096", FULL_FP8, 64, 256, 4096, 8,
                                         mask_frac=0.5),
+    "batch64_fp8a8_ctx256_4096": Workload("batch64_fp8a8_ctx256_4096", FULL_FP8A8, 64, 256, 4096, 8,
+                                          mask_frac=0.5),
 }
 
 

@@ -423,3 +423,53 @@ def test_fp8_drafter_weight_quantisation():
     bits = (b.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
     assert np.array_equal(O.fp8_weight(bits), q)
 
+
+
+def test_fp8_activation_rows():
+    """E4M3 activation rows of the W8A8 head: each row's largest magnitude is
+    kept (code 448), every element lies within half an E4M3 step of its
+    float32 value, a zero row stays zero, and on bf16 values the recipe is
+    the drafter-weight quantisation (the same per-row absmax mirror)."""
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((40, 256)) * np.exp(rng.uniform(-3, 3, size=(40, 1)))
+    x[5] = 0.0
+    q = O.fp8_rows(x)
+    x32 = x.astype(np.float32).astype(np.float64)
+    amax = np.abs(x32).max(axis=1)
+    assert np.allclose(np.abs(q).max(axis=1), amax, rtol=2.0 ** -22, atol=0.0)
+    s = np.where(amax > 0, amax / 448.0, 1.0)
+    assert np.all(np.abs(q - x32) <= np.maximum(np.abs(x32) * 2.0 ** -4, s[:, None] * 2.0 ** -10) * (1 + 2.0 ** -20))
+    assert np.array_equal(q[5], np.zeros(256))
+    # sign symmetry: enc(-x) = -enc(x)
+    assert np.array_equal(O.fp8_rows(-x), -q)
+    b = O.bf16_round(x32)
+    assert np.array_equal(O.fp8_rows(b), O.fp8_weight(b.astype(np.float32)))
+
+
+def test_w8a8_logits_within_activation_error_bound():
+    """W8A8 head logits differ from the weight-only FP8 head's by at most the
+    activation quantisation error carried through |W~|: for every vocab row v,
+    |l8_v - l_v| <= sum_k |s_v dec(q_vk)| e_k with e_k the half-step bound of
+    row k's E4M3 activation. A dropped activation scale, a transposed operand
+    or quantising the wrong tensor breaks it by orders of magnitude; the bound
+    is also not vacuous (the observed error is a sizeable fraction of it)."""
+    from dataclasses import replace
+    geo = replace(synth.TINY, lm_head_dtype="fp8")
+    w = synth.make_weights(geo)
+    h_w = O.OracleHead(geo.as_dict(), w)
+    h_a = O.OracleHead(replace(geo, lm_act_dtype="fp8").as_dict(), w)
+    rng = np.random.default_rng(12)
+    hid = rng.standard_normal((6, geo.hidden))
+    lw, la = h_w.logits(hid), h_a.logits(hid)
+    z = O.rms_norm(hid, h_w.final_norm, h_w.eps).astype(np.float32).astype(np.float64)
+    s = np.abs(z).max(axis=1) / 448.0
+    e = np.maximum(np.abs(z) * 2.0 ** -4, s[:, None] * 2.0 ** -10)
+    wabs = np.abs(h_w.lm) * h_w.lm_scale.astype(np.float64)[:, None]
+    bound = e @ wabs.T
+    # the float32 rounding of z itself is below 2^-24 relative
+    slack = (np.abs(z) * 2.0 ** -23) @ wabs.T
+    diff = np.abs(la - lw)
+    assert np.all(diff <= bound + slack)
+    assert diff.max() > 0.05 * bound.max()
+    with pytest.raises(ValueError):
+        O.OracleHead(replace(synth.TINY, lm_act_dtype="fp8").as_dict(), synth.make_weights(synth.TINY))
