@@ -29,6 +29,7 @@ if ROOT not in sys.path:
 METRIC = "draft blocks/sec and µs/propose (γ=16, L=8, vocab 248320); % HBM roofline"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix peak of MI355X
+MFMA_FP8_PEAK_TFLOPS = 5000.0   # dense fp8 matrix peak of MI355X
 PREFILL_ROWS = 4096  # rows of the prompt-scale precompute timed beside the step
 
 
@@ -51,7 +52,8 @@ def algorithmic_bytes(geo, ctx_rows, lm_rows_per_launch):
     kv = sum(min(c, geo.ctx_window) for c in ctx_rows) * L * 2 * kv_dim * kv_elem
     n = len(ctx_rows)
     embed = n * geo.gamma * h * 2
-    lm_launch = lm + lm_rows_per_launch * h * 2
+    a8 = getattr(geo, "lm_act_dtype", "bf16") == "fp8"  # W8A8 head: E4M3 rows + one f32 scale per row
+    lm_launch = lm + lm_rows_per_launch * (h + 4 if a8 else h * 2)
     return layer_w + lm + kv + embed, lm_launch
 
 
@@ -327,12 +329,15 @@ def main():
     lm_gbs = lm_bytes / lm_avg_s / 1e9
     lm_tflops = lm_flops / lm_avg_s / 1e12
     blocks_per_s = wl.n_seqs / (ms_step / 1e3)
-    if rows > (64 if geo.layer_dtype == "fp8" else 32):
+    if rows > (64 if geo.layer_dtype == "fp8" else 32) or getattr(geo, "lm_act_dtype", "bf16") == "fp8":
         # many rows (the library's switch to the tiled kernels): the LM head is an
-        # MFMA-bound GEMM (bf16 MFMA, also for the E4M3 head)
-        roofline = {"kernel": "k_blm_head (tiled LM-head GEMM + argmax stage 1)", "bound": "mfma",
-                    "achieved": round(lm_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(lm_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+        # MFMA-bound GEMM (bf16 MFMA, also for the E4M3 head widened to bf16; the
+        # W8A8 head runs on the E4M3 matrix cores and takes their peak)
+        a8 = getattr(geo, "lm_act_dtype", "bf16") == "fp8"
+        peak = MFMA_FP8_PEAK_TFLOPS if a8 else MFMA_BF16_PEAK_TFLOPS
+        roofline = {"kernel": "k_blm_head (tiled LM-head GEMM + argmax stage 1" + (", W8A8)" if a8 else ")"),
+                    "bound": "mfma", "achieved": round(lm_tflops, 1), "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(lm_tflops / peak, 4), "traffic": None,
                     "flops_per_launch": lm_flops, "avg_launch_us": round(lm_avg_s * 1e6, 2),
                     "launches": lm_launches}
     else:
@@ -357,7 +362,8 @@ def main():
         "config": {"workload": wl.name, "n_seqs": wl.n_seqs, "ctx_rows": ctx_rows if wl.n_seqs <= 4 else
                    [min(ctx_rows), max(ctx_rows)], "gamma": geo.gamma, "layers": geo.num_layers,
                    "vocab": geo.vocab, "hidden": geo.hidden, "new_rows_per_step": wl.new_rows,
-                   "lm_head": geo.lm_head_dtype, "drafter_weights": geo.layer_dtype, "kv_cache": geo.kv_dtype,
+                   "lm_head": geo.lm_head_dtype + ("a8" if getattr(geo, "lm_act_dtype", "bf16") == "fp8" else ""),
+                   "drafter_weights": geo.layer_dtype, "kv_cache": geo.kv_dtype,
                    "grammar_mask": wl.mask_frac, "parallelism": "none"},
         "us_per_propose": round(ms_prop * 1e3, 2),
         "us_per_propose_in_step": round(prop_ms / max(1, prop_n) * 1e3, 2),

@@ -42,7 +42,7 @@ class Config(C.Structure):
         ("ctx_window", C.c_int32), ("rope_theta", C.c_float), ("rms_eps", C.c_float),
         ("kv_block_size", C.c_int32), ("kv_pool_blocks", C.c_int32), ("max_batch", C.c_int32),
         ("max_seq_len", C.c_int32), ("weight_dtype", C.c_int), ("lm_head_dtype", C.c_int), ("kv_dtype", C.c_int),
-        ("shifted_rows", C.c_int32), ("fp8_weights", C.c_int32)]
+        ("shifted_rows", C.c_int32), ("fp8_weights", C.c_int32), ("lm_act_fp8", C.c_int32)]
 
 
 class LayerWeights(C.Structure):
@@ -179,7 +179,8 @@ class Head:
                      max_seq_len=max_seq_len, weight_dtype=DTYPE[geo.weight_dtype],
                      lm_head_dtype=DTYPE[geo.lm_head_dtype], kv_dtype=DTYPE[geo.kv_dtype],
                      shifted_rows=int(getattr(geo, "shifted_rows", 0)),
-                     fp8_weights=int(getattr(geo, "layer_dtype", "bf16") == "fp8"))
+                     fp8_weights=int(getattr(geo, "layer_dtype", "bf16") == "fp8"),
+                     lm_act_fp8=int(getattr(geo, "lm_act_dtype", "bf16") == "fp8"))
         self.cfg = cfg
 
         def dev(a):

@@ -106,6 +106,8 @@ struct dflash_head {
   // scratch
   float *hid = nullptr;
   uint16_t *act = nullptr, *qkv = nullptr, *attn = nullptr, *mlp = nullptr;
+  uint8_t *act8 = nullptr;     // W8A8 head: E4M3 codes of the final-normed rows [M][h]
+  float *act8_scale = nullptr; // and their row scales [M]
   float2 *cs = nullptr;
   uint16_t *o_part = nullptr;
   float *ml_part = nullptr;
@@ -409,6 +411,10 @@ int build_impl(dflash_head *H, const dflash_weights *w, hipStream_t st) {
   const size_t M = g.m_max;
   TRY(H->alloc(&H->hid, M * h));
   TRY(H->alloc(&H->act, M * h));
+  if (g.a8) {
+    TRY(H->alloc(&H->act8, M * h));
+    TRY(H->alloc(&H->act8_scale, M));
+  }
   TRY(H->alloc(&H->qkv, M * g.qkv_dim));
   TRY(H->alloc(&H->attn, M * g.q_dim));
   TRY(H->alloc(&H->mlp, M * g.I));
@@ -587,7 +593,8 @@ int propose_impl(dflash_head *H, dflash_state *const *states, int n, const uint3
   sa.inv_freq = H->inv_freq;
   // few rows: the residual GEMMs finish their own splits and every consumer
   // applies the RMSNorm row scale from per-unit sums of squares (H->ss)
-  const bool fused = M <= (g.fp8w ? GEMM_MAX_ROWS : PROPOSE_FEW_ROWS);
+  // the W8A8 head needs the final-normed rows in act (no deferred row scale)
+  const bool fused = !g.a8 && M <= (g.fp8w ? GEMM_MAX_ROWS : PROPOSE_FEW_ROWS);
   sa.hid = H->hid;
   sa.a = H->act;
   sa.ss_out = fused ? H->ss : nullptr;
@@ -710,14 +717,20 @@ int propose_impl(dflash_head *H, dflash_state *const *states, int n, const uint3
   la.part_se = H->lm_se;
   la.part_idx = H->lm_idx;
   la.rs = rs;
-  const bool tiled_lm = !fused && (M > GEMM_MAX_ROWS || !g.fp8w) && blm_ok(g.V, h);
+  const bool tiled_lm = !fused && (M > GEMM_MAX_ROWS || !g.fp8w || g.a8) && blm_ok(g.V, h);
+  if (g.a8 && !tiled_lm) return set_err(DFLASH_E_INVALID, "the W8A8 LM head needs the tiled head");
   if (tiled_lm) {
     la.z = H->act;
     la.M = M;
     la.row0 = 0;
     la.logits = logits;
+    if (g.a8) {
+      HIP_TRY(launch_fp8_mirror(H->act, M, h, H->act8, H->act8_scale, st));
+      la.z8 = H->act8;
+      la.ascale = H->act8_scale;
+    }
     hipEvent_t t_lm = H->interval_begin(DFLASH_PHASE_LM_HEAD, st);
-    HIP_TRY(launch_blm_head(g.head_fp8, la, st));
+    HIP_TRY(launch_blm_head(g.head_fp8, g.a8, la, st));
     if (t_lm) HIP_TRY(hipEventRecord(t_lm, st));
   }
   for (int r0 = 0; !tiled_lm && r0 < M; r0 += GEMM_MAX_ROWS) {

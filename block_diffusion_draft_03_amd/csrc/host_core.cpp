@@ -45,6 +45,10 @@ int validate_config(const dflash_config &c, Geo *g, std::string *err) {
   if (c.kv_dtype == DFLASH_FP8_E4M3 && c.head_dim < 64) return bad("an FP8_E4M3 KV cache needs head_dim >= 64");
   if (c.shifted_rows != 0 && c.shifted_rows != 1) return bad("shifted_rows must be 0 or 1");
   if (c.fp8_weights != 0 && c.fp8_weights != 1) return bad("fp8_weights must be 0 or 1");
+  if (c.lm_act_fp8 != 0 && c.lm_act_fp8 != 1) return bad("lm_act_fp8 must be 0 or 1");
+  if (c.lm_act_fp8 && c.lm_head_dtype != DFLASH_FP8_E4M3) return bad("lm_act_fp8 needs an FP8_E4M3 LM head");
+  if (c.lm_act_fp8 && (c.vocab % 256 != 0 || c.hidden % 128 != 0))
+    return bad("lm_act_fp8 needs vocab a multiple of 256 and hidden a multiple of 128");
   if (g) {
     g->L = c.num_layers;
     g->h = c.hidden;
@@ -72,6 +76,7 @@ int validate_config(const dflash_config &c, Geo *g, std::string *err) {
     g->w_f32 = c.weight_dtype == DFLASH_F32;
     g->shifted = c.shifted_rows != 0;
     g->fp8w = c.fp8_weights != 0;
+    g->a8 = c.lm_act_fp8 != 0;
   }
   return DFLASH_OK;
 }

@@ -17,7 +17,7 @@ struct Geo {
   int L, h, I, n_q, n_kv, d, V, gamma, T, Ht, W;
   int q_dim, kv_dim, qkv_dim, fc_in, fkv_dim, words, rep, max_batch, m_max;
   uint32_t mask_id;
-  bool kv_fp8, head_fp8, w_f32, shifted, fp8w;
+  bool kv_fp8, head_fp8, w_f32, shifted, fp8w, a8;
 };
 
 // Validate a config; on success fill *g. Returns a dflash_status.

@@ -211,6 +211,47 @@ __device__ __forceinline__ void mma_stage(const uint4 *slot, int wn, int wm, int
   }
 }
 
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// acc += A B^T over 128 columns of E4M3 codes (format 0 for both operands,
+// unit E8M0 block scales).
+__device__ __forceinline__ f32x4 mfma16x16x128_e4m3(const i32x8 &a, const i32x8 &b, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// W8A8 stage: 128 columns of E4M3 weights and E4M3 activation codes, staged
+// with the bf16 stage shape (a weight tile's two 1 KB pieces are the two
+// 64-column halves of its 128-column step; an activation row is 128 code
+// bytes). Lane group g of a weight tile holds, in its two pieces, the codes
+// of columns 32c + 8g + e (c = 0..3, e = 0..7) in that order; the product
+// only needs both operands in one K order, so each lane takes the same
+// columns of its activation row: byte 8 (g & 1) of 16-byte chunk 2c + g / 2.
+template <class TL>
+__device__ __forceinline__ void mma_stage_a8(const uint4 *slot, int wn, int wm, int lane,
+                                             f32x4 (&acc)[TL::WN][TL::WM]) {
+  using S = StageShape<false, TL>;
+  constexpr int WN = TL::WN, WM = TL::WM;
+  const int r16 = lane & 15, g = lane >> 4, swz = (r16 >> 1) & 7;
+  const uint4 *arow = slot + S::WF * 64 + (wm * WM * 16 + r16) * 8;
+  // all activation fragments, then one weight tile at a time (register budget)
+  i32x8 af[WM];
+#pragma unroll
+  for (int j = 0; j < WM; ++j) {
+    const uint4 *row = arow + j * 16 * 8;
+    uint2 q[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) q[c] = ((const uint2 *)(row + ((2 * c + (g >> 1)) ^ swz)))[g & 1];
+    af[j] = i32x8{(int)q[0].x, (int)q[0].y, (int)q[1].x, (int)q[1].y, (int)q[2].x, (int)q[2].y, (int)q[3].x, (int)q[3].y};
+  }
+#pragma unroll
+  for (int i = 0; i < WN; ++i) {
+    const uint4 lo = slot[((wn * WN + i) * 2) * 64 + lane], hi = slot[((wn * WN + i) * 2 + 1) * 64 + lane];
+    const i32x8 wf = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+#pragma unroll
+    for (int j = 0; j < WM; ++j) acc[i][j] = mfma16x16x128_e4m3(wf, af[j], acc[i][j]);
+  }
+}
+
 // Fragments of one stage held in registers (bf16 weights): [k-group][tile].
 template <class TL>
 struct StageFrags {
@@ -268,19 +309,20 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// acc += W[tile0 .. tile0 + 8 tiles) x A[m0 .. m0 + 128) over columns
-// [kb, kb + 128 * S), summed sequentially. NSTAGE - 1 stages are in flight
-// ahead of the one being multiplied (ring of NSTAGE slots in `lds`); one
-// barrier per stage. Every iteration issues one stage (the last ones reload
-// the final stage into a slot nobody reads), so the wait count is constant.
-template <bool WFP8, int NSTAGE, class TL>
-__device__ __forceinline__ void block_product(const LoadPlan<WFP8, TL> &p, int kb, int S, uint4 *lds,
+// acc += W[block tiles] x A[block rows] over NS stages from column kb,
+// summed sequentially. NSTAGE - 1 stages are in flight ahead of the one
+// being multiplied (ring of NSTAGE slots in `lds`); one barrier per stage.
+// Every iteration issues one stage (the last ones reload the final stage
+// into a slot nobody reads), so the wait count is constant. A8: W8A8 stages
+// (bf16 stage shape holding E4M3 codes, mma_stage_a8).
+template <bool WFP8, int NSTAGE, class TL, bool A8 = false>
+__device__ __forceinline__ void block_product(const LoadPlan<WFP8, TL> &p, int kb, int NS, uint4 *lds,
                                               f32x4 (&acc)[TL::WN][TL::WM]) {
+  static_assert(!(A8 && WFP8), "W8A8 stages use the bf16 stage shape");
   constexpr int SLOT = StageShape<WFP8, TL>::F * 64;
   constexpr uint32_t SLOT_BYTES = SLOT * 16;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int wn = wave % TL::WAVES_N, wm = wave / TL::WAVES_N;
-  const int NS = 2 * S;
   const uint32_t base = lds_addr(lds);
 #pragma unroll
   for (int s = 0; s < NSTAGE - 1; ++s)
@@ -291,7 +333,8 @@ __device__ __forceinline__ void block_product(const LoadPlan<WFP8, TL> &p, int k
     stage_barrier();
     const int sn = s + NSTAGE - 1;
     issue_stage<WFP8, TL>(base + (sn % NSTAGE) * SLOT_BYTES, p, wave, kb + 64 * min(sn, NS - 1));
-    mma_stage<WFP8, TL>(lds + (s % NSTAGE) * SLOT, wn, wm, lane, acc);
+    if constexpr (A8) mma_stage_a8<TL>(lds + (s % NSTAGE) * SLOT, wn, wm, lane, acc);
+    else mma_stage<WFP8, TL>(lds + (s % NSTAGE) * SLOT, wn, wm, lane, acc);
   }
   wait_stages<WFP8, TL>(0);
   __syncthreads();
@@ -372,13 +415,23 @@ __global__ __launch_bounds__(TL::NTHR) void k_bgemm(GemmArgs ga, EpiArgs ea, int
 // words of the block's sequences are brought into LDS by direct loads issued
 // ahead of the block's product (they complete before its first stage), so the
 // epilogue reads no global memory.
-template <bool WFP8, int NSTAGE, class TL>
+//
+// MODE: LM_BF16 (bf16 weights and rows), LM_W8 (E4M3 weights widened to
+// bf16, bf16 rows), LM_W8A8 (E4M3 weights and E4M3 row codes z8 with row
+// scales ascale, 128-column stages on the E4M3 matrix cores; logit =
+// acc * s_v * a_m).
+enum { LM_BF16 = 0, LM_W8 = 1, LM_W8A8 = 2 };
+
+template <int MODE, int NSTAGE, class TL>
 __global__ __launch_bounds__(TL::NTHR) void k_blm_head(LmArgs a, int n_p, int n_mb) {
+  constexpr bool WFP8 = MODE != LM_BF16;          // E4M3 weights with row scales
+  constexpr bool A8 = MODE == LM_W8A8;
+  constexpr bool SW8 = MODE == LM_W8;             // E4M3 stage shape
   constexpr int WN = TL::WN, WM = TL::WM, BN = TL::BN, BM = TL::BM, NT = TL::NT;
   constexpr int MW = BN / 32;        // mask words of a vocab block
   constexpr int MSEQ = BM / 2 + 1;   // sequences one block of rows can touch (gamma >= 2)
   static_assert(TL::WAVES_N == 2, "two waves share each activation row");
-  __shared__ uint4 lds[NSTAGE * StageShape<WFP8, TL>::F * 64];
+  __shared__ uint4 lds[NSTAGE * StageShape<SW8, TL>::F * 64];
   __shared__ float s_mx[2][BM], s_se[2][BM];
   __shared__ uint32_t s_idx[2][BM];
   __shared__ float s_scale[BN];
@@ -396,11 +449,14 @@ __global__ __launch_bounds__(TL::NTHR) void k_blm_head(LmArgs a, int n_p, int n_
   const int4v r_mask = make_rsrc(a.bitmask, a.bitmask ? (uint32_t)((a.M + a.gamma - 1) / a.gamma) * a.words * 4u : 0u);
   const bool masked = a.bitmask != nullptr;
   ArgState st[WM];
-  int sl[WM];  // local sequence of each row this lane holds
+  int sl[WM];     // local sequence of each row this lane holds
+  float am[WM];   // W8A8: the rows' activation scales
 #pragma unroll
   for (int j = 0; j < WM; ++j) {
     arg_init(st[j]);
-    sl[j] = min(mb * BM + (wm * WM + j) * 16 + r16, a.M - 1) / a.gamma - seq0;
+    const int m = min(mb * BM + (wm * WM + j) * 16 + r16, a.M - 1);
+    sl[j] = m / a.gamma - seq0;
+    am[j] = A8 ? a.ascale[m] : 1.0f;
   }
   for (int vb = p * LM_TILES; vb < min(n_vb, (p + 1) * LM_TILES); ++vb) {
     if (WFP8 || masked) __syncthreads();  // the previous block's epilogue is done with s_scale / s_mask
@@ -412,9 +468,19 @@ __global__ __launch_bounds__(TL::NTHR) void k_blm_head(LmArgs a, int n_p, int n_
       }
     f32x4 acc[WN][WM];
     zero_acc(acc);
-    const LoadPlan<WFP8, TL> pl = make_plan<WFP8, TL>(a.W, (size_t)a.V * a.K * (WFP8 ? 1 : 2), steps_w, vb * NT, a.z, a.K, a.M,
-                                        mb * BM, wave, lane);
-    block_product<WFP8, NSTAGE, TL>(pl, 0, steps_w, lds, acc);
+    if constexpr (A8) {
+      // codes staged as if bf16 of half the width: a 64-"column" stage is 128
+      // code columns, one 2 KB step of a weight tile
+      LoadPlan<false, TL> pl = make_plan<false, TL>(a.W, (size_t)a.V * a.K, steps_w, vb * NT,
+                                                    (const uint16_t *)a.z8, a.K / 2, a.M, mb * BM, wave, lane);
+      pl.w_tile = (uint32_t)steps_w * 2048u;
+      pl.w_base = (uint32_t)(vb * NT) * pl.w_tile;
+      block_product<false, NSTAGE, TL, true>(pl, 0, steps_w, lds, acc);
+    } else {
+      const LoadPlan<SW8, TL> pl = make_plan<SW8, TL>(a.W, (size_t)a.V * a.K * (WFP8 ? 1 : 2), steps_w, vb * NT, a.z,
+                                                      a.K, a.M, mb * BM, wave, lane);
+      block_product<SW8, NSTAGE, TL>(pl, 0, 2 * steps_w, lds, acc);
+    }
 #pragma unroll
     for (int i = 0; i < WN; ++i)
 #pragma unroll
@@ -423,7 +489,7 @@ __global__ __launch_bounds__(TL::NTHR) void k_blm_head(LmArgs a, int n_p, int n_
         const float sc = WFP8 ? s_scale[vl] : 1.0f;
 #pragma unroll
         for (int j = 0; j < WM; ++j) {
-          const float x = acc[i][j][r] * sc;
+          const float x = A8 ? acc[i][j][r] * sc * am[j] : acc[i][j][r] * sc;
           const int m = mb * BM + (wm * WM + j) * 16 + r16;
           if (a.logits && m < a.M) a.logits[(size_t)m * a.V + v] = x;
           const bool ok = !masked || ((s_mask[sl[j] * MW + (vl >> 5)] >> (vl & 31)) & 1u);
@@ -522,12 +588,14 @@ int blm_parts(int V) { return (V / TileL::BN + LM_TILES - 1) / LM_TILES; }
 
 bool blm_ok(int V, int K) { return V > 0 && K > 0 && V % TileL::BN == 0 && K % 128 == 0; }
 
-hipError_t launch_blm_head(bool w_fp8, const LmArgs &a, hipStream_t s) {
+hipError_t launch_blm_head(bool w_fp8, bool a_fp8, const LmArgs &a, hipStream_t s) {
   if (a.M < 1 || a.V % TileL::BN != 0 || a.K % 128 != 0 || a.row0 != 0) return hipErrorInvalidValue;
+  if (a_fp8 && (!w_fp8 || !a.z8 || !a.ascale)) return hipErrorInvalidValue;
   const int n_p = blm_parts(a.V), n_mb = (a.M + TileL::BM - 1) / TileL::BM;
   dim3 grid(((n_p + 7) / 8) * 8 * n_mb);
-  if (w_fp8) hipLaunchKernelGGL((k_blm_head<true, NSTAGE_LM, TileL>), grid, dim3(TileL::NTHR), 0, s, a, n_p, n_mb);
-  else hipLaunchKernelGGL((k_blm_head<false, NSTAGE_LM, TileL>), grid, dim3(TileL::NTHR), 0, s, a, n_p, n_mb);
+  if (a_fp8) hipLaunchKernelGGL((k_blm_head<LM_W8A8, NSTAGE_LM, TileL>), grid, dim3(TileL::NTHR), 0, s, a, n_p, n_mb);
+  else if (w_fp8) hipLaunchKernelGGL((k_blm_head<LM_W8, NSTAGE_LM, TileL>), grid, dim3(TileL::NTHR), 0, s, a, n_p, n_mb);
+  else hipLaunchKernelGGL((k_blm_head<LM_BF16, NSTAGE_LM, TileL>), grid, dim3(TileL::NTHR), 0, s, a, n_p, n_mb);
   return hipGetLastError();
 }
 

@@ -126,15 +126,18 @@ struct LmArgs {
   float *part_mx, *part_se;
   uint32_t *part_idx;    // [P, ld_part]
   RowScale rs;           // weight-streaming kernel only (rows row0 + m)
+  const uint8_t *z8;     // tiled W8A8 head only: [M, K] E4M3 codes of z
+  const float *ascale;   // and their [M] row scales
 };
 int lm_parts(int V);     // P of launch_lm_head, a function of V only
 hipError_t launch_lm_head(bool w_fp8, const LmArgs &a, hipStream_t s);
 // Tiled LM head for any M (one launch for all rows; row0 = 0, ld_part = M)
 // when blm_ok(V, K), blm_parts(V) partials per row. Logits are bit-identical
-// to launch_lm_head's (both sum K in one pass).
+// to launch_lm_head's (both sum K in one pass). a_fp8 (needs w_fp8): W8A8,
+// the rows come as E4M3 codes z8 with row scales ascale (z unused).
 bool blm_ok(int V, int K);
 int blm_parts(int V);
-hipError_t launch_blm_head(bool w_fp8, const LmArgs &a, hipStream_t s);
+hipError_t launch_blm_head(bool w_fp8, bool a_fp8, const LmArgs &a, hipStream_t s);
 
 struct LmFinishArgs {
   const float *part_mx, *part_se;

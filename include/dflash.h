@@ -90,6 +90,13 @@ typedef struct {
                                  values (scale = row amax / 448, code = enc(w / scale), as the LM-head
                                  mirror); weight-only, the products still run in bf16 ([Head/metrale] field
                                  lm_head_shared_fp8: the FP8 LM head of FP8 drafter weights) */
+  int32_t lm_act_fp8;         /* 0: the final-normed rows enter the LM head in bf16; 1 (needs an FP8_E4M3
+                                 head, vocab a multiple of 256, hidden a multiple of 128): W8A8 head, each
+                                 row is quantised to E4M3 with one f32 scale (scale = row amax / 448, code
+                                 = enc(z / scale), as the LM-head mirror) and the head's products run on
+                                 the E4M3 matrix cores, logit = s_v * scale * sum_k q_vk c_k; every
+                                 propose then takes the tiled path ([Head/atlas] field lm_head_shared_fp8
+                                 gives the FP8 head; its activation format is this library's reading) */
 } dflash_config;
 
 /* One drafter layer's tensors: device pointers in weight_dtype, matrices in

@@ -143,10 +143,15 @@ def test_full_batch32(bf16_pair):
         s.free()
 
 
-def test_full_batch64_fp8(weights):
+@pytest.mark.parametrize("a8", [False, True], ids=["w8", "w8a8"])
+def test_full_batch64_fp8(weights, a8):
+    """The FP8 batch workload; w8a8: the same with E4M3 activation rows into
+    the LM head (W8A8 head on the E4M3 matrix cores)."""
+    from dataclasses import replace
     from block_diffusion_draft_03_amd import Head
-    say("[setup] fp8 head")
-    head = Head(GEO8, weights, kv_pool_blocks=16800, max_batch=64, max_seq_len=8192)
+    geo8 = replace(GEO8, lm_act_dtype="fp8") if a8 else GEO8
+    say(f"[setup] fp8 head a8={a8}")
+    head = Head(geo8, weights, kv_pool_blocks=16800, max_batch=64, max_seq_len=8192)
     # the mirror's codes and scales, bit for bit, on sampled rows
     codes, scale = head.read_lm_head_fp8()
     torch.cuda.synchronize()
@@ -160,7 +165,7 @@ def test_full_batch64_fp8(weights):
     assert np.array_equal(e4m3_decode(gc), e4m3_decode(rc))
     del codes, scale
     say("[setup] fp8 oracle")
-    orc = OracleHead(GEO8.as_dict(), weights)
+    orc = OracleHead(geo8.as_dict(), weights)
     n = 64
     lens = synth.make_ctx_lengths(n, 256, 4096, tag=1)
     sample = [3, int(np.argmax(lens)), int(np.argmin(lens))]
@@ -189,11 +194,11 @@ def test_full_batch64_fp8(weights):
     masks = np.stack([synth.make_bitmask(GEO.vocab, 0.5, tag=i) for i in range(n)])
     toks = synth.make_tokens(GEO, n, tag=88)
     pos = [s.ctx_len for s in states]
-    say("[case] batch64 fp8 propose")
+    say(f"[case] batch64 fp8 propose a8={a8}")
     res = head.propose_batch(states, toks, pos, GEO.gamma - 1, bitmasks=masks, logits=True)
     torch.cuda.synchronize()
     for i in sample:
-        say(f"[case] batch64 fp8 seq {i} ctx {pos[i]}")
+        say(f"[case] batch64 fp8 a8={a8} seq {i} ctx {pos[i]}")
         ref = orc.propose(ostates[i], int(toks[i]), pos[i], GEO.gamma - 1, masks[i])
         check_propose(split_batch(res, i), ref, bitmask=masks[i], logit_tol=6e-2, label=f"fp8 seq {i}")
     for s in states:

@@ -46,6 +46,11 @@ CASES = {
     # FP8 drafter weights (every drafter matrix as E4M3 + row scales; bf16 head and cache);
     # the batch of 96 rows takes the weight-streaming GEMMs in 64-row chunks
     "d64_fp8w": replace(MID, num_q_heads=4, head_dim=64, layer_dtype="fp8"),
+    # W8A8 LM head (E4M3 activation rows on the E4M3 matrix cores; every propose, the single
+    # one included, takes the tiled head), with a full and a ragged block
+    "d64_fp8a8": replace(MID, num_q_heads=4, head_dim=64, kv_dtype="fp8", lm_head_dtype="fp8", lm_act_dtype="fp8"),
+    "d64_gamma33_fp8a8": replace(MID, num_q_heads=4, head_dim=64, gamma=33, lm_head_dtype="fp8",
+                                 lm_act_dtype="fp8"),
 }
 YARN = {"d64_yarn": (64.0, 32.0, 1.0, 4096)}
 LENS = [0, 17, 64, 300, 129, 45]

@@ -68,7 +68,8 @@ def test_valid_configs(host):
     ("gamma", 1), ("gamma", 65), ("vocab", 1), ("mask_token_id", 248320), ("ctx_window", -1),
     ("kv_block_size", 32), ("kv_pool_blocks", 0), ("max_batch", 0), ("max_batch", 65), ("max_seq_len", 0),
     ("rope_theta", 0.5), ("rms_eps", -1.0), ("weight_dtype", 2), ("lm_head_dtype", 0), ("kv_dtype", 0),
-    ("target_hidden", 0), ("gamma", 32), ("shifted_rows", 2), ("shifted_rows", -1)])
+    ("target_hidden", 0), ("gamma", 32), ("shifted_rows", 2), ("shifted_rows", -1),
+    ("lm_act_fp8", 2)])
 def test_invalid_configs(host, field, value):
     # gamma 32 with 8 query heads per kv head gives 256 query rows per kv head
     cfg = make_cfg(**{field: value})
@@ -82,6 +83,14 @@ def test_fp8_kv_needs_wide_heads(host):
     assert host.dfh_validate(C.byref(cfg)) == E_INVALID
     assert "head_dim" in host.dfh_last_error().decode()
     assert host.dfh_validate(C.byref(make_cfg(head_dim=64, kv_dtype=2))) == OK
+
+
+def test_w8a8_head_needs_fp8_head_and_tiled_shapes(host):
+    # E4M3 activations go into the tiled E4M3 head only
+    assert host.dfh_validate(C.byref(make_cfg(lm_act_fp8=1, lm_head_dtype=1))) == E_INVALID
+    assert "FP8_E4M3 LM head" in host.dfh_last_error().decode()
+    assert host.dfh_validate(C.byref(make_cfg(lm_act_fp8=1, lm_head_dtype=2, vocab=248000))) == E_INVALID
+    assert host.dfh_validate(C.byref(make_cfg(lm_act_fp8=1, lm_head_dtype=2))) == OK
 
 
 def _seq(host, pool, budget=INT64_MAX, ids=None, max_seq_len=8192):
