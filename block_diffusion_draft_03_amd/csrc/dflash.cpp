@@ -725,7 +725,7 @@ int propose_impl(dflash_head *H, dflash_state *const *states, int n, const uint3
     la.row0 = 0;
     la.logits = logits;
     if (g.a8) {
-      HIP_TRY(launch_fp8_mirror(H->act, M, h, H->act8, H->act8_scale, st));
+      HIP_TRY(launch_quant_rows_a8(H->act, M, h, H->act8, H->act8_scale, st));
       la.z8 = H->act8;
       la.ascale = H->act8_scale;
     }

@@ -224,8 +224,10 @@ __device__ __forceinline__ f32x4 mfma16x16x128_e4m3(const i32x8 &a, const i32x8 
 // 64-column halves of its 128-column step; an activation row is 128 code
 // bytes). Lane group g of a weight tile holds, in its two pieces, the codes
 // of columns 32c + 8g + e (c = 0..3, e = 0..7) in that order; the product
-// only needs both operands in one K order, so each lane takes the same
-// columns of its activation row: byte 8 (g & 1) of 16-byte chunk 2c + g / 2.
+// only needs both operands in one K order, and the activation rows come
+// with each step's codes stored in exactly that order per lane group
+// (launch_quant_rows_a8), so a lane's operand is 16-byte chunks 2g and
+// 2g + 1 of its row. Weight fragments are read one tile ahead.
 template <class TL>
 __device__ __forceinline__ void mma_stage_a8(const uint4 *slot, int wn, int wm, int lane,
                                              f32x4 (&acc)[TL::WN][TL::WM]) {
@@ -233,22 +235,25 @@ __device__ __forceinline__ void mma_stage_a8(const uint4 *slot, int wn, int wm, 
   constexpr int WN = TL::WN, WM = TL::WM;
   const int r16 = lane & 15, g = lane >> 4, swz = (r16 >> 1) & 7;
   const uint4 *arow = slot + S::WF * 64 + (wm * WM * 16 + r16) * 8;
-  // all activation fragments, then one weight tile at a time (register budget)
+  auto wfrag = [&](int i) {
+    const uint4 lo = slot[((wn * WN + i) * 2) * 64 + lane], hi = slot[((wn * WN + i) * 2 + 1) * 64 + lane];
+    return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  };
   i32x8 af[WM];
+  i32x8 wcur = wfrag(0);
 #pragma unroll
   for (int j = 0; j < WM; ++j) {
     const uint4 *row = arow + j * 16 * 8;
-    uint2 q[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) q[c] = ((const uint2 *)(row + ((2 * c + (g >> 1)) ^ swz)))[g & 1];
-    af[j] = i32x8{(int)q[0].x, (int)q[0].y, (int)q[1].x, (int)q[1].y, (int)q[2].x, (int)q[2].y, (int)q[3].x, (int)q[3].y};
+    const uint4 x0 = row[(2 * g) ^ swz], x1 = row[(2 * g + 1) ^ swz];
+    af[j] = i32x8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
   }
 #pragma unroll
   for (int i = 0; i < WN; ++i) {
-    const uint4 lo = slot[((wn * WN + i) * 2) * 64 + lane], hi = slot[((wn * WN + i) * 2 + 1) * 64 + lane];
-    const i32x8 wf = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    i32x8 wnext = wcur;
+    if (i + 1 < WN) wnext = wfrag(i + 1);
 #pragma unroll
-    for (int j = 0; j < WM; ++j) acc[i][j] = mfma16x16x128_e4m3(wf, af[j], acc[i][j]);
+    for (int j = 0; j < WM; ++j) acc[i][j] = mfma16x16x128_e4m3(wcur, af[j], acc[i][j]);
+    wcur = wnext;
   }
 }
 

@@ -199,6 +199,43 @@ __global__ __launch_bounds__(256) void k_fp8_mirror(const uint16_t *src, int h, 
   for (int i = threadIdx.x; i < h; i += blockDim.x) out[i] = f32_to_e4m3(bf16_to_f32(row[i]) / s);
 }
 
+// E4M3 activation rows of the W8A8 LM head, one workgroup per row: the
+// mirror's recipe (s = amax / 448, 1 for an all-zero row; code = E4M3(x / s)
+// with IEEE float32 division), stored in the head's K order: inside each
+// 128-column step, bytes 32g + 8c .. + 7 hold columns 32c + 8g .. + 7, so the
+// 32 codes that lane group g of a 16x16x128 operand takes are contiguous.
+__global__ __launch_bounds__(256) void k_quant_rows_a8(const uint16_t *src, int h, uint8_t *codes, float *scale) {
+  __shared__ float red[4];
+  const int m = blockIdx.x;
+  const uint16_t *row = src + (size_t)m * h;
+  float amax = 0.0f;
+  for (int i = threadIdx.x; i < h; i += blockDim.x) amax = fmaxf(amax, fabsf(bf16_to_f32(row[i])));
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, WAVE));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = amax > 0.0f ? amax / E4M3_MAX : 1.0f;
+  if (threadIdx.x == 0) scale[m] = s;
+  uint8_t *out = codes + (size_t)m * h;
+  for (int p = threadIdx.x; p < h / 8; p += blockDim.x) {
+    // output piece p: step p / 16, piece q = 4g + c of the step, from columns 32c + 8g
+    const int step = p >> 4, q = p & 15, g = q >> 2, c = q & 3;
+    const uint4 x = *(const uint4 *)(row + step * 128 + 32 * c + 8 * g);
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t v = w[e];
+      const uint32_t c0 = (uint32_t)f32_to_e4m3(bf16_to_f32((uint16_t)(v & 0xFFFFu)) / s);
+      const uint32_t c1 = (uint32_t)f32_to_e4m3(bf16_to_f32((uint16_t)(v >> 16)) / s);
+      if (e < 2) lo |= (c0 | (c1 << 8)) << (16 * e);
+      else hi |= (c0 | (c1 << 8)) << (16 * (e - 2));
+    }
+    *(uint2 *)(out + (size_t)p * 8) = uint2{lo, hi};
+  }
+}
+
 // Cached K is stored with its head dimensions in RoPE pair order (dim i at
 // position 2i for i < d/2, at 2(i - d/2) + 1 otherwise); the copy restores
 // the natural order.
@@ -275,6 +312,12 @@ hipError_t launch_to_f32(float *dst, const void *src, int n, bool src_f32, hipSt
 
 hipError_t launch_fp8_mirror(const uint16_t *src, int V, int h, uint8_t *codes, float *scale, hipStream_t s) {
   hipLaunchKernelGGL(k_fp8_mirror, dim3(V), dim3(256), 0, s, src, h, codes, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_rows_a8(const uint16_t *src, int M, int h, uint8_t *codes, float *scale, hipStream_t s) {
+  if (M < 1 || h % 128 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_quant_rows_a8, dim3(M), dim3(256), 0, s, src, h, codes, scale);
   return hipGetLastError();
 }
 

@@ -226,6 +226,9 @@ hipError_t launch_to_f32(float *dst, const void *src, int n, bool src_f32, hipSt
 
 // FP8 mirror of a bf16 [V, h] head: per-row scale amax / 448, E4M3 codes.
 hipError_t launch_fp8_mirror(const uint16_t *src, int V, int h, uint8_t *codes, float *scale, hipStream_t s);
+// E4M3 rows for the W8A8 LM head: launch_fp8_mirror's codes and scales, each
+// 128-column step's codes permuted into the head's K order (h % 128 == 0)
+hipError_t launch_quant_rows_a8(const uint16_t *src, int M, int h, uint8_t *codes, float *scale, hipStream_t s);
 
 // Gather ctx rows of one layer out of the paged pool (storage dtype bytes).
 hipError_t launch_read_kv(const void *pool, const int32_t *bt, int L, int layer, int n_kv, int d, int elem_bytes,
