@@ -428,7 +428,7 @@ __global__ __launch_bounds__(TL::NTHR) void k_bgemm(GemmArgs ga, EpiArgs ea, int
 enum { LM_BF16 = 0, LM_W8 = 1, LM_W8A8 = 2 };
 
 template <int MODE, int NSTAGE, class TL>
-__global__ __launch_bounds__(TL::NTHR) void k_blm_head(LmArgs a, int n_p, int n_mb) {
+__global__ __launch_bounds__(TL::NTHR) void k_blm_head(LmArgs a, int n_p, int n_mb, int stride_p) {
   constexpr bool WFP8 = MODE != LM_BF16;          // E4M3 weights with row scales
   constexpr bool A8 = MODE == LM_W8A8;
   constexpr bool SW8 = MODE == LM_W8;             // E4M3 stage shape
@@ -441,95 +441,104 @@ __global__ __launch_bounds__(TL::NTHR) void k_blm_head(LmArgs a, int n_p, int n_
   __shared__ uint32_t s_idx[2][BM];
   __shared__ float s_scale[BN];
   __shared__ uint32_t s_mask[((MSEQ + 7) / 8) * 8 * MW];  // [local sequence][word], whole loads of 8 sequences
-  int p, mb;
-  if (!place(blockIdx.x, n_p, n_mb, p, mb)) return;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63, g = lane >> 4,
-            r16 = lane & 15;
-  const int wn = wave % TL::WAVES_N, wm = wave / TL::WAVES_N;
-  const int n_vb = a.V / BN;
-  const int steps_w = a.K >> 7;
-  const int seq0 = (mb * BM) / a.gamma;
-  const int n_s = (min(mb * BM + BM, a.M) - 1) / a.gamma - seq0 + 1;  // <= MSEQ
-  const int4v r_scale = make_rsrc(a.scale, WFP8 ? (uint32_t)a.V * 4u : 0u);
-  const int4v r_mask = make_rsrc(a.bitmask, a.bitmask ? (uint32_t)((a.M + a.gamma - 1) / a.gamma) * a.words * 4u : 0u);
-  const bool masked = a.bitmask != nullptr;
-  ArgState st[WM];
-  int sl[WM];     // local sequence of each row this lane holds
-  float am[WM];   // W8A8: the rows' activation scales
-#pragma unroll
-  for (int j = 0; j < WM; ++j) {
-    arg_init(st[j]);
-    const int m = min(mb * BM + (wm * WM + j) * 16 + r16, a.M - 1);
-    sl[j] = m / a.gamma - seq0;
-    am[j] = A8 ? a.ascale[m] : 1.0f;
-  }
-  for (int vb = p * LM_TILES; vb < min(n_vb, (p + 1) * LM_TILES); ++vb) {
-    if (WFP8 || masked) __syncthreads();  // the previous block's epilogue is done with s_scale / s_mask
-    if (WFP8 && wave == 0) dma16(r_scale, lane * 16, (uint32_t)vb * BN * 4, lds_addr(s_scale));
-    if (masked)
-      for (int q = wave; q * 8 < n_s; q += TL::NWAVES) {
-        const int ls = min(q * 8 + (lane >> 3), n_s - 1);
-        dma4(r_mask, (uint32_t)(((seq0 + ls) * a.words + vb * MW + (lane & 7)) * 4), 0, lds_addr(s_mask + q * 64));
-      }
-    f32x4 acc[WN][WM];
-    zero_acc(acc);
-    if constexpr (A8) {
-      // codes staged as if bf16 of half the width: a 64-"column" stage is 128
-      // code columns, one 2 KB step of a weight tile
-      LoadPlan<false, TL> pl = make_plan<false, TL>(a.W, (size_t)a.V * a.K, steps_w, vb * NT,
-                                                    (const uint16_t *)a.z8, a.K / 2, a.M, mb * BM, wave, lane);
-      pl.w_tile = (uint32_t)steps_w * 2048u;
-      pl.w_base = (uint32_t)(vb * NT) * pl.w_tile;
-      block_product<false, NSTAGE, TL, true>(pl, 0, steps_w, lds, acc);
-    } else {
-      const LoadPlan<SW8, TL> pl = make_plan<SW8, TL>(a.W, (size_t)a.V * a.K * (WFP8 ? 1 : 2), steps_w, vb * NT, a.z,
-                                                      a.K, a.M, mb * BM, wave, lane);
-      block_product<SW8, NSTAGE, TL>(pl, 0, 2 * steps_w, lds, acc);
+  // Persistent placement: workgroup b sits on XCD x = b % 8 with activation
+  // block mb and group q of its XCD, and loops over the vocab ranges
+  // q * 8 + x, + stride_p, ...: the n_mb workgroups that share a range run
+  // side by side on one XCD for the whole launch and stay in step, so more of
+  // a range's weight lines are still in that XCD's L2 when the partners read
+  // them than when each range's workgroups are dispatched as others finish.
+  const int xcd = blockIdx.x & 7, slot_k = blockIdx.x >> 3;
+  const int mb = slot_k % n_mb;
+  for (int p = (slot_k / n_mb) * 8 + xcd; p < n_p; p += stride_p) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63, g = lane >> 4,
+              r16 = lane & 15;
+    const int wn = wave % TL::WAVES_N, wm = wave / TL::WAVES_N;
+    const int n_vb = a.V / BN;
+    const int steps_w = a.K >> 7;
+    const int seq0 = (mb * BM) / a.gamma;
+    const int n_s = (min(mb * BM + BM, a.M) - 1) / a.gamma - seq0 + 1;  // <= MSEQ
+    const int4v r_scale = make_rsrc(a.scale, WFP8 ? (uint32_t)a.V * 4u : 0u);
+    const int4v r_mask = make_rsrc(a.bitmask, a.bitmask ? (uint32_t)((a.M + a.gamma - 1) / a.gamma) * a.words * 4u : 0u);
+    const bool masked = a.bitmask != nullptr;
+    ArgState st[WM];
+    int sl[WM];     // local sequence of each row this lane holds
+    float am[WM];   // W8A8: the rows' activation scales
+  #pragma unroll
+    for (int j = 0; j < WM; ++j) {
+      arg_init(st[j]);
+      const int m = min(mb * BM + (wm * WM + j) * 16 + r16, a.M - 1);
+      sl[j] = m / a.gamma - seq0;
+      am[j] = A8 ? a.ascale[m] : 1.0f;
     }
-#pragma unroll
-    for (int i = 0; i < WN; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int vl = (wn * WN + i) * 16 + 4 * g + r, v = vb * BN + vl;
-        const float sc = WFP8 ? s_scale[vl] : 1.0f;
-#pragma unroll
-        for (int j = 0; j < WM; ++j) {
-          const float x = A8 ? acc[i][j][r] * sc * am[j] : acc[i][j][r] * sc;
-          const int m = mb * BM + (wm * WM + j) * 16 + r16;
-          if (a.logits && m < a.M) a.logits[(size_t)m * a.V + v] = x;
-          const bool ok = !masked || ((s_mask[sl[j] * MW + (vl >> 5)] >> (vl & 31)) & 1u);
-          arg_push(st[j], x, (uint32_t)v, ok);
+    for (int vb = p * LM_TILES; vb < min(n_vb, (p + 1) * LM_TILES); ++vb) {
+      if (WFP8 || masked) __syncthreads();  // the previous block's epilogue is done with s_scale / s_mask
+      if (WFP8 && wave == 0) dma16(r_scale, lane * 16, (uint32_t)vb * BN * 4, lds_addr(s_scale));
+      if (masked)
+        for (int q = wave; q * 8 < n_s; q += TL::NWAVES) {
+          const int ls = min(q * 8 + (lane >> 3), n_s - 1);
+          dma4(r_mask, (uint32_t)(((seq0 + ls) * a.words + vb * MW + (lane & 7)) * 4), 0, lds_addr(s_mask + q * 64));
         }
+      f32x4 acc[WN][WM];
+      zero_acc(acc);
+      if constexpr (A8) {
+        // codes staged as if bf16 of half the width: a 64-"column" stage is 128
+        // code columns, one 2 KB step of a weight tile
+        LoadPlan<false, TL> pl = make_plan<false, TL>(a.W, (size_t)a.V * a.K, steps_w, vb * NT,
+                                                      (const uint16_t *)a.z8, a.K / 2, a.M, mb * BM, wave, lane);
+        pl.w_tile = (uint32_t)steps_w * 2048u;
+        pl.w_base = (uint32_t)(vb * NT) * pl.w_tile;
+        block_product<false, NSTAGE, TL, true>(pl, 0, steps_w, lds, acc);
+      } else {
+        const LoadPlan<SW8, TL> pl = make_plan<SW8, TL>(a.W, (size_t)a.V * a.K * (WFP8 ? 1 : 2), steps_w, vb * NT, a.z,
+                                                        a.K, a.M, mb * BM, wave, lane);
+        block_product<SW8, NSTAGE, TL>(pl, 0, 2 * steps_w, lds, acc);
       }
-  }
-#pragma unroll
-  for (int j = 0; j < WM; ++j) {
-    st[j] = arg_merge(st[j], arg_shfl_xor(st[j], 16));
-    st[j] = arg_merge(st[j], arg_shfl_xor(st[j], 32));
-    if (g == 0) {
-      const int row = (wm * WM + j) * 16 + r16;
-      s_mx[wn][row] = st[j].mx;
-      s_se[wn][row] = st[j].se;
-      s_idx[wn][row] = st[j].idx;
+  #pragma unroll
+      for (int i = 0; i < WN; ++i)
+  #pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int vl = (wn * WN + i) * 16 + 4 * g + r, v = vb * BN + vl;
+          const float sc = WFP8 ? s_scale[vl] : 1.0f;
+  #pragma unroll
+          for (int j = 0; j < WM; ++j) {
+            const float x = A8 ? acc[i][j][r] * sc * am[j] : acc[i][j][r] * sc;
+            const int m = mb * BM + (wm * WM + j) * 16 + r16;
+            if (a.logits && m < a.M) a.logits[(size_t)m * a.V + v] = x;
+            const bool ok = !masked || ((s_mask[sl[j] * MW + (vl >> 5)] >> (vl & 31)) & 1u);
+            arg_push(st[j], x, (uint32_t)v, ok);
+          }
+        }
     }
-  }
-  __syncthreads();
-  if (threadIdx.x < BM) {
-    const int row = threadIdx.x, m = mb * BM + row;
-    ArgState x, y;
-    x.mx = s_mx[0][row];
-    x.se = s_se[0][row];
-    x.idx = s_idx[0][row];
-    y.mx = s_mx[1][row];
-    y.se = s_se[1][row];
-    y.idx = s_idx[1][row];
-    x = arg_merge(x, y);
-    if (m < a.M) {
-      const size_t o = (size_t)p * a.ld_part + m;
-      a.part_mx[o] = x.mx;
-      a.part_se[o] = x.se;
-      a.part_idx[o] = x.idx;
+  #pragma unroll
+    for (int j = 0; j < WM; ++j) {
+      st[j] = arg_merge(st[j], arg_shfl_xor(st[j], 16));
+      st[j] = arg_merge(st[j], arg_shfl_xor(st[j], 32));
+      if (g == 0) {
+        const int row = (wm * WM + j) * 16 + r16;
+        s_mx[wn][row] = st[j].mx;
+        s_se[wn][row] = st[j].se;
+        s_idx[wn][row] = st[j].idx;
+      }
     }
+    __syncthreads();
+    if (threadIdx.x < BM) {
+      const int row = threadIdx.x, m = mb * BM + row;
+      ArgState x, y;
+      x.mx = s_mx[0][row];
+      x.se = s_se[0][row];
+      x.idx = s_idx[0][row];
+      y.mx = s_mx[1][row];
+      y.se = s_se[1][row];
+      y.idx = s_idx[1][row];
+      x = arg_merge(x, y);
+      if (m < a.M) {
+        const size_t o = (size_t)p * a.ld_part + m;
+        a.part_mx[o] = x.mx;
+        a.part_se[o] = x.se;
+        a.part_idx[o] = x.idx;
+      }
+    }
+    __syncthreads();  // s_mx / s_se / s_idx are read before the next range writes them
   }
 }
 
@@ -597,10 +606,14 @@ hipError_t launch_blm_head(bool w_fp8, bool a_fp8, const LmArgs &a, hipStream_t 
   if (a.M < 1 || a.V % TileL::BN != 0 || a.K % 128 != 0 || a.row0 != 0) return hipErrorInvalidValue;
   if (a_fp8 && (!w_fp8 || !a.z8 || !a.ascale)) return hipErrorInvalidValue;
   const int n_p = blm_parts(a.V), n_mb = (a.M + TileL::BM - 1) / TileL::BM;
-  dim3 grid(((n_p + 7) / 8) * 8 * n_mb);
-  if (a_fp8) hipLaunchKernelGGL((k_blm_head<LM_W8A8, NSTAGE_LM, TileL>), grid, dim3(TileL::NTHR), 0, s, a, n_p, n_mb);
-  else if (w_fp8) hipLaunchKernelGGL((k_blm_head<LM_W8, NSTAGE_LM, TileL>), grid, dim3(TileL::NTHR), 0, s, a, n_p, n_mb);
-  else hipLaunchKernelGGL((k_blm_head<LM_BF16, NSTAGE_LM, TileL>), grid, dim3(TileL::NTHR), 0, s, a, n_p, n_mb);
+  // one workgroup per CU (the ring fills the LDS): groups of n_mb per XCD,
+  // at most as many groups as there are vocab ranges per XCD
+  const int groups = std::max(1, std::min(NUM_CUS / 8 / n_mb, (n_p + 7) / 8));
+  const int stride_p = groups * 8;
+  dim3 grid(stride_p * n_mb);
+  if (a_fp8) hipLaunchKernelGGL((k_blm_head<LM_W8A8, NSTAGE_LM, TileL>), grid, dim3(TileL::NTHR), 0, s, a, n_p, n_mb, stride_p);
+  else if (w_fp8) hipLaunchKernelGGL((k_blm_head<LM_W8, NSTAGE_LM, TileL>), grid, dim3(TileL::NTHR), 0, s, a, n_p, n_mb, stride_p);
+  else hipLaunchKernelGGL((k_blm_head<LM_BF16, NSTAGE_LM, TileL>), grid, dim3(TileL::NTHR), 0, s, a, n_p, n_mb, stride_p);
   return hipGetLastError();
 }
 
