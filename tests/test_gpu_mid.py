@@ -165,3 +165,47 @@ def test_mid_prompt_scale_precompute_matches_oracle(case):
         for st in sts:
             st.free()
     head.destroy()
+
+
+@pytest.mark.parametrize("case", ["bf16", "fp8a8"])
+def test_mid_largest_batch_matches_oracle(case):
+    """The largest call the library takes: 64 sequences (the batch ceiling) of
+    64 block rows (the block ceiling), 4096 rows in one propose_batch, so the
+    tiled LM head runs sixteen 256-row activation blocks per vocab range;
+    contexts of 0..40 rows (empty ones included). bf16 head, and the W8A8
+    head over an E4M3 cache with grammar masks. Every sequence is checked."""
+    from block_diffusion_draft_03_amd import Head
+    geo = replace(MID, num_q_heads=4, head_dim=64, gamma=64)
+    if case == "fp8a8":
+        geo = replace(geo, kv_dtype="fp8", lm_head_dtype="fp8", lm_act_dtype="fp8")
+    fp8 = geo.lm_head_dtype == "fp8"
+    n = 64
+    w = synth.make_weights(geo)
+    say(f"[build] mid largest batch {case}")
+    head = Head(geo, w, kv_pool_blocks=n * 8, max_batch=n, max_seq_len=256)
+    orc = OracleHead(geo.as_dict(), w)
+    lens = synth.make_ctx_lengths(n, 0, 40, tag=77)
+    lens[0] = 0
+    states, ostates = [], []
+    for i in range(n):
+        st, os_ = head.state_create(), orc.new_state()
+        if lens[i]:
+            stk = synth.make_stack(geo, int(lens[i]), tag=1200 + i)
+            head.precompute([st], [int(lens[i])], stk)
+            orc.precompute(os_, stk)
+        states.append(st)
+        ostates.append(os_)
+    toks = synth.make_tokens(geo, n, tag=78)
+    pos = [s.ctx_len for s in states]
+    masks = np.stack([synth.make_bitmask(geo.vocab, 0.5, tag=300 + i) for i in range(n)]) if fp8 else None
+    say(f"[case] mid largest batch {case}: {n} x {geo.gamma} rows")
+    res = head.propose_batch(states, toks, pos, geo.gamma - 1, bitmasks=masks, logits=True)
+    torch.cuda.synchronize()
+    for i in range(n):
+        mk = None if masks is None else masks[i]
+        ref = orc.propose(ostates[i], int(toks[i]), pos[i], geo.gamma - 1, mk)
+        check_propose(split_batch(res, i), ref, bitmask=mk, logit_tol=6e-2 if fp8 else 2e-2,
+                      label=f"largest {case} seq {i} ctx {pos[i]}")
+    for s in states:
+        s.free()
+    head.destroy()
