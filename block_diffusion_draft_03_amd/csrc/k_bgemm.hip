@@ -463,7 +463,7 @@ __global__ __launch_bounds__(TL::NTHR) void k_blm_head(LmArgs a, int n_p, int n_
     ArgState st[WM];
     int sl[WM];     // local sequence of each row this lane holds
     float am[WM];   // W8A8: the rows' activation scales
-  #pragma unroll
+#pragma unroll
     for (int j = 0; j < WM; ++j) {
       arg_init(st[j]);
       const int m = min(mb * BM + (wm * WM + j) * 16 + r16, a.M - 1);
@@ -493,13 +493,13 @@ __global__ __launch_bounds__(TL::NTHR) void k_blm_head(LmArgs a, int n_p, int n_
                                                         a.K, a.M, mb * BM, wave, lane);
         block_product<SW8, NSTAGE, TL>(pl, 0, 2 * steps_w, lds, acc);
       }
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < WN; ++i)
-  #pragma unroll
+#pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int vl = (wn * WN + i) * 16 + 4 * g + r, v = vb * BN + vl;
           const float sc = WFP8 ? s_scale[vl] : 1.0f;
-  #pragma unroll
+#pragma unroll
           for (int j = 0; j < WM; ++j) {
             const float x = A8 ? acc[i][j][r] * sc * am[j] : acc[i][j][r] * sc;
             const int m = mb * BM + (wm * WM + j) * 16 + r16;
@@ -509,7 +509,7 @@ __global__ __launch_bounds__(TL::NTHR) void k_blm_head(LmArgs a, int n_p, int n_
           }
         }
     }
-  #pragma unroll
+#pragma unroll
     for (int j = 0; j < WM; ++j) {
       st[j] = arg_merge(st[j], arg_shfl_xor(st[j], 16));
       st[j] = arg_merge(st[j], arg_shfl_xor(st[j], 32));
