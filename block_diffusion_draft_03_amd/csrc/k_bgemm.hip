@@ -493,6 +493,16 @@ __global__ __launch_bounds__(TL::NTHR) void k_blm_head(LmArgs a, int n_p, int n_
                                                         a.K, a.M, mb * BM, wave, lane);
         block_product<SW8, NSTAGE, TL>(pl, 0, 2 * steps_w, lds, acc);
       }
+      // Two passes per row: the block's logits (masked ones as -inf, kept in
+      // acc) with this lane's largest and its first index, then one
+      // exponential per logit against the row's merged maximum.
+      float bm[WM];
+      uint32_t bi[WM];
+#pragma unroll
+      for (int j = 0; j < WM; ++j) {
+        bm[j] = -__builtin_huge_valf();
+        bi[j] = 0xFFFFFFFFu;
+      }
 #pragma unroll
       for (int i = 0; i < WN; ++i)
 #pragma unroll
@@ -505,9 +515,28 @@ __global__ __launch_bounds__(TL::NTHR) void k_blm_head(LmArgs a, int n_p, int n_
             const int m = mb * BM + (wm * WM + j) * 16 + r16;
             if (a.logits && m < a.M) a.logits[(size_t)m * a.V + v] = x;
             const bool ok = !masked || ((s_mask[sl[j] * MW + (vl >> 5)] >> (vl & 31)) & 1u);
-            arg_push(st[j], x, (uint32_t)v, ok);
+            const float xo = ok ? x : -__builtin_huge_valf();
+            acc[i][j][r] = xo;
+            // values come in increasing v, so a strict > keeps the lowest id of a tie
+            bi[j] = xo > bm[j] ? (uint32_t)v : bi[j];
+            bm[j] = fmaxf(bm[j], xo);
           }
         }
+#pragma unroll
+      for (int j = 0; j < WM; ++j) {
+        const float mn = fmaxf(st[j].mx, bm[j]);
+        const float off = -mn * LOG2E;
+        float s = 0.0f;
+#pragma unroll
+        for (int i = 0; i < WN; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) s += fast_exp2(fmaf(acc[i][j][r], LOG2E, off));
+        const bool any = mn > -__builtin_huge_valf();  // else every value so far is masked
+        const float se = st[j].se * fast_exp2(fmaf(st[j].mx, LOG2E, off)) + s;
+        st[j].se = any ? se : st[j].se;
+        st[j].idx = bm[j] > st[j].mx ? bi[j] : st[j].idx;
+        st[j].mx = any ? mn : st[j].mx;
+      }
     }
 #pragma unroll
     for (int j = 0; j < WM; ++j) {
