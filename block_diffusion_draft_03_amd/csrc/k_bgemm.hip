@@ -226,8 +226,8 @@ __device__ __forceinline__ f32x4 mfma16x16x128_e4m3(const i32x8 &a, const i32x8 
 // of columns 32c + 8g + e (c = 0..3, e = 0..7) in that order; the product
 // only needs both operands in one K order, and the activation rows come
 // with each step's codes stored in exactly that order per lane group
-// (launch_quant_rows_a8), so a lane's operand is 16-byte chunks 2g and
-// 2g + 1 of its row. Weight fragments are read one tile ahead.
+// (launch_quant_rows_a8), so a lane's operand is 16-byte chunks g and g + 4
+// of its row. Weight fragments are read one tile ahead.
 template <class TL>
 __device__ __forceinline__ void mma_stage_a8(const uint4 *slot, int wn, int wm, int lane,
                                              f32x4 (&acc)[TL::WN][TL::WM]) {
@@ -244,7 +244,7 @@ __device__ __forceinline__ void mma_stage_a8(const uint4 *slot, int wn, int wm, 
 #pragma unroll
   for (int j = 0; j < WM; ++j) {
     const uint4 *row = arow + j * 16 * 8;
-    const uint4 x0 = row[(2 * g) ^ swz], x1 = row[(2 * g + 1) ^ swz];
+    const uint4 x0 = row[g ^ swz], x1 = row[(g + 4) ^ swz];
     af[j] = i32x8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
   }
 #pragma unroll

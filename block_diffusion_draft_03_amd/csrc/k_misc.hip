@@ -202,8 +202,9 @@ __global__ __launch_bounds__(256) void k_fp8_mirror(const uint16_t *src, int h, 
 // E4M3 activation rows of the W8A8 LM head, one workgroup per row: the
 // mirror's recipe (s = amax / 448, 1 for an all-zero row; code = E4M3(x / s)
 // with IEEE float32 division), stored in the head's K order: inside each
-// 128-column step, bytes 32g + 8c .. + 7 hold columns 32c + 8g .. + 7, so the
-// 32 codes that lane group g of a 16x16x128 operand takes are contiguous.
+// 128-column step, the 8 codes of columns 32c + 8g .. + 7 sit in half c & 1
+// of 16-byte chunk g + 4 (c >> 1), so lane group g of a 16x16x128 operand
+// takes chunks g and g + 4 (the bf16 head's read pattern).
 __global__ __launch_bounds__(256) void k_quant_rows_a8(const uint16_t *src, int h, uint8_t *codes, float *scale) {
   __shared__ float red[4];
   const int m = blockIdx.x;
@@ -219,8 +220,9 @@ __global__ __launch_bounds__(256) void k_quant_rows_a8(const uint16_t *src, int 
   if (threadIdx.x == 0) scale[m] = s;
   uint8_t *out = codes + (size_t)m * h;
   for (int p = threadIdx.x; p < h / 8; p += blockDim.x) {
-    // output piece p: step p / 16, piece q = 4g + c of the step, from columns 32c + 8g
-    const int step = p >> 4, q = p & 15, g = q >> 2, c = q & 3;
+    // output piece p: step p / 16, piece q of the step = half q & 1 of chunk
+    // q / 2 = g + 4 (c >> 1), from columns 32c + 8g
+    const int step = p >> 4, q = p & 15, g = (q >> 1) & 3, c = 2 * (q >> 3) + (q & 1);
     const uint4 x = *(const uint4 *)(row + step * 128 + 32 * c + 8 * g);
     const uint32_t w[4] = {x.x, x.y, x.z, x.w};
     uint32_t lo = 0, hi = 0;
