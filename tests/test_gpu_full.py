@@ -9,7 +9,8 @@ oracle on the same seeded inputs:
 * batch of 32 sequences, ctx ~ U[512, 4096], 8 new rows each (sampled
   sequences checked one by one against the oracle);
 * batch of 64 with the FP8 LM-head mirror, FP8 KV cache and 50% grammar
-  bitmasks (mirror codes bit-exact on sampled rows; sampled sequences);
+  bitmasks (mirror codes bit-exact on sampled rows; sampled sequences), and
+  the same with E4M3 activation rows into the LM head (W8A8);
 * single sequence, 1024 ctx rows, with FP8 drafter weights and LM head.
 """
 import sys
