@@ -27,9 +27,14 @@ down``), each a matrix in PyTorch Linear layout ``[out, in]`` or a gain
 vector; ``kv_scale`` ``[L, 2, n_kv]`` f32 when the KV cache is FP8.
 
 Parity status: each step is pinned by tests/test_oracle_*.py (closed forms,
-library routines, the explicit-loop twin in ``brute``); the composition of the
-steps is the reading stated in each docstring and is otherwise unpinned (the
-pages print no worked example).
+library routines, the explicit-loop twin in ``brute`` with its own storage
+codecs, on every variant: bf16 / FP8 KV cache, bf16 / FP8 / W8A8 LM head, FP8
+drafter weights, a given RoPE table, both draft-row conventions); the YaRN
+table at every pair index against the wavelength-ratio form of its
+definition; ``top2_margin`` on hand-built rows and against a scan. The
+composition of the steps at full geometry is the reading stated in each
+docstring and is otherwise unpinned (the pages print no worked example), as is
+the RoPE pairing convention itself.
 """
 import math
 
@@ -137,6 +142,24 @@ def silu(x):
     return x / (1.0 + np.exp(-x))
 
 
+def gemm_input(x):
+    """The activation operand of one of the head's dense products, as that
+    product takes it: rounded to bf16 (round to nearest, ties to even).
+
+    Reading R10, applied to every dense product of the head (fc, the fused
+    ctx K/V projection, Q/K/V, o_proj, gate/up, down, the LM head): the pages
+    describe the head's products as bf16 dense GEMMs over BF16 weights (the
+    fused K/V projection as a single dense GEMM over a BF16 weight,
+    [Head/atlas] field ``fused_kv_weight``; the logits product over the
+    target's BF16 LM head as a BF16 dense GEMM, [Head/atlas] field
+    ``lm_head_nvfp4``), so both operands are
+    bf16 and only the accumulation is wider. The weights are used as stored
+    (bf16 for the full geometry; the tiny workload's fp32 weights as given);
+    the products themselves are exact float64 sums. The residual stream, the
+    norms, RoPE and attention stay in float64 (they are not dense GEMMs)."""
+    return bf16_round(x)
+
+
 def gqa_attention(q, k, v, num_kv_heads):
     """Grouped-query attention without a mask.
 
@@ -181,10 +204,15 @@ def fp8_head_mirror(lm_head_bf16_bits):
     s_v = amax_v / 448 and q_vk = enc(w_vk / s_v). Both the scale and the
     quotient are computed in float32, the precision of the stored scale, so
     the integer codes are a deterministic function of the bf16 head. An
-    all-zero row gets scale 1. Rows are independent, so they are processed
-    in blocks of 2048 on a thread pool (memory and time only).
+    all-zero row gets scale 1. The mirror is of the bf16 head ([Head/atlas]
+    field ``lm_head_shared``: the target's bf16 LM head), so a head given in
+    fp32 (the tiny workload) is taken at its bf16 value first. Rows are
+    independent, so they are processed in blocks of 2048 on a thread pool
+    (memory and time only).
     """
     src = np.asarray(lm_head_bf16_bits)
+    if src.dtype != np.uint16:
+        src = (bf16_round(stored_to_f64(src)).astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
     V, h = src.shape
     codes = np.empty((V, h), dtype=np.uint8)
     scale = np.empty(V, dtype=np.float32)
@@ -333,10 +361,12 @@ class OracleHead:
         ``stack_rows`` is ``[rows, T*Ht]`` (shallow-to-deep concatenation of
         the hiddens at the target layers, [DraftProposer] ``propose``
         argument ``target_hidden_stack``). u = S fc^T, c = RMSNorm(u;
-        hidden_norm) ([Head/atlas], fields ``fc`` and ``hidden_norm``).
+        hidden_norm) ([Head/atlas], fields ``fc`` and ``hidden_norm``). The
+        stack is stored as bf16, so it already is the fc product's bf16
+        operand (``gemm_input``).
         """
         s = stored_to_f64(stack_rows)
-        return rms_norm(s @ self.fc.T, self.hidden_norm, self.eps)
+        return rms_norm(gemm_input(s) @ self.fc.T, self.hidden_norm, self.eps)
 
     def ctx_kv(self, c_hat, positions):
         """Every layer's ctx K and V from one normalised ctx feature.
@@ -351,16 +381,14 @@ class OracleHead:
         field ``kv_cache``) or FP8 E4M3 with one f32 scale per (layer, K|V,
         kv head) ([Head/atlas], field ``kv_cache``).
 
-        The fused projection is one bf16 dense GEMM over a BF16 weight
-        ([Head/atlas], field ``fused_kv_weight``), so its input c enters as
-        bf16: c is rounded to bf16 here, and the products are exact float64
-        sums of those bf16 values. This fixes the values every cache code is
-        decided on.
+        The fused projection is a bf16 dense GEMM (``gemm_input``): c enters
+        rounded to bf16 and the products are exact float64 sums of those
+        bf16 values.
         Returns lists over layers of ``[rows, n_kv, d]`` K and V.
         """
         ks, vs = [], []
         n = c_hat.shape[0]
-        c_in = bf16_round(c_hat)
+        c_in = gemm_input(c_hat)
         for l, lw in enumerate(self.layers):
             k = (c_in @ lw["k"].T).reshape(n, self.n_kv, self.d)
             v = (c_in @ lw["v"].T).reshape(n, self.n_kv, self.d)
@@ -437,10 +465,11 @@ class OracleHead:
         """One drafter layer, pre-norm residual (reading of the layer form):
         a = RMSNorm(h), q/k/v projections, RoPE on q and k, GQA attention over
         [ctx window ; block], h += o_proj(o); b = RMSNorm(h),
-        h += down(silu(gate b) * up b)."""
+        h += down(silu(gate b) * up b). The operands a, o, b and the SwiGLU
+        product enter their dense products as bf16 (``gemm_input``)."""
         lw = self.layers[l]
         R = hid.shape[0]
-        a = rms_norm(hid, lw["in_norm"], self.eps)
+        a = gemm_input(rms_norm(hid, lw["in_norm"], self.eps))
         q = (a @ lw["q"].T).reshape(R, self.n_q, self.d)
         k = (a @ lw["k"].T).reshape(R, self.n_kv, self.d)
         v = (a @ lw["v"].T).reshape(R, self.n_kv, self.d)
@@ -449,17 +478,18 @@ class OracleHead:
         kk = np.concatenate([ctx_k, k], axis=0)
         vv = np.concatenate([ctx_v, v], axis=0)
         o = gqa_attention(q, kk, vv, self.n_kv)
-        hid = hid + o.reshape(R, self.n_q * self.d) @ lw["o"].T
-        b = rms_norm(hid, lw["post_norm"], self.eps)
-        m = silu(b @ lw["gate"].T) * (b @ lw["up"].T)
+        hid = hid + gemm_input(o.reshape(R, self.n_q * self.d)) @ lw["o"].T
+        b = gemm_input(rms_norm(hid, lw["post_norm"], self.eps))
+        m = gemm_input(silu(b @ lw["gate"].T) * (b @ lw["up"].T))
         return hid + m @ lw["down"].T
 
     def logits(self, hid):
         """Final RMSNorm then the shared LM head ([Head/atlas], fields
         ``norm``, ``lm_head_shared``). FP8 head: l_v = s_v * sum_k dec(q_vk)
         z_k ([Head/atlas], field ``lm_head_shared_fp8``); W8A8 head: z is
-        replaced by its per-row E4M3 value fp8_rows(z)."""
-        z = rms_norm(hid, self.final_norm, self.eps)
+        replaced by its per-row E4M3 value fp8_rows(z). z enters the product
+        as bf16 (``gemm_input``), so the W8A8 head quantises that bf16 row."""
+        z = gemm_input(rms_norm(hid, self.final_norm, self.eps))
         if self.head_a8:
             z = fp8_rows(z)
         l = z @ self.lm.T
@@ -550,7 +580,10 @@ def select(logits, bitmask, num_drafts, shifted=False):
 
 
 def top2_margin(logits, bitmask=None):
-    """Per-row gap between the largest and second-largest (masked) logit."""
+    """Per-row gap between the largest and second-largest (masked) logit: 0
+    for a tie at the top, +inf when one token is allowed, nan when none is.
+    The GPU acceptance rule compares ids on rows whose margin exceeds 0.05
+    (the tolerance stated for this path)."""
     lg = logits if bitmask is None else apply_bitmask(logits, bitmask)
     part = np.partition(lg, -2, axis=1)
     return part[:, -1] - part[:, -2]

@@ -237,13 +237,15 @@ def test_window_truncation_equals_shifted_short_context():
     head_w.precompute(st_w, stack[32 - W:])
     r_short = head_w.propose(st_w, 11, 32 - (32 - W), 3)
     # equal up to the bf16 rounding of the cached K, which is taken after the
-    # rotation (about 1e-5 here); a window off by one row moves the logits by
-    # about 1e-2
-    assert np.allclose(r_full["logits"], r_short["logits"], atol=3e-5)
+    # rotation (about 3e-5 on the logits), and the bf16 operands of the dense
+    # products, which that difference can tip into the neighbouring bf16 value
+    # (2^-9 relative each; at most ~7e-4 on the logits over seeds 3..6); a
+    # window off by one row moves the logits by 4e-2 or more
+    assert np.allclose(r_full["logits"], r_short["logits"], atol=2e-3)
     st_w1 = head_w.new_state()
     head_w.precompute(st_w1, stack[32 - W - 1:])
     r_off = head_w.propose(st_w1, 11, W + 1, 3)
-    assert not np.allclose(r_full["logits"], r_off["logits"], atol=1e-3)
+    assert np.abs(r_full["logits"] - r_off["logits"]).max() > 1e-2
 
 
 def test_trim_equals_recompute():
@@ -461,13 +463,14 @@ def test_w8a8_logits_within_activation_error_bound():
     rng = np.random.default_rng(12)
     hid = rng.standard_normal((6, geo.hidden))
     lw, la = h_w.logits(hid), h_a.logits(hid)
-    z = O.rms_norm(hid, h_w.final_norm, h_w.eps).astype(np.float32).astype(np.float64)
+    # the head's operand: the final-normed row as bf16 (exact in float32)
+    z = O.gemm_input(O.rms_norm(hid, h_w.final_norm, h_w.eps))
     s = np.abs(z).max(axis=1) / 448.0
     e = np.maximum(np.abs(z) * 2.0 ** -4, s[:, None] * 2.0 ** -10)
     wabs = np.abs(h_w.lm) * h_w.lm_scale.astype(np.float64)[:, None]
     bound = e @ wabs.T
-    # the float32 rounding of z itself is below 2^-24 relative
-    slack = (np.abs(z) * 2.0 ** -23) @ wabs.T
+    # float64 summation order only
+    slack = (np.abs(z) * 2.0 ** -40) @ wabs.T
     diff = np.abs(la - lw)
     assert np.all(diff <= bound + slack)
     assert diff.max() > 0.05 * bound.max()
