@@ -121,6 +121,16 @@ def _stream_handle(stream):
     return int(s.cuda_stream)
 
 
+def _on(stream):
+    """Context in which the call's tensors (outputs and uploaded temporaries)
+    are allocated on the stream the library enqueues on: torch's caching
+    allocator then hands a freed temporary out again only in that stream's
+    order, after the kernels that read it."""
+    import contextlib
+    import torch
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def to_device(arr, device="cuda"):
     """numpy array (uint16 = bf16 bits, uint8 = E4M3 codes, f32, i32) ->
     torch device tensor holding the same bytes."""
@@ -246,45 +256,48 @@ class Head:
     def precompute(self, states, n_new, stack, stream=None):
         """Append ctx rows: stack is a device tensor [sum(n_new), T*Ht] (bf16
         bits as int16) or a numpy uint16 array (uploaded)."""
-        if isinstance(stack, np.ndarray):
-            stack = to_device(stack, self.device)
-        arr = (C.c_void_p * len(states))(*[s.handle.value for s in states])
-        nn = np.ascontiguousarray(n_new, dtype=np.int32)
-        _check(self.lib, self.lib.dflash_precompute_ctx_kv(self.handle, arr, len(states),
-                                                           nn.ctypes.data_as(C.c_void_p), _ptr(stack),
-                                                           _stream_handle(stream)))
+        with _on(stream):
+            if isinstance(stack, np.ndarray):
+                stack = to_device(stack, self.device)
+            arr = (C.c_void_p * len(states))(*[s.handle.value for s in states])
+            nn = np.ascontiguousarray(n_new, dtype=np.int32)
+            _check(self.lib, self.lib.dflash_precompute_ctx_kv(self.handle, arr, len(states),
+                                                               nn.ctypes.data_as(C.c_void_p), _ptr(stack),
+                                                               _stream_handle(stream)))
         return stack
 
     def propose(self, state, last_token, position, num_drafts, bitmask=None, logits=False, stream=None):
         import torch
         g = self.geo.gamma
-        ids = torch.empty(g, dtype=torch.int32, device=self.device)
-        conf = torch.empty(1, dtype=torch.float32, device=self.device)
-        rp = torch.empty(g, dtype=torch.float32, device=self.device)
-        lg = torch.empty((g, self.geo.vocab), dtype=torch.float32, device=self.device) if logits else None
-        if isinstance(bitmask, np.ndarray):
-            bitmask = to_device(bitmask, self.device)
-        _check(self.lib, self.lib.dflash_propose(self.handle, state.handle, int(last_token), int(position),
-                                                 int(num_drafts), _ptr(bitmask), _ptr(ids), _ptr(conf), _ptr(rp),
-                                                 _ptr(lg), _stream_handle(stream)))
+        with _on(stream):
+            ids = torch.empty(g, dtype=torch.int32, device=self.device)
+            conf = torch.empty(1, dtype=torch.float32, device=self.device)
+            rp = torch.empty(g, dtype=torch.float32, device=self.device)
+            lg = torch.empty((g, self.geo.vocab), dtype=torch.float32, device=self.device) if logits else None
+            if isinstance(bitmask, np.ndarray):
+                bitmask = to_device(bitmask, self.device)
+            _check(self.lib, self.lib.dflash_propose(self.handle, state.handle, int(last_token), int(position),
+                                                     int(num_drafts), _ptr(bitmask), _ptr(ids), _ptr(conf),
+                                                     _ptr(rp), _ptr(lg), _stream_handle(stream)))
         return {"ids": ids, "conf": conf, "row_prob": rp, "logits": lg}
 
     def propose_batch(self, states, last_tokens, positions, num_drafts, bitmasks=None, logits=False, stream=None):
         import torch
         n, g = len(states), self.geo.gamma
-        ids = torch.empty((n, g), dtype=torch.int32, device=self.device)
-        conf = torch.empty(n, dtype=torch.float32, device=self.device)
-        rp = torch.empty((n, g), dtype=torch.float32, device=self.device)
-        lg = torch.empty((n, g, self.geo.vocab), dtype=torch.float32, device=self.device) if logits else None
-        if isinstance(bitmasks, np.ndarray):
-            bitmasks = to_device(bitmasks, self.device)
-        arr = (C.c_void_p * n)(*[s.handle.value for s in states])
-        toks = np.ascontiguousarray(last_tokens, dtype=np.uint32)
-        pos = np.ascontiguousarray(positions, dtype=np.int64)
-        _check(self.lib, self.lib.dflash_propose_batch(self.handle, arr, n, toks.ctypes.data_as(C.c_void_p),
-                                                       pos.ctypes.data_as(C.c_void_p), int(num_drafts),
-                                                       _ptr(bitmasks), _ptr(ids), _ptr(conf), _ptr(rp), _ptr(lg),
-                                                       _stream_handle(stream)))
+        with _on(stream):
+            ids = torch.empty((n, g), dtype=torch.int32, device=self.device)
+            conf = torch.empty(n, dtype=torch.float32, device=self.device)
+            rp = torch.empty((n, g), dtype=torch.float32, device=self.device)
+            lg = torch.empty((n, g, self.geo.vocab), dtype=torch.float32, device=self.device) if logits else None
+            if isinstance(bitmasks, np.ndarray):
+                bitmasks = to_device(bitmasks, self.device)
+            arr = (C.c_void_p * n)(*[s.handle.value for s in states])
+            toks = np.ascontiguousarray(last_tokens, dtype=np.uint32)
+            pos = np.ascontiguousarray(positions, dtype=np.int64)
+            _check(self.lib, self.lib.dflash_propose_batch(self.handle, arr, n, toks.ctypes.data_as(C.c_void_p),
+                                                           pos.ctypes.data_as(C.c_void_p), int(num_drafts),
+                                                           _ptr(bitmasks), _ptr(ids), _ptr(conf), _ptr(rp),
+                                                           _ptr(lg), _stream_handle(stream)))
         return {"ids": ids, "conf": conf, "row_prob": rp, "logits": lg}
 
     def after_verify(self, state, num_accepted):
@@ -294,18 +307,20 @@ class Head:
         import torch
         geo = self.geo
         dt = torch.uint8 if geo.kv_dtype == "fp8" else torch.int16
-        k = torch.empty((n_rows, geo.num_kv_heads, geo.head_dim), dtype=dt, device=self.device)
-        v = torch.empty_like(k)
-        _check(self.lib, self.lib.dflash_state_read_kv(self.handle, state.handle, layer, row0, n_rows, _ptr(k),
-                                                       _ptr(v), _stream_handle(stream)))
+        with _on(stream):
+            k = torch.empty((n_rows, geo.num_kv_heads, geo.head_dim), dtype=dt, device=self.device)
+            v = torch.empty_like(k)
+            _check(self.lib, self.lib.dflash_state_read_kv(self.handle, state.handle, layer, row0, n_rows, _ptr(k),
+                                                           _ptr(v), _stream_handle(stream)))
         return k, v
 
     def read_lm_head_fp8(self, stream=None):
         import torch
-        codes = torch.empty((self.geo.vocab, self.geo.hidden), dtype=torch.uint8, device=self.device)
-        scale = torch.empty(self.geo.vocab, dtype=torch.float32, device=self.device)
-        _check(self.lib, self.lib.dflash_read_lm_head_fp8(self.handle, _ptr(codes), _ptr(scale),
-                                                          _stream_handle(stream)))
+        with _on(stream):
+            codes = torch.empty((self.geo.vocab, self.geo.hidden), dtype=torch.uint8, device=self.device)
+            scale = torch.empty(self.geo.vocab, dtype=torch.float32, device=self.device)
+            _check(self.lib, self.lib.dflash_read_lm_head_fp8(self.handle, _ptr(codes), _ptr(scale),
+                                                              _stream_handle(stream)))
         return codes, scale
 
     def take_kv(self, state):

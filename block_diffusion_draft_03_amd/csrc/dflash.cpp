@@ -29,15 +29,12 @@ int set_err(int code, const std::string &m) {
 constexpr uint64_t HEAD_MAGIC = 0x44464c4153484844ull;   // "DFLASHHD"
 constexpr uint64_t STATE_MAGIC = 0x44464c4153485354ull;  // "DFLASHST"
 constexpr uint64_t DEAD_MAGIC = 0xdeadull;
-constexpr int ATTN_TARGET_WGS = 512;  // attention workgroups a launch aims for (two per CU)
-constexpr int ATTN_MAX_SPLITS = 64;   // splits per (sequence, kv head) merged by one wave
-constexpr int ATTN_PREF_SPLITS = 16;
 // bf16 proposes of up to this many rows stream the weights through the
 // few-row kernels; from one more row on the tiled kernels are faster
 // (measured at 48 and 64 rows: 16% less time per propose; at 32 rows the
 // few-row path is 16% faster)
 constexpr int PROPOSE_FEW_ROWS = 32;
-constexpr int PREFILL_ROWS = 1024;    // rows of one tiled precompute pass  // preferred bound: the merge reads every split's partial
+constexpr int PREFILL_ROWS = 1024;    // rows of one tiled precompute pass
 
 #define HIP_TRY(expr)                                                                          \
   do {                                                                                         \
@@ -431,12 +428,8 @@ int build_impl(dflash_head *H, const dflash_weights *w, hipStream_t st) {
   if (H->tiled_prefill) max_splits = std::max(max_splits, bgemm_splits(g.h, g.fc_in, PREFILL_ROWS));
   TRY(H->alloc(&H->part, (size_t)max_splits * std::max({M, (size_t)GEMM_MAX_ROWS, pre_rows}) * h));
   const size_t R = (size_t)g.rep * g.gamma;
-  {
-    // partial slots: the propose split rule never needs more
-    const int max_tiles = (std::min(g.W, H->cfg.max_seq_len) + 15 + 31) / 32 + 1;
-    const int per_seq = std::min(ATTN_MAX_SPLITS, (max_tiles + attn_max_tiles_per_split() - 1) / attn_max_tiles_per_split() + 1);
-    H->attn_slots = std::max({ATTN_TARGET_WGS * 2, g.max_batch * g.n_kv * per_seq, g.n_kv * ATTN_MAX_SPLITS});
-  }
+  // partial slots: every plan the propose takes fits (checked at build)
+  H->attn_slots = (int)attn_slots(g, H->cfg.max_seq_len, attn_max_tiles_per_split());
   TRY(H->alloc(&H->ss, (size_t)((g.h + 15) / 16) * GEMM_MAX_ROWS));
   TRY(H->alloc(&H->tile_ctr, (size_t)((g.h + 15) / 16)));
   HIP_TRY(hipMemsetAsync(H->tile_ctr, 0, (size_t)((g.h + 15) / 16) * sizeof(int), st));
@@ -580,6 +573,21 @@ int propose_impl(dflash_head *H, dflash_state *const *states, int n, const uint3
   }
   const int M = n * g.gamma;
   const int h = g.h;
+  // few rows: the residual GEMMs finish their own splits and every consumer
+  // applies the RMSNorm row scale from per-unit sums of squares (H->ss)
+  // the W8A8 head needs the final-normed rows in act (no deferred row scale)
+  const bool fused = !g.a8 && M <= (g.fp8w ? GEMM_MAX_ROWS : PROPOSE_FEW_ROWS);
+  const bool tiled_lm = !fused && (M > GEMM_MAX_ROWS || !g.fp8w || g.a8) && blm_ok(g.V, h);
+  if (g.a8 && !tiled_lm) return set_err(DFLASH_E_INVALID, "the W8A8 LM head needs the tiled head");
+  // attention splits, planned before anything is enqueued
+  AttnPlan plan;
+  {
+    int32_t tiles[DFLASH_MAX_BATCH];
+    for (int i = 0; i < n; ++i) tiles[i] = attn_tiles(states[i]->rows.ctx_len, g.W);
+    std::string err;
+    const int rc = attn_plan(n, tiles, g.n_kv, attn_max_tiles_per_split(), H->attn_slots / g.n_kv, &plan, &err);
+    if (rc != DFLASH_OK) return set_err(rc, err);
+  }
   hipEvent_t t_all = H->interval_begin(DFLASH_PHASE_PROPOSE, st);
 
   SetupArgs sa{};
@@ -591,10 +599,6 @@ int propose_impl(dflash_head *H, dflash_state *const *states, int n, const uint3
   sa.half_dim = g.d / 2;
   sa.mask_id = g.mask_id;
   sa.inv_freq = H->inv_freq;
-  // few rows: the residual GEMMs finish their own splits and every consumer
-  // applies the RMSNorm row scale from per-unit sums of squares (H->ss)
-  // the W8A8 head needs the final-normed rows in act (no deferred row scale)
-  const bool fused = !g.a8 && M <= (g.fp8w ? GEMM_MAX_ROWS : PROPOSE_FEW_ROWS);
   sa.hid = H->hid;
   sa.a = H->act;
   sa.ss_out = fused ? H->ss : nullptr;
@@ -623,49 +627,20 @@ int propose_impl(dflash_head *H, dflash_state *const *states, int n, const uint3
   aa.ml_part = H->ml_part;
   aa.out = H->attn;
   aa.out_ld = g.q_dim;
-  {
-    // ctx tiles of 32 positions from the block-aligned window start. The
-    // last split of a sequence also takes the block tile, which counts as one
-    // more tile: a sequence with T ctx tiles gets (T + tps) / tps splits of at
-    // most tps units, so the last one is no longer than the others (at T = 32,
-    // tps = 2: sixteen splits of two ctx tiles and one of the block tile). tps
-    // is the smallest that keeps the launch within ATTN_TARGET_WGS workgroups
-    // (one round, two per CU), no smaller than a sequence's preferred bound of
-    // ATTN_PREF_SPLITS splits.
-    std::vector<int> T(n);
-    int max_T = 0;
-    for (int i = 0; i < n; ++i) {
-      const int c = states[i]->rows.ctx_len;
-      const int lo = g.W > 0 ? std::max(0, c - g.W) : c;
-      aa.seq[i].ctx_len = c;
-      aa.seq[i].win_start = lo;
-      aa.seq[i].bt = states[i]->d_bt;
-      T[i] = lo < c ? (c - lo / 16 * 16 + 31) / 32 : 0;
-      max_T = std::max(max_T, T[i]);
-    }
-    const int max_tps = attn_max_tiles_per_split();
-    auto splits_of = [](int t, int tps) { return (t + tps) / tps; };
-    auto flat_splits = [&](int tps) {
-      long f = 0;
-      for (int i = 0; i < n; ++i) f += splits_of(T[i], tps);
-      return f;
-    };
-    const long cap = std::min<long>(ATTN_MAX_FLAT, H->attn_slots / g.n_kv);
-    int tps = std::max(1, (max_T + ATTN_PREF_SPLITS - 1) / ATTN_PREF_SPLITS);
-    tps = std::max(tps, (max_T + ATTN_MAX_SPLITS) / ATTN_MAX_SPLITS);
-    while (tps < max_tps && (flat_splits(tps) * g.n_kv > ATTN_TARGET_WGS || flat_splits(tps) > cap)) ++tps;
-    if (tps > max_tps || flat_splits(tps) > cap || splits_of(max_T, tps) > ATTN_MAX_SPLITS)
-      return set_err(DFLASH_E_INVALID, "context window too long for the attention splits");
-    aa.tps = tps;
-    int f = 0;
-    for (int i = 0; i < n; ++i) {
-      aa.seq[i].split0 = f;
-      aa.seq[i].nsplit = splits_of(T[i], tps);
-      for (int c = 0; c < aa.seq[i].nsplit; ++c) aa.split_seq[f + c] = (uint8_t)i;
-      f += aa.seq[i].nsplit;
-    }
-    aa.n_split = f;
+  // ctx tiles of 32 positions from the block-aligned window start, in the
+  // splits of the plan (attn_plan: the last split of a sequence also takes
+  // the block tile)
+  for (int i = 0; i < n; ++i) {
+    const int c = states[i]->rows.ctx_len;
+    aa.seq[i].ctx_len = c;
+    aa.seq[i].win_start = g.W > 0 ? std::max(0, c - g.W) : c;
+    aa.seq[i].bt = states[i]->d_bt;
+    aa.seq[i].split0 = plan.split0[i];
+    aa.seq[i].nsplit = plan.nsplit[i];
+    for (int c2 = 0; c2 < plan.nsplit[i]; ++c2) aa.split_seq[plan.split0[i] + c2] = (uint8_t)i;
   }
+  aa.tps = plan.tps;
+  aa.n_split = plan.n_split;
 
   // act holds RMSNorm(h) with the next consumer's gain: layer 0's input norm
   // comes from the setup kernel, every later one from the residual finish.
@@ -717,8 +692,6 @@ int propose_impl(dflash_head *H, dflash_state *const *states, int n, const uint3
   la.part_se = H->lm_se;
   la.part_idx = H->lm_idx;
   la.rs = rs;
-  const bool tiled_lm = !fused && (M > GEMM_MAX_ROWS || !g.fp8w || g.a8) && blm_ok(g.V, h);
-  if (g.a8 && !tiled_lm) return set_err(DFLASH_E_INVALID, "the W8A8 LM head needs the tiled head");
   if (tiled_lm) {
     la.z = H->act;
     la.M = M;
@@ -785,6 +758,7 @@ int dflash_build(const dflash_config *cfg, const dflash_weights *w, uint64_t str
   Geo g;
   std::string err;
   int rc = validate_config(*cfg, &g, &err);
+  if (rc == DFLASH_OK) rc = check_attn_capacity(g, cfg->max_seq_len, attn_max_tiles_per_split(), &err);
   if (rc != DFLASH_OK) return set_err(rc, err);
   int dev_count = 0;
   if (hipGetDeviceCount(&dev_count) != hipSuccess || dev_count < 1) return set_err(DFLASH_E_HIP, "no HIP device");
@@ -905,14 +879,17 @@ int dflash_precompute_ctx_kv(dflash_head *head, dflash_state *const *states, int
   }
   if (total > INT_MAX / 2) return set_err(DFLASH_E_INVALID, "too many rows");
   if (total > 0 && !stack) return set_err(DFLASH_E_INVALID, "stack is required when rows are appended");
-  // reserve blocks for every state first (no device work yet)
-  for (int i = 0; i < n; ++i) {
+  // reserve blocks for every state first, all or nothing (no device work yet)
+  {
+    std::vector<SeqRows *> rows(n);
+    std::vector<int32_t> caps(n);
+    for (int i = 0; i < n; ++i) {
+      rows[i] = &states[i]->rows;
+      caps[i] = states[i]->cap_blocks;
+    }
     std::string err;
-    int32_t first = 0;
-    int rc = seq_reserve(&states[i]->rows, &H->pool, n_new[i], &first, &err);
-    if (rc != DFLASH_OK) return set_err(rc, "state " + std::to_string(i) + ": " + err);
-    if ((int32_t)states[i]->rows.blocks.size() > states[i]->cap_blocks)
-      return set_err(DFLASH_E_NO_BLOCKS, "block table capacity exceeded");
+    const int rc = reserve_rows(rows.data(), n, n_new, caps.data(), &H->pool, &err);
+    if (rc != DFLASH_OK) return set_err(rc, err);
   }
   hipStream_t st = to_stream(stream);
   for (int i = 0; i < n; ++i) TRY(sync_block_table(states[i], st));
@@ -1063,7 +1040,7 @@ int dflash_install_kv(dflash_head *head, dflash_state *st, const int32_t *blocks
       return set_err(DFLASH_E_INVALID, "block " + std::to_string(blocks[i]) + " is held by a live state");
   HIP_TRY(hipDeviceSynchronize());  // no launch still reads the state's block table
   std::string err;
-  const int rc = seq_install(&st->rows, &head->pool, blocks, n_blocks, rows, &err);
+  const int rc = seq_install(&st->rows, &head->pool, blocks, n_blocks, rows, head->cfg.max_seq_len, &err);
   if (rc != DFLASH_OK) return set_err(rc, err);
   for (int32_t i = 0; i < n_blocks; ++i) st->h_bt[i] = blocks[i];
   HIP_TRY(hipMemcpy(st->d_bt, st->h_bt, (size_t)n_blocks * sizeof(int32_t), hipMemcpyHostToDevice));

@@ -71,9 +71,42 @@ int32_t dfh_seq_take(void *seq, int32_t *out, int32_t cap, int32_t *rows) {
   return (int32_t)b.size();
 }
 
-int dfh_seq_install(void *seq, void *pool, const int32_t *blocks, int32_t n, int32_t rows) {
+int dfh_seq_install(void *seq, void *pool, const int32_t *blocks, int32_t n, int32_t rows, int32_t max_seq_len) {
   g_err.clear();
-  return seq_install((SeqRows *)seq, (BlockPool *)pool, blocks, n, rows, &g_err);
+  return seq_install((SeqRows *)seq, (BlockPool *)pool, blocks, n, rows, max_seq_len, &g_err);
+}
+
+// the all-or-nothing reservation of a multi-state precompute
+int dfh_reserve_rows(void **seqs, int32_t n, const int32_t *n_new, const int32_t *cap_blocks, void *pool) {
+  g_err.clear();
+  return reserve_rows((SeqRows *const *)seqs, n, n_new, cap_blocks, (BlockPool *)pool, &g_err);
+}
+
+int32_t dfh_attn_tiles(int32_t ctx_len, int32_t window) { return attn_tiles(ctx_len, window); }
+
+// the propose's split plan: *tps and *n_split on success
+int dfh_attn_plan(int32_t n, const int32_t *tiles, int32_t n_kv, int32_t max_tps, int64_t slot_cap, int32_t *tps,
+                  int32_t *n_split, int32_t *nsplit_out) {
+  g_err.clear();
+  AttnPlan p;
+  const int rc = attn_plan(n, tiles, n_kv, max_tps, slot_cap, &p, &g_err);
+  if (rc == DFLASH_OK) {
+    *tps = p.tps;
+    *n_split = p.n_split;
+    if (nsplit_out)
+      for (int32_t i = 0; i < n; ++i) nsplit_out[i] = p.nsplit[i];
+  }
+  return rc;
+}
+
+// what dflash_build checks before it allocates: the config and the attention
+// capacity of its widest batch of longest contexts (max_tps ctx tiles per split)
+int dfh_build_check(const dflash_config *c, int32_t max_tps) {
+  g_err.clear();
+  Geo g;
+  int rc = validate_config(*c, &g, &g_err);
+  if (rc == DFLASH_OK) rc = check_attn_capacity(g, c->max_seq_len, max_tps, &g_err);
+  return rc;
 }
 
 int dflash_yarn_inv_freq(int32_t head_dim, float rope_theta, float factor, float beta_fast, float beta_slow,

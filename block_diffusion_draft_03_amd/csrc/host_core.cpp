@@ -124,7 +124,7 @@ int seq_init(SeqRows *s, BlockPool *pool, int64_t budget_tokens, const int32_t *
       pool->take(block_ids[i]);
     }
     s->blocks.assign(block_ids, block_ids + n_ids);
-    s->cap_rows = (int64_t)n_ids * DFLASH_KV_BLOCK;
+    s->cap_rows = std::min<int64_t>((int64_t)n_ids * DFLASH_KV_BLOCK, max_seq_len);
     if (budget_tokens != INT64_MAX && budget_tokens < s->cap_rows) s->cap_rows = budget_tokens;
     s->grow = false;
     return DFLASH_OK;
@@ -134,11 +134,11 @@ int seq_init(SeqRows *s, BlockPool *pool, int64_t budget_tokens, const int32_t *
     s->grow = true;
     return DFLASH_OK;
   }
-  if (budget_tokens > (int64_t)INT32_MAX - DFLASH_KV_BLOCK) return fail(err, DFLASH_E_INVALID, "budget_tokens too large");
-  int64_t nb = (budget_tokens + DFLASH_KV_BLOCK - 1) / DFLASH_KV_BLOCK;
+  const int64_t cap = std::min<int64_t>(budget_tokens, max_seq_len);
+  int64_t nb = (cap + DFLASH_KV_BLOCK - 1) / DFLASH_KV_BLOCK;
   if (nb > pool->free_count()) return fail(err, DFLASH_E_NO_BLOCKS, "KV pool has too few free blocks for the budget");
   for (int64_t i = 0; i < nb; ++i) s->blocks.push_back(pool->alloc());
-  s->cap_rows = budget_tokens;
+  s->cap_rows = cap;
   s->grow = false;
   return DFLASH_OK;
 }
@@ -154,6 +154,31 @@ int seq_reserve(SeqRows *s, BlockPool *pool, int32_t n, int32_t *first_new_block
   if (!s->grow) return fail(err, DFLASH_E_NO_BLOCKS, "the state's blocks are exhausted");
   if (need_blocks - have > pool->free_count()) return fail(err, DFLASH_E_NO_BLOCKS, "the KV pool is exhausted");
   for (int64_t i = have; i < need_blocks; ++i) s->blocks.push_back(pool->alloc());
+  return DFLASH_OK;
+}
+
+void seq_unreserve(SeqRows *s, BlockPool *pool, int32_t first_new_block) {
+  while ((int32_t)s->blocks.size() > first_new_block) {
+    pool->release(s->blocks.back());
+    s->blocks.pop_back();
+  }
+}
+
+int reserve_rows(SeqRows *const *s, int32_t n, const int32_t *n_new, const int32_t *cap_blocks, BlockPool *pool,
+                 std::string *err) {
+  std::vector<int32_t> first(n > 0 ? n : 0, 0);
+  for (int32_t i = 0; i < n; ++i) {
+    int rc = seq_reserve(s[i], pool, n_new[i], &first[i], err);
+    if (rc == DFLASH_OK && cap_blocks && (int32_t)s[i]->blocks.size() > cap_blocks[i]) {
+      seq_unreserve(s[i], pool, first[i]);
+      rc = fail(err, DFLASH_E_NO_BLOCKS, "block table capacity exceeded");
+    }
+    if (rc != DFLASH_OK) {
+      for (int32_t j = i - 1; j >= 0; --j) seq_unreserve(s[j], pool, first[j]);
+      if (err) *err = "state " + std::to_string(i) + ": " + *err;
+      return rc;
+    }
+  }
   return DFLASH_OK;
 }
 
@@ -183,11 +208,13 @@ void seq_take(SeqRows *s, std::vector<int32_t> *blocks, int32_t *rows) {
   s->grow = true;
 }
 
-int seq_install(SeqRows *s, BlockPool *pool, const int32_t *blocks, int32_t n, int32_t rows, std::string *err) {
+int seq_install(SeqRows *s, BlockPool *pool, const int32_t *blocks, int32_t n, int32_t rows, int32_t max_seq_len,
+                std::string *err) {
   if (s->ctx_len != 0) return fail(err, DFLASH_E_INVALID, "install needs a state that holds no rows");
   if (!blocks || n < 1) return fail(err, DFLASH_E_INVALID, "install needs at least one block");
   if (rows < 0 || (int64_t)rows > (int64_t)n * DFLASH_KV_BLOCK)
     return fail(err, DFLASH_E_INVALID, "installed rows must fit the installed blocks");
+  if (rows > max_seq_len) return fail(err, DFLASH_E_INVALID, "installed rows exceed max_seq_len");
   std::vector<uint8_t> seen(pool->size(), 0);
   for (int32_t i = 0; i < n; ++i) {
     const int32_t b = blocks[i];
@@ -199,8 +226,80 @@ int seq_install(SeqRows *s, BlockPool *pool, const int32_t *blocks, int32_t n, i
   s->blocks.assign(blocks, blocks + n);
   s->ctx_len = rows;
   s->pending_base = rows;
-  s->cap_rows = std::max<int64_t>(s->cap_rows, (int64_t)n * DFLASH_KV_BLOCK);
+  s->cap_rows = std::min<int64_t>(std::max<int64_t>(s->cap_rows, (int64_t)n * DFLASH_KV_BLOCK), max_seq_len);
   s->grow = true;
+  return DFLASH_OK;
+}
+
+int32_t attn_tiles(int32_t c, int32_t window) {
+  const int32_t lo = window > 0 ? std::max(0, c - window) : c;
+  return lo < c ? (c - lo / DFLASH_KV_BLOCK * DFLASH_KV_BLOCK + 31) / 32 : 0;
+}
+
+int32_t attn_tiles_worst(int32_t window, int32_t max_seq_len) {
+  // tiles grow with c up to the window; past it the aligned start adds up to
+  // 15 rows, so the worst case is among c = min(W, max) .. min(W + 15, max)
+  int32_t worst = 0;
+  const int32_t c0 = std::min(window, max_seq_len);
+  for (int32_t c = c0; c <= std::min(c0 + DFLASH_KV_BLOCK - 1, max_seq_len); ++c)
+    worst = std::max(worst, attn_tiles(c, window));
+  return worst;
+}
+
+int attn_plan(int32_t n, const int32_t *tiles, int32_t n_kv, int32_t max_tps, int64_t slot_cap, AttnPlan *plan,
+              std::string *err) {
+  if (n < 1 || n > DFLASH_MAX_BATCH || n_kv < 1 || max_tps < 1)
+    return fail(err, DFLASH_E_INVALID, "attention plan: bad batch, head count or tile limit");
+  int32_t max_T = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    if (tiles[i] < 0) return fail(err, DFLASH_E_INVALID, "attention plan: negative tile count");
+    max_T = std::max(max_T, tiles[i]);
+  }
+  // a sequence with t ctx tiles takes (t + tps) / tps splits of at most tps
+  // units (its block tile counted as one more), so its last split is no
+  // longer than the others
+  auto splits_of = [](int64_t t, int64_t tps) { return (t + tps) / tps; };
+  auto flat = [&](int32_t tps) {
+    int64_t f = 0;
+    for (int32_t i = 0; i < n; ++i) f += splits_of(tiles[i], tps);
+    return f;
+  };
+  const int64_t cap = std::min<int64_t>(ATTN_MAX_FLAT, slot_cap);
+  // the preferred split count, as far as the tile limit allows, and never
+  // more than ATTN_MAX_SPLITS splits
+  int32_t tps = std::min(max_tps, std::max(1, (max_T + ATTN_PREF_SPLITS - 1) / ATTN_PREF_SPLITS));
+  tps = std::max(tps, (max_T + ATTN_MAX_SPLITS) / ATTN_MAX_SPLITS);
+  while (tps < max_tps && (flat(tps) * n_kv > ATTN_TARGET_WGS || flat(tps) > cap)) ++tps;
+  if (tps > max_tps || flat(tps) > cap || splits_of(max_T, tps) > ATTN_MAX_SPLITS)
+    return fail(err, DFLASH_E_INVALID,
+                "context window too long for the attention splits (" + std::to_string(max_T) + " tiles of 32 keys, " +
+                    std::to_string(n) + " sequences)");
+  int32_t f = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    plan->split0[i] = f;
+    plan->nsplit[i] = (int32_t)splits_of(tiles[i], tps);
+    f += plan->nsplit[i];
+  }
+  plan->tps = tps;
+  plan->n_split = f;
+  return DFLASH_OK;
+}
+
+int64_t attn_slots(const Geo &g, int32_t max_seq_len, int32_t max_tps) {
+  const int64_t worst = attn_tiles_worst(g.W, max_seq_len);
+  const int64_t per_seq = std::min<int64_t>(ATTN_MAX_SPLITS, (worst + max_tps) / max_tps);
+  return std::max<int64_t>({(int64_t)ATTN_TARGET_WGS * 2, (int64_t)g.max_batch * g.n_kv * per_seq,
+                            (int64_t)g.n_kv * ATTN_MAX_SPLITS});
+}
+
+int check_attn_capacity(const Geo &g, int32_t max_seq_len, int32_t max_tps, std::string *err) {
+  std::vector<int32_t> tiles(g.max_batch, attn_tiles_worst(g.W, max_seq_len));
+  AttnPlan plan;
+  std::string e;
+  if (attn_plan(g.max_batch, tiles.data(), g.n_kv, max_tps, attn_slots(g, max_seq_len, max_tps) / g.n_kv, &plan, &e) !=
+      DFLASH_OK)
+    return fail(err, DFLASH_E_INVALID,
+                "config: max_batch sequences of min(ctx_window, max_seq_len) rows exceed the attention splits: " + e);
   return DFLASH_OK;
 }
 

@@ -51,7 +51,8 @@ struct SeqRows {
 };
 
 // Create the row bookkeeping: explicit blocks, a known budget (all blocks
-// taken now) or an unknown budget (grow up to max_seq_len).
+// taken now) or an unknown budget (grow up to max_seq_len). A state never
+// holds more than max_seq_len rows: a larger budget or block list is capped.
 int seq_init(SeqRows *s, BlockPool *pool, int64_t budget_tokens, const int32_t *block_ids, int32_t n_ids,
              int32_t max_seq_len, std::string *err);
 
@@ -59,6 +60,18 @@ int seq_init(SeqRows *s, BlockPool *pool, int64_t budget_tokens, const int32_t *
 // and *first_new_block is the logical index of the first one. Does not
 // change ctx_len. Returns DFLASH_E_NO_BLOCKS without side effects on failure.
 int seq_reserve(SeqRows *s, BlockPool *pool, int32_t n, int32_t *first_new_block, std::string *err);
+
+// Undo a seq_reserve: give back the blocks from logical index
+// first_new_block on (those the reservation appended).
+void seq_unreserve(SeqRows *s, BlockPool *pool, int32_t first_new_block);
+
+// Reserve n_new[i] more rows for each of n states, all or nothing: when state
+// i cannot take its rows (budget, pool, or more blocks than cap_blocks[i]
+// when cap_blocks is given), the reservations of states 0..i-1 are undone and
+// the pool is as before. A state may appear more than once (at most once with
+// rows to append). Does not change ctx_len.
+int reserve_rows(SeqRows *const *s, int32_t n, const int32_t *n_new, const int32_t *cap_blocks, BlockPool *pool,
+                 std::string *err);
 
 // Keep the first a pending rows (0 <= a <= ctx_len - pending_base).
 int seq_trim(SeqRows *s, int32_t a, std::string *err);
@@ -77,7 +90,48 @@ void seq_take(SeqRows *s, std::vector<int32_t> *blocks, int32_t *rows);
 // back to the pool first. Rows must fit the blocks and the state's row
 // capacity (which grows to the installed blocks). Errors leave the state
 // and the pool unchanged.
-int seq_install(SeqRows *s, BlockPool *pool, const int32_t *blocks, int32_t n, int32_t rows, std::string *err);
+int seq_install(SeqRows *s, BlockPool *pool, const int32_t *blocks, int32_t n, int32_t rows, int32_t max_seq_len,
+                std::string *err);
+
+// ---- attention split plan of a propose launch ----
+// The block's attention over a sequence's context runs in splits of up to
+// tps ctx tiles of 32 keys (from the window start aligned down to a KV
+// block); the sequence's last split also takes the block's own keys, which
+// count as one more tile. A launch aims for ATTN_TARGET_WGS workgroups (two
+// per compute unit) over all sequences and kv heads, prefers at most
+// ATTN_PREF_SPLITS splits per sequence, and cannot exceed ATTN_MAX_SPLITS
+// splits per sequence (one wave merges a row's splits) or ATTN_MAX_FLAT
+// splits in all (the split-to-sequence map travels in the launch arguments).
+constexpr int ATTN_MAX_FLAT = 1024;
+constexpr int ATTN_TARGET_WGS = 512;
+constexpr int ATTN_MAX_SPLITS = 64;
+constexpr int ATTN_PREF_SPLITS = 16;
+
+// Ctx tiles of 32 keys a sequence of ctx_len rows attends to: rows
+// [max(0, c - W), c), from that start aligned down to 16; W = 0 keeps none.
+int32_t attn_tiles(int32_t ctx_len, int32_t window);
+
+// The most tiles any state of a head can need (0 <= ctx_len <= max_seq_len).
+int32_t attn_tiles_worst(int32_t window, int32_t max_seq_len);
+
+struct AttnPlan {
+  int32_t tps = 0, n_split = 0;
+  int32_t split0[DFLASH_MAX_BATCH], nsplit[DFLASH_MAX_BATCH];
+};
+
+// Plan n sequences (tiles[i] ctx tiles each) over n_kv kv heads, with at most
+// max_tps tiles per split and slot_cap partial slots per kv head. Fails with
+// DFLASH_E_INVALID, touching nothing, when no split size fits.
+int attn_plan(int32_t n, const int32_t *tiles, int32_t n_kv, int32_t max_tps, int64_t slot_cap, AttnPlan *plan,
+              std::string *err);
+
+// Partial slots (per kv head) a head keeps for its attention splits.
+int64_t attn_slots(const Geo &g, int32_t max_seq_len, int32_t max_tps);
+
+// Build-time check that the widest batch of the longest contexts has a split
+// plan: then every propose the head accepts has one (the plan is monotone in
+// every sequence's tiles and in the batch width).
+int check_attn_capacity(const Geo &g, int32_t max_seq_len, int32_t max_tps, std::string *err);
 
 // YaRN-corrected RoPE table (dflash_yarn_inv_freq): out[head_dim / 2].
 int yarn_inv_freq(int32_t head_dim, double theta, double factor, double beta_fast, double beta_slow,

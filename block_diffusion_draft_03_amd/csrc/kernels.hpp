@@ -1,12 +1,13 @@
 // kernels.hpp - argument structs and host launchers of the gfx950 kernels.
 // Every launcher enqueues on `stream` and returns hipSuccess or the launch
-// error; shapes are validated by the caller (dflash.hip) before any launch.
+// error; shapes are validated by the caller (dflash.cpp) before any launch.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "../../include/dflash.h"
+#include "host_core.hpp"
 
 namespace dflash {
 
@@ -158,7 +159,7 @@ struct AttnSeq {
   int split0, nsplit;  // this sequence's first split (over all sequences of the launch) and split count (1..64)
 };
 
-constexpr int ATTN_MAX_FLAT = 1024;  // splits over all sequences of one launch
+// ATTN_MAX_FLAT (splits over all sequences of one launch): host_core.hpp
 
 struct AttnArgs {
   const uint16_t *qkv;   // [n_seq * gamma, ld] rows [Q | K | V], RoPE applied

@@ -17,11 +17,20 @@
  *   - Device pointers are HIP device addresses on the current device; host
  *     pointers are ordinary process memory. Each argument says which.
  *   - `stream` is a hipStream_t cast to uint64_t (0 = the null stream). All
- *     device work of a call is enqueued on it; no call synchronises the host
- *     except dflash_build, dflash_state_create and dflash_state_free.
+ *     device work of a call is enqueued on it. The calls that wait on the
+ *     host: dflash_build (its stream), dflash_destroy, dflash_state_create,
+ *     dflash_state_free, dflash_take_kv and dflash_install_kv (the device),
+ *     dflash_timing_read and dflash_timing_enable(0) (the recorded events),
+ *     and a dflash_precompute_ctx_kv of more than 64 rows when one of its two
+ *     pinned staging buffers (row positions and block tables of a 1024-row
+ *     pass) is still being copied by an earlier pass of it or of an earlier
+ *     such call: it waits for that copy. dflash_propose and
+ *     dflash_propose_batch never wait.
  *   - A negative return value is a dflash_status error; dflash_last_error()
  *     then describes it. Every argument check runs on the host before any
- *     kernel is enqueued, so a failed call leaves the device untouched.
+ *     kernel is enqueued, so a failed call leaves the device untouched and
+ *     the head's bookkeeping as it was (a HIP failure while enqueueing,
+ *     DFLASH_E_HIP, is the exception).
  *   - A head's scratch buffers are shared by all calls on that head: calls on
  *     one head must be ordered on the device (use one stream, or synchronise
  *     between streams). Host-side calls on one head are serialised by an
@@ -76,7 +85,7 @@ typedef struct {
   int32_t kv_block_size;     /* must be DFLASH_KV_BLOCK */
   int32_t kv_pool_blocks;    /* physical blocks in the head's paged KV pool */
   int32_t max_batch;         /* widest batch (1..DFLASH_MAX_BATCH) */
-  int32_t max_seq_len;       /* per-state row ceiling when its budget is unknown */
+  int32_t max_seq_len;       /* most ctx rows any state holds (larger budgets and block lists are capped) */
   dflash_dtype weight_dtype;  /* F32 or BF16: dtype of the drafter tensors given at build */
   dflash_dtype lm_head_dtype; /* BF16, or FP8_E4M3 (a mirror is built unless one is given) */
   dflash_dtype kv_dtype;      /* BF16, or FP8_E4M3 with per-(layer, K|V, kv head) scales */
@@ -139,6 +148,10 @@ typedef struct {
  * tensors to bf16, builds the FP8 LM-head mirror when asked ([Head/atlas]
  * field lm_head_shared_fp8: E4M3 codes, per-row scale amax / 448), and
  * allocates the paged KV pool and the scratch. Synchronises `stream`.
+ * DFLASH_E_INVALID, before anything is allocated, when max_batch sequences of
+ * min(ctx_window, max_seq_len) ctx rows would not fit the attention's splits
+ * (at most 64 splits of 64 tiles of 32 keys per sequence and 1024 splits per
+ * launch); a head that builds accepts every batch up to max_batch.
  * On success *out owns all of it until dflash_destroy. */
 int dflash_build(const dflash_config *cfg, const dflash_weights *w, uint64_t stream, dflash_head **out);
 
@@ -156,10 +169,12 @@ int dflash_propose_batch_max(const dflash_head *head);
 /* Per-sequence state ([DraftProposer] alloc_state / alloc_state_for).
  * budget_tokens: most ctx rows the sequence will hold; INT64_MAX = unknown
  * (the build's max_seq_len applies and blocks are taken from the pool as
- * rows arrive). With a known budget every block is taken now.
+ * rows arrive). With a known budget every block is taken now. No state
+ * holds more than max_seq_len rows: a larger budget is capped to it.
  * block_ids (host, optional): explicit physical pool blocks for the
- * sequence, in logical order; n_ids of them bound its capacity. They must be
- * free. Returns DFLASH_E_NO_BLOCKS when the pool cannot supply the blocks. */
+ * sequence, in logical order; n_ids of them bound its capacity (and
+ * max_seq_len). They must be free. Returns DFLASH_E_NO_BLOCKS when the pool
+ * cannot supply the blocks. */
 int dflash_state_create(dflash_head *head, int64_t budget_tokens, const int32_t *block_ids, int32_t n_ids,
                         dflash_state **out);
 
@@ -184,7 +199,9 @@ int dflash_state_ctx_len(const dflash_state *st);
  * larger call (prompt-scale prefill) runs in passes of up to 1024 rows through
  * MFMA-tiled GEMMs. A row's cached K/V is bit-identical for any call of the
  * same kind; the two kinds agree to rounding.
- * DFLASH_E_NO_BLOCKS if a state would exceed its budget or the pool. */
+ * DFLASH_E_NO_BLOCKS if a state would exceed its budget or the pool; the
+ * blocks are reserved for all states or for none (a failure gives back what
+ * the states before the failing one took). */
 int dflash_precompute_ctx_kv(dflash_head *head, dflash_state *const *states, int32_t n, const int32_t *n_new,
                              const void *stack, uint64_t stream);
 
@@ -241,7 +258,7 @@ int dflash_after_verify(dflash_head *head, dflash_state *st, int32_t num_accepte
  *
  * dflash_install_kv gives carried blocks (n_blocks >= 1 distinct allocated
  * blocks that no live state holds, at most the state's block-table capacity)
- * holding `rows` committed rows (0 <= rows <= 16 n_blocks) to a state that
+ * holding `rows` committed rows (0 <= rows <= min(16 n_blocks, max_seq_len)) to a state that
  * holds no rows; the state's own blocks return to the pool. A later propose
  * sees exactly the carried rows. DFLASH_E_INVALID otherwise, nothing changed.
  *

@@ -41,7 +41,12 @@ def host():
     lib.dfh_seq_release.argtypes = [vp, vp]
     lib.dfh_seq_delete.argtypes = [vp]
     lib.dfh_seq_take.argtypes = [vp, vp, C.c_int32, C.POINTER(C.c_int32)]
-    lib.dfh_seq_install.argtypes = [vp, vp, vp, C.c_int32, C.c_int32]
+    lib.dfh_seq_install.argtypes = [vp, vp, vp, C.c_int32, C.c_int32, C.c_int32]
+    lib.dfh_reserve_rows.argtypes = [vp, C.c_int32, vp, vp, vp]
+    lib.dfh_attn_tiles.argtypes = [C.c_int32, C.c_int32]
+    lib.dfh_attn_plan.argtypes = [C.c_int32, vp, C.c_int32, C.c_int32, C.c_int64, C.POINTER(C.c_int32),
+                                  C.POINTER(C.c_int32), vp]
+    lib.dfh_build_check.argtypes = [vp, C.c_int32]
     lib.dflash_yarn_inv_freq.argtypes = [C.c_int32, C.c_float, C.c_float, C.c_float, C.c_float, C.c_int32, vp]
     return lib
 
@@ -192,15 +197,16 @@ def test_kv_carry_take_and_install(host):
     assert host.dfh_seq_append(a, pool, 5) == OK                  # the emptied state grows again
     carried = out[:3].copy()
     p = lambda arr: arr.ctypes.data_as(C.c_void_p)
-    assert host.dfh_seq_install(a, pool, p(carried), 3, 40) == E_INVALID     # the state holds rows
+    assert host.dfh_seq_install(a, pool, p(carried), 3, 40, 8192) == E_INVALID     # the state holds rows
     b, _ = _seq(host, pool, budget=32)                             # a fresh state with 2 own blocks
     free_before = host.dfh_pool_free_count(pool)
-    assert host.dfh_seq_install(b, pool, p(carried), 3, 49) == E_INVALID     # 49 rows > 3 blocks
-    assert host.dfh_seq_install(b, pool, p(np.array([carried[0], carried[0]], np.int32)), 2, 10) == E_INVALID
+    assert host.dfh_seq_install(b, pool, p(carried), 3, 49, 8192) == E_INVALID     # 49 rows > 3 blocks
+    assert host.dfh_seq_install(b, pool, p(np.array([carried[0], carried[0]], np.int32)), 2, 10, 8192) == E_INVALID
     free_id = np.array([63], np.int32)
-    assert host.dfh_seq_install(b, pool, p(free_id), 1, 1) == E_INVALID      # not an allocated block
+    assert host.dfh_seq_install(b, pool, p(free_id), 1, 1, 8192) == E_INVALID      # not an allocated block
     assert host.dfh_pool_free_count(pool) == free_before          # errors change nothing
-    assert host.dfh_seq_install(b, pool, p(carried), 3, 40) == OK
+    assert host.dfh_seq_install(b, pool, p(carried), 3, 40, 39) == E_INVALID  # > max_seq_len
+    assert host.dfh_seq_install(b, pool, p(carried), 3, 40, 8192) == OK
     assert host.dfh_seq_ctx_len(b) == 40 and host.dfh_seq_pending(b) == 0
     got = np.zeros(8, dtype=np.int32)
     assert host.dfh_seq_blocks(b, p(got), 8) == 3 and np.array_equal(got[:3], carried)
@@ -245,3 +251,102 @@ def test_yarn_table_matches_oracle(host, theta, d):
         assert host.dflash_yarn_inv_freq(*args, out.ctypes.data_as(C.c_void_p)) == E_INVALID
     assert host.dflash_yarn_inv_freq(d, theta, 64.0, 32.0, 1.0, 4096, None) == E_INVALID
 
+
+
+# --------------------------------------------------------------------------
+# error contract: what the library checks before it enqueues anything
+# --------------------------------------------------------------------------
+
+def test_multi_state_reservation_is_all_or_nothing(host):
+    """A precompute over several states reserves blocks for all of them or
+    for none: when a later state cannot take its rows, the blocks the earlier
+    ones took go back and the pool and every state are as before."""
+    pool = host.dfh_pool_new(20)
+    a, _ = _seq(host, pool)                     # grows from the pool
+    b, _ = _seq(host, pool, budget=16)          # one block, 16 rows at most
+    c, _ = _seq(host, pool)
+    assert host.dfh_seq_append(a, pool, 5) == OK
+    blocks_a = _blocks(host, a)
+    free0 = host.dfh_pool_free_count(pool)
+    seqs = (C.c_void_p * 3)(a, c, b)
+    p = lambda arr: arr.ctypes.data_as(C.c_void_p)
+    # a and c fit, b's 20 rows exceed its budget: nothing is kept
+    assert host.dfh_reserve_rows(seqs, 3, p(np.array([40, 33, 20], np.int32)), None, pool) == E_NO_BLOCKS
+    assert "state 2" in host.dfh_last_error().decode()
+    assert host.dfh_pool_free_count(pool) == free0
+    assert _blocks(host, a) == blocks_a and _blocks(host, c) == []
+    # the pool runs dry at the second state (6 + 13 blocks > 18 free)
+    assert host.dfh_reserve_rows(seqs, 3, p(np.array([100, 200, 0], np.int32)), None, pool) == E_NO_BLOCKS
+    assert "state 1" in host.dfh_last_error().decode()
+    assert host.dfh_pool_free_count(pool) == free0 and _blocks(host, a) == blocks_a
+    # a block-table capacity below what a state needs is refused the same way
+    caps = np.array([8, 1, 1], np.int32)
+    assert host.dfh_reserve_rows(seqs, 3, p(np.array([40, 33, 0], np.int32)), p(caps), pool) == E_NO_BLOCKS
+    assert host.dfh_pool_free_count(pool) == free0 and _blocks(host, c) == []
+    # and when everything fits, all states get their blocks
+    assert host.dfh_reserve_rows(seqs, 3, p(np.array([40, 33, 16], np.int32)), None, pool) == OK
+    assert len(_blocks(host, a)) == 3 and len(_blocks(host, c)) == 3
+    for s in (a, b, c):
+        host.dfh_seq_release(s, pool)
+        host.dfh_seq_delete(s)
+    assert host.dfh_pool_free_count(pool) == 20
+    host.dfh_pool_delete(pool)
+
+
+def test_state_rows_capped_at_max_seq_len(host):
+    pool = host.dfh_pool_new(64)
+    s, st = _seq(host, pool, budget=1000, max_seq_len=100)   # budget above the ceiling: 7 blocks, 100 rows
+    assert st == OK and len(_blocks(host, s)) == 7
+    assert host.dfh_seq_append(s, pool, 100) == OK and host.dfh_seq_append(s, pool, 1) == E_NO_BLOCKS
+    t, st = _seq(host, pool, ids=np.arange(20, 30), max_seq_len=100)  # 10 blocks, still 100 rows
+    assert st == OK
+    assert host.dfh_seq_append(t, pool, 101) == E_NO_BLOCKS and host.dfh_seq_append(t, pool, 100) == OK
+    for x in (s, t):
+        host.dfh_seq_release(x, pool)
+        host.dfh_seq_delete(x)
+    host.dfh_pool_delete(pool)
+
+
+def _plan(host, tiles, n_kv=4, max_tps=64, cap=1 << 20):
+    t = np.ascontiguousarray(tiles, dtype=np.int32)
+    tps, n_split = C.c_int32(), C.c_int32()
+    per = np.zeros(len(t), np.int32)
+    rc = host.dfh_attn_plan(len(t), t.ctypes.data_as(C.c_void_p), n_kv, max_tps, cap, C.byref(tps), C.byref(n_split),
+                            per.ctypes.data_as(C.c_void_p))
+    return rc, tps.value, n_split.value, per.tolist()
+
+
+def test_attention_split_plan(host):
+    """Tiles from the 16-aligned window start; one sequence of 1024 ctx rows:
+    32 tiles in 16 splits of 2 plus the block tile's split; the preferred split
+    count yields to the tile limit for long windows; too many sequences of
+    long windows have no plan."""
+    assert host.dfh_attn_tiles(1024, 4096) == 32
+    assert host.dfh_attn_tiles(0, 4096) == 0 and host.dfh_attn_tiles(500, 0) == 0
+    assert host.dfh_attn_tiles(4100, 4096) == 129      # rows [4, 4100) from aligned start 0
+    assert host.dfh_attn_tiles(4112, 4096) == 128      # rows [16, 4112)
+    assert _plan(host, [32]) == (OK, 2, 17, [17])
+    assert _plan(host, [0]) == (OK, 1, 1, [1])           # the block tile alone
+    # a batch: splits grow until the launch fits two workgroups per CU
+    rc, tps, n_split, per = _plan(host, [32] * 32)
+    assert rc == OK and n_split * 4 <= 512 and per == [(32 + tps) // tps] * 32
+    # 1025 tiles (a 32768-row window): 64 tiles per split, 17 splits
+    assert _plan(host, [1025]) == (OK, 64, 17, [17])
+    # 64 such sequences need 1088 splits > 1024
+    rc, *_ = _plan(host, [1025] * 64)
+    assert rc == E_INVALID and "attention splits" in host.dfh_last_error().decode()
+    # more than 64 splits of 64 tiles for one sequence
+    assert _plan(host, [64 * 64])[0] == E_INVALID
+
+
+def test_build_rejects_configs_beyond_the_attention_splits(host):
+    """dflash_build's capacity check (the same host code): 64 sequences of a
+    32768-row window cannot be planned, 32 can, and the full workloads'
+    configs pass."""
+    assert host.dfh_build_check(C.byref(make_cfg(max_batch=64, ctx_window=32768, max_seq_len=32768)), 64) == E_INVALID
+    assert "attention splits" in host.dfh_last_error().decode()
+    assert host.dfh_build_check(C.byref(make_cfg(max_batch=32, ctx_window=32768, max_seq_len=32768)), 64) == OK
+    # a long window with short states is fine: the states bound the tiles
+    assert host.dfh_build_check(C.byref(make_cfg(max_batch=64, ctx_window=32768, max_seq_len=8192)), 64) == OK
+    for geo in (synth.TINY, synth.FULL, synth.FULL_FP8):
+        assert host.dfh_build_check(C.byref(make_cfg(geo, max_batch=64, max_seq_len=8192)), 64) == OK
