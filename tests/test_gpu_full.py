@@ -6,14 +6,20 @@ oracle on the same seeded inputs:
 * single sequence, 1024 ctx rows, 8 new rows per step;
 * single sequence, 4096 ctx rows in a permuted block table, 16-row verify
   appends trimmed by after_verify with num_accepted ~ U[0, 16];
-* batch of 32 sequences, ctx ~ U[512, 4096], 8 new rows each (sampled
-  sequences checked one by one against the oracle);
+* batch of 32 sequences, ctx ~ U[512, 4096], 8 new rows each;
 * batch of 64 with the FP8 LM-head mirror, FP8 KV cache and 50% grammar
-  bitmasks (mirror codes bit-exact on sampled rows; sampled sequences), and
-  the same with E4M3 activation rows into the LM head (W8A8);
+  bitmasks (mirror codes bit-exact on sampled rows), and the same with E4M3
+  activation rows into the LM head (W8A8);
 * single sequence, 1024 ctx rows, with FP8 drafter weights and LM head.
+
+Every sequence of the batches is checked (ids, probabilities, confidence and
+logits): the GPU runs a batch once (module fixture), then the sequences are
+checked against the oracle in chunks of eight, one test per chunk. Each test
+requires at least half of its rows to be margin-pinned (about three quarters
+are expected from the logit spread).
 """
 import sys
+from dataclasses import replace
 
 import numpy as np
 import pytest
@@ -21,13 +27,15 @@ import pytest
 import synth
 from oracle.dflash import OracleHead, fp8_head_mirror
 from oracle.numerics import bf16_to_f64, e4m3_decode
-from parity import check_propose, split_batch
+from parity import Tally, check_propose, split_batch
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 torch = pytest.importorskip("torch")
 
 GEO = synth.FULL
 GEO8 = synth.FULL_FP8
+CHUNK = 8
+MIN_SHARE = 0.5
 
 
 def say(*a):
@@ -52,22 +60,35 @@ def bf16_pair(weights):
     head.destroy()
 
 
-def _fill(head, orc, n_rows, tag, block_ids=None, budget=None, oracle=True):
+def _fill(head, n_rows, tag, block_ids=None, budget=None):
     st = head.state_create(budget_tokens=budget, block_ids=block_ids)
-    os_ = orc.new_state() if oracle else None
     stack = synth.make_stack(GEO, n_rows, tag=tag)
     head.precompute([st], [n_rows], stack)
     head.after_verify(st, n_rows)
-    if oracle:
-        orc.precompute(os_, stack)
-        orc.after_verify(os_, n_rows)
-    return st, os_
+    return st, stack
+
+
+def _oracle_state(orc, stack, new):
+    os_ = orc.new_state()
+    orc.precompute(os_, stack)
+    orc.after_verify(os_, len(stack))
+    orc.precompute(os_, new)
+    return os_
+
+
+def _host(res):
+    """The propose outputs as host arrays (the GPU's memory is released)."""
+    torch.cuda.synchronize()
+    return {k: (None if v is None else v.cpu().numpy()) for k, v in res.items()}
 
 
 def test_full_single_ctx1024(bf16_pair):
     head, orc = bf16_pair
-    st, os_ = _fill(head, orc, 1024, tag=1)
-    pinned = total = 0
+    st, stack = _fill(head, 1024, tag=1)
+    os_ = orc.new_state()
+    orc.precompute(os_, stack)
+    orc.after_verify(os_, 1024)
+    tally = Tally("full single_ctx1024")
     for step in range(2):
         new = synth.make_stack(GEO, 8, tag=1000 + step)
         head.precompute([st], [8], new)
@@ -76,12 +97,10 @@ def test_full_single_ctx1024(bf16_pair):
         say(f"[case] single ctx1024 step {step} ctx {st.ctx_len} tok {tok}")
         res = head.propose(st, tok, st.ctx_len, GEO.gamma - 1, logits=True)
         torch.cuda.synchronize()
-        p, _, n = check_propose(res, orc.propose(os_, tok, os_.ctx_len, GEO.gamma - 1), label=f"step {step}")
-        pinned += p
-        total += n
+        tally.add(check_propose(res, orc.propose(os_, tok, os_.ctx_len, GEO.gamma - 1), label=f"step {step}"))
         head.after_verify(st, 0)
         orc.after_verify(os_, 0)
-    say(f"[result] ctx1024: {pinned}/{total} rows margin-pinned, all pinned ids equal")
+    tally.finish(min_share=MIN_SHARE)
     # cached K/V of sampled rows and layers
     for layer in (0, 7):
         k, v = head.read_kv(st, layer, 1000, 24)
@@ -100,8 +119,12 @@ def test_full_single_ctx4096_permuted_trim(bf16_pair):
     steps = 2
     n_blocks = (4096 + 16 * steps) // 16
     perm = synth.make_block_permutation(n_blocks, 9000 - 64 * 3, tag=5) + 64 * 3
-    st, os_ = _fill(head, orc, 4096, tag=2, block_ids=perm)
+    st, stack = _fill(head, 4096, tag=2, block_ids=perm)
+    os_ = orc.new_state()
+    orc.precompute(os_, stack)
+    orc.after_verify(os_, 4096)
     acc = synth.make_accepted(steps, 16)
+    tally = Tally("full single_ctx4096_trim")
     for step in range(steps):
         new = synth.make_stack(GEO, 16, tag=2000 + step)
         head.precompute([st], [16], new)
@@ -112,48 +135,63 @@ def test_full_single_ctx4096_permuted_trim(bf16_pair):
         say(f"[case] ctx4096 step {step} accepted {acc[step]} ctx {st.ctx_len}")
         res = head.propose(st, tok, st.ctx_len, GEO.gamma - 1, logits=True)
         torch.cuda.synchronize()
-        check_propose(res, orc.propose(os_, tok, os_.ctx_len, GEO.gamma - 1), label=f"ctx4096 step {step}")
+        tally.add(check_propose(res, orc.propose(os_, tok, os_.ctx_len, GEO.gamma - 1), label=f"ctx4096 step {step}"))
+    tally.finish(min_share=MIN_SHARE)
     st.free()
 
 
-def test_full_batch32(bf16_pair):
-    head, orc = bf16_pair
-    n = 32
-    lens = synth.make_ctx_lengths(n, 512, 4096)
-    sample = [0, 7, int(np.argmax(lens)), int(np.argmin(lens))]
-    states, ostates = [], {}
-    for i in range(n):
-        st, os_ = _fill(head, orc, int(lens[i]), tag=300 + i, oracle=i in sample)
-        states.append(st)
-        if i in sample:
-            ostates[i] = os_
-    news = [synth.make_stack(GEO, 8, tag=3000 + i) for i in range(n)]
-    head.precompute(states, [8] * n, np.concatenate(news))
-    for i in sample:
-        orc.precompute(ostates[i], news[i])
-    toks = synth.make_tokens(GEO, n, tag=77)
+# ---------------------------------------------------------------- batch 32 --
+
+B32 = 32
+
+
+@pytest.fixture(scope="module")
+def batch32_run(bf16_pair):
+    """One propose_batch of the batch-32 workload; the inputs' recipe and the
+    GPU's outputs on the host."""
+    head, _ = bf16_pair
+    lens = synth.make_ctx_lengths(B32, 512, 4096)
+    states = [_fill(head, int(lens[i]), tag=300 + i)[0] for i in range(B32)]
+    news = [synth.make_stack(GEO, 8, tag=3000 + i) for i in range(B32)]
+    head.precompute(states, [8] * B32, np.concatenate(news))
+    toks = synth.make_tokens(GEO, B32, tag=77)
     pos = [s.ctx_len for s in states]
     say("[case] batch32 propose")
-    res = head.propose_batch(states, toks, pos, GEO.gamma - 1, logits=True)
-    torch.cuda.synchronize()
-    for i in sample:
-        say(f"[case] batch32 seq {i} ctx {pos[i]}")
-        ref = orc.propose(ostates[i], int(toks[i]), pos[i], GEO.gamma - 1)
-        check_propose(split_batch(res, i), ref, label=f"batch32 seq {i}")
+    out = _host(head.propose_batch(states, toks, pos, GEO.gamma - 1, logits=True))
     for s in states:
         s.free()
+    return {"lens": lens, "news": news, "toks": toks, "pos": pos, "gpu": out}
 
 
-@pytest.mark.parametrize("a8", [False, True], ids=["w8", "w8a8"])
-def test_full_batch64_fp8(weights, a8):
-    """The FP8 batch workload; w8a8: the same with E4M3 activation rows into
-    the LM head (W8A8 head on the E4M3 matrix cores)."""
-    from dataclasses import replace
+@pytest.mark.parametrize("chunk", range(B32 // CHUNK))
+def test_full_batch32(bf16_pair, batch32_run, chunk):
+    _, orc = bf16_pair
+    r = batch32_run
+    tally = Tally(f"full batch32 seqs {chunk * CHUNK}..{chunk * CHUNK + CHUNK - 1}")
+    for i in range(chunk * CHUNK, (chunk + 1) * CHUNK):
+        say(f"[case] batch32 seq {i} ctx {r['pos'][i]}")
+        os_ = _oracle_state(orc, synth.make_stack(GEO, int(r["lens"][i]), tag=300 + i), r["news"][i])
+        ref = orc.propose(os_, int(r["toks"][i]), r["pos"][i], GEO.gamma - 1)
+        tally.add(check_propose(split_batch(r["gpu"], i), ref, label=f"batch32 seq {i}"))
+    tally.finish(min_share=MIN_SHARE)
+
+
+# ------------------------------------------------------- batch 64, FP8 -----
+
+B64 = 64
+
+
+@pytest.fixture(scope="module", params=[False, True], ids=["w8", "w8a8"])
+def batch64_run(weights, request):
+    """The FP8 batch workload (and with a8 the same with E4M3 activation rows
+    into the LM head: the W8A8 head on the E4M3 matrix cores), run once on the
+    GPU; the mirror's codes and scales are checked bit for bit on sampled
+    rows first."""
     from block_diffusion_draft_03_amd import Head
+    a8 = request.param
     geo8 = replace(GEO8, lm_act_dtype="fp8") if a8 else GEO8
     say(f"[setup] fp8 head a8={a8}")
-    head = Head(geo8, weights, kv_pool_blocks=16800, max_batch=64, max_seq_len=8192)
-    # the mirror's codes and scales, bit for bit, on sampled rows
+    head = Head(geo8, weights, kv_pool_blocks=16800, max_batch=B64, max_seq_len=8192)
     codes, scale = head.read_lm_head_fp8()
     torch.cuda.synchronize()
     rows = np.sort(np.random.default_rng(3).choice(GEO.vocab, 2048, replace=False))
@@ -161,50 +199,66 @@ def test_full_batch64_fp8(weights, a8):
     rc, rs = fp8_head_mirror(weights["lm_head"][rows])
     gc = codes.cpu().numpy()[rows]
     gs = scale.cpu().numpy()[rows]
-    assert np.array_equal(gs, rs)
-    # codes may differ only in the sign of a zero
-    assert np.array_equal(e4m3_decode(gc), e4m3_decode(rc))
     del codes, scale
-    say("[setup] fp8 oracle")
-    orc = OracleHead(geo8.as_dict(), weights)
-    n = 64
-    lens = synth.make_ctx_lengths(n, 256, 4096, tag=1)
-    sample = [3, int(np.argmax(lens)), int(np.argmin(lens))]
-    states, ostates = [], {}
-    for i in range(n):
-        st, os_ = _fill(head, orc, int(lens[i]), tag=600 + i, oracle=i in sample)
-        states.append(st)
-        if i in sample:
-            ostates[i] = os_
-    news = [synth.make_stack(GEO, 8, tag=6000 + i) for i in range(n)]
-    head.precompute(states, [8] * n, np.concatenate(news))
-    for i in sample:
-        orc.precompute(ostates[i], news[i])
-    # FP8 cache of sampled rows: the GPU's K differs from the oracle's by the
-    # bf16 rounding of its GEMM inputs, about 2e-3 absolute (K elements are
-    # ~N(0, 0.9)); after quantisation the two may sit one E4M3 step apart
-    # plus that error. About 94% of the codes are identical.
-    k, _ = head.read_kv(states[sample[0]], 2, 0, 64)
-    torch.cuda.synchronize()
-    sk = weights["kv_scale"][2, 0].astype(np.float64)
-    kg = e4m3_decode(k.cpu().numpy()) * sk[None, :, None]
-    kr = np.stack(ostates[sample[0]].k[2][:64])
-    step = np.maximum(np.abs(kr) * 2.0 ** -3, sk[None, :, None] * 2.0 ** -9)
-    assert np.all(np.abs(kg - kr) <= step + 1e-2)
-    assert np.mean(kg == kr) > 0.9
-    masks = np.stack([synth.make_bitmask(GEO.vocab, 0.5, tag=i) for i in range(n)])
-    toks = synth.make_tokens(GEO, n, tag=88)
+    lens = synth.make_ctx_lengths(B64, 256, 4096, tag=1)
+    states = [_fill(head, int(lens[i]), tag=600 + i)[0] for i in range(B64)]
+    news = [synth.make_stack(GEO, 8, tag=6000 + i) for i in range(B64)]
+    head.precompute(states, [8] * B64, np.concatenate(news))
+    # FP8 cache of one sequence's first 64 rows, layer 2
+    k, _ = head.read_kv(states[3], 2, 0, 64)
+    kg = k.cpu().numpy()
+    masks = np.stack([synth.make_bitmask(GEO.vocab, 0.5, tag=i) for i in range(B64)])
+    toks = synth.make_tokens(GEO, B64, tag=88)
     pos = [s.ctx_len for s in states]
     say(f"[case] batch64 fp8 propose a8={a8}")
-    res = head.propose_batch(states, toks, pos, GEO.gamma - 1, bitmasks=masks, logits=True)
-    torch.cuda.synchronize()
-    for i in sample:
-        say(f"[case] batch64 fp8 a8={a8} seq {i} ctx {pos[i]}")
-        ref = orc.propose(ostates[i], int(toks[i]), pos[i], GEO.gamma - 1, masks[i])
-        check_propose(split_batch(res, i), ref, bitmask=masks[i], logit_tol=6e-2, label=f"fp8 seq {i}")
+    out = _host(head.propose_batch(states, toks, pos, GEO.gamma - 1, bitmasks=masks, logits=True))
     for s in states:
         s.free()
     head.destroy()
+    say("[setup] fp8 oracle")
+    orc = OracleHead(geo8.as_dict(), weights)
+    yield {"a8": a8, "orc": orc, "mirror": (gc, gs, rc, rs), "k_seq3_l2": kg, "lens": lens, "news": news,
+           "masks": masks, "toks": toks, "pos": pos, "gpu": out}
+
+
+def test_full_batch64_fp8_mirror_and_cache(batch64_run, weights):
+    r = batch64_run
+    gc, gs, rc, rs = r["mirror"]
+    assert np.array_equal(gs, rs)
+    # codes may differ only in the sign of a zero
+    assert np.array_equal(e4m3_decode(gc), e4m3_decode(rc))
+    # The GPU's K differs from the oracle's before quantisation by its float32
+    # arithmetic (a bf16 operand can also land on the neighbouring value where
+    # the float32 and float64 paths straddle a rounding boundary: ~1e-4 on K);
+    # after quantisation the two sit one E4M3 step apart near a code boundary,
+    # and near zero, where the step is s * 2^-9 ~ 2e-5, a few steps apart:
+    # one step plus 1e-2 absolute (a wrong scale moves most codes, below).
+    orc = r["orc"]
+    os_ = orc.new_state()
+    orc.precompute(os_, synth.make_stack(GEO, 64, tag=603))
+    sk = weights["kv_scale"][2, 0].astype(np.float64)
+    kg = e4m3_decode(r["k_seq3_l2"]) * sk[None, :, None]
+    kr = np.stack(os_.k[2][:64])
+    step = np.maximum(np.abs(kr) * 2.0 ** -3, sk[None, :, None] * 2.0 ** -9)
+    assert np.all(np.abs(kg - kr) <= step + 1e-2)
+    assert np.mean(kg == kr) > 0.9
+
+
+@pytest.mark.parametrize("chunk", range(B64 // CHUNK))
+def test_full_batch64_fp8(batch64_run, chunk):
+    r = batch64_run
+    orc = r["orc"]
+    tally = Tally(f"full batch64 fp8 a8={r['a8']} seqs {chunk * CHUNK}..{chunk * CHUNK + CHUNK - 1}")
+    for i in range(chunk * CHUNK, (chunk + 1) * CHUNK):
+        say(f"[case] batch64 fp8 a8={r['a8']} seq {i} ctx {r['pos'][i]}")
+        os_ = _oracle_state(orc, synth.make_stack(GEO, int(r["lens"][i]), tag=600 + i), r["news"][i])
+        ref = orc.propose(os_, int(r["toks"][i]), r["pos"][i], GEO.gamma - 1, r["masks"][i])
+        tally.add(check_propose(split_batch(r["gpu"], i), ref, bitmask=r["masks"][i], logit_tol=6e-2,
+                                label=f"fp8 a8={r['a8']} seq {i}", strict_ids=not r["a8"]))
+    # W8A8: ids above the 0.05 margin must agree on at least 90% of the rows
+    # (their noise is described in parity.py), every row within the
+    # near-argmax bound, ids forced by the logit tolerance exact
+    tally.finish(min_share=MIN_SHARE, min_pinned_agree=0.9 if r["a8"] else 1.0)
 
 
 def test_full_single_ctx1024_fp8_weights(weights):
@@ -215,17 +269,17 @@ def test_full_single_ctx1024_fp8_weights(weights):
     say("[setup] fp8-weight head + oracle")
     head = Head(geo, weights, kv_pool_blocks=200, max_batch=1, max_seq_len=2048)
     orc = OracleHead(geo.as_dict(), weights)
-    st, os_ = _fill(head, orc, 1024, tag=1)
+    st, stack = _fill(head, 1024, tag=1)
     new = synth.make_stack(GEO, 8, tag=1000)
     head.precompute([st], [8], new)
-    orc.precompute(os_, new)
+    os_ = _oracle_state(orc, stack, new)
     tok = int(synth.make_tokens(GEO, 1, tag=0)[0])
     say(f"[case] single ctx1024 fp8 weights ctx {st.ctx_len} tok {tok}")
     res = head.propose(st, tok, st.ctx_len, GEO.gamma - 1, logits=True)
     torch.cuda.synchronize()
-    p, _, n = check_propose(res, orc.propose(os_, tok, os_.ctx_len, GEO.gamma - 1), logit_tol=6e-2,
-                            label="fp8 weights")
-    say(f"[result] fp8 weights: {p}/{n} rows margin-pinned, all pinned ids equal")
+    tally = Tally("full single_ctx1024 fp8 weights")
+    tally.add(check_propose(res, orc.propose(os_, tok, os_.ctx_len, GEO.gamma - 1), logit_tol=6e-2,
+                            label="fp8 weights"))
+    tally.finish(min_share=MIN_SHARE)
     st.free()
     head.destroy()
-

@@ -15,7 +15,7 @@ import pytest
 
 import synth
 from oracle.dflash import OracleHead
-from parity import check_propose, split_batch
+from parity import Tally, as_u32, check_propose, split_batch
 
 pytestmark = pytest.mark.gpu
 
@@ -100,17 +100,20 @@ def test_mid_batch_and_single_match_oracle(case):
     say(f"[case] mid {case} batch of {len(LENS)}")
     res = head.propose_batch(states, toks, pos, geo.gamma - 1, bitmasks=masks, logits=True)
     torch.cuda.synchronize()
+    tally = Tally(f"mid {case}")
     for i in range(len(LENS)):
         mk = None if masks is None else masks[i]
         ref = orc.propose(ostates[i], int(toks[i]), pos[i], geo.gamma - 1, mk)
-        check_propose(split_batch(res, i), ref, bitmask=mk, logit_tol=tol, label=f"{case} batch seq {i} ctx {pos[i]}")
+        tally.add(check_propose(split_batch(res, i), ref, bitmask=mk, logit_tol=tol,
+                                label=f"{case} batch seq {i} ctx {pos[i]}"))
     say(f"[case] mid {case} single")
     i = 3
     mk = None if masks is None else masks[i]
     res1 = head.propose(states[i], int(toks[i]), pos[i], geo.gamma - 1, bitmask=mk, logits=True)
     torch.cuda.synchronize()
     ref = orc.propose(ostates[i], int(toks[i]), pos[i], geo.gamma - 1, mk)
-    check_propose(res1, ref, bitmask=mk, logit_tol=tol, label=f"{case} single ctx {pos[i]}")
+    tally.add(check_propose(res1, ref, bitmask=mk, logit_tol=tol, label=f"{case} single ctx {pos[i]}"))
+    tally.finish(min_pinned=1)
     for s in states:
         s.free()
     head.destroy()
@@ -158,10 +161,14 @@ def test_mid_prompt_scale_precompute_matches_oracle(case):
                     assert np.abs(kg - kr).max() <= 2e-2 * np.abs(kr).max()
                     assert np.abs(vg - vr).max() <= 2e-2 * np.abs(vr).max()
         tok = int(synth.make_tokens(geo, 1, tag=55)[0])
-        res = head.propose(sts[-1], tok, sts[-1].ctx_len, geo.gamma - 1, logits=True)
-        torch.cuda.synchronize()
-        ref = orc.propose(oss[-1], tok, oss[-1].ctx_len, geo.gamma - 1)
-        check_propose(res, ref, logit_tol=6e-2 if geo.lm_head_dtype == "fp8" else 2e-2, label=f"{case} after {lens}")
+        tally = Tally(f"mid prefill {case} {lens}")
+        for st, os_ in zip(sts, oss):
+            res = head.propose(st, tok, st.ctx_len, geo.gamma - 1, logits=True)
+            torch.cuda.synchronize()
+            ref = orc.propose(os_, tok, os_.ctx_len, geo.gamma - 1)
+            tally.add(check_propose(res, ref, logit_tol=6e-2 if geo.lm_head_dtype == "fp8" else 2e-2,
+                                    label=f"{case} after {lens}"))
+        tally.finish(min_pinned=1)
         for st in sts:
             st.free()
     head.destroy()
@@ -201,11 +208,83 @@ def test_mid_largest_batch_matches_oracle(case):
     say(f"[case] mid largest batch {case}: {n} x {geo.gamma} rows")
     res = head.propose_batch(states, toks, pos, geo.gamma - 1, bitmasks=masks, logits=True)
     torch.cuda.synchronize()
+    tally = Tally(f"mid largest batch {case}")
     for i in range(n):
         mk = None if masks is None else masks[i]
         ref = orc.propose(ostates[i], int(toks[i]), pos[i], geo.gamma - 1, mk)
-        check_propose(split_batch(res, i), ref, bitmask=mk, logit_tol=6e-2 if fp8 else 2e-2,
-                      label=f"largest {case} seq {i} ctx {pos[i]}")
+        tally.add(check_propose(split_batch(res, i), ref, bitmask=mk, logit_tol=6e-2 if fp8 else 2e-2,
+                                label=f"largest {case} seq {i} ctx {pos[i]}"))
+    tally.finish(min_pinned=1)
     for s in states:
         s.free()
     head.destroy()
+
+
+# vocab offsets from the argmax a that place its copy, in the tiled LM head's
+# 256-row vocab blocks (local row (wave * 8 + tile) * 16 + 4 * lane group + r),
+# in the same lane, the neighbouring lane group, another 16-row tile of the
+# same lanes, the other wave of the row, another vocab block of the workgroup
+# and another workgroup's vocab range
+TIE_XOR = {"same lane": 1, "lane group": 4, "tile": 16, "wave": 128, "vocab block": 256, "vocab range": 1024}
+
+
+@pytest.mark.parametrize("case", ["d64", "d64_fp8", "d64_fp8a8"])
+def test_mid_tiled_head_ties_and_empty_mask(case):
+    """The tiled LM head (a batch of six sequences, 96 rows; bf16, E4M3 and
+    W8A8 heads): a copy of a row's argmax vocab row at each of the placements
+    above gives bit-identical logits and the lower id wins; a sequence whose
+    mask allows nothing gets DFLASH_NO_TOKEN, p1 = 0 and confidence 0 on
+    every entry while the others match the oracle."""
+    from block_diffusion_draft_03_amd import Head
+    from oracle.dflash import NO_TOKEN
+    geo = CASES[case]
+    w = synth.make_weights(geo)
+    words = (geo.vocab + 31) // 32
+    n = len(LENS)
+    masks = np.full((n, words), -1, dtype=np.int32)
+    masks[2] = 0
+    stacks = [synth.make_stack(geo, ln, tag=900 + i) for i, ln in enumerate(LENS)]
+    toks = synth.make_tokens(geo, n, tag=31)
+
+    def run(wts):
+        head = Head(geo, wts, kv_pool_blocks=160, max_batch=n, max_seq_len=1024)
+        states = [head.state_create() for _ in range(n)]
+        for st, stk, ln in zip(states, stacks, LENS):
+            if ln:
+                head.precompute([st], [ln], stk)
+        res = head.propose_batch(states, toks, list(LENS), geo.gamma - 1, bitmasks=masks, logits=True)
+        torch.cuda.synchronize()
+        out = {k: v.cpu().numpy() for k, v in res.items()}
+        for st in states:
+            st.free()
+        head.destroy()
+        return out
+
+    say(f"[case] mid tiled head {case}: base and empty mask")
+    base = run(w)
+    assert as_u32(base["ids"][2]).tolist() == [NO_TOKEN] * geo.gamma
+    assert base["row_prob"][2].tolist() == [0.0] * geo.gamma and float(base["conf"][2]) == 0.0
+    orc = OracleHead(geo.as_dict(), w)
+    tally = Tally(f"mid tiled head {case}")
+    for i in range(n):
+        os_ = orc.new_state()
+        if LENS[i]:
+            orc.precompute(os_, stacks[i])
+        ref = orc.propose(os_, int(toks[i]), LENS[i], geo.gamma - 1, masks[i])
+        tally.add(check_propose(split_batch(base, i), ref, bitmask=masks[i], logit_tol=6e-2 if "fp8" in case else 2e-2,
+                                label=f"{case} seq {i}"))
+    tally.finish(min_pinned=1)
+    seq, row = 1, 1
+    a = int(as_u32(base["ids"][seq])[row])
+    for where, x in TIE_XOR.items():
+        b = a ^ x
+        w2 = dict(w)
+        lm = w["lm_head"].copy()
+        lm[b] = lm[a]
+        w2["lm_head"] = lm
+        say(f"[case] mid tiled head {case}: tie {where} a={a} b={b}")
+        out = run(w2)
+        lg = out["logits"][seq, row]
+        assert lg[a] == lg[b], where
+        assert int(as_u32(out["ids"][seq])[row]) == min(a, b), where
+        assert as_u32(out["ids"][2]).tolist() == [NO_TOKEN] * geo.gamma

@@ -11,7 +11,7 @@ import pytest
 import synth
 from oracle.dflash import NO_TOKEN, OracleHead
 from oracle.numerics import bf16_to_f64
-from parity import as_u32, check_propose, split_batch
+from parity import Tally, as_u32, check_propose, split_batch
 
 pytestmark = pytest.mark.gpu
 
@@ -58,12 +58,14 @@ def test_tiny_propose_matches_oracle(window, n_ctx):
     if n_ctx:
         head.precompute([st], [n_ctx], stack)
         orc.precompute(os_, stack)
-    for tok in synth.make_tokens(geo, 3, tag=window + n_ctx):
+    tally = Tally(f"tiny W={window} c={n_ctx}")
+    for tok in synth.make_tokens(geo, 8, tag=window + n_ctx):
         say(f"[case] tiny W={window} c={n_ctx} tok={tok}")
         res = head.propose(st, int(tok), n_ctx, 3, logits=True)
         torch.cuda.synchronize()
         ref = orc.propose(os_, int(tok), n_ctx, 3)
-        check_propose(res, ref, label=f"W={window} c={n_ctx} tok={tok}")
+        tally.add(check_propose(res, ref, label=f"W={window} c={n_ctx} tok={tok}"))
+    tally.finish(min_pinned=1)
     head.destroy()
 
 
@@ -94,6 +96,7 @@ def test_tiny_multi_step_with_trim_matches_oracle(tiny):
     stacks = synth.make_stack(geo, 80, tag=11)
     used = 0
     acc = synth.make_accepted(6, 8, tag=3)
+    tally = Tally("tiny multi-step trim")
     for step in range(6):
         n = 8
         head.precompute([st], [n], stacks[used:used + n])
@@ -106,7 +109,8 @@ def test_tiny_multi_step_with_trim_matches_oracle(tiny):
         say(f"[case] tiny step {step} ctx {st.ctx_len}")
         res = head.propose(st, tok, st.ctx_len, 3, logits=True)
         torch.cuda.synchronize()
-        check_propose(res, orc.propose(os_, tok, os_.ctx_len, 3), label=f"step {step}")
+        tally.add(check_propose(res, orc.propose(os_, tok, os_.ctx_len, 3), label=f"step {step}"))
+    tally.finish(min_pinned=1)
     st.free()
 
 
@@ -234,13 +238,15 @@ def test_tiny_batch_matches_single_and_oracle(tiny):
     say("[case] tiny batch of 4 with masks")
     res = head.propose_batch(states, toks, pos, 3, bitmasks=masks, logits=True)
     torch.cuda.synchronize()
+    tally = Tally("tiny batch of 4")
     for i in range(4):
         ref = orc.propose(ostates[i], int(toks[i]), pos[i], 3, masks[i])
-        check_propose(split_batch(res, i), ref, bitmask=masks[i], label=f"batch seq {i}")
+        tally.add(check_propose(split_batch(res, i), ref, bitmask=masks[i], label=f"batch seq {i}"))
         single = head.propose(states[i], int(toks[i]), pos[i], 3, bitmask=masks[i], logits=True)
         torch.cuda.synchronize()
         assert np.array_equal(as_u32(single["ids"]), as_u32(res["ids"][i]))
         assert np.allclose(single["logits"].cpu().numpy(), res["logits"][i].cpu().numpy(), atol=1e-5)
+    tally.finish(min_pinned=1)
     for s in states:
         s.free()
 
@@ -286,7 +292,8 @@ def test_tiny_zero_final_gain_and_ties():
     assert as_u32(r["ids"]).tolist() == [0] * geo.gamma
     assert np.allclose(r["row_prob"].cpu().numpy(), 1.0 / geo.vocab, rtol=1e-5)
     head.destroy()
-    # duplicate LM rows: identical logits, the lower id wins
+    # duplicate LM rows: identical logits, the lower id wins, whichever of the
+    # two is the copy (the copy placed below the observed argmax a, and above)
     head = build(geo, w)
     st = head.state_create()
     head.precompute([st], [32], synth.make_stack(geo, 32))
@@ -294,21 +301,21 @@ def test_tiny_zero_final_gain_and_ties():
     torch.cuda.synchronize()
     a = int(as_u32(r["ids"])[1])
     head.destroy()
-    if a == 0:
-        pytest.skip("argmax already at id 0")
-    w2 = dict(w)
-    lm = w["lm_head"].copy()
-    lm[0] = lm[a]
-    w2["lm_head"] = lm
-    head = build(geo, w2)
-    st = head.state_create()
-    head.precompute([st], [32], synth.make_stack(geo, 32))
-    r = head.propose(st, 3, 32, 3, logits=True)
-    torch.cuda.synchronize()
-    lg = r["logits"].cpu().numpy()
-    assert lg[1, 0] == lg[1, a]
-    assert int(as_u32(r["ids"])[1]) == 0
-    head.destroy()
+    for b in ((a + 1) % geo.vocab, (a - 1) % geo.vocab, (a + 37) % geo.vocab):
+        w2 = dict(w)
+        lm = w["lm_head"].copy()
+        lm[b] = lm[a]
+        w2["lm_head"] = lm
+        head = build(geo, w2)
+        st = head.state_create()
+        head.precompute([st], [32], synth.make_stack(geo, 32))
+        say(f"[case] tiny tie a={a} b={b}")
+        r = head.propose(st, 3, 32, 3, logits=True)
+        torch.cuda.synchronize()
+        lg = r["logits"].cpu().numpy()
+        assert lg[1, b] == lg[1, a]
+        assert int(as_u32(r["ids"])[1]) == min(a, b)
+        head.destroy()
 
 
 def test_tiny_error_paths(tiny):

@@ -192,21 +192,21 @@ def test_zero_final_gain_gives_uniform():
 
 
 def test_duplicate_lm_rows_tie_to_lowest_id():
+    """A copy of the argmax row a placed at b gives bit-identical logits and
+    the lower of a and b wins, with the copy below a and above it."""
     geo, w, stack = tiny_case(2)
     head, st = _head_with_ctx(geo, w, stack)
     base = head.propose(st, 5, 32, 3)
     a = int(base["ids"][1])
-    b = 0 if a != 0 else 1
-    if b > a:
-        pytest.skip("argmax already at id 0")
-    w2 = dict(w)
-    lm = w["lm_head"].copy()
-    lm[b] = lm[a]
-    w2["lm_head"] = lm
-    head2, st2 = _head_with_ctx(geo, w2, stack)
-    res = head2.propose(st2, 5, 32, 3)
-    assert res["logits"][1, a] == res["logits"][1, b]
-    assert int(res["ids"][1]) == b
+    for b in ((a + 1) % geo.vocab, (a - 1) % geo.vocab, 0 if a else geo.vocab - 1):
+        w2 = dict(w)
+        lm = w["lm_head"].copy()
+        lm[b] = lm[a]
+        w2["lm_head"] = lm
+        head2, st2 = _head_with_ctx(geo, w2, stack)
+        res = head2.propose(st2, 5, 32, 3)
+        assert res["logits"][1, a] == res["logits"][1, b]
+        assert int(res["ids"][1]) == min(a, b)
 
 
 def test_window_zero_ignores_ctx():
