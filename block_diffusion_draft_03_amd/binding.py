@@ -21,7 +21,7 @@ INT64_MAX = (1 << 63) - 1
 EXPORTED_SYMBOLS = (
     "dflash_build", "dflash_destroy", "dflash_block_gamma", "dflash_propose_batch_max",
     "dflash_state_create", "dflash_state_free", "dflash_state_ctx_len", "dflash_precompute_ctx_kv",
-    "dflash_propose", "dflash_propose_batch", "dflash_after_verify", "dflash_take_kv", "dflash_install_kv",
+    "dflash_propose", "dflash_propose_batch", "dflash_propose_noalloc", "dflash_after_verify", "dflash_take_kv", "dflash_install_kv",
     "dflash_free_kv", "dflash_state_read_kv",
     "dflash_read_lm_head_fp8", "dflash_yarn_inv_freq", "dflash_timing_enable", "dflash_timing_read",
     "dflash_last_error",
@@ -85,6 +85,7 @@ def load_library(path=None):
         "dflash_precompute_ctx_kv": ([vp, vp, i32, vp, vp, u64], C.c_int),
         "dflash_propose": ([vp, vp, u32, i64, i32, vp, vp, vp, vp, vp, u64], C.c_int),
         "dflash_propose_batch": ([vp, vp, i32, vp, vp, i32, vp, vp, vp, vp, vp, u64], C.c_int),
+        "dflash_propose_noalloc": ([vp, vp, u32, i64, i32, vp, vp, vp, vp, vp, u64], C.c_int),
         "dflash_after_verify": ([vp, vp, i32], C.c_int),
         "dflash_take_kv": ([vp, vp, vp, i32, C.POINTER(i32), C.POINTER(i32), C.POINTER(i64)], C.c_int),
         "dflash_install_kv": ([vp, vp, vp, i32, i32, i64], C.c_int),
@@ -280,6 +281,26 @@ class Head:
                                                      int(num_drafts), _ptr(bitmask), _ptr(ids), _ptr(conf),
                                                      _ptr(rp), _ptr(lg), _stream_handle(stream)))
         return {"ids": ids, "conf": conf, "row_prob": rp, "logits": lg}
+
+    def propose_noalloc(self, state, last_token, position, num_drafts, bitmask=None, out=None, stream=None):
+        """dflash_propose_noalloc: the library allocates nothing; `out` holds
+        caller-allocated device tensors ids (int32 [gamma]), conf (f32 [1]),
+        row_prob (f32 [gamma] or None) and logits (f32 [gamma, V] or None),
+        allocated here when not given; `bitmask` is a device tensor or None."""
+        import torch
+        g = self.geo.gamma
+        with _on(stream):
+            if out is None:
+                out = {"ids": torch.empty(g, dtype=torch.int32, device=self.device),
+                       "conf": torch.empty(1, dtype=torch.float32, device=self.device),
+                       "row_prob": torch.empty(g, dtype=torch.float32, device=self.device), "logits": None}
+            if isinstance(bitmask, np.ndarray):
+                bitmask = to_device(bitmask, self.device)
+            _check(self.lib, self.lib.dflash_propose_noalloc(self.handle, state.handle, int(last_token), int(position),
+                                                             int(num_drafts), _ptr(bitmask), _ptr(out["ids"]),
+                                                             _ptr(out["conf"]), _ptr(out.get("row_prob")),
+                                                             _ptr(out.get("logits")), _stream_handle(stream)))
+        return out
 
     def propose_batch(self, states, last_tokens, positions, num_drafts, bitmasks=None, logits=False, stream=None):
         import torch

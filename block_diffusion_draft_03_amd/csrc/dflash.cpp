@@ -9,6 +9,7 @@
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <type_traits>
 #include <vector>
 
 #include "../../include/dflash.h"
@@ -57,6 +58,30 @@ struct dflash_state {
   int64_t pair_key = -1;     // opaque key carried with installed blocks (-1: none)
 };
 
+// Device scratch of one propose: written and read within the call (the
+// split counters and the block V^T copy's padding must be zero when the call
+// starts; the kernels leave the counters at zero). The head owns one sized for
+// max_batch sequences; dflash_propose_noalloc carves one out of a static array.
+struct Scratch {
+  float *hid = nullptr;                        // residual stream [M][h]
+  uint16_t *act = nullptr;                     // next GEMM's bf16 operand [M][h]
+  uint8_t *act8 = nullptr;                     // W8A8 head: E4M3 codes of the final-normed rows [M][h]
+  float *act8_scale = nullptr;                 // and their row scales [M]
+  uint16_t *qkv = nullptr, *attn = nullptr, *mlp = nullptr;
+  float2 *cs = nullptr;                        // RoPE (cos, sin) per row [M][d / 2]
+  uint16_t *o_part = nullptr;                  // attention split partials [n_kv][splits][R][d]
+  float *ml_part = nullptr;                    // and their (max, sum)
+  int attn_slots = 0;                          // splits over all kv heads o_part holds
+  float *lm_mx = nullptr, *lm_se = nullptr;    // LM-head partials [P][M]
+  uint32_t *lm_idx = nullptr;
+  float *lm_p1 = nullptr;                      // [M]
+  int *fin_counters = nullptr;                 // [sequences], zero between launches
+  float *ss = nullptr;                         // per-unit row sums of squares [h / 16][M] (few-row path)
+  int *tile_ctr = nullptr;                     // split counters of the residual GEMMs [h / 16], zero between launches
+  uint16_t *vtb = nullptr;                     // V^T of the block rows [seqs][n_kv][d][gp], zero padded
+  float *part = nullptr;                       // split-K partial sums [splits][rows][h]
+};
+
 // A repacked drafter matrix: tile-major bf16 (s null) or tile-major E4M3
 // codes with one f32 scale per output row.
 struct Wt {
@@ -100,24 +125,11 @@ struct dflash_head {
   void *kv_pool = nullptr;
   size_t kv_elem = 2;
 
-  // scratch
-  float *hid = nullptr;
-  uint16_t *act = nullptr, *qkv = nullptr, *attn = nullptr, *mlp = nullptr;
-  uint8_t *act8 = nullptr;     // W8A8 head: E4M3 codes of the final-normed rows [M][h]
-  float *act8_scale = nullptr; // and their row scales [M]
-  float2 *cs = nullptr;
-  uint16_t *o_part = nullptr;
-  float *ml_part = nullptr;
-  float *lm_mx = nullptr, *lm_se = nullptr;
-  uint32_t *lm_idx = nullptr;
-  float *lm_p1 = nullptr;
-  int *fin_counters = nullptr;
+  // scratch of the propose (max_batch sequences) and of the precompute
+  Scratch sc;
+  int dev = 0;  // device the head lives on
   int lm_P = 0;
-  int attn_slots = 0;
-  float *ss = nullptr;        // per-unit row sums of squares [h / 16][M] (few-row path)
-  int *tile_ctr = nullptr;    // split counters of the residual GEMMs [h / 16], zero between launches
-  uint16_t *vtb = nullptr;  // V^T of the block rows [max_batch][n_kv][d][gp], zero padded
-  int gp = 0;
+  int gp = 0;   // block rows padded to 32 (the vtb copy's row stride)
   float *pre_u = nullptr;
   uint16_t *pre_c = nullptr;
   // tiled precompute of many rows: row positions and block tables, double
@@ -127,7 +139,6 @@ struct dflash_head {
   const int32_t **h_bts = nullptr, **d_bts = nullptr;
   hipEvent_t pre_ev[2] = {nullptr, nullptr};
   bool pre_ev_used[2] = {false, false};
-  float *part = nullptr;  // split-K partial sums [splits][rows][h]
 
   // benchmark timing: recorded (start, stop) event pairs per phase
   bool timing = false;
@@ -406,16 +417,16 @@ int build_impl(dflash_head *H, const dflash_weights *w, hipStream_t st) {
 
   // scratch sized for max_batch * gamma rows
   const size_t M = g.m_max;
-  TRY(H->alloc(&H->hid, M * h));
-  TRY(H->alloc(&H->act, M * h));
+  TRY(H->alloc(&H->sc.hid, M * h));
+  TRY(H->alloc(&H->sc.act, M * h));
   if (g.a8) {
-    TRY(H->alloc(&H->act8, M * h));
-    TRY(H->alloc(&H->act8_scale, M));
+    TRY(H->alloc(&H->sc.act8, M * h));
+    TRY(H->alloc(&H->sc.act8_scale, M));
   }
-  TRY(H->alloc(&H->qkv, M * g.qkv_dim));
-  TRY(H->alloc(&H->attn, M * g.q_dim));
-  TRY(H->alloc(&H->mlp, M * g.I));
-  TRY(H->alloc(&H->cs, M * (g.d / 2)));
+  TRY(H->alloc(&H->sc.qkv, M * g.qkv_dim));
+  TRY(H->alloc(&H->sc.attn, M * g.q_dim));
+  TRY(H->alloc(&H->sc.mlp, M * g.I));
+  TRY(H->alloc(&H->sc.cs, M * (g.d / 2)));
   // split-K partials of the GEMMs that feed the residual stream (N = h)
   int max_splits = 1;
   for (int K : {g.q_dim, g.I, g.fc_in}) {
@@ -426,26 +437,26 @@ int build_impl(dflash_head *H, const dflash_weights *w, hipStream_t st) {
   H->tiled_prefill = !g.fp8w && bgemm_ok(EPI_PARTIAL, g.h, g.fc_in) && bgemm_ok(EPI_KV_SCATTER, g.fkv_dim, g.h);
   const size_t pre_rows = H->tiled_prefill ? PREFILL_ROWS : GEMM_MAX_ROWS;
   if (H->tiled_prefill) max_splits = std::max(max_splits, bgemm_splits(g.h, g.fc_in, PREFILL_ROWS));
-  TRY(H->alloc(&H->part, (size_t)max_splits * std::max({M, (size_t)GEMM_MAX_ROWS, pre_rows}) * h));
+  TRY(H->alloc(&H->sc.part, (size_t)max_splits * std::max({M, (size_t)GEMM_MAX_ROWS, pre_rows}) * h));
   const size_t R = (size_t)g.rep * g.gamma;
   // partial slots: every plan the propose takes fits (checked at build)
-  H->attn_slots = (int)attn_slots(g, H->cfg.max_seq_len, attn_max_tiles_per_split());
-  TRY(H->alloc(&H->ss, (size_t)((g.h + 15) / 16) * GEMM_MAX_ROWS));
-  TRY(H->alloc(&H->tile_ctr, (size_t)((g.h + 15) / 16)));
-  HIP_TRY(hipMemsetAsync(H->tile_ctr, 0, (size_t)((g.h + 15) / 16) * sizeof(int), st));
+  H->sc.attn_slots = (int)attn_slots(g, H->cfg.max_seq_len, attn_max_tiles_per_split());
+  TRY(H->alloc(&H->sc.ss, (size_t)((g.h + 15) / 16) * GEMM_MAX_ROWS));
+  TRY(H->alloc(&H->sc.tile_ctr, (size_t)((g.h + 15) / 16)));
+  HIP_TRY(hipMemsetAsync(H->sc.tile_ctr, 0, (size_t)((g.h + 15) / 16) * sizeof(int), st));
   H->gp = (g.gamma + 31) / 32 * 32;
-  TRY(H->alloc(&H->vtb, (size_t)g.max_batch * g.n_kv * g.d * H->gp));
-  HIP_TRY(hipMemsetAsync(H->vtb, 0, (size_t)g.max_batch * g.n_kv * g.d * H->gp * sizeof(uint16_t), st));
-  TRY(H->alloc(&H->o_part, (size_t)H->attn_slots * R * g.d));
-  TRY(H->alloc(&H->ml_part, (size_t)H->attn_slots * R * 2));
+  TRY(H->alloc(&H->sc.vtb, (size_t)g.max_batch * g.n_kv * g.d * H->gp));
+  HIP_TRY(hipMemsetAsync(H->sc.vtb, 0, (size_t)g.max_batch * g.n_kv * g.d * H->gp * sizeof(uint16_t), st));
+  TRY(H->alloc(&H->sc.o_part, (size_t)H->sc.attn_slots * R * g.d));
+  TRY(H->alloc(&H->sc.ml_part, (size_t)H->sc.attn_slots * R * 2));
   H->lm_P = lm_parts(g.V);
   const size_t lm_slots = (size_t)std::max(H->lm_P, blm_parts(g.V)) * M;
-  TRY(H->alloc(&H->lm_mx, lm_slots));
-  TRY(H->alloc(&H->lm_se, lm_slots));
-  TRY(H->alloc(&H->lm_idx, lm_slots));
-  TRY(H->alloc(&H->lm_p1, M));
-  TRY(H->alloc(&H->fin_counters, (size_t)g.max_batch));
-  HIP_TRY(hipMemsetAsync(H->fin_counters, 0, (size_t)g.max_batch * sizeof(int), st));
+  TRY(H->alloc(&H->sc.lm_mx, lm_slots));
+  TRY(H->alloc(&H->sc.lm_se, lm_slots));
+  TRY(H->alloc(&H->sc.lm_idx, lm_slots));
+  TRY(H->alloc(&H->sc.lm_p1, M));
+  TRY(H->alloc(&H->sc.fin_counters, (size_t)g.max_batch));
+  HIP_TRY(hipMemsetAsync(H->sc.fin_counters, 0, (size_t)g.max_batch * sizeof(int), st));
   TRY(H->alloc(&H->pre_u, pre_rows * h));
   TRY(H->alloc(&H->pre_c, pre_rows * h));
   if (H->tiled_prefill) {
@@ -513,16 +524,16 @@ int gemm_rows(dflash_head *H, int epi, const uint16_t *A, int lda, int M, Wt W, 
 
 // h += W A^T for a GEMM into the residual stream (split over K, then the
 // splits are added in order), followed by out = bf16(RMSNorm(h) * gain).
-int resid_gemm(dflash_head *H, const uint16_t *A, int lda, int M, Wt W, int K, float *h,
+int resid_gemm(dflash_head *H, const Scratch &sc, const uint16_t *A, int lda, int M, Wt W, int K, float *h,
                const float *gain, uint16_t *out, bool init_zero, hipStream_t st, bool tiled = false) {
   EpiArgs e{};
-  e.out_f32 = H->part;
+  e.out_f32 = sc.part;
   e.ldo = H->g.h;
   int splits = 1;
   TRY(gemm_rows(H, EPI_PARTIAL, A, lda, M, W, H->g.h, K, e, st, &splits, RowScale{}, tiled));
   ResidNormArgs r{};
   r.h = h;
-  r.part = H->part;
+  r.part = sc.part;
   r.splits = splits;
   r.ld_split = M;
   r.n = H->g.h;
@@ -536,28 +547,37 @@ int resid_gemm(dflash_head *H, const uint16_t *A, int lda, int M, Wt W, int K, f
 
 // h += W A^T into the residual stream for few rows: the split GEMM's last
 // split of every 16-row unit adds the splits in order, writes bf16(h * gain)
-// and the unit's per-row sums of squares (H->ss); the consumer applies the
+// and the unit's per-row sums of squares (Scratch::ss); the consumer applies the
 // RMSNorm row scale. Returns the units the consumer sums.
-int resid_gemm_fused(dflash_head *H, const uint16_t *A, int lda, int M, Wt W, int K, const float *gain,
-                     hipStream_t st, int *units) {
+int resid_gemm_fused(dflash_head *H, const Scratch &sc, const uint16_t *A, int lda, int M, Wt W, int K,
+                     const float *gain, hipStream_t st, int *units) {
   EpiArgs e{};
-  e.out_f32 = H->part;
+  e.out_f32 = sc.part;
   e.ldo = H->g.h;
-  e.res_h = H->hid;
+  e.res_h = sc.hid;
   e.res_gain = gain;
-  e.res_act = H->act;
-  e.ss_out = H->ss;
+  e.res_act = sc.act;
+  e.ss_out = sc.ss;
   e.ss_ld = M;
-  e.tile_ctr = H->tile_ctr;
+  e.tile_ctr = sc.tile_ctr;
   TRY(gemm_rows(H, EPI_PARTIAL, A, lda, M, W, H->g.h, K, e, st));
   const GemmPlan p = gemm_plan(H->g.h, K, true);
   *units = (H->g.h + 16 * p.tn - 1) / (16 * p.tn);
   return DFLASH_OK;
 }
 
-int propose_impl(dflash_head *H, dflash_state *const *states, int n, const uint32_t *tokens, const int64_t *positions,
-                 int num_drafts, const int32_t *bitmasks, uint32_t *ids, float *conf, float *row_prob, float *logits,
-                 hipStream_t st) {
+// few rows: the residual GEMMs finish their own splits and every consumer
+// applies the RMSNorm row scale from per-unit sums of squares (Scratch::ss);
+// the W8A8 head needs the final-normed rows in act (no deferred row scale)
+bool propose_fused(const Geo &g, int M) { return !g.a8 && M <= (g.fp8w ? GEMM_MAX_ROWS : PROPOSE_FEW_ROWS); }
+
+bool propose_tiled_lm(const Geo &g, int M) {
+  return !propose_fused(g, M) && (M > GEMM_MAX_ROWS || !g.fp8w || g.a8) && blm_ok(g.V, g.h);
+}
+
+// Argument checks of a propose and its attention plan: nothing is enqueued.
+int propose_check(dflash_head *H, dflash_state *const *states, int n, const uint32_t *tokens, const int64_t *positions,
+                  int num_drafts, uint32_t *ids, float *conf, int attn_slots, AttnPlan *plan) {
   const Geo &g = H->g;
   if (n < 1 || n > g.max_batch)
     return set_err(DFLASH_E_DECLINED, "batch of " + std::to_string(n) + " outside [1, " + std::to_string(g.max_batch) + "]");
@@ -572,23 +592,26 @@ int propose_impl(dflash_head *H, dflash_state *const *states, int n, const uint3
       return set_err(DFLASH_E_INVALID, "position out of range");
   }
   const int M = n * g.gamma;
-  const int h = g.h;
-  // few rows: the residual GEMMs finish their own splits and every consumer
-  // applies the RMSNorm row scale from per-unit sums of squares (H->ss)
-  // the W8A8 head needs the final-normed rows in act (no deferred row scale)
-  const bool fused = !g.a8 && M <= (g.fp8w ? GEMM_MAX_ROWS : PROPOSE_FEW_ROWS);
-  const bool tiled_lm = !fused && (M > GEMM_MAX_ROWS || !g.fp8w || g.a8) && blm_ok(g.V, h);
-  if (g.a8 && !tiled_lm) return set_err(DFLASH_E_INVALID, "the W8A8 LM head needs the tiled head");
+  if (g.a8 && !propose_tiled_lm(g, M)) return set_err(DFLASH_E_INVALID, "the W8A8 LM head needs the tiled head");
   // attention splits, planned before anything is enqueued
-  AttnPlan plan;
-  {
-    int32_t tiles[DFLASH_MAX_BATCH];
-    for (int i = 0; i < n; ++i) tiles[i] = attn_tiles(states[i]->rows.ctx_len, g.W);
-    std::string err;
-    const int rc = attn_plan(n, tiles, g.n_kv, attn_max_tiles_per_split(), H->attn_slots / g.n_kv, &plan, &err);
-    if (rc != DFLASH_OK) return set_err(rc, err);
-  }
-  hipEvent_t t_all = H->interval_begin(DFLASH_PHASE_PROPOSE, st);
+  int32_t tiles[DFLASH_MAX_BATCH];
+  for (int i = 0; i < n; ++i) tiles[i] = attn_tiles(states[i]->rows.ctx_len, g.W);
+  std::string err;
+  const int rc = attn_plan(n, tiles, g.n_kv, attn_max_tiles_per_split(), attn_slots / g.n_kv, plan, &err);
+  if (rc != DFLASH_OK) return set_err(rc, err);
+  return DFLASH_OK;
+}
+
+// The launches of a checked propose, with its scratch.
+int propose_launch(dflash_head *H, const Scratch &sc, const AttnPlan &plan, dflash_state *const *states, int n,
+                   const uint32_t *tokens, const int64_t *positions, int num_drafts, const int32_t *bitmasks,
+                   uint32_t *ids, float *conf, float *row_prob, float *logits, hipStream_t st, bool timed) {
+  const Geo &g = H->g;
+  const int M = n * g.gamma;
+  const int h = g.h;
+  const bool fused = propose_fused(g, M);
+  const bool tiled_lm = propose_tiled_lm(g, M);
+  hipEvent_t t_all = timed ? H->interval_begin(DFLASH_PHASE_PROPOSE, st) : nullptr;
 
   SetupArgs sa{};
   sa.embed = H->embed;
@@ -599,10 +622,10 @@ int propose_impl(dflash_head *H, dflash_state *const *states, int n, const uint3
   sa.half_dim = g.d / 2;
   sa.mask_id = g.mask_id;
   sa.inv_freq = H->inv_freq;
-  sa.hid = H->hid;
-  sa.a = H->act;
-  sa.ss_out = fused ? H->ss : nullptr;
-  sa.cs = H->cs;
+  sa.hid = sc.hid;
+  sa.a = sc.act;
+  sa.ss_out = fused ? sc.ss : nullptr;
+  sa.cs = sc.cs;
   for (int i = 0; i < n; ++i) {
     sa.token[i] = tokens[i];
     sa.position[i] = (int32_t)positions[i];
@@ -610,8 +633,8 @@ int propose_impl(dflash_head *H, dflash_state *const *states, int n, const uint3
   HIP_TRY(launch_setup(sa, M, st));
 
   AttnArgs aa{};
-  aa.qkv = H->qkv;
-  aa.vtb = H->vtb;
+  aa.qkv = sc.qkv;
+  aa.vtb = sc.vtb;
   aa.ld = g.qkv_dim;
   aa.gamma = g.gamma;
   aa.rep = g.rep;
@@ -623,9 +646,9 @@ int propose_impl(dflash_head *H, dflash_state *const *states, int n, const uint3
   aa.L = g.L;
   aa.kv_fp8 = g.kv_fp8;
   aa.kv_scale = H->kv_scale;
-  aa.o_part = H->o_part;
-  aa.ml_part = H->ml_part;
-  aa.out = H->attn;
+  aa.o_part = sc.o_part;
+  aa.ml_part = sc.ml_part;
+  aa.out = sc.attn;
   aa.out_ld = g.q_dim;
   // ctx tiles of 32 positions from the block-aligned window start, in the
   // splits of the plan (attn_plan: the last split of a sequence also takes
@@ -646,36 +669,36 @@ int propose_impl(dflash_head *H, dflash_state *const *states, int n, const uint3
   // comes from the setup kernel, every later one from the residual finish.
   EpiArgs e{};
   RowScale rs{};
-  if (fused) rs = RowScale{H->ss, 1, M, H->cfg.rms_eps};
+  if (fused) rs = RowScale{sc.ss, 1, M, H->cfg.rms_eps};
   for (int l = 0; l < g.L; ++l) {
     e = EpiArgs{};
-    e.out_bf16 = H->qkv;
+    e.out_bf16 = sc.qkv;
     e.ldo = g.qkv_dim;
-    e.cs = H->cs;
+    e.cs = sc.cs;
     e.head_dim = g.d;
     e.q_dim = g.q_dim;
     e.kv_dim = g.kv_dim;
-    e.vtb = H->vtb;
+    e.vtb = sc.vtb;
     e.gamma = g.gamma;
     e.gp = H->gp;
-    TRY(gemm_rows(H, EPI_QKV_ROPE, H->act, h, M, H->wqkv(l), g.qkv_dim, h, e, st, nullptr, rs, !fused));
+    TRY(gemm_rows(H, EPI_QKV_ROPE, sc.act, h, M, H->wqkv(l), g.qkv_dim, h, e, st, nullptr, rs, !fused));
     aa.layer = l;
     HIP_TRY(launch_attention(aa, n, st));
     const float *post_gain = H->g_post + (size_t)l * h;
     if (fused) {
-      TRY(resid_gemm_fused(H, H->attn, g.q_dim, M, H->wo(l), g.q_dim, post_gain, st, &rs.units));
+      TRY(resid_gemm_fused(H, sc, sc.attn, g.q_dim, M, H->wo(l), g.q_dim, post_gain, st, &rs.units));
     } else {
-      TRY(resid_gemm(H, H->attn, g.q_dim, M, H->wo(l), g.q_dim, H->hid, post_gain, H->act, false, st, true));
+      TRY(resid_gemm(H, sc, sc.attn, g.q_dim, M, H->wo(l), g.q_dim, sc.hid, post_gain, sc.act, false, st, true));
     }
     e = EpiArgs{};
-    e.out_bf16 = H->mlp;
+    e.out_bf16 = sc.mlp;
     e.ldo = g.I;
-    TRY(gemm_rows(H, EPI_SWIGLU, H->act, h, M, H->wgu(l), 2 * g.I, h, e, st, nullptr, rs, !fused));
+    TRY(gemm_rows(H, EPI_SWIGLU, sc.act, h, M, H->wgu(l), 2 * g.I, h, e, st, nullptr, rs, !fused));
     const float *next_gain = l + 1 < g.L ? H->g_in + (size_t)(l + 1) * h : H->g_final;
     if (fused) {
-      TRY(resid_gemm_fused(H, H->mlp, g.I, M, H->wdown(l), g.I, next_gain, st, &rs.units));
+      TRY(resid_gemm_fused(H, sc, sc.mlp, g.I, M, H->wdown(l), g.I, next_gain, st, &rs.units));
     } else {
-      TRY(resid_gemm(H, H->mlp, g.I, M, H->wdown(l), g.I, H->hid, next_gain, H->act, false, st, true));
+      TRY(resid_gemm(H, sc, sc.mlp, g.I, M, H->wdown(l), g.I, sc.hid, next_gain, sc.act, false, st, true));
     }
   }
 
@@ -688,37 +711,37 @@ int propose_impl(dflash_head *H, dflash_state *const *states, int n, const uint3
   la.words = g.words;
   la.gamma = g.gamma;
   la.ld_part = M;
-  la.part_mx = H->lm_mx;
-  la.part_se = H->lm_se;
-  la.part_idx = H->lm_idx;
+  la.part_mx = sc.lm_mx;
+  la.part_se = sc.lm_se;
+  la.part_idx = sc.lm_idx;
   la.rs = rs;
   if (tiled_lm) {
-    la.z = H->act;
+    la.z = sc.act;
     la.M = M;
     la.row0 = 0;
     la.logits = logits;
     if (g.a8) {
-      HIP_TRY(launch_quant_rows_a8(H->act, M, h, H->act8, H->act8_scale, st));
-      la.z8 = H->act8;
-      la.ascale = H->act8_scale;
+      HIP_TRY(launch_quant_rows_a8(sc.act, M, h, sc.act8, sc.act8_scale, st));
+      la.z8 = sc.act8;
+      la.ascale = sc.act8_scale;
     }
-    hipEvent_t t_lm = H->interval_begin(DFLASH_PHASE_LM_HEAD, st);
+    hipEvent_t t_lm = timed ? H->interval_begin(DFLASH_PHASE_LM_HEAD, st) : nullptr;
     HIP_TRY(launch_blm_head(g.head_fp8, g.a8, la, st));
     if (t_lm) HIP_TRY(hipEventRecord(t_lm, st));
   }
   for (int r0 = 0; !tiled_lm && r0 < M; r0 += GEMM_MAX_ROWS) {
-    la.z = H->act + (size_t)r0 * h;
+    la.z = sc.act + (size_t)r0 * h;
     la.M = std::min(GEMM_MAX_ROWS, M - r0);
     la.row0 = r0;
     la.logits = logits ? logits + (size_t)r0 * g.V : nullptr;
-    hipEvent_t t_lm = H->interval_begin(DFLASH_PHASE_LM_HEAD, st);
+    hipEvent_t t_lm = timed ? H->interval_begin(DFLASH_PHASE_LM_HEAD, st) : nullptr;
     HIP_TRY(launch_lm_head(g.head_fp8, la, st));
     if (t_lm) HIP_TRY(hipEventRecord(t_lm, st));
   }
   LmFinishArgs fa{};
-  fa.part_mx = H->lm_mx;
-  fa.part_se = H->lm_se;
-  fa.part_idx = H->lm_idx;
+  fa.part_mx = sc.lm_mx;
+  fa.part_se = sc.lm_se;
+  fa.part_idx = sc.lm_idx;
   fa.P = tiled_lm ? blm_parts(g.V) : H->lm_P;
   fa.M = M;
   fa.gamma = g.gamma;
@@ -727,8 +750,8 @@ int propose_impl(dflash_head *H, dflash_state *const *states, int n, const uint3
   fa.ids = ids;
   fa.conf = conf;
   fa.row_prob = row_prob;
-  fa.p1 = H->lm_p1;
-  fa.counters = H->fin_counters;
+  fa.p1 = sc.lm_p1;
+  fa.counters = sc.fin_counters;
   HIP_TRY(launch_lm_finish(fa, n, st));
   if (t_all) HIP_TRY(hipEventRecord(t_all, st));
   return DFLASH_OK;
@@ -744,6 +767,91 @@ int sync_block_table(dflash_state *s, hipStream_t st) {
                          hipMemcpyHostToDevice, st));
   s->uploaded = nb;
   return DFLASH_OK;
+}
+
+}  // namespace
+
+// ---- allocation-free propose ------------------------------------------------
+// Scratch of dflash_propose_noalloc, for callers that cannot allocate device
+// memory. Every device the library runs on holds its own copy of this array
+// (at its own address) until the process ends; host code reaches it only
+// through the address hipGetSymbolAddress returns on that device, never
+// through the array's name. All calls on one device share it.
+constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(16) << 20;
+static __device__ __align__(256) uint8_t scratch[NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[MAX_DEVICES] = {};
+
+// Device address of `scratch` on device dev: resolved once per device, with
+// dev current (dflash_build calls this for its device; a later call on
+// another current device cannot resolve it).
+int scratch_address(int dev, void **out) {
+  if (dev < 0 || dev >= MAX_DEVICES) return set_err(DFLASH_E_INVALID, "device id out of range");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    HIP_TRY(hipGetDevice(&cur));
+    if (cur != dev) return set_err(DFLASH_E_INVALID, "the static scratch is resolved with the head's device current");
+    void *p = nullptr;
+    HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return set_err(DFLASH_E_HIP, "hipGetSymbolAddress gave no address for the static scratch");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DFLASH_OK;
+}
+
+// Lay out the scratch of a one-sequence propose with attention plan `plan`
+// from `base` (256-byte aligned pieces); with base null only the size is
+// computed. The split counters and the block V^T copy (which must be zero
+// when a call starts) are placed side by side, from sc->fin_counters on, and
+// *zero_bytes is their extent.
+size_t carve_scratch(const dflash_head *H, const AttnPlan &plan, uint8_t *base, Scratch *sc, size_t *zero_bytes) {
+  const Geo &g = H->g;
+  const size_t M = g.gamma, h = g.h, R = (size_t)g.rep * g.gamma;
+  size_t off = 0;
+  auto take = [&](auto **p, size_t count) {
+    off = (off + 255) & ~(size_t)255;
+    *p = base ? (std::remove_reference_t<decltype(*p)>)(base + off) : nullptr;
+    off += count * sizeof(**p);
+  };
+  take(&sc->hid, M * h);
+  take(&sc->act, M * h);
+  if (g.a8) {
+    take(&sc->act8, M * h);
+    take(&sc->act8_scale, M);
+  }
+  take(&sc->qkv, M * g.qkv_dim);
+  take(&sc->attn, M * g.q_dim);
+  take(&sc->mlp, M * g.I);
+  take(&sc->cs, M * (g.d / 2));
+  sc->attn_slots = plan.n_split * g.n_kv;
+  take(&sc->o_part, (size_t)sc->attn_slots * R * g.d);
+  take(&sc->ml_part, (size_t)sc->attn_slots * R * 2);
+  const size_t P = (size_t)std::max(lm_parts(g.V), blm_parts(g.V));
+  take(&sc->lm_mx, P * M);
+  take(&sc->lm_se, P * M);
+  take(&sc->lm_idx, P * M);
+  take(&sc->lm_p1, M);
+  take(&sc->ss, (h + 15) / 16 * M);
+  int splits = 1;
+  for (int K : {g.q_dim, g.I}) {
+    splits = std::max(splits, gemm_plan(g.h, K, true).splits);
+    if (bgemm_ok(EPI_PARTIAL, g.h, K)) splits = std::max(splits, bgemm_splits(g.h, K, (int)M));
+  }
+  take(&sc->part, (size_t)splits * M * h);
+  off = (off + 255) & ~(size_t)255;
+  const size_t zero0 = off;  // sc->fin_counters starts here
+  take(&sc->fin_counters, 1);
+  take(&sc->tile_ctr, (h + 15) / 16);
+  take(&sc->vtb, (size_t)g.n_kv * g.d * H->gp);
+  off = (off + 255) & ~(size_t)255;
+  *zero_bytes = off - zero0;
+  return off;
 }
 
 }  // namespace
@@ -765,6 +873,7 @@ int dflash_build(const dflash_config *cfg, const dflash_weights *w, uint64_t str
   dflash_head *H = new dflash_head();
   H->cfg = *cfg;
   H->g = g;
+  if (hipGetDevice(&H->dev) != hipSuccess) H->dev = 0;
   rc = build_impl(H, w, to_stream(stream));
   if (rc != DFLASH_OK) {
     (void)hipStreamSynchronize(to_stream(stream));
@@ -773,6 +882,10 @@ int dflash_build(const dflash_config *cfg, const dflash_weights *w, uint64_t str
     delete H;
     return rc;
   }
+  // the static scratch of dflash_propose_noalloc, resolved on the head's
+  // device while it is current (a failure is reported by that call)
+  void *unused = nullptr;
+  (void)scratch_address(H->dev, &unused);
   *out = H;
   g_err.clear();
   return DFLASH_OK;
@@ -926,7 +1039,7 @@ int dflash_precompute_ctx_kv(dflash_head *head, dflash_state *const *states, int
       HIP_TRY(hipMemcpyAsync((void *)db, (const void *)hb, m * sizeof(const int32_t *), hipMemcpyHostToDevice, st));
       HIP_TRY(hipEventRecord(H->pre_ev[b], st));
       H->pre_ev_used[b] = true;
-      TRY(resid_gemm(H, (const uint16_t *)stack + (size_t)r0 * g.fc_in, g.fc_in, m, H->wfc(), g.fc_in, H->pre_u,
+      TRY(resid_gemm(H, H->sc, (const uint16_t *)stack + (size_t)r0 * g.fc_in, g.fc_in, m, H->wfc(), g.fc_in, H->pre_u,
                      H->g_hidden, H->pre_c, true, st));
       EpiArgs e{};
       e.head_dim = g.d;
@@ -947,7 +1060,7 @@ int dflash_precompute_ctx_kv(dflash_head *head, dflash_state *const *states, int
   for (int r0 = 0; r0 < (int)total; r0 += GEMM_MAX_ROWS) {
     const int m = std::min<int>(GEMM_MAX_ROWS, (int)total - r0);
     // u = S fc^T (split over K, summed in split order), c = RMSNorm(u) bf16
-    TRY(resid_gemm(H, (const uint16_t *)stack + (size_t)r0 * g.fc_in, g.fc_in, m, H->wfc(), g.fc_in, H->pre_u,
+    TRY(resid_gemm(H, H->sc, (const uint16_t *)stack + (size_t)r0 * g.fc_in, g.fc_in, m, H->wfc(), g.fc_in, H->pre_u,
                    H->g_hidden, H->pre_c, true, st));
     EpiArgs e{};
     e.head_dim = g.d;
@@ -974,10 +1087,12 @@ int dflash_propose(dflash_head *head, dflash_state *st, uint32_t last_token, int
   if (!head_ok(head)) return set_err(DFLASH_E_INVALID, "invalid head");
   std::lock_guard<std::mutex> lk(head->mu);
   dflash_state *states[1] = {st};
-  int rc = propose_impl(head, states, 1, &last_token, &position, num_drafts, bitmask, ids, conf, row_prob, logits,
-                        to_stream(stream));
+  AttnPlan plan;
+  int rc = propose_check(head, states, 1, &last_token, &position, num_drafts, ids, conf, head->sc.attn_slots, &plan);
   if (rc == DFLASH_E_DECLINED) return set_err(DFLASH_E_INVALID, g_err);
-  return rc;
+  if (rc != DFLASH_OK) return rc;
+  return propose_launch(head, head->sc, plan, states, 1, &last_token, &position, num_drafts, bitmask, ids, conf,
+                        row_prob, logits, to_stream(stream), true);
 }
 
 int dflash_propose_batch(dflash_head *head, dflash_state *const *states, int32_t n, const uint32_t *last_tokens,
@@ -985,8 +1100,38 @@ int dflash_propose_batch(dflash_head *head, dflash_state *const *states, int32_t
                          float *conf, float *row_prob, float *logits, uint64_t stream) {
   if (!head_ok(head)) return set_err(DFLASH_E_INVALID, "invalid head");
   std::lock_guard<std::mutex> lk(head->mu);
-  return propose_impl(head, states, n, last_tokens, positions, num_drafts, bitmasks, ids, conf, row_prob, logits,
-                      to_stream(stream));
+  AttnPlan plan;
+  const int rc = propose_check(head, states, n, last_tokens, positions, num_drafts, ids, conf, head->sc.attn_slots, &plan);
+  if (rc != DFLASH_OK) return rc;
+  return propose_launch(head, head->sc, plan, states, n, last_tokens, positions, num_drafts, bitmasks, ids, conf,
+                        row_prob, logits, to_stream(stream), true);
+}
+
+int dflash_propose_noalloc(dflash_head *head, dflash_state *st, uint32_t last_token, int64_t position,
+                           int32_t num_drafts, const int32_t *bitmask, uint32_t *ids, float *conf, float *row_prob,
+                           float *logits, uint64_t stream) {
+  if (!head_ok(head)) return set_err(DFLASH_E_INVALID, "invalid head");
+  std::lock_guard<std::mutex> lk(head->mu);
+  dflash_state *states[1] = {st};
+  // the plan of dflash_propose, so the two give the same result bit for bit
+  AttnPlan plan;
+  int rc = propose_check(head, states, 1, &last_token, &position, num_drafts, ids, conf, head->sc.attn_slots, &plan);
+  if (rc == DFLASH_E_DECLINED) return set_err(DFLASH_E_INVALID, g_err);
+  if (rc != DFLASH_OK) return rc;
+  Scratch sc;
+  size_t zero_bytes = 0;
+  const size_t need = carve_scratch(head, plan, nullptr, &sc, &zero_bytes);
+  if (need > NOALLOC_SCRATCH_BYTES)
+    return set_err(DFLASH_E_INVALID, "this propose needs " + std::to_string(need) + " bytes of scratch, more than the " +
+                                         std::to_string(NOALLOC_SCRATCH_BYTES) + " of the static array");
+  void *base = nullptr;
+  TRY(scratch_address(head->dev, &base));
+  carve_scratch(head, plan, (uint8_t *)base, &sc, &zero_bytes);
+  const hipStream_t s = to_stream(stream);
+  // the previous call on this device left its own counters and V^T rows here
+  HIP_TRY(launch_zero(sc.fin_counters, zero_bytes, s));
+  return propose_launch(head, sc, plan, states, 1, &last_token, &position, num_drafts, bitmask, ids, conf, row_prob,
+                        logits, s, false);
 }
 
 int dflash_after_verify(dflash_head *head, dflash_state *st, int32_t num_accepted) {

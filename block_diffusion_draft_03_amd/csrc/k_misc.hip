@@ -1,6 +1,8 @@
 // k_misc.hip - row-wise kernels of the DFlash head for gfx950: block setup
 // (embedding gather, first RMSNorm, RoPE table), RMSNorm, build-time weight
 // conversion and repacking, the FP8 LM-head mirror, and KV inspection.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -264,6 +266,12 @@ __global__ void k_read_kv(const uint8_t *pool, const int32_t *bt, int L, int lay
   }
 }
 
+// Zero n 32-bit words (a fill kernel rather than a memset, so the launch can
+// sit in a captured graph).
+__global__ void k_zero_u32(uint32_t *p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0u;
+}
+
 int grid_for(size_t total, int block) {
   size_t b = (total + block - 1) / block;
   if (b > 65535) b = 65535;
@@ -271,6 +279,14 @@ int grid_for(size_t total, int block) {
 }
 
 }  // namespace
+
+hipError_t launch_zero(void *p, size_t bytes, hipStream_t s) {
+  if (bytes % 4 != 0 || ((uintptr_t)p & 3u) != 0) return hipErrorInvalidValue;
+  const size_t n = bytes / 4;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_zero_u32, dim3(std::min(grid_for(n, 256), 1024)), dim3(256), 0, s, (uint32_t *)p, n);
+  return hipGetLastError();
+}
 
 hipError_t launch_setup(const SetupArgs &a, int M, hipStream_t s) {
   hipLaunchKernelGGL(k_setup, dim3(M), dim3(256), 0, s, a);

@@ -230,6 +230,8 @@ hipError_t launch_fp8_mirror(const uint16_t *src, int V, int h, uint8_t *codes, 
 // E4M3 rows for the W8A8 LM head: launch_fp8_mirror's codes and scales, each
 // 128-column step's codes permuted into the head's K order (h % 128 == 0)
 hipError_t launch_quant_rows_a8(const uint16_t *src, int M, int h, uint8_t *codes, float *scale, hipStream_t s);
+// Zero `bytes` (a multiple of 4, 4-byte aligned) at device address p.
+hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
 
 // Gather ctx rows of one layer out of the paged pool (storage dtype bytes).
 hipError_t launch_read_kv(const void *pool, const int32_t *bt, int L, int layer, int n_kv, int d, int elem_bytes,

@@ -235,6 +235,25 @@ int dflash_propose_batch(dflash_head *head, dflash_state *const *states, int32_t
                          const int64_t *positions, int32_t num_drafts, const int32_t *bitmasks, uint32_t *ids,
                          float *conf, float *row_prob, float *logits, uint64_t stream);
 
+/* dflash_propose without the head's scratch, for callers that cannot
+ * allocate device memory or must not touch the head's buffers: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation. The
+ * arguments, checks and results are those of dflash_propose (bit for bit the
+ * same outputs); the call's scratch (activations, split partials, counters,
+ * the block's V^T copy) lives in a static device array of the library, 16 MiB
+ * per device, held from library load until the process ends. The call clears
+ * what must start at zero with a fill kernel on `stream` and allocates
+ * nothing (no hipMalloc, no events). Every call on one device shares that
+ * array and it keeps the last call's contents: calls that overlap on one
+ * device (other streams, other heads, other threads) race and must be
+ * ordered by the caller. DFLASH_E_INVALID, before anything is enqueued, when
+ * the propose needs more scratch than the array holds (the full DFlash
+ * geometry needs at most ~10 MiB: 16 block rows, 64 attention splits per kv
+ * head), or when the head's device could not resolve the array at build. */
+int dflash_propose_noalloc(dflash_head *head, dflash_state *st, uint32_t last_token, int64_t position,
+                           int32_t num_drafts, const int32_t *bitmask, uint32_t *ids, float *conf, float *row_prob,
+                           float *logits, uint64_t stream);
+
 /* Trim after verification ([DraftProposer] after_verify): keep the first
  * num_accepted rows appended since the previous dflash_after_verify (or since
  * the state was created) and drop the rest; the kept rows become committed.
