@@ -14,7 +14,11 @@ its own stream during the timed steps. `cpu_baseline` times the float64 oracle
 on the host on a bounded sample of the same workload.
 
 Workloads (--workload): single_ctx1024 (default), single_ctx4096_trim,
-batch32_ctx512_4096, batch64_fp8_ctx256_4096.
+batch32_ctx512_4096, batch64_fp8_ctx256_4096, batch64_fp8a8_ctx256_4096,
+single_ctx1024_fp8w. Unless --no-extra, the batch-64 FP8 workload
+(64 sequences, E4M3 LM head and KV cache, 50% grammar masks) is measured in
+the same run after the headline one and reported under "batch64_fp8" with its
+own µs/propose, MFMA fraction and LM-head roofline.
 """
 import argparse
 import json
@@ -113,9 +117,11 @@ def precompute_bytes(geo, rows):
 
 
 class Workload:
-    """Head, states and inputs of one workload, plus its step."""
+    """Head, states and inputs of one workload, plus its step. `weights`
+    reuses a weight set drawn for another workload of the same matrices (the
+    FP8 KV scales are added when this one needs them)."""
 
-    def __init__(self, name, steps_planned):
+    def __init__(self, name, steps_planned, weights=None):
         import numpy as np
         import synth
         from block_diffusion_draft_03_amd import Head
@@ -123,8 +129,12 @@ class Workload:
         wl = self.wl
         geo = wl.geo
         self.geo = geo
-        log(f"[bench] {name}: generating weights")
-        self.weights = synth.make_weights(geo)
+        if weights is None:
+            log(f"[bench] {name}: generating weights")
+            weights = synth.make_weights(geo)
+        elif geo.kv_dtype == "fp8" and "kv_scale" not in weights:
+            weights = dict(weights, kv_scale=synth.make_kv_scales(geo))
+        self.weights = weights
         n = wl.n_seqs
         self.lens = [wl.ctx_lo] * n if wl.ctx_lo == wl.ctx_hi else [int(x) for x in synth.make_ctx_lengths(n, wl.ctx_lo, wl.ctx_hi)]
         grow = wl.new_rows * (steps_planned + 2) if wl.trim else wl.new_rows
@@ -222,18 +232,25 @@ def time_loop(fn, steps):
 def cpu_baseline(wl_obj, budget_s=12.0, max_seqs=2):
     """Time the float64 oracle on the host on a bounded sample: at most
     max_seqs sequences of the workload, whole steps (precompute of the new
-    rows + propose + trim), for about budget_s seconds after one warm-up."""
+    rows + propose + trim), for about budget_s seconds after one warm-up;
+    with the BLAS threads numpy has (all host cores), then with one."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    out = _cpu_baseline_run(wl_obj, budget_s, max_seqs, cores)
+    with threadpool_limits(limits=1):
+        one = _cpu_baseline_run(wl_obj, budget_s, 1, 1)
+    out["single_thread"] = one
+    out["precision"] = "float64"
+    return out
+
+
+def _cpu_baseline_run(wl_obj, budget_s, max_seqs, cores):
     import numpy as np
     import synth
     from oracle.dflash import OracleHead
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:
-        cores = os.cpu_count() or 1
     wl = wl_obj.wl
     geo = wl_obj.geo
-    log("[bench] cpu baseline: oracle setup")
+    log(f"[bench] cpu baseline ({cores} threads): oracle setup")
     orc = OracleHead(geo.as_dict(), wl_obj.weights)
     idx = list(range(min(max_seqs, wl.n_seqs)))
     states = []
@@ -278,46 +295,41 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_bytes_each_way": n * 4, "launches": 3}))
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="single_ctx1024")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: the propose path is data-parallel over sequences and each GPU "
-              f"would run its own head; --gpus {args.gpus} is not supported", file=sys.stderr)
-        sys.exit(2)
-    import torch
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    if args.copy_calibration:
-        copy_calibration(args.copy_calibration)
-        return
+def same_matrices(a, b):
+    """Whether two geometries draw the same weight matrices (synth draws them
+    from the shapes and the stored dtype only)."""
+    key = lambda g: (g.num_layers, g.hidden, g.intermediate, g.num_q_heads, g.num_kv_heads, g.head_dim, g.vocab,
+                     g.num_target_layers, g.target_hidden, g.weight_dtype)
+    return key(a) == key(b)
 
-    w = Workload(args.workload, args.steps + args.warmup)
+
+EXTRA_WORKLOAD = "batch64_fp8_ctx256_4096"
+EXTRA_KEY = "batch64_fp8"
+
+
+def measure(w, steps, warmup):
+    """Warm up, time `steps` whole steps (instrumented: per-phase HIP events on
+    the library's stream), then the forward alone (uninstrumented) and a
+    prompt-scale precompute; returns the workload's measurements."""
+    import torch
     geo, wl = w.geo, w.wl
-    log(f"[bench] warmup {args.warmup}")
-    for _ in range(args.warmup):
+    log(f"[bench] {wl.name}: warmup {warmup}")
+    for _ in range(warmup):
         w.step()
     torch.cuda.synchronize()
 
-    log(f"[bench] timing {args.steps} steps")
+    log(f"[bench] {wl.name}: timing {steps} steps")
     w.head.timing_enable(True)
     w.head.timing_read(0)
     w.head.timing_read(1)
     w.head.timing_read(2)
-    ms_step, wall = time_loop(w.step, args.steps)
+    ms_step, wall = time_loop(w.step, steps)
     lm_ms, lm_launches = w.head.timing_read(0)
     prop_ms, prop_n = w.head.timing_read(1)
     pre_ms, pre_n = w.head.timing_read(2)
     w.head.timing_enable(False)
     # forward alone, uninstrumented
-    ms_prop, _ = time_loop(w.propose, args.steps)
+    ms_prop, _ = time_loop(w.propose, steps)
     us_prefill, prefill_flops = time_prefill(w)
 
     ctx_rows = [s.ctx_len + (0 if wl.trim else wl.new_rows) for s in w.states]
@@ -328,7 +340,6 @@ def main():
     lm_avg_s = lm_ms / max(1, lm_launches) / 1e3
     lm_gbs = lm_bytes / lm_avg_s / 1e9
     lm_tflops = lm_flops / lm_avg_s / 1e12
-    blocks_per_s = wl.n_seqs / (ms_step / 1e3)
     if rows > (64 if geo.layer_dtype == "fp8" else 32) or getattr(geo, "lm_act_dtype", "bf16") == "fp8":
         # many rows (the library's switch to the tiled kernels): the LM head is an
         # MFMA-bound GEMM (bf16 MFMA, also for the E4M3 head widened to bf16; the
@@ -346,19 +357,10 @@ def main():
                     "frac": round(lm_gbs / HBM_PEAK_GBS, 4), "traffic": lm_head_traffic(wl.name),
                     "bytes_per_launch": lm_bytes, "avg_launch_us": round(lm_avg_s * 1e6, 2),
                     "launches": lm_launches}
-    out = {
-        "metric": METRIC,
-        "value": round(blocks_per_s, 3),
-        "unit": "blocks/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+    return {
+        "blocks_per_s": round(wl.n_seqs / (ms_step / 1e3), 3),
         "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
         "dtype": "bf16" if geo.lm_head_dtype == "bf16" and geo.layer_dtype == "bf16" else "bf16+fp8",
-        "data": "synthetic",
         "config": {"workload": wl.name, "n_seqs": wl.n_seqs, "ctx_rows": ctx_rows if wl.n_seqs <= 4 else
                    [min(ctx_rows), max(ctx_rows)], "gamma": geo.gamma, "layers": geo.num_layers,
                    "vocab": geo.vocab, "hidden": geo.hidden, "new_rows_per_step": wl.new_rows,
@@ -378,12 +380,71 @@ def main():
         "prefill_mfma_frac": round(prefill_flops / (us_prefill / 1e6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "wall_s_timed": round(wall, 3),
     }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="single_ctx1024")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
+    ap.add_argument("--no-extra", dest="extra", action="store_false",
+                    help=f"skip the {EXTRA_WORKLOAD} measurement reported under '{EXTRA_KEY}'")
+    ap.add_argument("--extra-steps", type=int, default=20)
+    ap.add_argument("--extra-warmup", type=int, default=5)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the propose path is data-parallel over sequences and each GPU "
+              f"would run its own head; --gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+
+    w = Workload(args.workload, args.steps + args.warmup)
+    m = measure(w, args.steps, args.warmup)
+    geo, wl = w.geo, w.wl
+    out = {
+        "metric": METRIC,
+        "value": m["blocks_per_s"],
+        "unit": "blocks/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": m["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": m["dtype"],
+        "data": "synthetic",
+        "config": m["config"],
+    }
+    out.update({k: v for k, v in m.items() if k not in ("blocks_per_s", "ms_per_step", "dtype", "config")})
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
-    print(json.dumps(out), flush=True)
+    import synth
+    weights = w.weights if same_matrices(w.geo, synth.WORKLOADS[EXTRA_WORKLOAD].geo) else None
     for st in w.states:
         st.free()
     w.head.destroy()
+    del w
+    if args.extra and args.workload != EXTRA_WORKLOAD:
+        # the batched FP8 workload beside the headline, in the same run
+        torch.cuda.empty_cache()
+        x = Workload(EXTRA_WORKLOAD, args.extra_steps + args.extra_warmup, weights=weights)
+        mx = measure(x, args.extra_steps, args.extra_warmup)
+        mx["steps"], mx["warmup"] = args.extra_steps, args.extra_warmup
+        out[EXTRA_KEY] = mx
+        for st in x.states:
+            st.free()
+        x.head.destroy()
+    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":

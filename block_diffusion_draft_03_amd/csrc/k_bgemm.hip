@@ -51,6 +51,7 @@ struct Tiling {
 using TileG = Tiling<128, 128, 4, 2>;   // waves of 32 x 64
 using TileW = Tiling<256, 128, 4, 2>;   // waves of 64 x 64
 using TileL = Tiling<256, 256, 2, 4>;
+using TileLW = Tiling<256, 256, 2, 4>;  // the E4M3-weight LM head (weights widened in registers)
 
 constexpr int NSTAGE_G = 4;            // LDS ring depth (stages in flight + the one multiplied): 128 KB
 constexpr int NSTAGE_W = 3;            // 144 KB
@@ -435,10 +436,10 @@ __global__ __launch_bounds__(TL::NTHR) void k_blm_head(LmArgs a, int n_p, int n_
   constexpr int WN = TL::WN, WM = TL::WM, BN = TL::BN, BM = TL::BM, NT = TL::NT;
   constexpr int MW = BN / 32;        // mask words of a vocab block
   constexpr int MSEQ = BM / 2 + 1;   // sequences one block of rows can touch (gamma >= 2)
-  static_assert(TL::WAVES_N == 2, "two waves share each activation row");
+  constexpr int WNS = TL::WAVES_N;  // waves that share each activation row
   __shared__ uint4 lds[NSTAGE * StageShape<SW8, TL>::F * 64];
-  __shared__ float s_mx[2][BM], s_se[2][BM];
-  __shared__ uint32_t s_idx[2][BM];
+  __shared__ float s_mx[WNS][BM], s_se[WNS][BM];
+  __shared__ uint32_t s_idx[WNS][BM];
   __shared__ float s_scale[BN];
   __shared__ uint32_t s_mask[((MSEQ + 7) / 8) * 8 * MW];  // [local sequence][word], whole loads of 8 sequences
   // Persistent placement: workgroup b sits on XCD x = b % 8 with activation
@@ -552,14 +553,19 @@ __global__ __launch_bounds__(TL::NTHR) void k_blm_head(LmArgs a, int n_p, int n_
     __syncthreads();
     if (threadIdx.x < BM) {
       const int row = threadIdx.x, m = mb * BM + row;
-      ArgState x, y;
+      ArgState x;
       x.mx = s_mx[0][row];
       x.se = s_se[0][row];
       x.idx = s_idx[0][row];
-      y.mx = s_mx[1][row];
-      y.se = s_se[1][row];
-      y.idx = s_idx[1][row];
-      x = arg_merge(x, y);
+      // the row's waves in wave order
+#pragma unroll
+      for (int w = 1; w < WNS; ++w) {
+        ArgState y;
+        y.mx = s_mx[w][row];
+        y.se = s_se[w][row];
+        y.idx = s_idx[w][row];
+        x = arg_merge(x, y);
+      }
       if (m < a.M) {
         const size_t o = (size_t)p * a.ld_part + m;
         a.part_mx[o] = x.mx;
@@ -641,7 +647,7 @@ hipError_t launch_blm_head(bool w_fp8, bool a_fp8, const LmArgs &a, hipStream_t 
   const int stride_p = groups * 8;
   dim3 grid(stride_p * n_mb);
   if (a_fp8) hipLaunchKernelGGL((k_blm_head<LM_W8A8, NSTAGE_LM, TileL>), grid, dim3(TileL::NTHR), 0, s, a, n_p, n_mb, stride_p);
-  else if (w_fp8) hipLaunchKernelGGL((k_blm_head<LM_W8, NSTAGE_LM, TileL>), grid, dim3(TileL::NTHR), 0, s, a, n_p, n_mb, stride_p);
+  else if (w_fp8) hipLaunchKernelGGL((k_blm_head<LM_W8, NSTAGE_LM, TileLW>), grid, dim3(TileLW::NTHR), 0, s, a, n_p, n_mb, stride_p);
   else hipLaunchKernelGGL((k_blm_head<LM_BF16, NSTAGE_LM, TileL>), grid, dim3(TileL::NTHR), 0, s, a, n_p, n_mb, stride_p);
   return hipGetLastError();
 }
