@@ -53,6 +53,37 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8 &a, const bf16x8 &b, 
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4 &u) { return __builtin_bit_cast(bf16x8, u); }
 
+// ---- fp16 (the attention operands: Q, K, V and P) ----
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// float -> fp16 pair, round to nearest even (fp16 is stored as uint16_t bit patterns).
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const f16x2_t v = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Two bf16 (one dword) -> two fp16: exact for magnitudes in fp16's normal
+// range [2^-14, 65504] (a bf16 significand has 8 bits, fp16's 11).
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  return pack_f16x2(__uint_as_float(w << 16), __uint_as_float(w & 0xFFFF0000u));
+}
+
+// Four E4M3FN codes (one dword) -> four fp16 (two dwords), bytes 0, 1 into
+// the first dword and 2, 3 into the second; exact (every E4M3 value is an
+// fp16 value).
+__device__ __forceinline__ uint2 e4m3x4_to_f16x4(uint32_t w) {
+  const f16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.0f, false);
+  const f16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.0f, true);
+  return uint2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+}
+
+__device__ __forceinline__ f16x8 as_f16x8(const uint4 &u) { return __builtin_bit_cast(f16x8, u); }
+
+__device__ __forceinline__ f32x4 mfma16x16x32_f16(const f16x8 &a, const f16x8 &b, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + fast_exp2(-x * LOG2E)); }

@@ -69,7 +69,7 @@ struct Scratch {
   float *act8_scale = nullptr;                 // and their row scales [M]
   uint16_t *qkv = nullptr, *attn = nullptr, *mlp = nullptr;
   float2 *cs = nullptr;                        // RoPE (cos, sin) per row [M][d / 2]
-  uint16_t *o_part = nullptr;                  // attention split partials [n_kv][splits][R][d]
+  uint16_t *o_part = nullptr;                  // attention split outputs (fp16) [n_kv][splits][R][d]
   float *ml_part = nullptr;                    // and their (max, sum)
   int attn_slots = 0;                          // splits over all kv heads o_part holds
   float *lm_mx = nullptr, *lm_se = nullptr;    // LM-head partials [P][M]
@@ -597,7 +597,8 @@ int propose_check(dflash_head *H, dflash_state *const *states, int n, const uint
   int32_t tiles[DFLASH_MAX_BATCH];
   for (int i = 0; i < n; ++i) tiles[i] = attn_tiles(states[i]->rows.ctx_len, g.W);
   std::string err;
-  const int rc = attn_plan(n, tiles, g.n_kv, attn_max_tiles_per_split(), attn_slots / g.n_kv, plan, &err);
+  const int rc = attn_plan(n, tiles, g.n_kv, attn_max_tiles_per_split(), attn_slots / g.n_kv,
+                           g.kv_fp8 ? ATTN_TARGET_WGS_E4M3 : ATTN_TARGET_WGS, plan, &err);
   if (rc != DFLASH_OK) return set_err(rc, err);
   return DFLASH_OK;
 }

@@ -32,9 +32,11 @@ __device__ __forceinline__ void epilogue4_qkv(const f32x4 v, int m, int n, const
     y[2] = v[2] * cs.z - v[3] * cs.w;
     y[3] = v[3] * cs.z + v[2] * cs.w;
   }
+  // fp16: Q, K and V are only read by the attention kernel, which multiplies
+  // in fp16 (8 more significand bits than bf16 on the same matrix cores)
   uint2 o;
-  o.x = pack_bf16x2(y[0], y[1]);
-  o.y = pack_bf16x2(y[2], y[3]);
+  o.x = pack_f16x2(y[0], y[1]);
+  o.y = pack_f16x2(y[2], y[3]);
   *(uint2 *)(ea.out_bf16 + (size_t)m * ea.ldo + n) = o;
   if (n >= ea.q_dim + ea.kv_dim && ea.vtb) {
     // V of the block rows, transposed per kv head for the attention kernel
@@ -43,14 +45,14 @@ __device__ __forceinline__ void epilogue4_qkv(const f32x4 v, int m, int n, const
     const int n_kv = ea.kv_dim / ea.head_dim, nb16 = ea.gp / 16;
     uint16_t *vt = ea.vtb + (((size_t)(seq * n_kv + hd) * nb16 + j / 16) * ea.head_dim + dim) * 16 + (j & 15);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) vt[(size_t)r * 16] = f32_to_bf16(y[r]);
+    for (int r = 0; r < 4; ++r) vt[(size_t)r * 16] = (uint16_t)(pack_f16x2(y[r], 0.0f) & 0xFFFFu);
   }
 }
 
 // EPI_F32:      out_f32[m, n..n+3] = v
 // EPI_PARTIAL:  out_f32[split][m][n..n+3] = v   (row stride ldo, split stride ld_split rows)
 // EPI_SWIGLU:   out_bf16[m, n/2], [m, n/2 + 1] = silu(gate) * up
-// EPI_QKV_ROPE: out_bf16[m, n..n+3] = v, rotated by row m's (cos, sin) when n is a Q or K column
+// EPI_QKV_ROPE: out_bf16[m, n..n+3] = v as fp16, rotated by row m's (cos, sin) when n is a Q or K column
 // EPI_KV_SCATTER: columns [K0 | V0 | K1 | V1 ...]; K rotated at the row's position; stored
 //               (bf16 or E4M3 with the per-head scale) into the row's pool slot
 template <int EPI>

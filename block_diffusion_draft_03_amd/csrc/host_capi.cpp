@@ -85,11 +85,11 @@ int dfh_reserve_rows(void **seqs, int32_t n, const int32_t *n_new, const int32_t
 int32_t dfh_attn_tiles(int32_t ctx_len, int32_t window) { return attn_tiles(ctx_len, window); }
 
 // the propose's split plan: *tps and *n_split on success
-int dfh_attn_plan(int32_t n, const int32_t *tiles, int32_t n_kv, int32_t max_tps, int64_t slot_cap, int32_t *tps,
-                  int32_t *n_split, int32_t *nsplit_out) {
+int dfh_attn_plan(int32_t n, const int32_t *tiles, int32_t n_kv, int32_t max_tps, int64_t slot_cap, int32_t target_wgs,
+                  int32_t *tps, int32_t *n_split, int32_t *nsplit_out) {
   g_err.clear();
   AttnPlan p;
-  const int rc = attn_plan(n, tiles, n_kv, max_tps, slot_cap, &p, &g_err);
+  const int rc = attn_plan(n, tiles, n_kv, max_tps, slot_cap, target_wgs, &p, &g_err);
   if (rc == DFLASH_OK) {
     *tps = p.tps;
     *n_split = p.n_split;

@@ -246,9 +246,9 @@ int32_t attn_tiles_worst(int32_t window, int32_t max_seq_len) {
   return worst;
 }
 
-int attn_plan(int32_t n, const int32_t *tiles, int32_t n_kv, int32_t max_tps, int64_t slot_cap, AttnPlan *plan,
-              std::string *err) {
-  if (n < 1 || n > DFLASH_MAX_BATCH || n_kv < 1 || max_tps < 1)
+int attn_plan(int32_t n, const int32_t *tiles, int32_t n_kv, int32_t max_tps, int64_t slot_cap, int32_t target_wgs,
+              AttnPlan *plan, std::string *err) {
+  if (n < 1 || n > DFLASH_MAX_BATCH || n_kv < 1 || max_tps < 1 || target_wgs < 1)
     return fail(err, DFLASH_E_INVALID, "attention plan: bad batch, head count or tile limit");
   int32_t max_T = 0;
   for (int32_t i = 0; i < n; ++i) {
@@ -269,7 +269,7 @@ int attn_plan(int32_t n, const int32_t *tiles, int32_t n_kv, int32_t max_tps, in
   // more than ATTN_MAX_SPLITS splits
   int32_t tps = std::min(max_tps, std::max(1, (max_T + ATTN_PREF_SPLITS - 1) / ATTN_PREF_SPLITS));
   tps = std::max(tps, (max_T + ATTN_MAX_SPLITS) / ATTN_MAX_SPLITS);
-  while (tps < max_tps && (flat(tps) * n_kv > ATTN_TARGET_WGS || flat(tps) > cap)) ++tps;
+  while (tps < max_tps && (flat(tps) * n_kv > target_wgs || flat(tps) > cap)) ++tps;
   if (tps > max_tps || flat(tps) > cap || splits_of(max_T, tps) > ATTN_MAX_SPLITS)
     return fail(err, DFLASH_E_INVALID,
                 "context window too long for the attention splits (" + std::to_string(max_T) + " tiles of 32 keys, " +
@@ -288,7 +288,7 @@ int attn_plan(int32_t n, const int32_t *tiles, int32_t n_kv, int32_t max_tps, in
 int64_t attn_slots(const Geo &g, int32_t max_seq_len, int32_t max_tps) {
   const int64_t worst = attn_tiles_worst(g.W, max_seq_len);
   const int64_t per_seq = std::min<int64_t>(ATTN_MAX_SPLITS, (worst + max_tps) / max_tps);
-  return std::max<int64_t>({(int64_t)ATTN_TARGET_WGS * 2, (int64_t)g.max_batch * g.n_kv * per_seq,
+  return std::max<int64_t>({(int64_t)std::max(ATTN_TARGET_WGS, ATTN_TARGET_WGS_E4M3) * 2, (int64_t)g.max_batch * g.n_kv * per_seq,
                             (int64_t)g.n_kv * ATTN_MAX_SPLITS});
 }
 
@@ -296,7 +296,8 @@ int check_attn_capacity(const Geo &g, int32_t max_seq_len, int32_t max_tps, std:
   std::vector<int32_t> tiles(g.max_batch, attn_tiles_worst(g.W, max_seq_len));
   AttnPlan plan;
   std::string e;
-  if (attn_plan(g.max_batch, tiles.data(), g.n_kv, max_tps, attn_slots(g, max_seq_len, max_tps) / g.n_kv, &plan, &e) !=
+  if (attn_plan(g.max_batch, tiles.data(), g.n_kv, max_tps, attn_slots(g, max_seq_len, max_tps) / g.n_kv,
+                g.kv_fp8 ? ATTN_TARGET_WGS_E4M3 : ATTN_TARGET_WGS, &plan, &e) !=
       DFLASH_OK)
     return fail(err, DFLASH_E_INVALID,
                 "config: max_batch sequences of min(ctx_window, max_seq_len) rows exceed the attention splits: " + e);

@@ -97,13 +97,19 @@ int seq_install(SeqRows *s, BlockPool *pool, const int32_t *blocks, int32_t n, i
 // The block's attention over a sequence's context runs in splits of up to
 // tps ctx tiles of 32 keys (from the window start aligned down to a KV
 // block); the sequence's last split also takes the block's own keys, which
-// count as one more tile. A launch aims for ATTN_TARGET_WGS workgroups (two
-// per compute unit) over all sequences and kv heads, prefers at most
+// count as one more tile. A launch aims for a target number of workgroups
+// over all sequences and kv heads: ATTN_TARGET_WGS (two per compute unit)
+// with a bf16 cache, ATTN_TARGET_WGS_E4M3 with an E4M3 cache, whose tiles
+// are cheaper to load, so that shorter splits (more of them, the last ones
+// starting as the first finish) balance better (measured on 64 sequences of
+// 256 to 4096 ctx rows: 82 us against 91 us per layer; with a bf16 cache the
+// larger target is slower). It prefers at most
 // ATTN_PREF_SPLITS splits per sequence, and cannot exceed ATTN_MAX_SPLITS
 // splits per sequence (one wave merges a row's splits) or ATTN_MAX_FLAT
 // splits in all (the split-to-sequence map travels in the launch arguments).
 constexpr int ATTN_MAX_FLAT = 1024;
 constexpr int ATTN_TARGET_WGS = 512;
+constexpr int ATTN_TARGET_WGS_E4M3 = 768;
 constexpr int ATTN_MAX_SPLITS = 64;
 constexpr int ATTN_PREF_SPLITS = 16;
 
@@ -120,10 +126,11 @@ struct AttnPlan {
 };
 
 // Plan n sequences (tiles[i] ctx tiles each) over n_kv kv heads, with at most
-// max_tps tiles per split and slot_cap partial slots per kv head. Fails with
-// DFLASH_E_INVALID, touching nothing, when no split size fits.
-int attn_plan(int32_t n, const int32_t *tiles, int32_t n_kv, int32_t max_tps, int64_t slot_cap, AttnPlan *plan,
-              std::string *err);
+// max_tps tiles per split, slot_cap partial slots per kv head and about
+// target_wgs workgroups. Fails with DFLASH_E_INVALID, touching nothing, when
+// no split size fits.
+int attn_plan(int32_t n, const int32_t *tiles, int32_t n_kv, int32_t max_tps, int64_t slot_cap, int32_t target_wgs,
+              AttnPlan *plan, std::string *err);
 
 // Partial slots (per kv head) a head keeps for its attention splits.
 int64_t attn_slots(const Geo &g, int32_t max_seq_len, int32_t max_tps);

@@ -8,7 +8,8 @@
 // 16-row KV blocks (positions outside [win_start, ctx_len) are masked), and
 // the gamma block rows form the block tile(s), whose K rows come straight
 // from the QKV output and whose V^T from the copy the QKV epilogue writes.
-// A split owns a run of ctx tiles; the last split also owns the block tiles.
+// A sequence's ctx tiles and its block tile(s), counted as two more tiles,
+// are divided evenly among its splits; the last split owns the block tile(s).
 //
 // The pool stores K row-major and V transposed ([dim][16 slots]) per block,
 // so every 16-byte piece of an MFMA fragment is contiguous in global memory.
@@ -23,16 +24,23 @@
 // sub-tile u hold keys (r / 4) * 8 + 4u + r % 4, so lane group g ends with
 // the scores of keys 8g .. 8g+7 for its query; those are exactly the B
 // operand of O^T = V^T P^T, whose A operand (16 dims x keys 8g .. 8g+7) is a
-// 16-byte piece of V^T. Online softmax in base 2; the FP8 V scale of ctx keys
-// is folded into P. With an E4M3 cache the K fragments of k-steps 2j and 2j+1
+// 16-byte piece of V^T. Online softmax in base 2. Both products run on the
+// fp16 matrix cores (f32 accumulation): the block rows' Q, K and V come from
+// the QKV epilogue as fp16, a bf16 ctx tile is widened to fp16 in LDS by the
+// waves that loaded it, E4M3 codes are decoded to fp16 as fragments are read,
+// and P is rounded to fp16 (three more significand bits than bf16 at every
+// step). With an E4M3 cache O accumulates ctx V in code units (the block
+// tile's P is divided by the V scale) and is multiplied by the scale at the
+// end. With an E4M3 cache the K fragments of k-steps 2j and 2j+1
 // take dims 64j + 16g .. +15 of lane group g (one 16-byte piece of an E4M3
 // row), and Q (and the block tile's K) use the same dim order. Q and K also
 // carry their head dims in RoPE pair order; every score is unchanged by these
 // permutations.
 //
-// Each split writes an unnormalised partial (O in bf16, max and sum in f32)
-// that the combine kernel merges (one wave per query row); with a single
-// split the output is written directly.
+// Each split writes its own normalised output (fp16, bounded by max |V|) with
+// its max and sum (f32); the combine kernel merges them (one wave per query
+// row) with weights exp2(m_s - M) l_s. With a single split the output is
+// written directly.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -88,6 +96,9 @@ struct Geom {
   static constexpr int PW = (CF + NWAVE - 1) / NWAVE;         // ctx-tile loads per wave
   static constexpr int PB = (BF + NWAVE - 1) / NWAVE;         // block-tile loads per wave
   static constexpr int NSTAGE = FP8 ? 4 : 3;
+  // a bf16 ctx tile is widened to fp16 in LDS by the waves that loaded it
+  // (each fragment has exactly one loader when CF is a multiple of NWAVE)
+  static constexpr bool CONV = !FP8 && CF % NWAVE == 0;
 };
 
 // First dim of the 8 that lane group gq holds in k-step ks.
@@ -232,10 +243,19 @@ __device__ __forceinline__ float max_lane_groups(float x) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-__device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint2 q) {
-  const uint2 lo = e4m3x4_to_bf16x4(q.x), hi = e4m3x4_to_bf16x4(q.y);
-  return uint4{lo.x, lo.y, hi.x, hi.y};
+__device__ __forceinline__ f16x8 e4m3x8_to_f16x8(uint2 q) {
+  const uint2 lo = e4m3x4_to_f16x4(q.x), hi = e4m3x4_to_f16x4(q.y);
+  return as_f16x8(uint4{lo.x, lo.y, hi.x, hi.y});
 }
+
+__device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 u) {
+  return uint4{bf16x2_to_f16x2(u.x), bf16x2_to_f16x2(u.y), bf16x2_to_f16x2(u.z), bf16x2_to_f16x2(u.w)};
+}
+
+// What a tile slot holds: fp16 (the block tile, or a bf16 ctx tile already
+// widened in place), bf16 (widened to fp16 as its fragments are read) or
+// E4M3 codes (decoded to fp16 as they are read).
+enum TileFmt { T_F16 = 0, T_BF16 = 1, T_E4M3 = 2 };
 
 template <int D>
 struct WaveState {
@@ -243,25 +263,29 @@ struct WaveState {
   float m[QT], l[QT];
 };
 
-// One tile for this wave's two query tiles. `valid` says whether key kt of
-// the tile takes part; sc scales the raw scores into base-2 units; vs is
-// folded into P (E4M3 V of ctx keys).
-template <int D, bool FP8CTX, class Valid>
-__device__ __forceinline__ void tile_step(const uint4 *slot, const bf16x8 (&qf)[QT][Geom<D, false>::KS], bool full,
-                                          Valid valid, float sc, float vs, WaveState<D> &w, int lane) {
-  using G = Geom<D, FP8CTX>;
+// One tile for this wave's query tiles. `valid` says whether key kt of the
+// tile takes part; sc scales the raw scores into base-2 units; P is
+// multiplied by ps before it meets V (1 / V scale on the block tile of an
+// E4M3 cache, whose ctx V stays in code units until the end). Both products
+// run on the fp16 matrix cores with f32 accumulation.
+template <int D, int FMT, class Valid>
+__device__ __forceinline__ void tile_step(const uint4 *slot, const f16x8 (&qf)[QT][Geom<D, false>::KS], bool full,
+                                          Valid valid, float sc, float ps, WaveState<D> &w, int lane) {
+  using G = Geom<D, FMT == T_E4M3>;
   const int gq = lane >> 4;
-  bf16x8 kf[2][G::KS];
+  f16x8 kf[2][G::KS];
 #pragma unroll
   for (int u = 0; u < 2; ++u)
 #pragma unroll
     for (int ks = 0; ks < G::KS; ++ks) {
       const int piece = k_piece(lane & 15, gq);
-      if constexpr (FP8CTX) {
+      if constexpr (FMT == T_E4M3) {
         const uint8_t *p = (const uint8_t *)(slot + (u * (G::KS / 2) + ks / 2) * 64 + piece) + 8 * (ks & 1);
-        kf[u][ks] = as_bf16x8(e4m3x8_to_bf16x8(*(const uint2 *)p));
+        kf[u][ks] = e4m3x8_to_f16x8(*(const uint2 *)p);
+      } else if constexpr (FMT == T_BF16) {
+        kf[u][ks] = as_f16x8(bf16x8_to_f16x8(slot[(u * G::KS + ks) * 64 + piece]));
       } else {
-        kf[u][ks] = as_bf16x8(slot[(u * G::KS + ks) * 64 + piece]);
+        kf[u][ks] = as_f16x8(slot[(u * G::KS + ks) * 64 + piece]);
       }
     }
   uint4 pk[QT];
@@ -273,7 +297,7 @@ __device__ __forceinline__ void tile_step(const uint4 *slot, const bf16x8 (&qf)[
     for (int u = 0; u < 2; ++u) {
       sacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < G::KS; ++ks) sacc[u] = mfma16x16x32(kf[u][ks], qf[qt][ks], sacc[u]);
+      for (int ks = 0; ks < G::KS; ++ks) sacc[u] = mfma16x16x32_f16(kf[u][ks], qf[qt][ks], sacc[u]);
     }
     // raw scores; sc > 0, so the max commutes with the scaling
     float x[2][4];
@@ -300,14 +324,14 @@ __device__ __forceinline__ void tile_step(const uint4 *slot, const bf16x8 (&qf)[
       for (int r = 0; r < 4; ++r) {
         const float e = fast_exp2(fmaf(x[u][r], sc, -m_new));
         psum += e;
-        p[u][r] = FP8CTX ? e * vs : e;
+        p[u][r] = e * ps;
       }
     w.l[qt] = w.l[qt] * alpha[qt] + psum;
     w.m[qt] = m_new;
-    pk[qt].x = pack_bf16x2(p[0][0], p[0][1]);
-    pk[qt].y = pack_bf16x2(p[0][2], p[0][3]);
-    pk[qt].z = pack_bf16x2(p[1][0], p[1][1]);
-    pk[qt].w = pack_bf16x2(p[1][2], p[1][3]);
+    pk[qt].x = pack_f16x2(p[0][0], p[0][1]);
+    pk[qt].y = pack_f16x2(p[0][2], p[0][3]);
+    pk[qt].z = pack_f16x2(p[1][0], p[1][1]);
+    pk[qt].w = pack_f16x2(p[1][2], p[1][3]);
   }
   // rescale O only when some lane's running max moved (alpha == 1 is exact)
   bool moved = false;
@@ -321,16 +345,18 @@ __device__ __forceinline__ void tile_step(const uint4 *slot, const bf16x8 (&qf)[
   }
 #pragma unroll
   for (int dt = 0; dt < G::DT; ++dt) {
-    bf16x8 vf;
-    if constexpr (FP8CTX) {
+    f16x8 vf;
+    if constexpr (FMT == T_E4M3) {
       const uint8_t *base = (const uint8_t *)(slot + (G::KS + dt / 2) * 64);
       const uint8_t *p = base + (((dt & 1) * 32 + (gq >> 1) * 16 + (lane & 15)) * 16) + 8 * (gq & 1);
-      vf = as_bf16x8(e4m3x8_to_bf16x8(*(const uint2 *)p));
+      vf = e4m3x8_to_f16x8(*(const uint2 *)p);
+    } else if constexpr (FMT == T_BF16) {
+      vf = as_f16x8(bf16x8_to_f16x8(slot[(2 * G::KS + dt) * 64 + v_piece(lane & 15, gq)]));
     } else {
-      vf = as_bf16x8(slot[(2 * G::KS + dt) * 64 + v_piece(lane & 15, gq)]);
+      vf = as_f16x8(slot[(2 * G::KS + dt) * 64 + v_piece(lane & 15, gq)]);
     }
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) w.o[qt][dt] = mfma16x16x32(vf, as_bf16x8(pk[qt]), w.o[qt][dt]);
+    for (int qt = 0; qt < QT; ++qt) w.o[qt][dt] = mfma16x16x32_f16(vf, as_f16x8(pk[qt]), w.o[qt][dt]);
   }
 }
 
@@ -340,7 +366,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(AttnArgs a) {
   using GB = Geom<D, false>;
   __shared__ uint4 ring[NS][G::CF * 64];
   __shared__ uint4 blkt[GB::BF * 64];
-  __shared__ int32_t s_bt[2 * MAX_TPS];
+  __shared__ int32_t s_bt[2 * (MAX_TPS + 1)];
 
   const int flat = blockIdx.x, g = blockIdx.y;
   const int s = a.split_seq[flat];
@@ -352,7 +378,14 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(AttnArgs a) {
   const bool has_ctx = sq.win_start < sq.ctx_len;
   const int p0 = has_ctx ? (sq.win_start >> 4) << 4 : 0;
   const int T = has_ctx ? (sq.ctx_len - p0 + KT - 1) / KT : 0;
-  const int t0 = c * a.tps, nt = max(0, min(T, t0 + a.tps) - t0);
+  // the sequence's T ctx tiles and its block tile, which costs about two
+  // (its own load, ahead of the ctx loop), are divided evenly among its
+  // splits: T + 2 units, the last split owning the block tile. The planner
+  // sized the splits for T + 1 units of at most tps, so a split holds at most
+  // tps + 1 ctx tiles.
+  const int U = T + 2;
+  const int t0 = (int)((int64_t)c * U / sq.nsplit), t1 = min(T, (int)((int64_t)(c + 1) * U / sq.nsplit));
+  const int nt = max(0, t1 - t0);
   const bool last = c == sq.nsplit - 1;
   const int NBT = (a.gamma + KT - 1) / KT;
 
@@ -362,16 +395,10 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(AttnArgs a) {
     for (int i = threadIdx.x; i < NS * G::CF * 64; i += NTHR) z[i] = uint4{0u, 0u, 0u, 0u};
     for (int i = threadIdx.x; i < GB::BF * 64; i += NTHR) blkt[i] = uint4{0u, 0u, 0u, 0u};
   }
-  {
-    // block ids of this split's tiles; blocks past the sequence reuse its
-    // last block (their keys are masked)
-    const int nbv = (sq.ctx_len + 15) >> 4;
-    for (int i = threadIdx.x; i < 2 * nt; i += NTHR) s_bt[i] = sq.bt[min((p0 >> 4) + 2 * t0 + i, nbv - 1)];
-  }
-
   // Q fragments (B operand of S^T): query column r16 of this wave's tiles
-  // (rows past R repeat row R - 1 and are not written)
-  bf16x8 qf[QT][GB::KS];
+  // (rows past R repeat row R - 1 and are not written), loaded first so that
+  // their latency overlaps the block table's
+  f16x8 qf[QT][GB::KS];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const int q = min((wave * QT + qt) * 16 + r16, R - 1);
@@ -380,8 +407,15 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(AttnArgs a) {
 #pragma unroll
     for (int ks = 0; ks < GB::KS; ++ks) {
       const int dd = kdim<FP8>(ks, gq);
-      qf[qt][ks] = as_bf16x8(dd < D ? *(const uint4 *)(qrow + dd) : uint4{0u, 0u, 0u, 0u});
+      qf[qt][ks] = as_f16x8(dd < D ? *(const uint4 *)(qrow + dd) : uint4{0u, 0u, 0u, 0u});
     }
+  }
+
+  {
+    // block ids of this split's tiles; blocks past the sequence reuse its
+    // last block (their keys are masked)
+    const int nbv = (sq.ctx_len + 15) >> 4;
+    for (int i = threadIdx.x; i < 2 * nt; i += NTHR) s_bt[i] = sq.bt[min((p0 >> 4) + 2 * t0 + i, nbv - 1)];
   }
 
   float kscale = 1.0f, vscale = 1.0f;
@@ -401,6 +435,11 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(AttnArgs a) {
     for (int dt = 0; dt < GB::DT; ++dt) w.o[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   __syncthreads();  // s_bt, zeroed LDS
+  // The Q loads complete here, before any direct-to-LDS load is issued. The
+  // tile loads are assembly, which the compiler does not see but the hardware
+  // counts: a Q load still pending in the compiler's view would make it wait
+  // for vmcnt(0) inside the tile loop, i.e. for every tile in flight.
+  wait_vm<0>();
 
   TileSrc src;
   src.pool = (const uint8_t *)a.pool;
@@ -435,7 +474,9 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(AttnArgs a) {
       }
       lds_barrier();
       const int nvalid = min(KT, a.gamma - 32 * bt);
-      tile_step<D, false>(blkt, qf, nvalid >= KT, [&](int kt) { return kt < nvalid; }, sc_blk, 1.0f, w, lane);
+      // with an E4M3 cache O is kept in V-code units (times vscale at the end)
+      tile_step<D, T_F16>(blkt, qf, nvalid >= KT, [&](int kt) { return kt < nvalid; }, sc_blk,
+                          FP8 ? 1.0f / vscale : 1.0f, w, lane);
     }
   }
 
@@ -443,12 +484,25 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(AttnArgs a) {
 #pragma unroll 1
   for (int t = 0; t < nt; ++t) {
     wait_vm<(NS - 2) * G::PW>();
+    if constexpr (G::CONV) {
+      // this wave's own fragments of tile t, bf16 -> fp16 in place, then
+      // published by the barrier
+      asm volatile("" ::: "memory");
+      uint4 *sl = &ring[t % NS][0];
+#pragma unroll
+      for (int j = 0; j < G::PW; ++j) {
+        uint4 *q = sl + (plan.dst[j] >> 4) + lane;
+        *q = bf16x8_to_f16x8(*q);
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    }
     lds_barrier();
     issue_tile(min(t + NS - 1, nt - 1), (t + NS - 1) % NS);
     const int pos0 = pos_base + t * KT;
     const int lo = sq.win_start - pos0, hi = sq.ctx_len - pos0;
-    tile_step<D, FP8>(&ring[t % NS][0], qf, lo <= 0 && hi >= KT, [&](int kt) { return kt >= lo && kt < hi; },
-                      sc_ctx, FP8 ? vscale : 1.0f, w, lane);
+    constexpr int FMT = FP8 ? T_E4M3 : G::CONV ? T_F16 : T_BF16;
+    tile_step<D, FMT>(&ring[t % NS][0], qf, lo <= 0 && hi >= KT, [&](int kt) { return kt >= lo && kt < hi; },
+                      sc_ctx, 1.0f, w, lane);
   }
   wait_vm<0>();
 
@@ -463,7 +517,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(AttnArgs a) {
     if (sq.nsplit == 1) {
       const int hq = g * a.rep + q / a.gamma, j = q % a.gamma;
       uint16_t *out = a.out + (size_t)(s * a.gamma + j) * a.out_ld + hq * D;
-      const float inv = 1.0f / l_tot;
+      const float inv = vscale / l_tot;  // vscale 1 without an E4M3 cache
 #pragma unroll
       for (int dt = 0; dt < GB::DT; ++dt) {
         const f32x4 v = w.o[qt][dt];
@@ -474,7 +528,8 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(AttnArgs a) {
 #pragma unroll
       for (int dt = 0; dt < GB::DT; ++dt) {
         const f32x4 v = w.o[qt][dt];
-        *(uint2 *)(a.o_part + part * D + dt * 16 + 4 * gq) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        const float nrm = vscale / l_tot;  // the split's own softmax output, |O| <= max |V|
+        *(uint2 *)(a.o_part + part * D + dt * 16 + 4 * gq) = uint2{pack_f16x2(v[0] * nrm, v[1] * nrm), pack_f16x2(v[2] * nrm, v[3] * nrm)};
       }
       if (gq == 0) {
         a.ml_part[part * 2 + 0] = w.m[qt];
@@ -509,10 +564,11 @@ __device__ __forceinline__ float wave_reduce_dpp(float x) {
 }
 
 // Merge the splits of one query row per wave: lane s reads split s's (max,
-// sum); the weights exp2(m_s - M) are read lane by lane and every lane
-// accumulates its dimensions (two adjacent ones for head_dim 128) over the
-// splits in order. The O parts of the first PRE splits are loaded together
-// with the (max, sum) pairs, before the weights are known.
+// sum); the weights exp2(m_s - M) l_s are read lane by lane and every lane
+// accumulates its dimensions (lane, lane + 64, ...; two adjacent ones, 2 lane
+// and 2 lane + 1, for head_dim 128) over the splits in order. The O parts of
+// the first PRE splits are loaded together with the (max, sum) pairs, before
+// the weights are known.
 template <int D>
 __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a, int n_seq) {
   constexpr int DPL = D >= 64 ? D / 64 : 1;  // dims per lane
@@ -526,72 +582,67 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a, int n_seq) {
   if (nsplit == 1) return;             // written by the attention kernel
   const size_t base = (size_t)g * a.n_split + a.seq[s].split0;
   const bool active = D >= 64 || lane < D;
-  // O part of split c at this lane's dimensions: lane, lane + 64, ... (two
-  // adjacent ones, 2 lane and 2 lane + 1, for head_dim 128)
-  auto o_at = [&](int c) {
+  // output of split c at this lane's dimensions, as fp16 bits (two dims in
+  // one dword for head_dim 128); widened only when accumulated, so the
+  // PRE loads below stay in flight together
+  auto o_bits = [&](int c, int i) -> uint32_t {
     const uint16_t *op = a.o_part + ((base + c) * R + q) * D;
     if constexpr (D == 128) return *(const uint32_t *)(op + 2 * lane);
-    else return active ? (uint32_t)op[lane] : 0u;
+    else return (uint32_t)op[min(lane, D - 1) + 64 * i];  // lanes past head_dim write nothing
   };
-  uint32_t pre[PRE][DPL == 2 ? 1 : DPL];
-#pragma unroll
-  for (int c = 0; c < PRE; ++c) {
+  constexpr int NB = D == 128 ? 1 : DPL;  // dwords per lane and split
+  auto widen = [&](const uint32_t (&b)[NB], float (&v)[DPL]) {
     if constexpr (D == 128) {
-      pre[c][0] = c < nsplit ? o_at(c) : 0u;
+      const f16x2_t x = __builtin_bit_cast(f16x2_t, b[0]);
+      v[0] = (float)x[0];
+      v[1] = (float)x[1];
     } else {
 #pragma unroll
-      for (int i = 0; i < DPL; ++i)
-        pre[c][i] = (c < nsplit && active) ? (uint32_t)a.o_part[((base + c) * R + q) * D + lane + 64 * i] : 0u;
+      for (int i = 0; i < DPL; ++i) v[i] = (float)__builtin_bit_cast(_Float16, (uint16_t)b[i]);
     }
-  }
+  };
+  uint32_t pre[PRE][NB];
+#pragma unroll
+  for (int c = 0; c < PRE; ++c)
+#pragma unroll
+    for (int i = 0; i < NB; ++i) pre[c][i] = c < nsplit ? o_bits(c, i) : 0u;
   float m = -__builtin_huge_valf(), l = 0.0f;
   if (lane < nsplit) {
     m = a.ml_part[((base + lane) * R + q) * 2];
     l = a.ml_part[((base + lane) * R + q) * 2 + 1];
   }
   const float M = wave_reduce_dpp<true>(m);
-  const float w = lane < nsplit ? fast_exp2(m - M) : 0.0f;
-  const float den = wave_reduce_dpp<false>(w * l);
+  const float w = lane < nsplit ? fast_exp2(m - M) * l : 0.0f;  // weight of split `lane`'s normalised output
+  const float den = wave_reduce_dpp<false>(w);
   const int hq = g * a.rep + q / a.gamma, j = q % a.gamma;
   uint16_t *out = a.out + (size_t)(s * a.gamma + j) * a.out_ld + hq * D;
+  float acc[DPL];
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) acc[i] = 0.0f;
+#pragma unroll
+  for (int c = 0; c < PRE; ++c) {
+    if (c < nsplit) {
+      const float wc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), c));
+      float v[DPL];
+      widen(pre[c], v);
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) acc[i] += wc * v[i];
+    }
+  }
+#pragma unroll 16
+  for (int c = PRE; c < nsplit; ++c) {
+    const float wc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), c));
+    uint32_t b[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) b[i] = o_bits(c, i);
+    float v[DPL];
+    widen(b, v);
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) acc[i] += wc * v[i];
+  }
   if constexpr (D == 128) {
-    float acc0 = 0.0f, acc1 = 0.0f;
-#pragma unroll
-    for (int c = 0; c < PRE; ++c) {
-      if (c < nsplit) {
-        const float wc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), c));
-        acc0 += wc * __uint_as_float(pre[c][0] << 16);
-        acc1 += wc * __uint_as_float(pre[c][0] & 0xFFFF0000u);
-      }
-    }
-#pragma unroll 16
-    for (int c = PRE; c < nsplit; ++c) {
-      const float wc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), c));
-      const uint32_t pr = o_at(c);
-      acc0 += wc * __uint_as_float(pr << 16);
-      acc1 += wc * __uint_as_float(pr & 0xFFFF0000u);
-    }
-    *(uint32_t *)(out + 2 * lane) = pack_bf16x2(acc0 / den, acc1 / den);
+    *(uint32_t *)(out + 2 * lane) = pack_bf16x2(acc[0] / den, acc[1] / den);
   } else {
-    float acc[DPL];
-#pragma unroll
-    for (int i = 0; i < DPL; ++i) acc[i] = 0.0f;
-#pragma unroll
-    for (int c = 0; c < PRE; ++c) {
-      if (c < nsplit) {
-        const float wc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), c));
-#pragma unroll
-        for (int i = 0; i < DPL; ++i) acc[i] += wc * __uint_as_float(pre[c][i] << 16);
-      }
-    }
-#pragma unroll 16
-    for (int c = PRE; c < nsplit; ++c) {
-      const float wc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), c));
-      const uint16_t *op = a.o_part + ((base + c) * R + q) * D;
-#pragma unroll
-      for (int i = 0; i < DPL; ++i)
-        if (active) acc[i] += wc * bf16_to_f32(op[lane + 64 * i]);
-    }
 #pragma unroll
     for (int i = 0; i < DPL; ++i)
       if (active) out[lane + 64 * i] = f32_to_bf16(acc[i] / den);

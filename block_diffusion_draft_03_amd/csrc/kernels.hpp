@@ -61,12 +61,12 @@ struct GemmArgs {
 
 struct EpiArgs {
   float *out_f32;
-  uint16_t *out_bf16;
+  uint16_t *out_bf16;  // bf16 bit patterns (SwiGLU), fp16 (QKV)
   int ldo, ld_split;
   // QKV RoPE
   const float2 *cs;   // [M][head_dim / 2] (cos, sin) of each row's position
   int head_dim, q_dim, kv_dim;
-  uint16_t *vtb;      // QKV: V^T of the block rows, [seq][n_kv][gp / 16][head_dim][16] (gp = gamma rounded up to 32)
+  uint16_t *vtb;      // QKV: V^T of the block rows (fp16), [seq][n_kv][gp / 16][head_dim][16] (gp = gamma rounded up to 32)
   int gamma, gp, row0;  // row0: row of the call that this launch's row 0 is
   // KV scatter
   void *pool;
@@ -162,14 +162,14 @@ struct AttnSeq {
 // ATTN_MAX_FLAT (splits over all sequences of one launch): host_core.hpp
 
 struct AttnArgs {
-  const uint16_t *qkv;   // [n_seq * gamma, ld] rows [Q | K | V], RoPE applied
-  const uint16_t *vtb;   // V^T of the block rows, [n_seq][n_kv][roundup(gamma, 32) / 16][head_dim][16], zero padded
+  const uint16_t *qkv;   // [n_seq * gamma, ld] fp16 rows [Q | K | V], RoPE applied
+  const uint16_t *vtb;   // fp16 V^T of the block rows, [n_seq][n_kv][roundup(gamma, 32) / 16][head_dim][16], zero padded
   int ld, gamma, rep, n_kv, head_dim, k_off, v_off;
   const void *pool;      // [block][L][K|V][n_kv] tiles: K [16][head_dim], V^T [head_dim][16]
   int L, layer, kv_fp8;
   const float *kv_scale;
   int tps, n_split;      // ctx tiles (32 positions) per split; splits over all sequences (per kv head)
-  uint16_t *o_part;      // bf16 unnormalised O of each split [slot][R][head_dim]
+  uint16_t *o_part;      // fp16 normalised output of each split [slot][R][head_dim]
   float *ml_part;        // (max, sum) of each split's rows
   uint16_t *out;         // [n_seq * gamma, n_q * head_dim] bf16
   int out_ld;

@@ -44,7 +44,7 @@ def host():
     lib.dfh_seq_install.argtypes = [vp, vp, vp, C.c_int32, C.c_int32, C.c_int32]
     lib.dfh_reserve_rows.argtypes = [vp, C.c_int32, vp, vp, vp]
     lib.dfh_attn_tiles.argtypes = [C.c_int32, C.c_int32]
-    lib.dfh_attn_plan.argtypes = [C.c_int32, vp, C.c_int32, C.c_int32, C.c_int64, C.POINTER(C.c_int32),
+    lib.dfh_attn_plan.argtypes = [C.c_int32, vp, C.c_int32, C.c_int32, C.c_int64, C.c_int32, C.POINTER(C.c_int32),
                                   C.POINTER(C.c_int32), vp]
     lib.dfh_build_check.argtypes = [vp, C.c_int32]
     lib.dflash_yarn_inv_freq.argtypes = [C.c_int32, C.c_float, C.c_float, C.c_float, C.c_float, C.c_int32, vp]
@@ -307,12 +307,12 @@ def test_state_rows_capped_at_max_seq_len(host):
     host.dfh_pool_delete(pool)
 
 
-def _plan(host, tiles, n_kv=4, max_tps=64, cap=1 << 20):
+def _plan(host, tiles, n_kv=4, max_tps=64, cap=1 << 20, target=512):
     t = np.ascontiguousarray(tiles, dtype=np.int32)
     tps, n_split = C.c_int32(), C.c_int32()
     per = np.zeros(len(t), np.int32)
-    rc = host.dfh_attn_plan(len(t), t.ctypes.data_as(C.c_void_p), n_kv, max_tps, cap, C.byref(tps), C.byref(n_split),
-                            per.ctypes.data_as(C.c_void_p))
+    rc = host.dfh_attn_plan(len(t), t.ctypes.data_as(C.c_void_p), n_kv, max_tps, cap, target, C.byref(tps),
+                            C.byref(n_split), per.ctypes.data_as(C.c_void_p))
     return rc, tps.value, n_split.value, per.tolist()
 
 
@@ -330,6 +330,10 @@ def test_attention_split_plan(host):
     # a batch: splits grow until the launch fits two workgroups per CU
     rc, tps, n_split, per = _plan(host, [32] * 32)
     assert rc == OK and n_split * 4 <= 512 and per == [(32 + tps) // tps] * 32
+    # the E4M3 cache's larger target: shorter splits, at most 768 workgroups
+    rc8, tps8, n_split8, _ = _plan(host, [32] * 32, target=768)
+    assert rc8 == OK and tps8 < tps and 512 < n_split8 * 4 <= 768
+    assert _plan(host, [32], target=0)[0] == E_INVALID
     # 1025 tiles (a 32768-row window): 64 tiles per split, 17 splits
     assert _plan(host, [1025]) == (OK, 64, 17, [17])
     # 64 such sequences need 1088 splits > 1024
