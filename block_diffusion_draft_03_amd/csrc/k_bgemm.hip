@@ -440,7 +440,7 @@ __global__ __launch_bounds__(TL::NTHR) void k_blm_head(LmArgs a, int n_p, int n_
   __shared__ uint4 lds[NSTAGE * StageShape<SW8, TL>::F * 64];
   __shared__ float s_mx[WNS][BM], s_se[WNS][BM];
   __shared__ uint32_t s_idx[WNS][BM];
-  __shared__ float s_scale[BN];
+  __shared__ __align__(16) float s_scale[BN];
   __shared__ uint32_t s_mask[((MSEQ + 7) / 8) * 8 * MW];  // [local sequence][word], whole loads of 8 sequences
   // Persistent placement: workgroup b sits on XCD x = b % 8 with activation
   // block mb and group q of its XCD, and loops over the vocab ranges
@@ -494,6 +494,32 @@ __global__ __launch_bounds__(TL::NTHR) void k_blm_head(LmArgs a, int n_p, int n_
                                                         a.K, a.M, mb * BM, wave, lane);
         block_product<SW8, NSTAGE, TL>(pl, 0, 2 * steps_w, lds, acc);
       }
+      // This lane's entries: vocab vl = (wn * WN + i) * 16 + 4 g + r of the
+      // block, rows (wm * WM + j) * 16 + r16. Their row scales (four
+      // consecutive entries per read) and the rows' mask words (two vocab
+      // tiles per 32-bit word) are read from LDS once per block.
+      static_assert(BN % 32 == 0 && (WN * 16) % 32 == 0, "a wave's vocab range covers whole mask words");
+      f32x4 scv[WN];
+#pragma unroll
+      for (int i = 0; i < WN; ++i)
+        scv[i] = WFP8 ? *(const f32x4 *)(s_scale + (wn * WN + i) * 16 + 4 * g) : f32x4{1.f, 1.f, 1.f, 1.f};
+      uint32_t mw[WM][WN / 2];
+#pragma unroll
+      for (int j = 0; j < WM; ++j)
+#pragma unroll
+        for (int w = 0; w < WN / 2; ++w) mw[j][w] = masked ? s_mask[sl[j] * MW + (wn * WN) / 2 + w] : ~0u;
+      if (a.logits) {
+        // the optional logits output (before the mask)
+#pragma unroll
+        for (int i = 0; i < WN; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int j = 0; j < WM; ++j) {
+              const int m = mb * BM + (wm * WM + j) * 16 + r16, v = vb * BN + (wn * WN + i) * 16 + 4 * g + r;
+              if (m < a.M) a.logits[(size_t)m * a.V + v] = A8 ? acc[i][j][r] * scv[i][r] * am[j] : acc[i][j][r] * scv[i][r];
+            }
+      }
       // Two passes per row: the block's logits (masked ones as -inf, kept in
       // acc) with this lane's largest and its first index, then one
       // exponential per logit against the row's merged maximum.
@@ -509,13 +535,11 @@ __global__ __launch_bounds__(TL::NTHR) void k_blm_head(LmArgs a, int n_p, int n_
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int vl = (wn * WN + i) * 16 + 4 * g + r, v = vb * BN + vl;
-          const float sc = WFP8 ? s_scale[vl] : 1.0f;
+          const int bit = (i & 1) * 16 + 4 * g + r;  // vl & 31
 #pragma unroll
           for (int j = 0; j < WM; ++j) {
-            const float x = A8 ? acc[i][j][r] * sc * am[j] : acc[i][j][r] * sc;
-            const int m = mb * BM + (wm * WM + j) * 16 + r16;
-            if (a.logits && m < a.M) a.logits[(size_t)m * a.V + v] = x;
-            const bool ok = !masked || ((s_mask[sl[j] * MW + (vl >> 5)] >> (vl & 31)) & 1u);
+            const float x = A8 ? acc[i][j][r] * scv[i][r] * am[j] : acc[i][j][r] * scv[i][r];
+            const bool ok = (mw[j][i >> 1] >> bit) & 1u;
             const float xo = ok ? x : -__builtin_huge_valf();
             acc[i][j][r] = xo;
             // values come in increasing v, so a strict > keeps the lowest id of a tie
