@@ -52,10 +52,14 @@ using TileG = Tiling<128, 128, 4, 2>;   // waves of 32 x 64
 using TileW = Tiling<256, 128, 4, 2>;   // waves of 64 x 64
 using TileL = Tiling<256, 256, 2, 4>;
 using TileLW = Tiling<256, 256, 2, 4>;  // the E4M3-weight LM head (weights widened in registers)
+using TileH = Tiling<192, 256, 2, 4>;   // waves of 96 x 64: layer GEMMs over many rows (fewer L2 bytes per product)
+using TileQ = Tiling<160, 128, 2, 2>;   // 4 waves of 80 x 64: N = 32 x 160 (the QKV product) in one round
 
 constexpr int NSTAGE_G = 4;            // LDS ring depth (stages in flight + the one multiplied): 128 KB
 constexpr int NSTAGE_W = 3;            // 144 KB
 constexpr int NSTAGE_LM = 2;
+constexpr int NSTAGE_H = 2;             // 112 KB
+constexpr int NSTAGE_Q = 4;             // 144 KB
 constexpr int NUM_CUS = 256;           // compute units of the MI355X
 constexpr int LM_TILES = 4;            // vocab blocks per LM-head workgroup
 
@@ -402,7 +406,10 @@ __global__ __launch_bounds__(TL::NTHR) void k_bgemm(GemmArgs ga, EpiArgs ea, int
   zero_acc(acc);
   const LoadPlan<false, TL> p = make_plan<false, TL>(ga.W, (size_t)ga.N * ga.K * 2, ga.K >> 7, nb * TL::NT, ga.A, ga.lda, ga.M,
                                       mb * BM, __builtin_amdgcn_readfirstlane(wave), lane);
-  block_product_pipelined<NSTAGE, TL>(p, kb, (ke - kb) >> 7, lds, acc);
+  // the 256-row blocks hold too many accumulators for a second register set
+  // of fragments: their reads are not overlapped with the matrix cores
+  if constexpr (TL::BM == 256) block_product<false, NSTAGE, TL>(p, kb, (ke - kb) >> 6, lds, acc);
+  else block_product_pipelined<NSTAGE, TL>(p, kb, (ke - kb) >> 7, lds, acc);
 #pragma unroll
   for (int i = 0; i < WN; ++i)
 #pragma unroll
@@ -622,10 +629,43 @@ bool wide_tiles(int epi, int N, int M) {
   return 31 * rounds(N, M, TileW::BN, TileW::BM, 1) < 20 * rounds(N, M, TileG::BN, TileG::BM, 1);
 }
 
+// The tiled GEMMs are bound by L2 -> LDS traffic: a round of workgroups over
+// the chip takes about (BN + BM) x K bytes per compute unit, so a launch
+// costs about rounds x (BN + BM). Each launch takes the eligible tiling of
+// least cost (ties to the earlier one): 128 x 128 and 256 x 128 for any
+// epilogue, 192 x 256 and 160 x 128 for the others when N is a multiple of
+// their BN (the gate/up product of 1024 rows: one round of 256 blocks of
+// 192 x 256 instead of three of 768; the QKV product, N = 5120: one round of
+// 256 blocks of 160 x 128 instead of 160 blocks of 256 x 128). The 256 x 128
+// tiling is taken over 128 x 128 only at less than 20 / 31 of its cost
+// (measured: the wider blocks do twice the work in about 1.55 times the time).
+enum TileId { T_G = 0, T_W = 1, T_H = 2, T_Q = 3 };
+
+int pick_tiles(int epi, int N, int M) {
+  auto cost = [&](int bn, int bm) { return (long)rounds(N, M, bn, bm, 1) * (bn + bm); };
+  int best = T_G;
+  long c_best = cost(TileG::BN, TileG::BM);
+  if (wide_tiles(epi, N, M)) {
+    best = T_W;
+    c_best = cost(TileW::BN, TileW::BM);
+  }
+  if (epi == EPI_PARTIAL) return best;
+  if (N % TileH::BN == 0 && cost(TileH::BN, TileH::BM) < c_best) {
+    best = T_H;
+    c_best = cost(TileH::BN, TileH::BM);
+  }
+  if (N % TileQ::BN == 0 && cost(TileQ::BN, TileQ::BM) < c_best) best = T_Q;
+  return best;
+}
+
 template <int EPI>
 hipError_t launch_pick(const GemmArgs &g, const EpiArgs &e, hipStream_t s) {
-  if (wide_tiles(EPI, g.N, g.M)) return launch_epi<EPI, TileW, NSTAGE_W>(g, e, s);
-  return launch_epi<EPI, TileG, NSTAGE_G>(g, e, s);
+  switch (pick_tiles(EPI, g.N, g.M)) {
+    case T_H: return launch_epi<EPI, TileH, NSTAGE_H>(g, e, s);
+    case T_Q: return launch_epi<EPI, TileQ, NSTAGE_Q>(g, e, s);
+    case T_W: return launch_epi<EPI, TileW, NSTAGE_W>(g, e, s);
+    default: return launch_epi<EPI, TileG, NSTAGE_G>(g, e, s);
+  }
 }
 
 }  // namespace
