@@ -539,113 +539,149 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(AttnArgs a) {
   }
 }
 
-// Reductions over all 64 lanes without LDS: quad permutes and row rotates
-// (DPP) inside each 16-lane row, then the row swaps across rows. Every lane
-// ends with the result; the order is fixed.
+// Reduction over the 16 lanes of each DPP row (lanes 16k .. 16k + 15): quad
+// permutes, then row rotates. Every lane of the row ends with the result; the
+// order is fixed.
 template <bool MAX>
-__device__ __forceinline__ float wave_reduce_dpp(float x) {
+__device__ __forceinline__ float row16_reduce(float x) {
   auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
-  auto dpp = [](float v, int ctrl) -> float {
-    switch (ctrl) {
-      case 0xB1: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
-      case 0x4E: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
-      case 0x124: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));
-      default: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
-    }
-  };
-  x = op(x, dpp(x, 0xB1));   // quad_perm [1, 0, 3, 2]
-  x = op(x, dpp(x, 0x4E));   // quad_perm [2, 3, 0, 1]
-  x = op(x, dpp(x, 0x124));  // row_ror 4
-  x = op(x, dpp(x, 0x128));  // row_ror 8
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return op(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  x = op(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false)));   // quad_perm [1, 0, 3, 2]
+  x = op(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false)));   // quad_perm [2, 3, 0, 1]
+  x = op(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false)));  // row_ror 4
+  x = op(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false)));  // row_ror 8
+  return x;
 }
 
-// Merge the splits of one query row per wave: lane s reads split s's (max,
-// sum); the weights exp2(m_s - M) l_s are read lane by lane and every lane
-// accumulates its dimensions (lane, lane + 64, ...; two adjacent ones, 2 lane
-// and 2 lane + 1, for head_dim 128) over the splits in order. The O parts of
-// the first PRE splits are loaded together with the (max, sum) pairs, before
-// the weights are known.
+// Merge the splits of four query rows per wave, one 16-lane row group per
+// row. Lane l of a group reads the (max, sum) of splits l, l + 16, ... and
+// holds dims DPL l .. DPL l + DPL - 1 (DPL = head_dim / 16) of every split's
+// output; the row's maximum M and the sum of the weights exp2(m_s - M) l_s
+// come from reductions inside the group, each split's weight from the lane
+// that holds it. The outputs of the first PRE splits are loaded together
+// with the (max, sum) pairs, before the weights are known; splits are added
+// in order.
 template <int D>
 __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a, int n_seq) {
-  constexpr int DPL = D >= 64 ? D / 64 : 1;  // dims per lane
+  constexpr int DPL = D / 16;                  // dims per lane
+  constexpr int NW = DPL >= 2 ? DPL / 2 : 1;   // 32-bit words of fp16 per lane and split
   constexpr int PRE = 16;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  constexpr int SL = ATTN_MAX_SPLITS / 16;     // (max, sum) slots per lane
+  static_assert(SL == 4, "the weight sum pairs four 16-split slots");
+  static_assert(D % 16 == 0, "head_dim a multiple of 16");
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, sl = lane & 15;
   const int R = a.rep * a.gamma;
-  const int row = blockIdx.x * 4 + wave;  // (s, g, q)
-  if (row >= n_seq * a.n_kv * R) return;
-  const int q = row % R, g = (row / R) % a.n_kv, s = row / (R * a.n_kv);
+  const int rows = n_seq * a.n_kv * R;
+  const int row = (blockIdx.x * 4 + wave) * 4 + (lane >> 4);  // (s, g, q)
+  const int rowc = min(row, rows - 1);
+  const int q = rowc % R, g = (rowc / R) % a.n_kv, s = rowc / (R * a.n_kv);
   const int nsplit = a.seq[s].nsplit;  // <= 64
-  if (nsplit == 1) return;             // written by the attention kernel
+  // a row with one split was written by the attention kernel
+  const int ns = (row < rows && nsplit > 1) ? nsplit : 0;
   const size_t base = (size_t)g * a.n_split + a.seq[s].split0;
-  const bool active = D >= 64 || lane < D;
-  // output of split c at this lane's dimensions, as fp16 bits (two dims in
-  // one dword for head_dim 128); widened only when accumulated, so the
-  // PRE loads below stay in flight together
-  auto o_bits = [&](int c, int i) -> uint32_t {
-    const uint16_t *op = a.o_part + ((base + c) * R + q) * D;
-    if constexpr (D == 128) return *(const uint32_t *)(op + 2 * lane);
-    else return (uint32_t)op[min(lane, D - 1) + 64 * i];  // lanes past head_dim write nothing
-  };
-  constexpr int NB = D == 128 ? 1 : DPL;  // dwords per lane and split
-  auto widen = [&](const uint32_t (&b)[NB], float (&v)[DPL]) {
-    if constexpr (D == 128) {
-      const f16x2_t x = __builtin_bit_cast(f16x2_t, b[0]);
-      v[0] = (float)x[0];
-      v[1] = (float)x[1];
+  auto o_bits = [&](int c, uint32_t (&b)[NW]) {
+    const uint16_t *op = a.o_part + ((base + c) * R + q) * D + DPL * sl;
+    if constexpr (DPL == 8) {
+      const uint4 v = *(const uint4 *)op;
+      b[0] = v.x, b[1] = v.y, b[2] = v.z, b[3] = v.w;
+    } else if constexpr (DPL == 4) {
+      const uint2 v = *(const uint2 *)op;
+      b[0] = v.x, b[1] = v.y;
+    } else if constexpr (DPL == 2) {
+      b[0] = *(const uint32_t *)op;
     } else {
-#pragma unroll
-      for (int i = 0; i < DPL; ++i) v[i] = (float)__builtin_bit_cast(_Float16, (uint16_t)b[i]);
+      b[0] = *op;
     }
   };
-  uint32_t pre[PRE][NB];
+  auto widen = [&](const uint32_t (&b)[NW], float (&v)[DPL]) {
+    if constexpr (DPL == 1) {
+      v[0] = (float)__builtin_bit_cast(_Float16, (uint16_t)b[0]);
+    } else {
 #pragma unroll
-  for (int c = 0; c < PRE; ++c)
+      for (int i = 0; i < NW; ++i) {
+        const f16x2_t x = __builtin_bit_cast(f16x2_t, b[i]);
+        v[2 * i] = (float)x[0];
+        v[2 * i + 1] = (float)x[1];
+      }
+    }
+  };
+  uint32_t pre[PRE][NW];
 #pragma unroll
-    for (int i = 0; i < NB; ++i) pre[c][i] = c < nsplit ? o_bits(c, i) : 0u;
-  float m = -__builtin_huge_valf(), l = 0.0f;
-  if (lane < nsplit) {
-    m = a.ml_part[((base + lane) * R + q) * 2];
-    l = a.ml_part[((base + lane) * R + q) * 2 + 1];
+  for (int c = 0; c < PRE; ++c) {
+#pragma unroll
+    for (int i = 0; i < NW; ++i) pre[c][i] = 0u;
+    if (c < ns) o_bits(c, pre[c]);
   }
-  const float M = wave_reduce_dpp<true>(m);
-  const float w = lane < nsplit ? fast_exp2(m - M) * l : 0.0f;  // weight of split `lane`'s normalised output
-  const float den = wave_reduce_dpp<false>(w);
-  const int hq = g * a.rep + q / a.gamma, j = q % a.gamma;
-  uint16_t *out = a.out + (size_t)(s * a.gamma + j) * a.out_ld + hq * D;
+  float mm[SL], ll[SL];
+#pragma unroll
+  for (int k = 0; k < SL; ++k) {
+    const int c = sl + 16 * k;
+    mm[k] = -__builtin_huge_valf();
+    ll[k] = 0.0f;
+    if (c < ns) {
+      mm[k] = a.ml_part[((base + c) * R + q) * 2];
+      ll[k] = a.ml_part[((base + c) * R + q) * 2 + 1];
+    }
+  }
+  float mx = mm[0];
+#pragma unroll
+  for (int k = 1; k < SL; ++k) mx = fmaxf(mx, mm[k]);
+  const float M = row16_reduce<true>(mx);
+  float w[SL], t[SL];
+#pragma unroll
+  for (int k = 0; k < SL; ++k) {
+    w[k] = sl + 16 * k < ns ? fast_exp2(mm[k] - M) * ll[k] : 0.0f;  // weight of split sl + 16 k
+    t[k] = row16_reduce<false>(w[k]);
+  }
+  // splits 0..15, 16..31, 32..47, 48..63 each by the same 16-lane tree, then
+  // the four sums pairwise
+  const float den = (t[0] + t[1]) + (t[2] + t[3]);
+  // the wave's largest split count (row groups may differ)
+  int ns_max = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) ns_max = max(ns_max, __builtin_amdgcn_readlane(ns, 16 * r));
   float acc[DPL];
 #pragma unroll
   for (int i = 0; i < DPL; ++i) acc[i] = 0.0f;
+  static_assert(PRE == 16, "the preloaded splits are the first weight slot");
 #pragma unroll
   for (int c = 0; c < PRE; ++c) {
-    if (c < nsplit) {
-      const float wc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), c));
-      float v[DPL];
-      widen(pre[c], v);
+    const float wc = __shfl(w[0], (lane & 48) | c, WAVE);
+    float v[DPL];
+    widen(pre[c], v);
+    if (c < ns)
 #pragma unroll
       for (int i = 0; i < DPL; ++i) acc[i] += wc * v[i];
-    }
   }
-#pragma unroll 16
-  for (int c = PRE; c < nsplit; ++c) {
-    const float wc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), c));
-    uint32_t b[NB];
+  for (int c = PRE; c < ns_max; ++c) {
+    const int k = c >> 4;  // wave-uniform
+    const float wk = k == 1 ? w[1] : k == 2 ? w[2] : w[3];
+    const float wc = __shfl(wk, (lane & 48) | (c & 15), WAVE);
+    uint32_t b[NW];
+    if (c < ns) {
+      o_bits(c, b);
+    } else {
 #pragma unroll
-    for (int i = 0; i < NB; ++i) b[i] = o_bits(c, i);
+      for (int i = 0; i < NW; ++i) b[i] = 0u;
+    }
     float v[DPL];
     widen(b, v);
+    if (c < ns)
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) acc[i] += wc * v[i];
+      for (int i = 0; i < DPL; ++i) acc[i] += wc * v[i];
   }
-  if constexpr (D == 128) {
-    *(uint32_t *)(out + 2 * lane) = pack_bf16x2(acc[0] / den, acc[1] / den);
-  } else {
+  if (ns > 0) {
+    const int hq = g * a.rep + q / a.gamma, j = q % a.gamma;
+    uint16_t *out = a.out + (size_t)(s * a.gamma + j) * a.out_ld + hq * D + DPL * sl;
+    if constexpr (DPL == 1) {
+      out[0] = f32_to_bf16(acc[0] / den);
+    } else {
+      uint32_t o[NW];
 #pragma unroll
-    for (int i = 0; i < DPL; ++i)
-      if (active) out[lane + 64 * i] = f32_to_bf16(acc[i] / den);
+      for (int i = 0; i < NW; ++i) o[i] = pack_bf16x2(acc[2 * i] / den, acc[2 * i + 1] / den);
+      if constexpr (DPL == 8) *(uint4 *)out = uint4{o[0], o[1], o[2], o[3]};
+      else if constexpr (DPL == 4) *(uint2 *)out = uint2{o[0], o[1]};
+      else *(uint32_t *)out = o[0];
+    }
   }
 }
 
@@ -655,7 +691,7 @@ hipError_t launch_d(const AttnArgs &a, int n_seq, bool merge, hipStream_t s) {
   hipLaunchKernelGGL((k_attn<D, FP8>), grid, dim3(NTHR), 0, s, a);
   if (merge) {
     const int rows = n_seq * a.n_kv * a.rep * a.gamma;
-    hipLaunchKernelGGL(k_attn_combine<D>, dim3((rows + 3) / 4), dim3(256), 0, s, a, n_seq);
+    hipLaunchKernelGGL(k_attn_combine<D>, dim3((rows + 15) / 16), dim3(256), 0, s, a, n_seq);
   }
   return hipGetLastError();
 }
