@@ -210,6 +210,10 @@ int dflash_precompute_ctx_kv(dflash_head *head, dflash_state *const *states, int
  * position .. position + gamma - 1 attends to the state's ctx rows
  * [max(0, ctx_len - ctx_window), ctx_len) and to itself; after the final norm
  * and LM head each row takes its argmax (ties to the lowest id).
+ * Numerics: the dense products take bf16 operands with f32 accumulation;
+ * attention runs in fp16 (Q, K, V and the softmax weights, f32 accumulation),
+ * so the block rows' Q/K/V and the cached K/V must lie within fp16's range
+ * (|x| < 65504; larger values become infinite and poison the row).
  *   last_token < vocab; 0 <= position < 2^31 - gamma; 1 <= num_drafts <= gamma - 1.
  *   bitmask: optional device int32 [ceil(V/32)]; bit v&31 of word v>>5 set
  *            means token v is allowed ([DraftProposer] propose, grammar_bitmask).
