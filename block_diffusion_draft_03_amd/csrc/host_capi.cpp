@@ -86,15 +86,17 @@ int32_t dfh_attn_tiles(int32_t ctx_len, int32_t window) { return attn_tiles(ctx_
 
 // the propose's split plan: *tps and *n_split on success
 int dfh_attn_plan(int32_t n, const int32_t *tiles, int32_t n_kv, int32_t max_tps, int64_t slot_cap, int32_t target_wgs,
-                  int32_t *tps, int32_t *n_split, int32_t *nsplit_out) {
+                  int32_t *tps, int32_t *n_split, int32_t *nsplit_out, int32_t *split0_out) {
   g_err.clear();
   AttnPlan p;
   const int rc = attn_plan(n, tiles, n_kv, max_tps, slot_cap, target_wgs, &p, &g_err);
   if (rc == DFLASH_OK) {
     *tps = p.tps;
     *n_split = p.n_split;
-    if (nsplit_out)
-      for (int32_t i = 0; i < n; ++i) nsplit_out[i] = p.nsplit[i];
+    for (int32_t i = 0; i < n; ++i) {
+      if (nsplit_out) nsplit_out[i] = p.nsplit[i];
+      if (split0_out) split0_out[i] = p.split0[i];
+    }
   }
   return rc;
 }

@@ -274,11 +274,24 @@ int attn_plan(int32_t n, const int32_t *tiles, int32_t n_kv, int32_t max_tps, in
     return fail(err, DFLASH_E_INVALID,
                 "context window too long for the attention splits (" + std::to_string(max_T) + " tiles of 32 keys, " +
                     std::to_string(n) + " sequences)");
-  int32_t f = 0;
+  // Each sequence's splits are one run of split numbers; the runs go out
+  // longest split first (the kernel divides a sequence's T + 2 units evenly
+  // among its splits). Workgroups start in split order, so when a launch takes
+  // more than one round of workgroups the last to start are the shortest
+  // (longest processing time first); ties keep the sequence order.
+  int32_t order[DFLASH_MAX_BATCH];
   for (int32_t i = 0; i < n; ++i) {
-    plan->split0[i] = f;
+    order[i] = i;
     plan->nsplit[i] = (int32_t)splits_of(tiles[i], tps);
-    f += plan->nsplit[i];
+  }
+  auto units = [&](int32_t i) { return (int64_t)tiles[i] + 2; };
+  std::stable_sort(order, order + n, [&](int32_t x, int32_t y) {
+    return units(x) * plan->nsplit[y] > units(y) * plan->nsplit[x];
+  });
+  int32_t f = 0;
+  for (int32_t k = 0; k < n; ++k) {
+    plan->split0[order[k]] = f;
+    f += plan->nsplit[order[k]];
   }
   plan->tps = tps;
   plan->n_split = f;

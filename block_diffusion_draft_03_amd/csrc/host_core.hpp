@@ -127,8 +127,10 @@ struct AttnPlan {
 
 // Plan n sequences (tiles[i] ctx tiles each) over n_kv kv heads, with at most
 // max_tps tiles per split, slot_cap partial slots per kv head and about
-// target_wgs workgroups. Fails with DFLASH_E_INVALID, touching nothing, when
-// no split size fits.
+// target_wgs workgroups. Sequence i owns splits [split0[i], split0[i] +
+// nsplit[i]); the runs cover [0, n_split), sequences with longer splits
+// first. Fails with DFLASH_E_INVALID, touching nothing, when no split size
+// fits.
 int attn_plan(int32_t n, const int32_t *tiles, int32_t n_kv, int32_t max_tps, int64_t slot_cap, int32_t target_wgs,
               AttnPlan *plan, std::string *err);
 

@@ -2,7 +2,9 @@
 // the block itself, for gfx950.
 //
 // One workgroup (NWAVE waves) per (split, kv head); a sequence has as many splits
-// as its own context needs, so short sequences take no idle workgroups. The rep = n_q / n_kv
+// as its own context needs, so short sequences take no idle workgroups.
+// Workgroups start split by split in the planner's numbering, which puts the
+// sequences with the longest splits first. The rep = n_q / n_kv
 // query heads of the kv head times the gamma block rows form up to 128 query
 // rows, 16 QT per wave. Keys come in tiles of 32: ctx tiles are aligned to two
 // 16-row KV blocks (positions outside [win_start, ctx_len) are masked), and
@@ -368,7 +370,7 @@ __global__ __launch_bounds__(NTHR, 2) void k_attn(AttnArgs a) {
   __shared__ uint4 blkt[GB::BF * 64];
   __shared__ int32_t s_bt[2 * (MAX_TPS + 1)];
 
-  const int flat = blockIdx.x, g = blockIdx.y;
+  const int flat = blockIdx.y, g = blockIdx.x;
   const int s = a.split_seq[flat];
   const AttnSeq sq = a.seq[s];
   const int c = flat - sq.split0;
@@ -687,7 +689,8 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a, int n_seq) {
 
 template <int D, bool FP8>
 hipError_t launch_d(const AttnArgs &a, int n_seq, bool merge, hipStream_t s) {
-  dim3 grid(a.n_split, a.n_kv);
+  // kv heads fastest: workgroups start split by split, in the plan's order
+  dim3 grid(a.n_kv, a.n_split);
   hipLaunchKernelGGL((k_attn<D, FP8>), grid, dim3(NTHR), 0, s, a);
   if (merge) {
     const int rows = n_seq * a.n_kv * a.rep * a.gamma;
@@ -704,18 +707,20 @@ hipError_t launch_attention(const AttnArgs &a, int n_seq, hipStream_t s) {
   if (a.tps < 1 || a.tps > MAX_TPS || a.n_split < n_seq || a.n_split > ATTN_MAX_FLAT || a.gamma > 64 ||
       a.rep * a.gamma > 128 || n_seq < 1 || n_seq > DFLASH_MAX_BATCH)
     return hipErrorInvalidValue;
-  // the splits of the sequences are consecutive runs that cover [0, n_split)
+  // each sequence's splits are one run [split0, split0 + nsplit) mapped back
+  // to it by split_seq; runs of distinct sequences cannot overlap, so runs
+  // whose sizes add up to n_split cover [0, n_split) exactly
   bool merge = false;
-  int next = 0;
+  int total = 0;
   for (int i = 0; i < n_seq; ++i) {
     const AttnSeq &q = a.seq[i];
-    if (q.split0 != next || q.nsplit < 1 || q.nsplit > 64) return hipErrorInvalidValue;
+    if (q.nsplit < 1 || q.nsplit > 64 || q.split0 < 0 || q.split0 + q.nsplit > a.n_split) return hipErrorInvalidValue;
     for (int c = 0; c < q.nsplit; ++c)
-      if (a.split_seq[next + c] != i) return hipErrorInvalidValue;
-    next += q.nsplit;
+      if (a.split_seq[q.split0 + c] != i) return hipErrorInvalidValue;
+    total += q.nsplit;
     merge = merge || q.nsplit > 1;
   }
-  if (next != a.n_split) return hipErrorInvalidValue;
+  if (total != a.n_split) return hipErrorInvalidValue;
   if (a.kv_fp8) {
     switch (a.head_dim) {
       case 64: return launch_d<64, true>(a, n_seq, merge, s);

@@ -45,7 +45,7 @@ def host():
     lib.dfh_reserve_rows.argtypes = [vp, C.c_int32, vp, vp, vp]
     lib.dfh_attn_tiles.argtypes = [C.c_int32, C.c_int32]
     lib.dfh_attn_plan.argtypes = [C.c_int32, vp, C.c_int32, C.c_int32, C.c_int64, C.c_int32, C.POINTER(C.c_int32),
-                                  C.POINTER(C.c_int32), vp]
+                                  C.POINTER(C.c_int32), vp, vp]
     lib.dfh_build_check.argtypes = [vp, C.c_int32]
     lib.dflash_yarn_inv_freq.argtypes = [C.c_int32, C.c_float, C.c_float, C.c_float, C.c_float, C.c_int32, vp]
     return lib
@@ -307,12 +307,15 @@ def test_state_rows_capped_at_max_seq_len(host):
     host.dfh_pool_delete(pool)
 
 
-def _plan(host, tiles, n_kv=4, max_tps=64, cap=1 << 20, target=512):
+def _plan(host, tiles, n_kv=4, max_tps=64, cap=1 << 20, target=512, split0=None):
     t = np.ascontiguousarray(tiles, dtype=np.int32)
     tps, n_split = C.c_int32(), C.c_int32()
     per = np.zeros(len(t), np.int32)
+    s0 = np.full(len(t), -1, np.int32)
     rc = host.dfh_attn_plan(len(t), t.ctypes.data_as(C.c_void_p), n_kv, max_tps, cap, target, C.byref(tps),
-                            C.byref(n_split), per.ctypes.data_as(C.c_void_p))
+                            C.byref(n_split), per.ctypes.data_as(C.c_void_p), s0.ctypes.data_as(C.c_void_p))
+    if split0 is not None:
+        split0[:] = s0.tolist()
     return rc, tps.value, n_split.value, per.tolist()
 
 
@@ -341,6 +344,28 @@ def test_attention_split_plan(host):
     assert rc == E_INVALID and "attention splits" in host.dfh_last_error().decode()
     # more than 64 splits of 64 tiles for one sequence
     assert _plan(host, [64 * 64])[0] == E_INVALID
+
+
+def test_attention_split_order(host):
+    """Each sequence's splits are one run of split numbers; the runs cover
+    [0, n_split) exactly, go out in non-increasing order of split length (the
+    kernel divides T + 2 units among a sequence's splits), and keep the
+    sequence order between equal lengths."""
+    rng = np.random.default_rng(5)
+    for tiles in ([32, 8, 120, 0, 64, 8, 127, 31], list(rng.integers(0, 128, 64)), [16] * 10):
+        s0 = [0] * len(tiles)
+        rc, tps, n_split, per = _plan(host, tiles, target=768, split0=s0)
+        assert rc == OK
+        runs = sorted((s0[i], per[i], i) for i in range(len(tiles)))
+        pos = 0
+        for start, cnt, _ in runs:
+            assert start == pos
+            pos += cnt
+        assert pos == n_split
+        # split length (T + 2) / nsplit, in dispatch order
+        lens = [((tiles[i] + 2) / per[i], i) for _, _, i in runs]
+        for (a, ia), (b, ib) in zip(lens, lens[1:]):
+            assert a > b or (a == b and ia < ib)
 
 
 def test_build_rejects_configs_beyond_the_attention_splits(host):
