@@ -16,7 +16,7 @@ It is written from three documentation pages, cited by title and section:
 The pages describe the head's fields and API but print no layer equations, so
 the layer internals (RMSNorm, Q/K/V projections, rotate-half RoPE, GQA
 attention without a mask, o_proj, SwiGLU MLP) follow the plain textbook forms;
-every such reading is listed in the design doc and in the docstrings below.
+each such reading is stated in the docstring of the function that takes it.
 
 Modules:
 
