@@ -598,7 +598,7 @@ int propose_check(dflash_head *H, dflash_state *const *states, int n, const uint
   for (int i = 0; i < n; ++i) tiles[i] = attn_tiles(states[i]->rows.ctx_len, g.W);
   std::string err;
   const int rc = attn_plan(n, tiles, g.n_kv, attn_max_tiles_per_split(), attn_slots / g.n_kv,
-                           g.kv_fp8 ? ATTN_TARGET_WGS_E4M3 : ATTN_TARGET_WGS, plan, &err);
+                           ATTN_TARGET_WGS, plan, &err);
   if (rc != DFLASH_OK) return set_err(rc, err);
   return DFLASH_OK;
 }

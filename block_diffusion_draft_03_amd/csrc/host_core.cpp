@@ -301,7 +301,7 @@ int attn_plan(int32_t n, const int32_t *tiles, int32_t n_kv, int32_t max_tps, in
 int64_t attn_slots(const Geo &g, int32_t max_seq_len, int32_t max_tps) {
   const int64_t worst = attn_tiles_worst(g.W, max_seq_len);
   const int64_t per_seq = std::min<int64_t>(ATTN_MAX_SPLITS, (worst + max_tps) / max_tps);
-  return std::max<int64_t>({(int64_t)std::max(ATTN_TARGET_WGS, ATTN_TARGET_WGS_E4M3) * 2, (int64_t)g.max_batch * g.n_kv * per_seq,
+  return std::max<int64_t>({(int64_t)ATTN_TARGET_WGS * 2, (int64_t)g.max_batch * g.n_kv * per_seq,
                             (int64_t)g.n_kv * ATTN_MAX_SPLITS});
 }
 
@@ -310,7 +310,7 @@ int check_attn_capacity(const Geo &g, int32_t max_seq_len, int32_t max_tps, std:
   AttnPlan plan;
   std::string e;
   if (attn_plan(g.max_batch, tiles.data(), g.n_kv, max_tps, attn_slots(g, max_seq_len, max_tps) / g.n_kv,
-                g.kv_fp8 ? ATTN_TARGET_WGS_E4M3 : ATTN_TARGET_WGS, &plan, &e) !=
+                ATTN_TARGET_WGS, &plan, &e) !=
       DFLASH_OK)
     return fail(err, DFLASH_E_INVALID,
                 "config: max_batch sequences of min(ctx_window, max_seq_len) rows exceed the attention splits: " + e);

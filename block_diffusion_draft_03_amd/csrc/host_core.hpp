@@ -97,19 +97,17 @@ int seq_install(SeqRows *s, BlockPool *pool, const int32_t *blocks, int32_t n, i
 // The block's attention over a sequence's context runs in splits of up to
 // tps ctx tiles of 32 keys (from the window start aligned down to a KV
 // block); the sequence's last split also takes the block's own keys, which
-// count as one more tile. A launch aims for a target number of workgroups
-// over all sequences and kv heads: ATTN_TARGET_WGS (two per compute unit)
-// with a bf16 cache, ATTN_TARGET_WGS_E4M3 with an E4M3 cache, whose tiles
-// are cheaper to load, so that shorter splits (more of them, the last ones
-// starting as the first finish) balance better (measured on 64 sequences of
-// 256 to 4096 ctx rows: 82 us against 91 us per layer; with a bf16 cache the
-// larger target is slower). It prefers at most
+// count as one more tile. A launch aims for at most ATTN_TARGET_WGS
+// workgroups over all sequences and kv heads: two per compute unit, one
+// round in which every workgroup is resident (measured on batches of 32 and
+// 64 sequences of 256 or 512 to 4096 ctx rows with bf16 and E4M3 caches:
+// targets of 384, 640 and 768 were slower or, with an E4M3 cache, 0.3%
+// slower). It prefers at most
 // ATTN_PREF_SPLITS splits per sequence, and cannot exceed ATTN_MAX_SPLITS
 // splits per sequence (one wave merges a row's splits) or ATTN_MAX_FLAT
 // splits in all (the split-to-sequence map travels in the launch arguments).
 constexpr int ATTN_MAX_FLAT = 1024;
 constexpr int ATTN_TARGET_WGS = 512;
-constexpr int ATTN_TARGET_WGS_E4M3 = 768;
 constexpr int ATTN_MAX_SPLITS = 64;
 constexpr int ATTN_PREF_SPLITS = 16;
 

@@ -333,7 +333,7 @@ def test_attention_split_plan(host):
     # a batch: splits grow until the launch fits two workgroups per CU
     rc, tps, n_split, per = _plan(host, [32] * 32)
     assert rc == OK and n_split * 4 <= 512 and per == [(32 + tps) // tps] * 32
-    # the E4M3 cache's larger target: shorter splits, at most 768 workgroups
+    # a larger target: shorter splits, at most 768 workgroups
     rc8, tps8, n_split8, _ = _plan(host, [32] * 32, target=768)
     assert rc8 == OK and tps8 < tps and 512 < n_split8 * 4 <= 768
     assert _plan(host, [32], target=0)[0] == E_INVALID
